@@ -1,0 +1,320 @@
+/*
+ * oracle.c -- plain CPU reference for the Q4_K / Q6_K x int8 prefill GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test-suite, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source, header, table or helper with the
+ * GPU library.
+ *
+ * What it computes (each step cites the page it follows):
+ *
+ *  - The method: a batched prefill matmul y[M x N] = x[M x K] . W[N x K]^T in
+ *    which the weights stay in their GGUF Q4_K / Q6_K super-blocks, are decoded
+ *    to small integers in place, the activation rows are quantised to int8, the
+ *    contraction is an int8 x int8 -> int32 dot product and the block scales are
+ *    applied afterwards.  Pages: sparkinfer PR #464 "fused Q4K/Q6K->int8 dequant
+ *    + token-parallel GDN conv + lane-parallel fallback attention", section
+ *    "Summary" (decode super-blocks in registers, int8 tensor-core GEMM);
+ *    aprender issue #5475 "Qwen3.5 on CPU prefills one token at a time",
+ *    section "Ask" (the row-batched fused Q4_K x int8-activation kernel, as
+ *    opposed to dequantising a tile to F32); aprender issue #5305 "Qwen3.5
+ *    speed: prefill and decode parity with llama.cpp", sub-ticket #4313 (int8
+ *    MMQ prefill matmul plus the LM head on the last token only).
+ *  - Activation encoding: per 32 consecutive values of a row, int8 codes with
+ *    one fp32 scale and the int32 sum of the codes, the q8_1-style block the
+ *    CRUX parity issue #4220 ranks as technique 5 (quantised-activation GEMV,
+ *    "q8_1 + dp4a").  The pages give no formula; the plainest symmetric reading
+ *    is taken: scale d = amax/127 in fp32, codes rint(x * (1/d)) with ties to
+ *    even, clamped to [-127, 127], code 0 wherever x = 0.
+ *  - Block layout: the public GGUF K-quant layout (the pages name Q4_K / Q6_K
+ *    but do not print their bytes):
+ *      Q4_K, 144 B / 256 values: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block
+ *        scales sc[8] and mins m[8], 128 bytes of 4-bit codes q in [0, 15];
+ *        w = d*sc[j]*q - dmin*m[j] for sub-block j = v/32.
+ *      Q6_K, 210 B / 256 values: ql[128] low nibbles, qh[64] high bit pairs,
+ *        16 int8 sub-block scales (16 values each), fp16 d;
+ *        w = d*sc[v/16]*(q6 - 32), q6 in [0, 63].
+ *
+ * The combine is done in fp64 in ascending block order.  Integer partials are
+ * exact int32.  All floating point here is IEEE binary32/binary64 with no
+ * contraction (built with -ffp-contract=off, no fast-math), so the fp32 steps
+ * of the activation quantiser are the correctly rounded ones.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_Q4_K = 0, ORACLE_Q6_K = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* IEEE binary16 bit pattern -> exact double (normals, subnormals, inf, nan). */
+double oracle_half_to_double(uint16_t h) {
+    int sign = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);                 /* 0 or subnormal: f * 2^-24 */
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(f | 0x400), e - 25);           /* (1024 + f) * 2^(e-25) */
+    return sign ? -v : v;
+}
+
+static inline uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ---------------------------------------------------------------- Q4_K decode */
+
+/* Decode one Q4_K block into codes q[256] (0..15), scales sc[8], mins m[8],
+ * and the two binary16 super-scales as doubles. */
+static void decode_q4k_block(const uint8_t *blk, uint8_t *q, uint8_t *sc, uint8_t *m,
+                             double *d, double *dmin) {
+    *d = oracle_half_to_double(rd16(blk));
+    *dmin = oracle_half_to_double(rd16(blk + 2));
+    const uint8_t *s = blk + 4;
+    for (int j = 0; j < 8; j++) {
+        if (j < 4) {
+            sc[j] = s[j] & 63;
+            m[j] = s[j + 4] & 63;
+        } else {
+            /* low 4 bits from byte j+4 (scale: low nibble, min: high nibble),
+             * high 2 bits from the top of byte j-4 (scale) or byte j (min) */
+            sc[j] = (uint8_t)((s[j + 4] & 0x0F) | ((s[j - 4] >> 6) << 4));
+            m[j] = (uint8_t)((s[j + 4] >> 4) | ((s[j] >> 6) << 4));
+        }
+    }
+    const uint8_t *qs = blk + 16;
+    for (int v = 0; v < 256; v++) {
+        uint8_t byte = qs[32 * (v / 64) + (v % 32)];
+        q[v] = (v % 64) < 32 ? (byte & 0x0F) : (byte >> 4);
+    }
+}
+
+/* Decode W [N x K] Q4_K: q [N*K], sc, m [N*K/32], d, dmin [N*K/256]. */
+void oracle_decode_q4k(const uint8_t *W, int64_t N, int64_t K, uint8_t *q, uint8_t *sc,
+                       uint8_t *m, double *d, double *dmin) {
+    int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N * nb; i++)
+        decode_q4k_block(W + i * 144, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);
+}
+
+/* ---------------------------------------------------------------- Q6_K decode */
+
+/* Decode one Q6_K block into 6-bit codes q6[256] (0..63), scales sc[16], d. */
+static void decode_q6k_block(const uint8_t *blk, uint8_t *q6, int8_t *sc, double *d) {
+    const uint8_t *ql = blk, *qh = blk + 128;
+    for (int v = 0; v < 256; v++) {
+        int half = v / 128, r = v % 128, quarter = r / 32, l = r % 32;
+        uint8_t lowbyte = ql[64 * half + 32 * (quarter % 2) + l];
+        int lo = quarter < 2 ? (lowbyte & 0x0F) : (lowbyte >> 4);
+        int hi = (qh[32 * half + l] >> (2 * quarter)) & 3;
+        q6[v] = (uint8_t)(lo | (hi << 4));
+    }
+    for (int s = 0; s < 16; s++) sc[s] = (int8_t)blk[192 + s];
+    *d = oracle_half_to_double(rd16(blk + 208));
+}
+
+/* Decode W [N x K] Q6_K: q6 [N*K], sc [N*K/16], d [N*K/256]. */
+void oracle_decode_q6k(const uint8_t *W, int64_t N, int64_t K, uint8_t *q6, int8_t *sc,
+                       double *d) {
+    int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N * nb; i++)
+        decode_q6k_block(W + i * 210, q6 + i * 256, sc + i * 16, d + i);
+}
+
+/* Dequantised weights w [N x K] in fp64 (brute-force reference values). */
+void oracle_dequant(int fmt, const uint8_t *W, int64_t N, int64_t K, double *w) {
+    int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N * nb; i++) {
+        uint8_t q[256];
+        double *o = w + i * 256;
+        if (fmt == ORACLE_Q4_K) {
+            uint8_t sc[8], m[8];
+            double d, dmin;
+            decode_q4k_block(W + i * 144, q, sc, m, &d, &dmin);
+            for (int v = 0; v < 256; v++) o[v] = d * sc[v / 32] * q[v] - dmin * m[v / 32];
+        } else {
+            int8_t sc[16];
+            double d;
+            decode_q6k_block(W + i * 210, q, sc, &d);
+            for (int v = 0; v < 256; v++) o[v] = d * sc[v / 16] * ((int)q[v] - 32);
+        }
+    }
+}
+
+/* ------------------------------------------------------- activation quantiser */
+
+static inline float load_x(const void *x, int x_dtype, int64_t i) {
+    if (x_dtype == ORACLE_F32) return ((const float *)x)[i];
+    uint32_t u = (uint32_t)((const uint16_t *)x)[i] << 16; /* bf16 -> f32 is exact */
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* One 32-value block: amax, d = amax/127 (fp32 division), id = 1/d (fp32
+ * division), q = rint(x*id) (one fp32 multiply, ties to even) clamped to
+ * [-127, 127]; q = 0 where x = 0; S = sum q.  All-zero block: d = 0, q = 0. */
+static void quantize_block(const float *xf, int8_t *q, float *d_out, int32_t *S_out) {
+    float amax = 0.0f;
+    for (int t = 0; t < 32; t++) {
+        float a = fabsf(xf[t]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        memset(q, 0, 32);
+        *d_out = 0.0f;
+        *S_out = 0;
+        return;
+    }
+    float d = amax / 127.0f;
+    float id = 1.0f / d;
+    int32_t S = 0;
+    for (int t = 0; t < 32; t++) {
+        int qi = 0;
+        if (xf[t] != 0.0f) {
+            float v = xf[t] * id;
+            float r = rintf(v);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            qi = (int)r;
+        }
+        q[t] = (int8_t)qi;
+        S += qi;
+    }
+    *d_out = d;
+    *S_out = S;
+}
+
+/* x [M x K] (fp32 or bf16 bits) -> q int8 [M x K], d fp32 [M x K/32], S int32 [M x K/32]. */
+void oracle_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *q,
+                         float *d, int32_t *S) {
+    int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++) {
+        float xf[32];
+        for (int64_t b = 0; b < nb; b++) {
+            for (int t = 0; t < 32; t++) xf[t] = load_x(x, x_dtype, r * K + 32 * b + t);
+            quantize_block(xf, q + r * K + 32 * b, d + r * nb + b, S + r * nb + b);
+        }
+    }
+}
+
+/* ----------------------------------------------------- integer block partials */
+
+/* Q4_K: out[m][n][b] = sum_{t<32} q_w[n][32b+t] * q_x[m][32b+t]      (K/32 per pair)
+ * Q6_K: out[m][n][s] = sum_{t<16} (q6[n][16s+t] - 32) * q_x[m][16s+t] (K/16 per pair) */
+void oracle_block_partials(int fmt, const uint8_t *W, const int8_t *qx, int64_t M, int64_t N,
+                           int64_t K, int32_t *out) {
+    uint8_t *qw = (uint8_t *)malloc((size_t)(N * K));
+    int64_t nb = K / 256;
+    if (fmt == ORACLE_Q4_K) {
+        uint8_t *sc = malloc((size_t)(N * K / 32)), *m = malloc((size_t)(N * K / 32));
+        double *d = malloc(sizeof(double) * (size_t)(N * nb)), *dm = malloc(sizeof(double) * (size_t)(N * nb));
+        oracle_decode_q4k(W, N, K, qw, sc, m, d, dm);
+        free(sc); free(m); free(d); free(dm);
+    } else {
+        int8_t *sc = malloc((size_t)(N * K / 16));
+        double *d = malloc(sizeof(double) * (size_t)(N * nb));
+        oracle_decode_q6k(W, N, K, qw, sc, d);
+        free(sc); free(d);
+    }
+    int L = fmt == ORACLE_Q4_K ? 32 : 16, off = fmt == ORACLE_Q4_K ? 0 : 32;
+    int64_t nblk = K / L;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t mi = 0; mi < M; mi++)
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t b = 0; b < nblk; b++) {
+                int32_t acc = 0;
+                for (int t = 0; t < L; t++)
+                    acc += ((int32_t)qw[n * K + b * L + t] - off) * (int32_t)qx[mi * K + b * L + t];
+                out[(mi * N + n) * nblk + b] = acc;
+            }
+    free(qw);
+}
+
+/* ------------------------------------------------------------------- the GEMM */
+
+/* y[i][j] for the selected rows m = rows[i] of x and columns n = cols[j] of W
+ * (rows == NULL: all M rows; cols == NULL: all N columns).  y is fp64
+ * [nrows x ncols].  Steps: quantise the activation rows, decode the weight
+ * rows, form every per-block int32 dot product, then combine in fp64 in
+ * ascending block order:
+ *   Q4_K: y = sum_b dx[b] * ( d*sc[b]*I[b] - dmin*m[b]*S[b] )
+ *   Q6_K: y = sum_b dx[b] * d * ( sc[2b]*I16[2b] + sc[2b+1]*I16[2b+1] )
+ * where b runs over 32-value activation blocks and d, dmin belong to the
+ * super-block holding b.  Returns 0, or -1 on allocation failure. */
+int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M, int64_t N,
+                int64_t K, const int64_t *rows, int64_t nrows, const int64_t *cols, int64_t ncols,
+                double *y) {
+    if (!rows) nrows = M;
+    if (!cols) ncols = N;
+    int64_t nb32 = K / 32, nsb = K / 256;
+    int64_t bbytes = fmt == ORACLE_Q4_K ? 144 : 210;
+
+    int8_t *qx = malloc((size_t)(nrows * K));
+    float *dx = malloc(sizeof(float) * (size_t)(nrows * nb32));
+    int32_t *Sx = malloc(sizeof(int32_t) * (size_t)(nrows * nb32));
+    uint8_t *qw = malloc((size_t)(ncols * K));
+    uint8_t *scw = malloc((size_t)(ncols * K / 16));   /* Q4_K uses K/32 of it */
+    uint8_t *mw = malloc((size_t)(ncols * nb32));
+    double *dw = malloc(sizeof(double) * (size_t)(ncols * nsb));
+    double *dmw = malloc(sizeof(double) * (size_t)(ncols * nsb));
+    if (!qx || !dx || !Sx || !qw || !scw || !mw || !dw || !dmw) {
+        free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw);
+        return -1;
+    }
+
+    /* 1. quantise the selected activation rows */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; i++) {
+        int64_t r = rows ? rows[i] : i;
+        float xf[32];
+        for (int64_t b = 0; b < nb32; b++) {
+            for (int t = 0; t < 32; t++) xf[t] = load_x(x, x_dtype, r * K + 32 * b + t);
+            quantize_block(xf, qx + i * K + 32 * b, dx + i * nb32 + b, Sx + i * nb32 + b);
+        }
+    }
+    /* 2. decode the selected weight rows */
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t sb = 0; sb < nsb; sb++) {
+            const uint8_t *blk = W + (n * nsb + sb) * bbytes;
+            if (fmt == ORACLE_Q4_K)
+                decode_q4k_block(blk, qw + j * K + 256 * sb, scw + j * nb32 + 8 * sb,
+                                 mw + j * nb32 + 8 * sb, dw + j * nsb + sb, dmw + j * nsb + sb);
+            else
+                decode_q6k_block(blk, qw + j * K + 256 * sb, (int8_t *)scw + j * (K / 16) + 16 * sb,
+                                 dw + j * nsb + sb);
+        }
+    }
+    /* 3. per-block int32 dots, fp64 combine in ascending b */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < nrows; i++)
+        for (int64_t j = 0; j < ncols; j++) {
+            const int8_t *xq = qx + i * K;
+            const uint8_t *wq = qw + j * K;
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb32; b++) {
+                double d = dw[j * nsb + b / 8];
+                double dxb = (double)dx[i * nb32 + b];
+                if (fmt == ORACLE_Q4_K) {
+                    int32_t I = 0;
+                    for (int t = 0; t < 32; t++) I += (int32_t)wq[32 * b + t] * (int32_t)xq[32 * b + t];
+                    double sc = scw[j * nb32 + b], m = mw[j * nb32 + b];
+                    double dmin = dmw[j * nsb + b / 8];
+                    acc += dxb * (d * sc * (double)I - dmin * m * (double)Sx[i * nb32 + b]);
+                } else {
+                    int32_t Ia = 0, Ib = 0;
+                    for (int t = 0; t < 16; t++) Ia += ((int32_t)wq[32 * b + t] - 32) * (int32_t)xq[32 * b + t];
+                    for (int t = 16; t < 32; t++) Ib += ((int32_t)wq[32 * b + t] - 32) * (int32_t)xq[32 * b + t];
+                    const int8_t *sc = (const int8_t *)scw + j * (K / 16);
+                    acc += dxb * d * ((double)sc[2 * b] * (double)Ia + (double)sc[2 * b + 1] * (double)Ib);
+                }
+            }
+            y[i * ncols + j] = acc;
+        }
+    free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw);
+    return 0;
+}

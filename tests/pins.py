@@ -1,0 +1,381 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each function takes an oracle object (the ``oracle`` package, or an
+``oracle.Oracle`` bound to another build of the same source) and raises
+AssertionError when the oracle disagrees with what the block format and the
+mathematics fix:
+
+  * hand-packed super-blocks whose decoded values are known in closed form
+    (tests/golden/*.txt),
+  * bit probes: every stored bit changes exactly one decoded field by a power
+    of two, and every field receives exactly its width in bits,
+  * binary16 values fixed by IEEE 754,
+  * quantiser properties that hold for any input (error bound, sign symmetry,
+    power-of-two covariance, the extreme element maps to +-127, zero blocks),
+  * brute-force fp64 dequantise-then-matmul on tiny shapes,
+  * the textbook special case (unit scales, zero mins, integer activations
+    whose blocks all reach +-127) where the result is a plain integer matmul,
+  * closed-form sums of the worked examples under an all-ones activation row,
+  * invariants (row / column selection, exact power-of-two scaling of x).
+
+The mutation tests plant plausible mistakes in a copy of oracle.c and require
+that at least one of these functions fails for each.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+Q4_K, Q6_K = 0, 1
+
+
+def read_fixture(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def _hex(s: str) -> list[int]:
+    return [int(t, 16) for t in s.split()]
+
+
+def q4k_example_block() -> tuple[np.ndarray, dict]:
+    fx = read_fixture("q4k_worked_example.txt")
+    b = _hex(fx["bytes_0_15"]) + _hex(fx["qs_chunk_32B_repeated_4x"]) * 4
+    assert len(b) == 144
+    return np.array(b, np.uint8), fx
+
+
+def q6k_example_block() -> tuple[np.ndarray, dict]:
+    fx = read_fixture("q6k_worked_example.txt")
+    b = (_hex(fx["ql_chunk_32B_repeated_4x"]) * 4 + _hex(fx["qh_chunk_32B_repeated_2x"]) * 2
+         + _hex(fx["scales_16B"]) + [0x00, 0x3C])
+    assert len(b) == 210
+    return np.array(b, np.uint8), fx
+
+
+# ------------------------------------------------------------------ binary16
+
+def pin_half(orc):
+    # IEEE 754 binary16 encodings with textbook values
+    cases = {0x0000: 0.0, 0x3C00: 1.0, 0x3800: 0.5, 0xC000: -2.0, 0x7BFF: 65504.0,
+             0x0400: 2.0 ** -14, 0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24,
+             0x3555: 0.333251953125, 0x7C00: float("inf"), 0xFC00: float("-inf")}
+    for h, v in cases.items():
+        got = orc.half_to_double(h)
+        assert got == v, (hex(h), got, v)
+
+
+# ------------------------------------------------------------------ decoders
+
+def pin_q4k_worked_example(orc):
+    blk, fx = q4k_example_block()
+    q, sc, m, d, dmin = orc.decode_q4k(blk, 1, 256)
+    assert d[0, 0] == 1.0 and dmin[0, 0] == 0.5, (d, dmin)
+    assert list(sc[0]) == [int(t) for t in fx["sc"].split()], sc
+    assert list(m[0]) == [int(t) for t in fx["m"].split()], m
+    v = np.arange(256)
+    expect_q = np.where((v // 32) % 2 == 0, v % 16, 15 - v % 16)
+    assert np.array_equal(q[0].astype(int), expect_q)
+    w = orc.dequant(Q4_K, blk, 1, 256)[0]
+    assert w.sum() == float(fx["sum_w"]) and w.min() == float(fx["min_w"]) and w.max() == float(fx["max_w"])
+
+
+def pin_q6k_worked_example(orc):
+    blk, fx = q6k_example_block()
+    q6, sc, d = orc.decode_q6k(blk, 1, 256)
+    assert d[0, 0] == 1.0
+    assert list(sc[0]) == [int(t) for t in fx["sc"].split()]
+    v = np.arange(256)
+    quarter = (v % 128) // 32
+    expect = np.where(quarter < 2, v % 64, 63 - v % 64)
+    assert np.array_equal(q6[0].astype(int), expect)
+    w = orc.dequant(Q6_K, blk, 1, 256)[0]
+    assert w.sum() == float(fx["sum_w"]) and w.min() == float(fx["min_w"]) and w.max() == float(fx["max_w"])
+
+
+def _fields_q4k(orc, blk):
+    q, sc, m, d, dmin = orc.decode_q4k(blk, 1, 256)
+    return {"q": q[0].astype(np.int64), "sc": sc[0].astype(np.int64), "m": m[0].astype(np.int64),
+            "d": d[0], "dmin": dmin[0]}
+
+
+def _fields_q6k(orc, blk):
+    q6, sc, d = orc.decode_q6k(blk, 1, 256)
+    return {"q": q6[0].astype(np.int64), "sc": sc[0].astype(np.int64), "d": d[0]}
+
+
+def _bit_probe(orc, blk, nbytes, fields_fn, widths, half_fields):
+    """Flip every bit: exactly one integer field element changes by +-2^k, or exactly
+    one binary16 field changes to the value of the flipped pattern.  Each integer
+    field element must receive exactly `width` distinct bit positions 0..width-1."""
+    base = fields_fn(orc, blk)
+    hits = {name: [set() for _ in range(len(base[name]))] for name in widths}
+    half_hits = {name: 0 for name in half_fields}
+    for byte in range(nbytes):
+        for bit in range(8):
+            b2 = blk.copy()
+            b2[byte] ^= np.uint8(1 << bit)
+            f2 = fields_fn(orc, b2)
+            changed = []
+            for name in widths:
+                idx = np.nonzero(f2[name] != base[name])[0]
+                for i in idx:
+                    changed.append((name, int(i), int(f2[name][i] - base[name][i])))
+            for name, off in half_fields.items():
+                if f2[name][0] != base[name][0]:
+                    h = int(b2[off]) | (int(b2[off + 1]) << 8)
+                    assert f2[name][0] == orc.half_to_double(h), (byte, bit, name)
+                    changed.append((name, 0, None))
+            assert len(changed) == 1, (byte, bit, changed)
+            name, i, delta = changed[0]
+            if name in half_fields:
+                half_hits[name] += 1
+                continue
+            k = int(np.log2(abs(delta)))
+            assert abs(delta) == 1 << k, (byte, bit, delta)
+            assert k not in hits[name][i], (byte, bit, name, i, k)
+            hits[name][i].add(k)
+    for name, w in widths.items():
+        for i, s in enumerate(hits[name]):
+            assert s == set(range(w)), (name, i, s)
+    for name in half_fields:
+        assert half_hits[name] == 16, (name, half_hits[name])
+
+
+def pin_q4k_bit_probe(orc):
+    blk = synth.random_blocks(Q4_K, 1, 256, seed=77, emin=1, emax=14, allow_negative=False)[0]
+    _bit_probe(orc, blk, 144, _fields_q4k, {"q": 4, "sc": 6, "m": 6}, {"d": 0, "dmin": 2})
+
+
+def pin_q6k_bit_probe(orc):
+    blk = synth.random_blocks(Q6_K, 1, 256, seed=78, emin=1, emax=14, allow_negative=False)[0]
+    _bit_probe(orc, blk, 210, _fields_q6k, {"q": 6, "sc": 8}, {"d": 208})
+
+
+# ------------------------------------------------------------------ quantiser
+
+def _acts(seed, M, K, scale=1.0):
+    x = synth.normal(seed, (M, K)) * np.float32(scale)
+    return x.astype(np.float32)
+
+
+def pin_quant_all_ones(orc):
+    fx = read_fixture("q4k_worked_example.txt")
+    x = np.ones((1, 256), np.float32)
+    q, d, S = orc.quantize_act(x)
+    assert np.all(q == 127) and np.all(S == 4064)
+    assert np.all(d == np.float32(float(fx["dx_all_ones"])))
+
+
+def pin_quant_zero_block(orc):
+    x = _acts(5, 2, 128)
+    x[1, 32:64] = 0.0
+    x[0, :32] = -0.0
+    q, d, S = orc.quantize_act(x)
+    assert d[1, 1] == 0.0 and S[1, 1] == 0 and np.all(q[1, 32:64] == 0)
+    assert d[0, 0] == 0.0 and np.all(q[0, :32] == 0)
+    assert np.all(d[0, 1:] > 0)
+
+
+def pin_quant_properties(orc):
+    x = _acts(11, 8, 1024)
+    x[3, :] *= np.float32(1e-30)          # tiny but normal
+    x[4, 100] = np.float32(37.0)          # outlier
+    x[5, ::7] = 0.0                       # scattered zeros
+    q, d, S = orc.quantize_act(x)
+    M, K = x.shape
+    qb = q.reshape(M, K // 32, 32).astype(np.int64)
+    xb = x.reshape(M, K // 32, 32).astype(np.float64)
+    db = d.astype(np.float64)[:, :, None]
+    assert np.all(np.abs(qb) <= 127)
+    assert np.array_equal(S, qb.sum(-1).astype(np.int32))
+    # the extreme element of every block maps to +-127
+    amax = np.abs(xb).max(-1)
+    imax = np.abs(xb).argmax(-1)
+    qmax = np.take_along_axis(qb, imax[:, :, None], -1)[:, :, 0]
+    assert np.all(np.abs(qmax) == 127)
+    # d is amax/127 correctly rounded to fp32: |d*127 - amax| <= 127 * ulp(d)/2
+    ulp = np.spacing(d.astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(d.astype(np.float64) * 127 - amax) <= 127 * ulp / 2 * 1.0000001)
+    # reconstruction error: |x - d*q| <= d/2 (plus the rounding of 1/d and x*id)
+    err = np.abs(xb - db * qb)
+    assert np.all(err <= db * 0.50002), err.max()
+    # zero maps to zero
+    assert np.all(q[5, ::7] == 0)
+
+
+def pin_quant_symmetry_and_scaling(orc):
+    x = _acts(12, 4, 512)
+    q, d, S = orc.quantize_act(x)
+    qn, dn, Sn = orc.quantize_act(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d) and np.array_equal(Sn, -S)
+    for k in (-20, -3, 1, 7):
+        xs = (x * np.float32(2.0 ** k)).astype(np.float32)
+        qs, ds, Ss = orc.quantize_act(xs)
+        assert np.array_equal(qs, q) and np.array_equal(Ss, S)
+        assert np.array_equal(ds, (d * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def pin_quant_integer_blocks(orc):
+    # blocks of integers in [-127, 127] that contain +-127 quantise to themselves with d = 1
+    rng = np.random.default_rng(3)
+    xi = rng.integers(-127, 128, size=(3, 256))
+    xi[:, ::32] = 127 * np.where(rng.random((3, 8)) < 0.5, -1, 1)
+    q, d, S = orc.quantize_act(xi.astype(np.float32))
+    assert np.all(d == 1.0) and np.array_equal(q.astype(np.int64), xi)
+    # with d = 1 exactly, half-integers are ties: IEEE round-half-to-even decides them
+    xh = np.zeros((1, 32), np.float32)
+    xh[0, :9] = [127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -3.5]
+    q, d, _ = orc.quantize_act(xh)
+    assert d[0, 0] == 1.0
+    assert list(q[0, :9]) == [127, 0, 2, 2, 0, -2, -2, 126, -4], q[0, :9]
+
+
+def pin_quant_bf16_matches_f32(orc):
+    xb = synth.to_bf16_bits(_acts(13, 4, 256))
+    xf = synth.bf16_bits_to_f32(xb)
+    a = orc.quantize_act(xb)
+    b = orc.quantize_act(xf)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _dequant_acts(orc, x):
+    q, d, S = orc.quantize_act(x)
+    M, K = q.shape
+    return (q.reshape(M, K // 32, 32).astype(np.float64) * d.astype(np.float64)[:, :, None]).reshape(M, K)
+
+
+def _bruteforce_case(orc, fmt, W, x, N):
+    y = orc.gemm(fmt, W, x, N)
+    w = orc.dequant(fmt, W, N, x.shape[1])
+    xh = _dequant_acts(orc, x)
+    ref = xh @ w.T
+    scale = np.abs(xh) @ np.abs(w).T + 1e-300
+    assert np.all(np.abs(y - ref) <= 1e-12 * scale), np.max(np.abs(y - ref) / scale)
+
+
+def pin_gemm_bruteforce(orc):
+    for fmt in (Q4_K, Q6_K):
+        for (M, N, K, seed) in ((1, 1, 256, 1), (3, 5, 256, 2), (4, 8, 512, 3), (2, 7, 768, 4)):
+            Wr = synth.random_blocks(fmt, N, K, seed=100 + seed, emin=3, emax=18)
+            Wp = synth.pack(fmt, synth.normal(200 + seed, (N, K), 0.0, 0.02))
+            x = _acts(300 + seed, M, K)
+            _bruteforce_case(orc, fmt, Wr, x, N)
+            _bruteforce_case(orc, fmt, Wp, synth.to_bf16_bits(x), N)
+
+
+def _textbook_blocks(fmt, N, K, seed):
+    """Blocks with unit scales and zero mins and random codes, plus those codes."""
+    rng = np.random.default_rng(seed)
+    nb = K // 256
+    if fmt == Q4_K:
+        W = np.zeros((N, nb, 144), np.uint8)
+        W[:, :, 0:2] = (0x00, 0x3C)              # d = 1
+        W[:, :, 2:4] = (0x00, 0x00)              # dmin = 0
+        W[:, :, 4:8] = 1                         # sc[0..3] = 1, top bits 0
+        W[:, :, 8:12] = 0                        # m[0..3] = 0
+        W[:, :, 12:16] = 0x01                    # sc[4..7] = 1, m[4..7] = 0
+        codes = rng.integers(0, 16, size=(N, nb, 256))
+        for v in range(256):
+            byte = 16 + 32 * (v // 64) + v % 32
+            shift = 0 if v % 64 < 32 else 4
+            W[:, :, byte] |= (codes[:, :, v] << shift).astype(np.uint8)
+        vals = codes
+    else:
+        W = np.zeros((N, nb, 210), np.uint8)
+        W[:, :, 192:208] = 1                     # sc = 1
+        W[:, :, 208:210] = (0x00, 0x3C)          # d = 1
+        codes = rng.integers(0, 64, size=(N, nb, 256))
+        for v in range(256):
+            h, r = divmod(v, 128)
+            c, l = divmod(r, 32)
+            lb = 64 * h + 32 * (c % 2) + l
+            W[:, :, lb] |= ((codes[:, :, v] & 15) << (0 if c < 2 else 4)).astype(np.uint8)
+            W[:, :, 128 + 32 * h + l] |= (((codes[:, :, v] >> 4) & 3) << (2 * c)).astype(np.uint8)
+        vals = codes - 32
+    return W.reshape(N, -1), vals.reshape(N, K).astype(np.int64)
+
+
+def _integer_acts(M, K, seed):
+    rng = np.random.default_rng(seed)
+    xi = rng.integers(-127, 128, size=(M, K))
+    xi[:, ::32] = 127 * np.where(rng.random((M, K // 32)) < 0.5, -1, 1)
+    return xi
+
+
+def pin_gemm_textbook(orc):
+    for fmt in (Q4_K, Q6_K):
+        M, N, K = 5, 6, 512
+        W, wv = _textbook_blocks(fmt, N, K, seed=9 + fmt)
+        xi = _integer_acts(M, K, seed=19 + fmt)
+        y = orc.gemm(fmt, W, xi.astype(np.float32), N)
+        exact = xi @ wv.T                          # int64 textbook matmul
+        assert np.array_equal(y, exact.astype(np.float64)), np.abs(y - exact).max()
+        # per-block integer partials are block-wise textbook matmuls
+        L = 32 if fmt == Q4_K else 16
+        P = orc.block_partials(fmt, W, xi.astype(np.int8), N)
+        ref = np.einsum("mbt,nbt->mnb", xi.reshape(M, K // L, L), wv.reshape(N, K // L, L))
+        assert np.array_equal(P.astype(np.int64), ref)
+
+
+def pin_gemm_worked_examples(orc):
+    x = np.ones((1, 256), np.float32)
+    dx = np.float64(np.float32(1.0) / np.float32(127.0))
+    blk4, fx4 = q4k_example_block()
+    y4 = orc.gemm(Q4_K, blk4, x, 1)[0, 0]
+    assert abs(y4 - float(fx4["sum_w"]) * 127 * dx) <= 1e-9, y4
+    blk6, fx6 = q6k_example_block()
+    y6 = orc.gemm(Q6_K, blk6, x, 1)[0, 0]
+    assert abs(y6 - float(fx6["sum_w"]) * 127 * dx) <= 1e-12, y6
+
+
+def pin_gemm_selection_and_scaling(orc):
+    for fmt in (Q4_K, Q6_K):
+        M, N, K = 6, 9, 512
+        W = synth.pack(fmt, synth.normal(41 + fmt, (N, K), 0.0, 0.02))
+        x = _acts(43 + fmt, M, K)
+        y = orc.gemm(fmt, W, x, N)
+        rows, cols = np.array([4, 0, 5]), np.array([8, 1, 3, 3])
+        ys = orc.gemm(fmt, W, x, N, rows=rows, cols=cols)
+        assert np.array_equal(ys, y[np.ix_(rows, cols)])
+        # each output row depends only on its own input row
+        assert np.array_equal(orc.gemm(fmt, W, x[2:4].copy(), N), y[2:4])
+        y2 = orc.gemm(fmt, W, (x * np.float32(8.0)).astype(np.float32), N)
+        assert np.array_equal(y2, y * 8.0)
+
+
+def pin_gemm_semantic_bound(orc):
+    """The quantised result stays within the activation-rounding bound of the
+    unquantised product (catches a quantiser that only agrees with itself)."""
+    for fmt in (Q4_K, Q6_K):
+        M, N, K = 4, 6, 768
+        W = synth.pack(fmt, synth.normal(51 + fmt, (N, K), 0.0, 0.02))
+        x = _acts(53 + fmt, M, K)
+        y = orc.gemm(fmt, W, x, N)
+        w = orc.dequant(fmt, W, N, K)
+        exact = x.astype(np.float64) @ w.T
+        _, d, _ = orc.quantize_act(x)
+        dk = np.repeat(d.astype(np.float64), 32, axis=1)       # d of the block holding k
+        bound = (dk * 0.50002) @ np.abs(w).T
+        assert np.all(np.abs(y - exact) <= bound + 1e-12)
+
+
+ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bit_probe,
+            pin_q6k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
+            pin_quant_symmetry_and_scaling, pin_quant_integer_blocks, pin_quant_bf16_matches_f32,
+            pin_gemm_bruteforce, pin_gemm_textbook, pin_gemm_worked_examples,
+            pin_gemm_selection_and_scaling, pin_gemm_semantic_bound]

@@ -1,0 +1,100 @@
+"""Plant plausible mistakes in a copy of oracle.c and require that the pins catch
+each one.  The mutants are built into a temporary directory on the CPU; the real
+oracle source is never modified."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+# (name, exact text in oracle.c, replacement) -- each a mistake a reader of the
+# block layout or of the method could plausibly make
+MUTANTS = [
+    ("q4k_scale_high_bits_from_wrong_byte",
+     "sc[j] = (uint8_t)((s[j + 4] & 0x0F) | ((s[j - 4] >> 6) << 4));",
+     "sc[j] = (uint8_t)((s[j + 4] & 0x0F) | ((s[j] >> 6) << 4));"),
+    ("q4k_min_low_bits_wrong_nibble",
+     "m[j] = (uint8_t)((s[j + 4] >> 4) | ((s[j] >> 6) << 4));",
+     "m[j] = (uint8_t)((s[j + 4] & 0x0F) | ((s[j] >> 6) << 4));"),
+    ("q4k_nibble_order_swapped",
+     "q[v] = (v % 64) < 32 ? (byte & 0x0F) : (byte >> 4);",
+     "q[v] = (v % 64) < 32 ? (byte >> 4) : (byte & 0x0F);"),
+    ("q4k_byte_index_wrong",
+     "uint8_t byte = qs[32 * (v / 64) + (v % 32)];",
+     "uint8_t byte = qs[(v / 2) % 128];"),
+    ("q4k_min_term_sign",
+     "acc += dxb * (d * sc * (double)I - dmin * m * (double)Sx[i * nb32 + b]);",
+     "acc += dxb * (d * sc * (double)I + dmin * m * (double)Sx[i * nb32 + b]);"),
+    ("q4k_min_term_dropped",
+     "acc += dxb * (d * sc * (double)I - dmin * m * (double)Sx[i * nb32 + b]);",
+     "acc += dxb * (d * sc * (double)I);"),
+    ("q6k_qh_shift",
+     "int hi = (qh[32 * half + l] >> (2 * quarter)) & 3;",
+     "int hi = (qh[32 * half + l] >> quarter) & 3;"),
+    ("q6k_ql_half_stride",
+     "uint8_t lowbyte = ql[64 * half + 32 * (quarter % 2) + l];",
+     "uint8_t lowbyte = ql[32 * half + 32 * (quarter % 2) + l];"),
+    ("q6k_offset_dropped_in_gemm",
+     "for (int t = 0; t < 16; t++) Ia += ((int32_t)wq[32 * b + t] - 32) * (int32_t)xq[32 * b + t];",
+     "for (int t = 0; t < 16; t++) Ia += ((int32_t)wq[32 * b + t]) * (int32_t)xq[32 * b + t];"),
+    ("q6k_second_scale_index",
+     "acc += dxb * d * ((double)sc[2 * b] * (double)Ia + (double)sc[2 * b + 1] * (double)Ib);",
+     "acc += dxb * d * ((double)sc[2 * b] * (double)Ia + (double)sc[2 * b] * (double)Ib);"),
+    ("q6k_scale_unsigned",
+     "for (int s = 0; s < 16; s++) sc[s] = (int8_t)blk[192 + s];",
+     "for (int s = 0; s < 16; s++) sc[s] = (int8_t)(blk[192 + s] & 0x7F);"),
+    ("half_exponent_bias",
+     "else v = ldexp((double)(f | 0x400), e - 25);",
+     "else v = ldexp((double)(f | 0x400), e - 24);"),
+    ("half_subnormal_scale",
+     "if (e == 0) v = ldexp((double)f, -24);",
+     "if (e == 0) v = ldexp((double)f, -25);"),
+    ("quant_divisor_128",
+     "float d = amax / 127.0f;",
+     "float d = amax / 128.0f;"),
+    ("quant_truncates",
+     "float r = rintf(v);",
+     "float r = truncf(v);"),
+    ("quant_rounds_half_away",
+     "float r = rintf(v);",
+     "float r = roundf(v);"),
+    ("quant_sum_of_magnitudes",
+     "S += qi;",
+     "S += qi < 0 ? -qi : qi;"),
+    ("gemm_activation_scale_wrong_block",
+     "double dxb = (double)dx[i * nb32 + b];",
+     "double dxb = (double)dx[i * nb32 + (b ^ 1)];"),
+    ("gemm_superblock_index",
+     "double d = dw[j * nsb + b / 8];",
+     "double d = dw[j * nsb + b / 16];"),
+    ("gemm_activation_reversed_in_block",
+     "for (int t = 0; t < 32; t++) I += (int32_t)wq[32 * b + t] * (int32_t)xq[32 * b + t];",
+     "for (int t = 0; t < 32; t++) I += (int32_t)wq[32 * b + t] * (int32_t)xq[32 * b + 31 - t];"),
+    ("partials_offset_dropped",
+     "acc += ((int32_t)qw[n * K + b * L + t] - off) * (int32_t)qx[mi * K + b * L + t];",
+     "acc += ((int32_t)qw[n * K + b * L + t]) * (int32_t)qx[mi * K + b * L + t];"),
+]
+
+
+def _fails_some_pin(orc):
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(oracle.source_path()).read()
+    assert src.count(old) >= 1, f"mutation site for {name} no longer in oracle.c"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "oracle_mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.build(src=path, out=os.path.join(d, "liboracle_mutant.so"))
+        caught = _fails_some_pin(oracle.Oracle(lib))
+    assert caught is not None, f"no pin catches mutant {name}"
