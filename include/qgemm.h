@@ -1,0 +1,151 @@
+/*
+ * qgemm.h -- C ABI of libqgemm.so: the batched prefill projection matmul over
+ * GGUF Q4_K / Q6_K weights on AMD Instinct MI355X (gfx950).
+ *
+ * Operation.  y[M x N] = x[M x K] . W[N x K]^T where W stays in its GGUF
+ * super-blocks and x is a whole prompt's activation rows.  The weights are
+ * decoded to small integers on the GPU, every activation row is quantised to
+ * int8 per 32 consecutive values (one fp32 scale d = amax/127 and the int32 sum
+ * of the codes per block), the contraction is int8 x int8 -> int32 on the
+ * matrix cores, and each weight sub-block's scale and min are applied to the
+ * int32 partial in fp32.  This is the fused "decode super-blocks in registers,
+ * int8 tensor-core GEMM" design of sparkinfer PR #464 ("fused Q4K/Q6K->int8
+ * dequant ...", section "Summary") and the "row-batched fused Q4_K x int8
+ * kernel" branch of the design question in aprender issue #5475 ("Qwen3.5 on
+ * CPU prefills one token at a time", section "Ask"); the activation block is
+ * the q8_1-style per-32 block that issue #4220 ("CRUX parity spike ...",
+ * technique 5) names for the quantised-activation GEMV.  The LM-head entry is
+ * the "LM head on the last token only" of aprender issue #5305 (sub-ticket
+ * #4313).
+ *
+ * Block layouts (public GGUF K-quant format; little-endian, binary16 scales):
+ *   Q4_K: 144 bytes per 256 values -- d, dmin, 12 bytes of packed 6-bit
+ *         sub-block scales/mins (8 sub-blocks of 32), 128 bytes of 4-bit codes;
+ *         w = d*sc*q - dmin*m.
+ *   Q6_K: 210 bytes per 256 values -- ql[128], qh[64], 16 int8 scales (16
+ *         sub-blocks of 16), d; w = d*sc*(q6 - 32).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no pointer after returning and has no mutable
+ *     global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is only enqueued; return value 0 means "enqueued".  The caller
+ *     synchronises.  Calls on different streams may run concurrently if they
+ *     use different workspaces.
+ *   - Errors are negative return codes (see QG_E*); on error nothing is
+ *     launched, except QG_ELAUNCH, which reports a launch failure after the
+ *     fact.  No C++ exception crosses this boundary.
+ *   - Non-finite activations or weight scales are a precondition violation;
+ *     the results are then unspecified.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* weight formats */
+enum { QG_Q4_K = 0, QG_Q6_K = 1 };
+/* activation element types: IEEE binary32, or bfloat16 (raw 16-bit patterns) */
+enum { QG_F32 = 0, QG_BF16 = 1 };
+/* kernel path selection for qgemm_prefill_ex */
+enum { QG_PATH_AUTO = 0, QG_PATH_TILED = 1, QG_PATH_SKINNY = 2 };
+/* return codes */
+enum {
+    QG_OK = 0,
+    QG_EINVAL = -1,     /* null pointer, M/N/K < 1, K % 256 != 0, size overflow, bad path */
+    QG_EFMT = -2,       /* fmt not QG_Q4_K / QG_Q6_K */
+    QG_EDTYPE = -3,     /* x_dtype not QG_F32 / QG_BF16 */
+    QG_EWORKSPACE = -4, /* workspace NULL, smaller than qgemm_workspace_bytes, or not 256-B aligned */
+    QG_EALIGN = -5,     /* q_weights not 16-B aligned, x not aligned to 16 B, y not 16-B aligned */
+    QG_ELAUNCH = -6,    /* the HIP runtime reported a launch error */
+    QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
+};
+
+/* Largest skinny-path batch: rows M <= QG_SKINNY_MAX_M go to the bandwidth-bound
+ * skinny kernel under QG_PATH_AUTO, larger M to the tiled matrix-core kernel. */
+#define QG_SKINNY_MAX_M 8
+
+/* Workspace bytes needed by qgemm_prefill / qgemm_lm_head for M activation rows
+ * of length K (int8 codes, per-block fp32 scales and scaled block sums).
+ * Returns 0 when M < 1, K < 1, K % 256 != 0 or the size overflows. */
+size_t qgemm_workspace_bytes(int64_t M, int64_t K);
+
+/* y[m][n] = sum_k x[m][k] * W[n][k] under the method's quantisation.
+ *   q_weights : GGUF tensor data of a 2-D weight with K contiguous: row n holds
+ *               K/256 consecutive blocks starting at byte n*(K/256)*bytes_per_block.
+ *               Must be 16-byte aligned.
+ *   fmt       : QG_Q4_K or QG_Q6_K.
+ *   x         : activations [M][K] row-major, element type x_dtype, 16-byte aligned.
+ *   M, N, K   : M, N >= 1; K >= 256 and K % 256 == 0.
+ *   y         : output [M][N] fp32 row-major (leading dimension N), overwritten.
+ *               Must be 16-byte aligned.
+ *   workspace : device scratch of at least qgemm_workspace_bytes(M, K) bytes,
+ *               256-byte aligned; its contents are scratch on entry and exit.
+ *   stream    : hipStream_t (NULL = default stream).
+ * Dispatch: M <= QG_SKINNY_MAX_M -> skinny kernel, otherwise the tiled kernel. */
+int qgemm_prefill(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
+                  int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* qgemm_prefill with an explicit kernel path (QG_PATH_AUTO / _TILED / _SKINNY).
+ * QG_PATH_SKINNY requires M <= QG_SKINNY_MAX_M (else QG_EINVAL).  Both paths
+ * compute the same quantities; they differ only in fp32 summation order. */
+int qgemm_prefill_ex(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
+                     int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,
+                     void *stream, int path);
+
+/* LM head on the last token only: qgemm_prefill with M = 1.  x_row points at the
+ * one activation row [K]; y receives [N] logits. */
+int qgemm_lm_head(const void *q_weights, int fmt, const void *x_row, int x_dtype, int64_t N,
+                  int64_t K, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The two halves of qgemm_prefill, for callers that feed one activation matrix
+ * to several projections (the fused QKV and gate/up projections of a layer
+ * read the same hidden rows): quantise once, then run one GEMM per weight.
+ *
+ * qgemm_quantize_workspace: quantise x [M][K] into `workspace` (layout private
+ * to the library, sized by qgemm_workspace_bytes(M, K)).
+ * qgemm_gemm_quantized: y = x . W^T from a workspace filled by
+ * qgemm_quantize_workspace with the same M and K (and not modified since);
+ * path as in qgemm_prefill_ex.  Argument rules and codes as qgemm_prefill. */
+int qgemm_quantize_workspace(const void *x, int x_dtype, int64_t M, int64_t K, void *workspace,
+                             size_t workspace_bytes, void *stream);
+int qgemm_gemm_quantized(const void *q_weights, int fmt, const void *workspace,
+                         size_t workspace_bytes, int64_t M, int64_t N, int64_t K, float *y,
+                         void *stream, int path);
+
+/* Static message for a return code (never NULL). */
+const char *qgemm_strerror(int code);
+
+/* ---- test hooks: the comparison points for bit-exact parity ---- */
+
+/* Activation quantiser alone: q [M][K] int8, d [M][K/32] fp32, S [M][K/32] int32
+ * (row-major).  d = amax/127 (IEEE division), codes rint(x * (1/d)) ties to even
+ * clamped to [-127, 127], code 0 where x == 0, S = sum of the block's codes;
+ * an all-zero block gives d = 0.  K % 32 == 0 is required here. */
+int qgemm_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *q, float *d,
+                       int32_t *S, void *stream);
+
+/* Decoded weights w [N][K] fp32, each the correctly rounded fp32 value of
+ * d*sc*q - dmin*m (Q4_K) or d*sc*(q6 - 32) (Q6_K). */
+int qgemm_dequant(const void *q_weights, int fmt, int64_t N, int64_t K, float *w, void *stream);
+
+/* Per-block int32 partials computed by the tiled kernel's own decode and matrix
+ * instructions: Q4_K out[m][n][b] = sum_{t<32} q[n][32b+t] * qx[m][32b+t]
+ * (K/32 per pair, q in 0..15); Q6_K out[m][n][s] = sum_{t<16} (q6[n][16s+t] - 32)
+ * * qx[m][16s+t] (K/16 per pair).  qx is int8 [M][K]; out has M*N*K/32 (Q4_K)
+ * or M*N*K/16 (Q6_K) elements.  Meant for small shapes. */
+int qgemm_block_partials(const void *q_weights, int fmt, const int8_t *qx, int64_t M, int64_t N,
+                         int64_t K, int32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,42 @@
+"""Build recipe for libqgemm.so: hipcc for gfx950, one object per source, in-tree."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libqgemm.so")
+SOURCES = ["act_quant.hip", "gemm_tiled.hip", "gemm_skinny.hip", "dequant.hip", "api.hip"]
+# -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
+HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = ["hipcc", *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        text = "\n".join(l for l in out.decode(errors="replace").splitlines()
+                         if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append((cmd, text))
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        msg = "\n".join(" ".join(c) + "\n" + t for c, t in failed)
+        raise RuntimeError("hipcc failed:\n" + msg)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                   check=True)
+    os.replace(tmp, LIB)
+    return LIB

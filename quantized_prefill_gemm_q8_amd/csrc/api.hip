@@ -1,0 +1,214 @@
+// Host side of the C ABI declared in include/qgemm.h: argument checks,
+// workspace carving and kernel dispatch.  No allocation, no global mutable
+// state apart from a once-per-device architecture check.
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kMaxDevices = 64;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t padded_rows(int64_t M) { return (M + qg::kRowPad - 1) / qg::kRowPad * qg::kRowPad; }
+
+// Byte offsets of the workspace sections, each 256-byte aligned.
+struct Layout {
+  int64_t Mp, q_off, dx_off, ds_off, total;
+};
+
+bool layout_for(int64_t M, int64_t K, Layout* L) {
+  if (M < 1 || K < 256 || K % 256 != 0) return false;
+  const int64_t Mp = padded_rows(M);
+  // overflow guard: Mp*K and the scale arrays must fit comfortably in int64
+  if (Mp > (INT64_C(1) << 40) / K) return false;
+  L->Mp = Mp;
+  L->q_off = 0;
+  L->dx_off = Mp * K;                       // multiple of 256*256
+  L->ds_off = L->dx_off + Mp * (K / 32) * 4;
+  L->total = L->ds_off + Mp * (K / 32) * 4;
+  return true;
+}
+
+// gfx950 check, cached per device (atomic so concurrent first calls are fine).
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QG_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return QG_EDEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QG_EDEVICE;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? QG_OK : QG_EDEVICE;
+}
+
+int check_common(const void* W, int fmt, int64_t N, int64_t K) {
+  if (!W) return QG_EINVAL;
+  if (fmt != QG_Q4_K && fmt != QG_Q6_K) return QG_EFMT;
+  if (N < 1 || K < 256 || K % 256 != 0) return QG_EINVAL;
+  if (N > (INT64_C(1) << 40) / K) return QG_EINVAL;
+  if (!aligned(W, 16)) return QG_EALIGN;
+  return QG_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t qgemm_workspace_bytes(int64_t M, int64_t K) {
+  Layout L;
+  if (!layout_for(M, K, &L)) return 0;
+  return static_cast<size_t>(L.total);
+}
+
+static QgWorkspace carve(void* workspace, const Layout& L) {
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  QgWorkspace ws;
+  ws.q = reinterpret_cast<int8_t*>(base + L.q_off);
+  ws.dxT = reinterpret_cast<float*>(base + L.dx_off);
+  ws.dST = reinterpret_cast<float*>(base + L.ds_off);
+  ws.Mp = L.Mp;
+  return ws;
+}
+
+static int check_workspace(const void* workspace, size_t workspace_bytes, const Layout& L) {
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < static_cast<size_t>(L.total))
+    return QG_EWORKSPACE;
+  return QG_OK;
+}
+
+int qgemm_quantize_workspace(const void* x, int x_dtype, int64_t M, int64_t K, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!x || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  int rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  if (!aligned(x, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const QgWorkspace ws = carve(workspace, L);
+  return launch_status(qg_launch_act_quant(x, x_dtype, M, K, ws.q, ws.dxT, L.Mp, 1, nullptr,
+                                           ws.dST, static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_gemm_quantized(const void* q_weights, int fmt, const void* workspace,
+                         size_t workspace_bytes, int64_t M, int64_t N, int64_t K, float* y,
+                         void* stream, int path) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (!y || M < 1) return QG_EINVAL;
+  if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return QG_EINVAL;
+  if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return QG_EINVAL;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / N) return QG_EINVAL;
+  rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  if (!aligned(y, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
+  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && M <= QG_SKINNY_MAX_M);
+  const uint8_t* W = static_cast<const uint8_t*>(q_weights);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(skinny ? qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s)
+                              : qg_launch_gemm_tiled(W, fmt, ws, M, N, K, y, s));
+}
+
+int qgemm_prefill_ex(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M,
+                     int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes,
+                     void* stream, int path) {
+  // validate everything the GEMM half checks before launching the quantiser
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (!x || !y || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return QG_EINVAL;
+  if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return QG_EINVAL;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / N) return QG_EINVAL;
+  rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  if (!aligned(x, 16) || !aligned(y, 16)) return QG_EALIGN;
+  rc = qgemm_quantize_workspace(x, x_dtype, M, K, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  return qgemm_gemm_quantized(q_weights, fmt, workspace, workspace_bytes, M, N, K, y, stream, path);
+}
+
+int qgemm_prefill(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M,
+                  int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return qgemm_prefill_ex(q_weights, fmt, x, x_dtype, M, N, K, y, workspace, workspace_bytes,
+                          stream, QG_PATH_AUTO);
+}
+
+int qgemm_lm_head(const void* q_weights, int fmt, const void* x_row, int x_dtype, int64_t N,
+                  int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return qgemm_prefill_ex(q_weights, fmt, x_row, x_dtype, 1, N, K, y, workspace, workspace_bytes,
+                          stream, QG_PATH_AUTO);
+}
+
+const char* qgemm_strerror(int code) {
+  switch (code) {
+    case QG_OK: return "success";
+    case QG_EINVAL: return "invalid argument (null pointer, size < 1, K not a multiple of 256, size overflow or bad path)";
+    case QG_EFMT: return "unsupported weight format (expected QG_Q4_K or QG_Q6_K)";
+    case QG_EDTYPE: return "unsupported activation type (expected QG_F32 or QG_BF16)";
+    case QG_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case QG_EALIGN: return "pointer not 16-byte aligned";
+    case QG_ELAUNCH: return "kernel launch failed";
+    case QG_EDEVICE: return "current device is not a gfx950 (MI355X) GPU";
+    default: return "unknown error code";
+  }
+}
+
+int qgemm_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* d,
+                       int32_t* S, void* stream) {
+  if (!x || !q || !d || !S || M < 1 || K < 32 || K % 32 != 0) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / K) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(d, 4) || !aligned(S, 4)) return QG_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_act_quant(x, x_dtype, M, K, q, d, 1, K / 32, S, nullptr,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_dequant(const void* q_weights, int fmt, int64_t N, int64_t K, float* w, void* stream) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (!w) return QG_EINVAL;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_dequant(static_cast<const uint8_t*>(q_weights), fmt, N, K, w,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_block_partials(const void* q_weights, int fmt, const int8_t* qx, int64_t M, int64_t N,
+                         int64_t K, int32_t* out, void* stream) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (!qx || !out || M < 1) return QG_EINVAL;
+  if (M > (INT64_C(1) << 34) / N / (K / 16)) return QG_EINVAL;
+  if (!aligned(qx, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_block_partials(static_cast<const uint8_t*>(q_weights), fmt, qx,
+                                                M, N, K, out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

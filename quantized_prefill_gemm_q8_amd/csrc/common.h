@@ -1,0 +1,99 @@
+// Device-side helpers shared by the gfx950 kernels of libqgemm.so.
+//
+// Everything here is written for CDNA4 (gfx950): 64-lane wavefronts, int8
+// matrix-core instructions, binary16 conversions in hardware.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qgemm.h"
+
+namespace qg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kQ4Bytes = 144;  // bytes per Q4_K super-block (256 values)
+constexpr int kQ6Bytes = 210;  // bytes per Q6_K super-block (256 values)
+constexpr int kRowPad = 256;   // activation rows are padded to this multiple in the workspace
+
+// 1.5 * 2^23 as an fp32 bit pattern.  An int32 accumulator started at this
+// value and increased by a small integer I (|I| < 2^22) reads back as the fp32
+// number 12582912 + I, so the matrix core's int32 result needs no conversion
+// instruction before the fp32 epilogue.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
+__device__ __forceinline__ float half_to_float(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+__device__ __forceinline__ float bits_to_float(int b) { return __builtin_bit_cast(float, b); }
+
+// Q4_K packed sub-block scales/mins: the 12 scale bytes as three little-endian
+// dwords s0 (bytes 0-3), s1 (4-7), s2 (8-11).  Returns the eight 6-bit scales
+// as two dwords of bytes (sc[0..3], sc[4..7]) and likewise the mins.
+//   j < 4 : sc = low 6 bits of byte j, m = low 6 bits of byte j+4
+//   j >= 4: low nibble from byte j+4 (sc: low half, m: high half), top 2 bits
+//           from bits 6-7 of byte j-4 (sc) or byte j (m)
+struct Q4Scales {
+  uint32_t sc_lo, sc_hi, m_lo, m_hi;
+};
+__device__ __forceinline__ Q4Scales unpack_q4_scales(uint32_t s0, uint32_t s1, uint32_t s2) {
+  Q4Scales r;
+  r.sc_lo = s0 & 0x3F3F3F3Fu;
+  r.m_lo = s1 & 0x3F3F3F3Fu;
+  r.sc_hi = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
+  r.m_hi = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
+  return r;
+}
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
+
+// Q6_K codes arrive as bytes q6 in [0, 63]; the matrix core wants the signed
+// value q6 - 32 in every byte.  Setting bit 7 first keeps the per-byte
+// subtraction from borrowing into the next byte; flipping bit 7 back leaves
+// (q6 - 32) mod 256 in each byte.
+__device__ __forceinline__ uint32_t q6_to_signed(uint32_t q) {
+  return ((q | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+}
+
+// Load 4 bytes from a 2-byte-aligned global address (Q6_K blocks are 210 bytes,
+// so odd blocks start at 2 mod 4) with dword loads only.  Reads the aligned
+// dword holding the first byte and, when the address is not dword aligned, the
+// dword after it; the caller guarantees both lie inside the buffer.
+__device__ __forceinline__ uint32_t load_u32_a2(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
+  const uint32_t lo = base[0];
+  if ((a & 3) == 0) return lo;
+  const uint32_t hi = base[1];
+  return __builtin_amdgcn_alignbyte(hi, lo, static_cast<uint32_t>(a & 3));
+}
+
+__device__ __forceinline__ uint16_t load_u16(const uint8_t* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+}  // namespace qg
+
+// ---- host-side launchers (defined in the kernel sources) ----
+struct QgWorkspace {
+  int8_t* q;    // [Mp][K] int8 codes
+  float* dxT;   // [K/32][Mp] activation block scales, block-major
+  float* dST;   // [K/32][Mp] d * S per block (fp32), block-major
+  int64_t Mp;   // padded row count
+};
+
+hipError_t qg_launch_act_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
+                               float* d, int64_t d_sb, int64_t d_sm, int32_t* S_int,
+                               float* dS, hipStream_t stream);
+hipError_t qg_launch_gemm_tiled(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
+                                int64_t N, int64_t K, float* y, hipStream_t stream);
+hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
+                                 int64_t N, int64_t K, float* y, hipStream_t stream);
+hipError_t qg_launch_dequant(const uint8_t* W, int fmt, int64_t N, int64_t K, float* w,
+                             hipStream_t stream);
+hipError_t qg_launch_block_partials(const uint8_t* W, int fmt, const int8_t* qx, int64_t M,
+                                    int64_t N, int64_t K, int32_t* out, hipStream_t stream);

@@ -1,0 +1,98 @@
+"""The C-ABI library (CPU only): it loads, exports every entry point that
+include/qgemm.h declares, sizes workspaces, and rejects bad arguments with the
+documented codes before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import __graft_entry__
+
+__graft_entry__.ensure_built()
+import quantized_prefill_gemm_q8_amd as qg  # noqa: E402
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "qgemm.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemm_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_symbols() == sorted(qg.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(qg.library_path())
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    for code in range(0, -8, -1):
+        s = qg.qgemm_strerror(code)
+        assert s and s != "unknown error code", code
+    assert qg.qgemm_strerror(-99) == "unknown error code"
+
+
+def test_workspace_bytes():
+    ws = qg.qgemm_workspace_bytes
+    assert ws(0, 256) == 0 and ws(1, 255) == 0 and ws(1, 300) == 0 and ws(-1, 256) == 0
+    # rows padded to 256: int8 codes plus two fp32 values per 32-value block
+    assert ws(1, 256) == 256 * 256 + 2 * 256 * 8 * 4
+    assert ws(512, 4096) == 512 * 4096 + 2 * 512 * 128 * 4
+    assert ws(513, 4096) == 768 * 4096 + 2 * 768 * 128 * 4
+    assert ws(1, 1 << 40) == 0          # overflow guard
+
+
+# fake but well-aligned device addresses: every call below must fail validation
+# before any HIP call, so nothing is dereferenced
+A = 1 << 20
+
+
+def _prefill(**kw):
+    lib = qg.load()
+    a = dict(w=A, fmt=0, x=A, xdt=1, M=4, N=8, K=256, y=A, ws=A,
+             wsb=qg.qgemm_workspace_bytes(4, 256), stream=None, path=0)
+    a.update(kw)
+    return lib.qgemm_prefill_ex(a["w"], a["fmt"], a["x"], a["xdt"], a["M"], a["N"], a["K"],
+                                a["y"], a["ws"], a["wsb"], a["stream"], a["path"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), -1), (dict(x=None), -1), (dict(y=None), -1),
+    (dict(M=0), -1), (dict(N=0), -1), (dict(K=0), -1), (dict(K=300), -1), (dict(K=128), -1),
+    (dict(M=-5), -1), (dict(N=1 << 40), -1),
+    (dict(fmt=2), -2), (dict(fmt=-1), -2),
+    (dict(xdt=2), -3),
+    (dict(path=3), -1), (dict(path=2, M=9), -1),
+    (dict(ws=None), -4), (dict(ws=A + 128), -4), (dict(wsb=100), -4),
+    (dict(w=A + 8), -5), (dict(x=A + 4), -5), (dict(y=A + 4), -5),
+])
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_other_entry_points_reject():
+    lib = qg.load()
+    assert lib.qgemm_lm_head(None, 0, A, 1, 8, 256, A, A, 1 << 20, None) == -1
+    assert lib.qgemm_lm_head(A, 7, A, 1, 8, 256, A, A, 1 << 20, None) == -2
+    assert lib.qgemm_quantize_act(A, 1, 4, 48, A, A, A, None) == -1      # K % 32 != 0
+    assert lib.qgemm_quantize_act(A, 5, 4, 64, A, A, A, None) == -3
+    assert lib.qgemm_quantize_act(A + 2, 1, 4, 64, A, A, A, None) == -5
+    assert lib.qgemm_dequant(A, 1, 8, 100, A, None) == -1
+    assert lib.qgemm_dequant(A, 3, 8, 256, A, None) == -2
+    assert lib.qgemm_block_partials(A, 0, None, 4, 8, 256, A, None) == -1
+    assert lib.qgemm_block_partials(A, 0, A + 1, 4, 8, 256, A, None) == -5
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    W = torch.zeros(144 * 8, dtype=torch.uint8)
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qg.prefill(W, qg.QG_Q4_K, x, 8, workspace=torch.zeros(16, dtype=torch.uint8))

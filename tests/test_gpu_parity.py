@@ -1,0 +1,255 @@
+"""GPU parity: libqgemm.so (through its C ABI) against the CPU oracle.
+
+Bit-exact: activation codes, scales and block sums; decoded weights (as the
+correctly rounded fp32 of the exact value); per-block int32 partials.  Within
+the acceptance bound |dy| <= 1e-3 * ||x_row||_2 * max|w|: the GEMM output, on
+every element at small sizes and on sampled elements at the workloads' full
+sizes.  Plus the exact cases (textbook integer matmul, power-of-two scaling,
+row-split and run-to-run identity) and the edge shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import __graft_entry__
+
+__graft_entry__.ensure_built()
+import oracle  # noqa: E402
+import synth  # noqa: E402
+import quantized_prefill_gemm_q8_amd as qg  # noqa: E402
+from gpu_util import DEV, bound, check, max_abs_w, to_dev, x_as_f32  # noqa: E402
+import pins  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [qg.QG_Q4_K, qg.QG_Q6_K]
+FMT_ID = {qg.QG_Q4_K: "q4k", qg.QG_Q6_K: "q6k"}
+
+
+def gpu_prefill(W: np.ndarray, fmt: int, x: np.ndarray, N: int, path=qg.QG_PATH_AUTO) -> np.ndarray:
+    y = qg.prefill(to_dev(W), fmt, to_dev(x), N, path=path)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ quantiser
+
+def _special_rows(K):
+    rows = []
+    r = np.zeros(K, np.float32); rows.append(r)                                  # all zero
+    r = synth.normal(501, K); r[:32] = 0; r[64:96] = -0.0; rows.append(r)       # zero blocks
+    r = np.float32(2.0 ** -140) * synth.normal(502, K); rows.append(r.astype(np.float32))  # subnormal
+    r = np.float32(1e-37) * synth.normal(503, K); rows.append(r.astype(np.float32))  # tiny normal
+    r = np.float32(1e30) * synth.normal(504, K); rows.append(r.astype(np.float32))   # huge
+    r = np.tile(np.float32([127, 0.5, 1.5, 2.5, -0.5, -2.5, 126.5, -3.5]), K // 8); rows.append(r)  # ties
+    r = synth.normal(505, K); r[::32] *= 1000; rows.append(r)                    # block outliers
+    r = np.full(K, 1.0, np.float32); rows.append(r)                              # all ones
+    r = np.full(K, 2.0 ** -149, np.float32); r[1::2] *= -1; rows.append(r)      # min subnormal
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_act_bitexact(dtype):
+    M, K = 37, 1024
+    x = synth.normal(510, (M, K))
+    x[::5] *= np.float32(8.0)
+    x = np.concatenate([x, _special_rows(K)])
+    if dtype == "bf16":
+        x = synth.to_bf16_bits(x)
+    M = x.shape[0]
+    xq, xd, xs = oracle.quantize_act(x)
+    q = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    d = torch.empty((M, K // 32), dtype=torch.float32, device=DEV)
+    S = torch.empty((M, K // 32), dtype=torch.int32, device=DEV)
+    qg.qgemm_quantize_act(to_dev(x), M, K, q, d, S)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), xq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), xd.view(np.uint32))
+    assert np.array_equal(S.cpu().numpy(), xs)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_quantize_act_bitexact_config_rows(cfg):
+    g = synth.CONFIGS[cfg][0]
+    x = synth.make_acts(g, rows=min(g.M, 64))
+    M, K = x.shape
+    xq, xd, xs = oracle.quantize_act(x)
+    q = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    d = torch.empty((M, K // 32), dtype=torch.float32, device=DEV)
+    S = torch.empty((M, K // 32), dtype=torch.int32, device=DEV)
+    qg.qgemm_quantize_act(to_dev(x), M, K, q, d, S)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), xq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), xd.view(np.uint32))
+    assert np.array_equal(S.cpu().numpy(), xs)
+
+
+# ------------------------------------------------------------------ decoders
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+@pytest.mark.parametrize("kind", ["packed", "random", "random_subnormal"])
+def test_dequant_bitexact(fmt, kind):
+    N, K = 33, 768
+    if kind == "packed":
+        W = synth.pack(fmt, synth.normal(520 + fmt, (N, K), 0.0, 0.02))
+    elif kind == "random":
+        W = synth.random_blocks(fmt, N, K, seed=521 + fmt, emin=1, emax=30)
+    else:
+        W = synth.random_blocks(fmt, N, K, seed=522 + fmt, emin=0, emax=3)
+    w = torch.empty((N, K), dtype=torch.float32, device=DEV)
+    qg.qgemm_dequant(to_dev(W), fmt, N, K, w)
+    torch.cuda.synchronize()
+    ref = oracle.dequant(fmt, W, N, K).astype(np.float32)
+    got = w.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+        f"{np.sum(got != ref)} of {got.size} decoded weights differ"
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+@pytest.mark.parametrize("shape", [(37, 45, 512), (64, 64, 256), (1, 1, 256), (65, 97, 768)])
+def test_block_partials_bitexact(fmt, shape):
+    M, N, K = shape
+    W = synth.random_blocks(fmt, N, K, seed=530 + M + fmt, emin=1, emax=20)
+    rng = np.random.default_rng(531 + N)
+    qx = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    qx[:, ::32] = 127
+    qx[0, :] = -128
+    L = 32 if fmt == qg.QG_Q4_K else 16
+    out = torch.empty((M, N, K // L), dtype=torch.int32, device=DEV)
+    qg.qgemm_block_partials(to_dev(W), fmt, to_dev(qx), M, N, K, out)
+    torch.cuda.synchronize()
+    ref = oracle.block_partials(fmt, W, qx, N)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.sum(got != ref)} of {got.size} partials differ"
+
+
+# ------------------------------------------------------------------ GEMM: small, every element
+
+@pytest.mark.parametrize("path", [qg.QG_PATH_AUTO, qg.QG_PATH_TILED])
+@pytest.mark.parametrize("cfg_idx", [(1, 0), (2, 0), (2, 1), (2, 2)],
+                         ids=lambda c: f"config{c[0]}_{synth.CONFIGS[c[0]][c[1]].name}")
+def test_gemm_small_configs_every_element(cfg_idx, path):
+    g = synth.CONFIGS[cfg_idx[0]][cfg_idx[1]]
+    W = synth.make_weights(g)
+    x = synth.make_acts(g)
+    y = gpu_prefill(W, g.fmt, x, g.N, path)
+    ref = oracle.gemm(g.fmt, W, x, g.N)
+    tol = bound(x, np.arange(g.M), max_abs_w(g.fmt, W, g.N, g.K))
+    r = check(y, ref, tol, g.name)
+    print(f"{g.name}: max err/tol {r:.2e}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+@pytest.mark.parametrize("N", [1, 31, 33, 1000])
+def test_gemm_edge_shapes(fmt, N):
+    K = 256 if N != 33 else 1280
+    W = synth.pack(fmt, synth.normal(540 + N, (N, K), 0.0, 0.02))
+    wmax = max_abs_w(fmt, W, N, K)
+    for M in (1, 2, 3, 5, 8, 9, 63, 65, 511, 513):
+        x = synth.to_bf16_bits(synth.normal(541 + M, (M, K)))
+        ref = oracle.gemm(fmt, W, x, N)
+        tol = bound(x, np.arange(M), wmax)
+        paths = [qg.QG_PATH_TILED] + ([qg.QG_PATH_SKINNY] if M <= qg.QG_SKINNY_MAX_M else [])
+        for p in paths:
+            check(gpu_prefill(W, fmt, x, N, p), ref, tol, f"M={M} N={N} K={K} path={p}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+def test_gemm_random_blocks(fmt):
+    """Random legal blocks: negative scales, saturating codes, subnormal binary16."""
+    M, N, K = 70, 130, 512
+    W = synth.random_blocks(fmt, N, K, seed=550 + fmt, emin=0, emax=16)
+    x = synth.normal(551, (M, K))
+    ref = oracle.gemm(fmt, W, x, N)
+    tol = bound(x, np.arange(M), max_abs_w(fmt, W, N, K))
+    for p in (qg.QG_PATH_TILED,):
+        check(gpu_prefill(W, fmt, x, N, p), ref, tol, f"random blocks path={p}")
+    check(gpu_prefill(W, fmt, x[:7].copy(), N, qg.QG_PATH_SKINNY), ref[:7], tol[:7], "skinny")
+
+
+# ------------------------------------------------------------------ exact cases
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+@pytest.mark.parametrize("path", [qg.QG_PATH_TILED, qg.QG_PATH_SKINNY])
+def test_textbook_integer_matmul_exact(fmt, path):
+    M = 37 if path == qg.QG_PATH_TILED else 8
+    N, K = 70, 1024
+    W, wv = pins._textbook_blocks(fmt, N, K, seed=560 + fmt)
+    xi = pins._integer_acts(M, K, seed=561)
+    y = gpu_prefill(W, fmt, xi.astype(np.float32), N, path)
+    exact = (xi @ wv.T).astype(np.float64)
+    assert np.array_equal(y.astype(np.float64), exact), np.abs(y - exact).max()
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+def test_worked_examples_all_ones(fmt):
+    blk, fx = pins.q4k_example_block() if fmt == qg.QG_Q4_K else pins.q6k_example_block()
+    x = np.ones((3, 256), np.float32)
+    ref = oracle.gemm(fmt, blk, x, 1)
+    for p in (qg.QG_PATH_TILED, qg.QG_PATH_SKINNY):
+        y = gpu_prefill(blk, fmt, x, 1, p)
+        tol = bound(x, np.arange(3), max_abs_w(fmt, blk, 1, 256))
+        check(y, ref, tol, f"worked example path={p}")
+        assert np.allclose(y[:, 0], float(fx["sum_w"]), rtol=1e-6)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+def test_invariants(fmt):
+    M, N, K = 100, 96, 1024
+    W = synth.pack(fmt, synth.normal(570 + fmt, (N, K), 0.0, 0.02))
+    x = synth.normal(571, (M, K))
+    y = gpu_prefill(W, fmt, x, N, qg.QG_PATH_TILED)
+    # run-to-run identity (no atomics, fixed order)
+    assert np.array_equal(y, gpu_prefill(W, fmt, x, N, qg.QG_PATH_TILED))
+    # a row depends only on its own input row: any split of M gives identical rows
+    ys = np.concatenate([gpu_prefill(W, fmt, x[a:b].copy(), N, qg.QG_PATH_TILED)
+                         for a, b in ((0, 33), (33, 34), (34, 100))])
+    assert np.array_equal(ys, y)
+    # power-of-two scaling of x scales y exactly
+    for k in (-7, 3):
+        xs = (x * np.float32(2.0 ** k)).astype(np.float32)
+        assert np.array_equal(gpu_prefill(W, fmt, xs, N, qg.QG_PATH_TILED), y * np.float32(2.0 ** k))
+    # zero rows give zero outputs
+    xz = x.copy(); xz[5] = 0
+    assert np.all(gpu_prefill(W, fmt, xz, N, qg.QG_PATH_TILED)[5] == 0)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+def test_lm_head_matches_prefill_last_row(fmt):
+    M, N, K = 40, 500, 1024
+    W = synth.pack(fmt, synth.normal(580 + fmt, (N, K), 0.0, 0.02))
+    x = synth.to_bf16_bits(synth.normal(581, (M, K)))
+    y = gpu_prefill(W, fmt, x, N)
+    xd = to_dev(x)
+    ws = qg.alloc_workspace(1, K, DEV)
+    yl = torch.empty(N, dtype=torch.float32, device=DEV)
+    qg.qgemm_lm_head(to_dev(W), fmt, xd[M - 1], N, K, yl, ws)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(fmt, W, x, N, rows=[M - 1])
+    tol = bound(x, [M - 1], max_abs_w(fmt, W, N, K))
+    check(yl.cpu().numpy()[None], ref, tol, "lm_head")
+    check(y[M - 1:M], ref, tol, "prefill last row")
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+
+def _full_cases():
+    out = []
+    for cfg in (2, 3, 4, 5):
+        for i, g in enumerate(synth.CONFIGS[cfg]):
+            out.append(pytest.param(g, id=f"config{cfg}_{g.name}"))
+    return out
+
+
+@pytest.mark.parametrize("g", _full_cases())
+def test_full_size_sampled(g):
+    W = synth.make_weights(g)
+    x = synth.make_acts(g)
+    y = gpu_prefill(W, g.fmt, x, g.N)
+    rng = np.random.default_rng(g.w_seed)
+    rows = np.unique(np.concatenate([[0, g.M - 1], rng.integers(0, g.M, 6)]))
+    cols = np.unique(np.concatenate([[0, g.N - 1], rng.integers(0, g.N, 96)]))
+    ref = oracle.gemm(g.fmt, W, x, g.N, rows=rows, cols=cols)
+    tol = bound(x, rows, max_abs_w(g.fmt, W, g.N, g.K))
+    r = check(y[np.ix_(rows, cols)], ref, tol, g.name)
+    print(f"{g.name}: max err/tol {r:.2e}")
