@@ -19,12 +19,29 @@
 
 namespace qg {
 
-template <int XDT>
+// Split an fp32 value exactly into three bfloat16 pieces by truncation: each
+// piece keeps the top 8 significant bits of what is left, so p0 + p1 + p2 == v
+// for every v whose last piece is not below the fp32 normal range.
+__device__ __forceinline__ void split3_bf16(float v, uint16_t& p0, uint16_t& p1, uint16_t& p2) {
+  const uint32_t b0 = __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u;
+  const float r1 = v - __builtin_bit_cast(float, b0);  // exact
+  const uint32_t b1 = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+  const float r2 = r1 - __builtin_bit_cast(float, b1);  // exact
+  p0 = static_cast<uint16_t>(b0 >> 16);
+  p1 = static_cast<uint16_t>(b1 >> 16);
+  p2 = static_cast<uint16_t>(__builtin_bit_cast(uint32_t, r2) >> 16);
+}
+
+// WS: write the GEMM workspace (q, dx, dS, dsp); otherwise the test-hook
+// layout (q [M][K], d [M][K/32], S [M][K/32] int32).
+template <int XDT, bool WS>
 __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ x, int64_t M,
                                                         int64_t K, int8_t* __restrict__ q,
-                                                        float* __restrict__ d, int64_t d_sb,
-                                                        int64_t d_sm, int32_t* __restrict__ S_int,
-                                                        float* __restrict__ dS) {
+                                                        float* __restrict__ d,
+                                                        int32_t* __restrict__ S_int,
+                                                        float* __restrict__ dS,
+                                                        uint16_t* __restrict__ dsp,
+                                                        float* __restrict__ dxT, int64_t Mp) {
   const int64_t per_row = K / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= M * per_row) return;  // whole groups of four lanes leave together
@@ -78,25 +95,49 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
 
   *reinterpret_cast<uint2*>(q + row * K + 8 * c8) = make_uint2(packed[0], packed[1]);
   if ((c8 & 3) == 0) {
-    const int64_t o = b * d_sb + row * d_sm;
-    d[o] = dv;
-    if (S_int) S_int[o] = s;
-    if (dS) dS[o] = dv * static_cast<float>(s);
+    const int64_t nb = K / 32;
+    if (WS) {
+      const float ds = dv * static_cast<float>(s);
+      d[row * nb + b] = dv;
+      dxT[b * Mp + row] = dv;
+      dS[row * nb + b] = ds;
+      uint16_t p0, p1, p2;
+      split3_bf16(ds, p0, p1, p2);
+      uint16_t* o = dsp + ((row * (K / 256) + (b >> 3)) * 3) * 8 + (b & 7);
+      o[0] = p0;
+      o[8] = p1;
+      o[16] = p2;
+    } else {
+      d[row * nb + b] = dv;
+      S_int[row * nb + b] = s;
+    }
   }
 }
 
 }  // namespace qg
 
-hipError_t qg_launch_act_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
-                               float* d, int64_t d_sb, int64_t d_sm, int32_t* S_int, float* dS,
-                               hipStream_t stream) {
-  const int64_t threads = M * (K / 8);
-  const int64_t blocks = (threads + 255) / 256;
+hipError_t qg_launch_act_quant_ws(const void* x, int x_dtype, int64_t M, int64_t K,
+                                  const QgWorkspace& ws, hipStream_t stream) {
+  const int64_t blocks = (M * (K / 8) + 255) / 256;
+  const dim3 g(static_cast<unsigned>(blocks));
   if (x_dtype == QG_BF16)
-    qg::act_quant_kernel<QG_BF16><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-        x, M, K, q, d, d_sb, d_sm, S_int, dS);
+    qg::act_quant_kernel<QG_BF16, true><<<g, dim3(256), 0, stream>>>(x, M, K, ws.q, ws.dx, nullptr,
+                                                                     ws.dS, ws.dsp, ws.dxT, ws.Mp);
   else
-    qg::act_quant_kernel<QG_F32><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-        x, M, K, q, d, d_sb, d_sm, S_int, dS);
+    qg::act_quant_kernel<QG_F32, true><<<g, dim3(256), 0, stream>>>(x, M, K, ws.q, ws.dx, nullptr,
+                                                                    ws.dS, ws.dsp, ws.dxT, ws.Mp);
+  return hipGetLastError();
+}
+
+hipError_t qg_launch_act_quant_hook(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
+                                    float* d, int32_t* S, hipStream_t stream) {
+  const int64_t blocks = (M * (K / 8) + 255) / 256;
+  const dim3 g(static_cast<unsigned>(blocks));
+  if (x_dtype == QG_BF16)
+    qg::act_quant_kernel<QG_BF16, false><<<g, dim3(256), 0, stream>>>(x, M, K, q, d, S, nullptr,
+                                                                      nullptr, nullptr, 0);
+  else
+    qg::act_quant_kernel<QG_F32, false><<<g, dim3(256), 0, stream>>>(x, M, K, q, d, S, nullptr,
+                                                                     nullptr, nullptr, 0);
   return hipGetLastError();
 }

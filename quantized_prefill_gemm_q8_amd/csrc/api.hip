@@ -18,7 +18,7 @@ int64_t padded_rows(int64_t M) { return (M + qg::kRowPad - 1) / qg::kRowPad * qg
 
 // Byte offsets of the workspace sections, each 256-byte aligned.
 struct Layout {
-  int64_t Mp, q_off, dx_off, ds_off, total;
+  int64_t Mp, q_off, dx_off, dxt_off, ds_off, dsp_off, total;
 };
 
 bool layout_for(int64_t M, int64_t K, Layout* L) {
@@ -28,9 +28,11 @@ bool layout_for(int64_t M, int64_t K, Layout* L) {
   if (Mp > (INT64_C(1) << 40) / K) return false;
   L->Mp = Mp;
   L->q_off = 0;
-  L->dx_off = Mp * K;                       // multiple of 256*256
-  L->ds_off = L->dx_off + Mp * (K / 32) * 4;
-  L->total = L->ds_off + Mp * (K / 32) * 4;
+  L->dx_off = Mp * K;                          // every section is a multiple of 256 bytes
+  L->dxt_off = L->dx_off + Mp * (K / 32) * 4;
+  L->ds_off = L->dxt_off + Mp * (K / 32) * 4;
+  L->dsp_off = L->ds_off + Mp * (K / 32) * 4;
+  L->total = L->dsp_off + Mp * (K / 32) * 3 * 2;
   return true;
 }
 
@@ -76,8 +78,10 @@ static QgWorkspace carve(void* workspace, const Layout& L) {
   uint8_t* base = static_cast<uint8_t*>(workspace);
   QgWorkspace ws;
   ws.q = reinterpret_cast<int8_t*>(base + L.q_off);
-  ws.dxT = reinterpret_cast<float*>(base + L.dx_off);
-  ws.dST = reinterpret_cast<float*>(base + L.ds_off);
+  ws.dx = reinterpret_cast<float*>(base + L.dx_off);
+  ws.dxT = reinterpret_cast<float*>(base + L.dxt_off);
+  ws.dS = reinterpret_cast<float*>(base + L.ds_off);
+  ws.dsp = reinterpret_cast<uint16_t*>(base + L.dsp_off);
   ws.Mp = L.Mp;
   return ws;
 }
@@ -100,8 +104,7 @@ int qgemm_quantize_workspace(const void* x, int x_dtype, int64_t M, int64_t K, v
   rc = check_device();
   if (rc) return rc;
   const QgWorkspace ws = carve(workspace, L);
-  return launch_status(qg_launch_act_quant(x, x_dtype, M, K, ws.q, ws.dxT, L.Mp, 1, nullptr,
-                                           ws.dST, static_cast<hipStream_t>(stream)));
+  return launch_status(qg_launch_act_quant_ws(x, x_dtype, M, K, ws, static_cast<hipStream_t>(stream)));
 }
 
 int qgemm_gemm_quantized(const void* q_weights, int fmt, const void* workspace,
@@ -124,8 +127,9 @@ int qgemm_gemm_quantized(const void* q_weights, int fmt, const void* workspace,
   const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && M <= QG_SKINNY_MAX_M);
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return launch_status(skinny ? qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s)
-                              : qg_launch_gemm_tiled(W, fmt, ws, M, N, K, y, s));
+  if (skinny) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
+  return launch_status(fmt == QG_Q4_K ? qg_launch_gemm_q4k(W, ws, M, N, K, y, s)
+                                      : qg_launch_gemm_q6k(W, ws, M, N, K, y, s));
 }
 
 int qgemm_prefill_ex(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M,
@@ -184,8 +188,8 @@ int qgemm_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int8_t*
   if (!aligned(x, 16) || !aligned(q, 8) || !aligned(d, 4) || !aligned(S, 4)) return QG_EALIGN;
   int rc = check_device();
   if (rc) return rc;
-  return launch_status(qg_launch_act_quant(x, x_dtype, M, K, q, d, 1, K / 32, S, nullptr,
-                                           static_cast<hipStream_t>(stream)));
+  return launch_status(qg_launch_act_quant_hook(x, x_dtype, M, K, q, d, S,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int qgemm_dequant(const void* q_weights, int fmt, int64_t N, int64_t K, float* w, void* stream) {

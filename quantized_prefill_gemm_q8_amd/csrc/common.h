@@ -14,6 +14,7 @@ namespace qg {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kQ4Bytes = 144;  // bytes per Q4_K super-block (256 values)
 constexpr int kQ6Bytes = 210;  // bytes per Q6_K super-block (256 values)
@@ -51,6 +52,15 @@ __device__ __forceinline__ Q4Scales unpack_q4_scales(uint32_t s0, uint32_t s1, u
 }
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
 
+// Byte j (0..7) of the eight-byte value hi:lo, for a run-time j.  Written as a
+// bitwise select on values so the compiler never spills the pair to memory to
+// index it.
+__device__ __forceinline__ uint32_t sub_byte(uint32_t lo, uint32_t hi, int j) {
+  const uint32_t mask = 0u - static_cast<uint32_t>(j >> 2);  // all ones when j >= 4
+  const uint32_t w = lo ^ ((lo ^ hi) & mask);
+  return __builtin_amdgcn_ubfe(w, 8 * (j & 3), 8);
+}
+
 // Q6_K codes arrive as bytes q6 in [0, 63]; the matrix core wants the signed
 // value q6 - 32 in every byte.  Setting bit 7 first keeps the per-byte
 // subtraction from borrowing into the next byte; flipping bit 7 back leaves
@@ -78,19 +88,32 @@ __device__ __forceinline__ uint16_t load_u16(const uint8_t* p) {
 
 }  // namespace qg
 
-// ---- host-side launchers (defined in the kernel sources) ----
+// ---- workspace: the quantised activations, as the GEMM kernels read them ----
+//   q   [Mp][K]             int8 codes
+//   dx  [Mp][K/32]          fp32 block scales, row-major
+//   dxT [K/32][Mp]          the same scales, block-major
+//   dS  [Mp][K/32]          fp32 dx * S (scaled block sums), row-major
+//   dsp [Mp][K/256][3][8]   dS split exactly into three bfloat16 pieces
+//                           (dS = p0 + p1 + p2), grouped per super-block
+// Mp is M rounded up to kRowPad; rows M..Mp-1 are never written and only ever
+// feed output rows that are discarded.
 struct QgWorkspace {
-  int8_t* q;    // [Mp][K] int8 codes
-  float* dxT;   // [K/32][Mp] activation block scales, block-major
-  float* dST;   // [K/32][Mp] d * S per block (fp32), block-major
-  int64_t Mp;   // padded row count
+  int8_t* q;
+  float* dx;
+  float* dxT;
+  float* dS;
+  uint16_t* dsp;
+  int64_t Mp;
 };
 
-hipError_t qg_launch_act_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
-                               float* d, int64_t d_sb, int64_t d_sm, int32_t* S_int,
-                               float* dS, hipStream_t stream);
-hipError_t qg_launch_gemm_tiled(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
-                                int64_t N, int64_t K, float* y, hipStream_t stream);
+hipError_t qg_launch_act_quant_ws(const void* x, int x_dtype, int64_t M, int64_t K,
+                                  const QgWorkspace& ws, hipStream_t stream);
+hipError_t qg_launch_act_quant_hook(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
+                                    float* d, int32_t* S, hipStream_t stream);
+hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream);
+hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream);
 hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
                                  int64_t N, int64_t K, float* y, hipStream_t stream);
 hipError_t qg_launch_dequant(const uint8_t* W, int fmt, int64_t N, int64_t K, float* w,

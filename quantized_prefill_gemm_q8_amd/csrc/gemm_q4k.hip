@@ -1,0 +1,287 @@
+// Tiled prefill GEMM for Q4_K weights on the int8 matrix cores (gfx950).
+//
+// The fused design of sparkinfer PR #464 ("fused Q4K/Q6K->int8 dequant ...",
+// section "Summary": super-blocks decoded in registers, an int8 tensor-core
+// GEMM, no wider dequantised scratch), carried to CDNA4 without that page's
+// second per-row weight quantisation: the 4-bit codes go to the matrix core as
+// they are and every sub-block's own scale and min are applied afterwards.
+//
+// Per 32-value activation block b of row m and weight row n (sub-block j of
+// super-block sb):
+//   I = sum_t q[n][t] * qx[m][t]                        int8 MFMA, int32
+//   y[m][n] += dx[m][b] * (d*sc[n][j]) * I              scale term, fp32
+//   y[m][n] -= dmin[n][sb] * sum_j m[n][j] * dS[m][b]   min term, per super-block
+//
+// Scale term -- two vector-ALU instructions per output element and block:
+//   * Weights sit on the lane axis (column n = lane % 32 of a 32x32 tile), so
+//     dsc = d*sc is one scalar per lane.  dsc has at most 17 significant bits
+//     (binary16 d times a 6-bit integer), hence c = -12582912*dsc is exact in
+//     fp32.  The MFMA accumulator starts at the bit pattern of 12582912.0f, so
+//     its int32 result reads as the float 12582912 + I, and fma(f, dsc, c) is
+//     exactly fl(I * dsc).
+//   * The activation scale dx differs per output row, i.e. per accumulator
+//     element.  Instead of one register per element, every lane holds the
+//     scale of one row and the accumulate is v_fmac_f32 with a DPP
+//     row_newbcast operand: element r of every 16-lane DPP row reads the value
+//     held by lane r of that row, which is arranged to be the scale of
+//     element r's output row.
+// Min term -- on the matrix core: the mins m are 6-bit integers (exact in
+// bfloat16) and dS = dx*S is split exactly into three bfloat16 pieces by the
+// activation quantiser, so two K=16 bf16 MFMAs per tile and super-block give
+// sum_j m_j * dS_j to fp32 accuracy; one FMA per element then applies -dmin.
+#include "common.h"
+#include "mfma_epilogue.h"
+
+namespace qg {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The eight 6-bit mins of a super-block as bfloat16 integers (exact): two
+// dwords m[0..3], m[4..7] of bytes -> four dwords of bf16 pairs.
+__device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t src = i < 2 ? m_lo : m_hi;
+    const float f0 = static_cast<float>(byte_of(src, 2 * (i & 1)));
+    const float f1 = static_cast<float>(byte_of(src, 2 * (i & 1) + 1));
+    // high halves of the two floats: integers below 256 are exact in bf16
+    w[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0),
+                                 0x07060302u);
+  }
+  return __builtin_bit_cast(v8bf, v4i{int(w[0]), int(w[1]), int(w[2]), int(w[3])});
+}
+
+// ---------------------------------------------------------------- LDS-staged kernel
+//
+// WM x WN waves share super-block stages in LDS; each wave owns TM x TN tiles
+// of 32x32 outputs.  One stage (256 values of K) holds, for the BM activation
+// rows and BN weight rows of the workgroup:
+//   A   [BM][256]  int8 codes; each row's sixteen 16-byte chunks are XOR-
+//                  swizzled by (row % 16) so that 16 lanes reading 16 rows at
+//                  the same column hit 16 different bank groups
+//   W   [BN][144]  raw Q4_K blocks (the 144-byte stride already spreads 16
+//                  consecutive rows over distinct bank groups)
+//   DX  [BM][8]    fp32 activation block scales
+//   DSP [BM][3][8] bfloat16 pieces of dS
+// Stages are filled by global_load_lds_dwordx4 (global memory straight into
+// LDS) in a two-deep ring: the loads for super-block sb+1 are in flight while
+// sb is computed, with one workgroup barrier per stage.
+// DPP: activation scales staged row-major and applied with the DPP-broadcast
+// epilogue; otherwise staged block-major ([8][BM], from dxT) and read as 16
+// per-element values per tile (four 16-byte broadcast reads).
+template <int TM, int TN, int WM, int WN, bool DPP>
+__global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
+    const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ y) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
+  constexpr int A_BYTES = BM * 256, W_BYTES = BN * kQ4Bytes, X_BYTES = BM * 32, P_BYTES = BM * 48;
+  constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES + P_BYTES;
+  constexpr int A_CH = A_BYTES / 16, W_CH = W_BYTES / 16, X_CH = X_BYTES / 16, P_CH = P_BYTES / 16;
+  constexpr int CH = A_CH + W_CH + X_CH + P_CH;
+  static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0 && P_CH % 64 == 0,
+                "stage regions must be whole wave loads");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
+  const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * BN;
+  const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
+  const int64_t nsb = K / 256, nb = K / 32;
+  const int64_t wrow_bytes = nsb * kQ4Bytes;
+  const int drow = dpp_scale_row(lane);
+
+  auto issue_stage = [&](int64_t sb, int buf) {
+    uint8_t* base = lds + buf * STAGE;
+    for (int q0 = wave * 64; q0 < CH; q0 += NT) {  // region tests are uniform per wave
+      const int q = q0 + lane;
+      const void* src;
+      if (q0 < A_CH) {
+        const int row = q >> 4, pos = q & 15, c16 = pos ^ (row & 15);
+        int64_t m = m_cta + row;
+        m = m < M ? m : M - 1;
+        src = qx + m * K + sb * 256 + 16 * c16;
+      } else if (q0 < A_CH + W_CH) {
+        const int qq = q - A_CH, row = qq / 9, part = qq - 9 * row;
+        int64_t n = n_cta + row;
+        n = n < N ? n : N - 1;
+        src = W + n * wrow_bytes + sb * kQ4Bytes + 16 * part;
+      } else if (q0 < A_CH + W_CH + X_CH) {
+        const int qq = q - A_CH - W_CH;
+        if (DPP) {
+          const int row = qq >> 1, half = qq & 1;
+          src = dx + (m_cta + row) * nb + 8 * sb + 4 * half;
+        } else {
+          const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
+          src = dxT + (8 * sb + jb) * Mp + m_cta + 4 * r4;
+        }
+      } else {
+        const int qq = q - A_CH - W_CH - X_CH, row = qq / 3, piece = qq - 3 * row;
+        src = dsp + ((m_cta + row) * nsb + sb) * 24 + 8 * piece;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(base + 16 * q0), 16, 0, 0);
+    }
+  };
+
+  v16i magic;
+#pragma unroll
+  for (int r = 0; r < 16; r++) magic[r] = kMagicBits;
+  float acc[TM][TN][16];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  issue_stage(0, 0);
+  for (int64_t sb = 0; sb < nsb; sb++) {
+    const int buf = static_cast<int>(sb & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads for stage sb have landed
+    __syncthreads();                     // ... and every wave's; stage sb-1 is no longer read
+    if (sb + 1 < nsb) issue_stage(sb + 1, buf ^ 1);
+
+    const uint8_t* sA = lds + buf * STAGE;
+    const uint8_t* sW = sA + A_BYTES;
+    const float* sX = reinterpret_cast<const float*>(sW + W_BYTES);
+    const uint8_t* sP = sW + W_BYTES + X_BYTES;
+
+    float d[TN], dmin[TN];
+    Q4Scales sc[TN];
+    const uint8_t* wr[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      wr[j] = sW + (nl0 + 32 * j + l32) * kQ4Bytes;
+      const uint4 hdr = *reinterpret_cast<const uint4*>(wr[j]);
+      d[j] = half_to_float(hdr.x & 0xFFFFu);
+      dmin[j] = half_to_float(hdr.x >> 16);
+      sc[j] = unpack_q4_scales(hdr.y, hdr.z, hdr.w);
+    }
+    float dxr[TM][8];
+    if (DPP) {
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const float4* p = reinterpret_cast<const float4*>(sX + (ml0 + 32 * i + drow) * 8);
+        const float4 v0 = p[0], v1 = p[1];
+        dxr[i][0] = v0.x; dxr[i][1] = v0.y; dxr[i][2] = v0.z; dxr[i][3] = v0.w;
+        dxr[i][4] = v1.x; dxr[i][5] = v1.y; dxr[i][6] = v1.z; dxr[i][7] = v1.w;
+      }
+    }
+
+#pragma unroll(NW >= 12 ? 1 : 4)
+    for (int c = 0; c < 4; c++) {
+      uint4 wraw[TN];
+#pragma unroll
+      for (int j = 0; j < TN; j++) wraw[j] = *reinterpret_cast<const uint4*>(wr[j] + 16 + 32 * c + 16 * h);
+      v4i a[TM][2];
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const int row = ml0 + 32 * i + l32;
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+          const int pos = (2 * (2 * c + e) + h) ^ (row & 15);
+          a[i][e] = *reinterpret_cast<const v4i*>(sA + row * 256 + 16 * pos);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        const int jb = 2 * c + e;
+        v4i b[TN];
+        float dsc[TN], cc[TN];
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+          b[j] = q4_codes(wraw[j], e);
+          dsc[j] = d[j] * static_cast<float>(sub_byte(sc[j].sc_lo, sc[j].sc_hi, jb));
+          cc[j] = -kMagic * dsc[j];
+        }
+        v16i D[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+          for (int j = 0; j < TN; j++)
+            D[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][e], b[j], magic, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+          if (DPP) {
+            // dxr[i][jb] with a run-time jb when the loop is not unrolled
+            float xs = dxr[i][0];
+#pragma unroll
+            for (int t = 1; t < 8; t++) xs = jb == t ? dxr[i][t] : xs;
+#pragma unroll
+            for (int j = 0; j < TN; j++) epilogue_scale(acc[i][j], D[i][j], dsc[j], cc[j], xs);
+          } else {
+            float dxv[16];
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+              const float4 v = *reinterpret_cast<const float4*>(sX + jb * BM + ml0 + 32 * i + 8 * g + 4 * h);
+              dxv[4 * g] = v.x; dxv[4 * g + 1] = v.y; dxv[4 * g + 2] = v.z; dxv[4 * g + 3] = v.w;
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+#pragma unroll
+              for (int r = 0; r < 16; r++) {
+                const float u = __builtin_fmaf(bits_to_float(D[i][j][r]), dsc[j], cc[j]);  // fl(I*dsc)
+                acc[i][j][r] = __builtin_fmaf(u, dxv[r], acc[i][j][r]);
+              }
+          }
+        }
+      }
+    }
+    // min term of the super-block on the matrix core
+    v8bf mb[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) mb[j] = mins_bf16(sc[j].m_lo, sc[j].m_hi);
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+      const uint8_t* prow = sP + (ml0 + 32 * i + l32) * 48;
+      const v8bf p01 = *reinterpret_cast<const v8bf*>(prow + 16 * h);  // piece 0 (h=0) / 1 (h=1)
+      v8bf p2z = *reinterpret_cast<const v8bf*>(prow + 32);           // piece 2 (h=0) / zero (h=1)
+      if (h) p2z = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        v16f T = {};
+        T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p01, mb[j], T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2z, mb[j], T, 0, 0, 0);
+        const float nd = -dmin[j];
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[i][j][r] = __builtin_fmaf(T[r], nd, acc[i][j][r]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < TN; j++) {
+    const int64_t n = n_cta + nl0 + 32 * j + l32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t m = m_cta + ml0 + 32 * i + acc_row(r, h);
+        if (m < M) y[m * N + n] = acc[i][j][r];
+      }
+  }
+}
+
+template <int TM, int TN, int WM, int WN, bool DPP>
+static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
+                       float* y, hipStream_t stream) {
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
+  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP><<<grid, dim3(64 * WM * WN), 0, stream>>>(
+      W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+}
+
+}  // namespace qg
+
+hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream) {
+  qg::launch_lds<2, 2, 2, 4, false>(W, ws, M, N, K, y, stream);
+  return hipGetLastError();
+}

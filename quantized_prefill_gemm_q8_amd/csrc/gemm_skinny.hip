@@ -27,9 +27,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int MR>
 __global__ __launch_bounds__(256) void skinny_q4k_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ qx,
-                                                         const float* __restrict__ dxT,
-                                                         const float* __restrict__ dST,
-                                                         int64_t Mp, int64_t N, int64_t K,
+                                                         const float* __restrict__ dx,
+                                                         const float* __restrict__ dS,
+                                                         int64_t N, int64_t K,
                                                          float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void skinny_q4k_kernel(const uint8_t* __restri
       I = dot4(w[1], a0.y, I); I = dot4(w[2], a0.z, I); I = dot4(w[3], a0.w, I);
       I = dot4(w[4], a1.x, I); I = dot4(w[5], a1.y, I); I = dot4(w[6], a1.z, I);
       I = dot4(w[7], a1.w, I);
-      const float dx = dxT[b * Mp + m], ds = dST[b * Mp + m];
-      acc[m] = __builtin_fmaf(dsc * static_cast<float>(I), dx, acc[m]);
+      const float dxm = dx[m * nb + b], ds = dS[m * nb + b];
+      acc[m] = __builtin_fmaf(dsc * static_cast<float>(I), dxm, acc[m]);
       acc[m] = __builtin_fmaf(-dmn, ds, acc[m]);
     }
   }
@@ -78,8 +78,8 @@ __global__ __launch_bounds__(256) void skinny_q4k_kernel(const uint8_t* __restri
 template <int MR>
 __global__ __launch_bounds__(256) void skinny_q6k_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ qx,
-                                                         const float* __restrict__ dxT,
-                                                         int64_t Mp, int64_t N, int64_t K,
+                                                         const float* __restrict__ dx,
+                                                         int64_t N, int64_t K,
                                                          float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void skinny_q6k_kernel(const uint8_t* __restri
       int Ib = dot4(w[4], a1.x, 0);
       Ib = dot4(w[5], a1.y, Ib); Ib = dot4(w[6], a1.z, Ib); Ib = dot4(w[7], a1.w, Ib);
       const float t = __builtin_fmaf(sa, static_cast<float>(Ia), sbv * static_cast<float>(Ib));
-      acc[m] = __builtin_fmaf(t, dxT[b * Mp + m], acc[m]);
+      acc[m] = __builtin_fmaf(t, dx[m * nb + b], acc[m]);
     }
   }
 #pragma unroll
@@ -131,9 +131,9 @@ static void launch_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int6
                           int64_t K, float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((N + 3) / 4));
   if (fmt == QG_Q4_K)
-    skinny_q4k_kernel<MR><<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dxT, ws.dST, ws.Mp, N, K, y);
+    skinny_q4k_kernel<MR><<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
   else
-    skinny_q6k_kernel<MR><<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, N, K, y);
+    skinny_q6k_kernel<MR><<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dx, N, K, y);
 }
 
 }  // namespace qg

@@ -1,0 +1,76 @@
+// Shared pieces of the int8-MFMA GEMM kernels: the 32x32 accumulator layout,
+// the weight-fragment decoders and the fp32 scale epilogue with a
+// DPP-broadcast activation scale.
+//
+// v_mfma_i32_32x32x32_i8 and v_mfma_i32_32x32x16_i8 split their K between the
+// two lane halves; A (activations) and B (weights) use the same assignment of
+// k to (lane half, byte), so any consistent assignment of a sub-block's values
+// to bytes gives the same dot product.
+#pragma once
+
+#include "common.h"
+
+namespace qg {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Row (0..31) of a 32x32 MFMA output tile held in accumulator element r by a
+// lane in half h of the wave.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Row whose activation scale a lane supplies for the DPP broadcast: lane k of
+// each 16-lane DPP row holds the scale of element k's output row.
+__device__ __forceinline__ int dpp_scale_row(int lane) { return acc_row(lane & 15, lane >> 5); }
+
+// acc[r] += dxr(broadcast from lane r of this DPP row) * u[r], r = 0..15.
+// The statements are not volatile, so the scheduler may interleave them with
+// other work (the next tile's MFMAs, LDS reads).  DPP reads of a VGPR written
+// by a VALU instruction need two wait states; dxr is written at most once
+// before the sixteen reads, and the s_nop in front of the first read covers it.
+#define QG_FMAC_DPP(R, PRE)                                                            \
+  asm(PRE "v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #R                                 \
+      " row_mask:0xf bank_mask:0xf bound_ctrl:1"                                        \
+      : "+v"(acc[R]) : "v"(dxr), "v"(u[R]))
+
+__device__ __forceinline__ void epilogue_scale(float (&acc)[16], const v16i& D, float dsc, float cc,
+                                               float dxr) {
+  float u[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) u[r] = __builtin_fmaf(bits_to_float(D[r]), dsc, cc);  // fl(I*dsc)
+  QG_FMAC_DPP(0, "s_nop 1\n\t"); QG_FMAC_DPP(1, ""); QG_FMAC_DPP(2, ""); QG_FMAC_DPP(3, "");
+  QG_FMAC_DPP(4, ""); QG_FMAC_DPP(5, ""); QG_FMAC_DPP(6, ""); QG_FMAC_DPP(7, "");
+  QG_FMAC_DPP(8, ""); QG_FMAC_DPP(9, ""); QG_FMAC_DPP(10, ""); QG_FMAC_DPP(11, "");
+  QG_FMAC_DPP(12, ""); QG_FMAC_DPP(13, ""); QG_FMAC_DPP(14, ""); QG_FMAC_DPP(15, "");
+}
+#undef QG_FMAC_DPP
+
+// Q4_K: the 16 codes of sub-block j (j = 2c or 2c+1) for lane half h.  Bytes
+// qs[32c + 16h .. +15] hold sub-block 2c in their low nibbles and 2c+1 in their
+// high nibbles; raw holds those 16 bytes.
+__device__ __forceinline__ v4i q4_codes(const uint4& raw, int high) {
+  const int sh = 4 * high;
+  return v4i{int((raw.x >> sh) & 0x0F0F0F0Fu), int((raw.y >> sh) & 0x0F0F0F0Fu),
+             int((raw.z >> sh) & 0x0F0F0F0Fu), int((raw.w >> sh) & 0x0F0F0F0Fu)};
+}
+
+// Q6_K: 8 codes, as signed bytes q6 - 32, of 16-value sub-block s for lane half
+// h: values v = 16s + 8h + i, i < 8.  With half = s/8, quarter c = (s%8)/2 and
+// l0 = 16*(s%2) + 8h, the low nibbles are ql[64*half + 32*(c%2) + l0 + i] (low
+// nibble for c < 2, high for c >= 2) and the top two bits are bits (2c, 2c+1)
+// of qh[32*half + l0 + i].  blk is the block's first byte in global memory.
+__device__ __forceinline__ long q6_codes(const uint8_t* blk, int s, int h) {
+  const int half = s >> 3, c = (s & 7) >> 1, l0 = 16 * (s & 1) + 8 * h;
+  const uint8_t* pl = blk + 64 * half + 32 * (c & 1) + l0;
+  const uint8_t* ph = blk + 128 + 32 * half + l0;
+  uint32_t lo0 = load_u32_a2(pl), lo1 = load_u32_a2(pl + 4);
+  uint32_t hi0 = load_u32_a2(ph), hi1 = load_u32_a2(ph + 4);
+  const int ls = (c >> 1) * 4, hs = 2 * c;
+  lo0 = (lo0 >> ls) & 0x0F0F0F0Fu;
+  lo1 = (lo1 >> ls) & 0x0F0F0F0Fu;
+  hi0 = ((hi0 >> hs) & 0x03030303u) << 4;
+  hi1 = ((hi1 >> hs) & 0x03030303u) << 4;
+  const uint32_t w0 = q6_to_signed(lo0 | hi0), w1 = q6_to_signed(lo1 | hi1);
+  return static_cast<long>((static_cast<uint64_t>(w1) << 32) | w0);
+}
+
+}  // namespace qg

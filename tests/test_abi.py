@@ -42,10 +42,12 @@ def test_error_strings():
 def test_workspace_bytes():
     ws = qg.qgemm_workspace_bytes
     assert ws(0, 256) == 0 and ws(1, 255) == 0 and ws(1, 300) == 0 and ws(-1, 256) == 0
-    # rows padded to 256: int8 codes plus two fp32 values per 32-value block
-    assert ws(1, 256) == 256 * 256 + 2 * 256 * 8 * 4
-    assert ws(512, 4096) == 512 * 4096 + 2 * 512 * 128 * 4
-    assert ws(513, 4096) == 768 * 4096 + 2 * 768 * 128 * 4
+    # rows padded to 256: int8 codes, three fp32 values and three bf16 pieces per
+    # 32-value block
+    per_row = lambda K: K + (K // 32) * (3 * 4 + 3 * 2)
+    assert ws(1, 256) == 256 * per_row(256)
+    assert ws(512, 4096) == 512 * per_row(4096)
+    assert ws(513, 4096) == 768 * per_row(4096)
     assert ws(1, 1 << 40) == 0          # overflow guard
 
 
