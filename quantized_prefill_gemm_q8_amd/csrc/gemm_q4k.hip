@@ -36,6 +36,26 @@ namespace qg {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// global_load_lds_dwordx4: 16 bytes per lane from global memory straight into
+// LDS; lane l writes lds_base + 16*l (lds_base is wave-uniform, passed in M0).
+// Issued from inline assembly on purpose: the compiler does not count these
+// loads, so it adds no wait for them before every LDS read (it cannot tell
+// the stage being filled from the one being read); the kernel waits for them
+// itself with an explicit vmcnt and a barrier.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds_dst)));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and its LDS reads are done, then meet the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // The eight 6-bit mins of a super-block as bfloat16 integers (exact): two
 // dwords m[0..3], m[4..7] of bytes -> four dwords of bf16 pairs.
 __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
@@ -65,12 +85,15 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 //   DX  [BM][8]    fp32 activation block scales
 //   DSP [BM][3][8] bfloat16 pieces of dS
 // Stages are filled by global_load_lds_dwordx4 (global memory straight into
-// LDS) in a two-deep ring: the loads for super-block sb+1 are in flight while
-// sb is computed, with one workgroup barrier per stage.
+// LDS) in an NS-deep ring: while super-block sb is computed, the loads of the
+// next NS-1 super-blocks are in flight; one workgroup barrier per stage.
+// Every wave issues the same number of loads per stage (the last ones of the
+// short waves land in a junk slot), so a fixed vmcnt waits for exactly one
+// stage.
 // DPP: activation scales staged row-major and applied with the DPP-broadcast
 // epilogue; otherwise staged block-major ([8][BM], from dxT) and read as 16
 // per-element values per tile (four 16-byte broadcast reads).
-template <int TM, int TN, int WM, int WN, bool DPP>
+template <int TM, int TN, int WM, int WN, bool DPP, int NS>
 __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
@@ -84,7 +107,10 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_
   constexpr int CH = A_CH + W_CH + X_CH + P_CH;
   static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0 && P_CH % 64 == 0,
                 "stage regions must be whole wave loads");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  constexpr int LPT = (CH + NT - 1) / NT;   // loads per thread per stage
+  constexpr int JUNK = 1024;                // landing slot of the padding loads
+  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE + JUNK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -99,7 +125,13 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_
 
   auto issue_stage = [&](int64_t sb, int buf) {
     uint8_t* base = lds + buf * STAGE;
-    for (int q0 = wave * 64; q0 < CH; q0 += NT) {  // region tests are uniform per wave
+#pragma unroll(LPT <= 6 ? LPT : 1)
+    for (int it = 0; it < LPT; it++) {
+      const int q0 = wave * 64 + it * NT;  // region tests are uniform per wave
+      if (q0 >= CH) {                      // padding load: same count on every wave
+        lds_dma16(qx, lds + NS * STAGE);
+        continue;
+      }
       const int q = q0 + lane;
       const void* src;
       if (q0 < A_CH) {
@@ -125,7 +157,7 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_
         const int qq = q - A_CH - W_CH - X_CH, row = qq / 3, piece = qq - 3 * row;
         src = dsp + ((m_cta + row) * nsb + sb) * 24 + 8 * piece;
       }
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(base + 16 * q0), 16, 0, 0);
+      lds_dma16(src, base + 16 * q0);
     }
   };
 
@@ -140,12 +172,18 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  issue_stage(0, 0);
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; s0++)
+    if (s0 < nsb) issue_stage(s0, s0);
   for (int64_t sb = 0; sb < nsb; sb++) {
-    const int buf = static_cast<int>(sb & 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads for stage sb have landed
-    __syncthreads();                     // ... and every wave's; stage sb-1 is no longer read
-    if (sb + 1 < nsb) issue_stage(sb + 1, buf ^ 1);
+    const int buf = static_cast<int>(sb % NS);
+    // This wave's loads of stage sb have landed once at most the loads of the
+    // NS-2 later stages are outstanding (near the end fewer are: wait for
+    // all); after the barrier every wave's have, and no wave still reads
+    // stage sb-1, whose buffer the next issue refills.
+    if (sb + NS - 1 <= nsb) wait_vm_barrier<LPT * (NS - 2)>();
+    else wait_vm_barrier<0>();
+    if (sb + NS - 1 < nsb) issue_stage(sb + NS - 1, static_cast<int>((sb + NS - 1) % NS));
 
     const uint8_t* sA = lds + buf * STAGE;
     const uint8_t* sW = sA + A_BYTES;
@@ -269,12 +307,151 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_
   }
 }
 
-template <int TM, int TN, int WM, int WN, bool DPP>
+// ---------------------------------------------------------------- small-grid kernel
+//
+// For problems whose output has too few 128x256 tiles to fill the chip (one
+// prompt ubatch through a small model's projections): one 32x32 output tile
+// per wave, and the SK waves of a workgroup split the K range of the same
+// tile between them.  Each wave loads its operands straight from global
+// memory (L2-resident) a whole super-block ahead: 8 x 16 bytes of activation
+// codes, 4 x 16 bytes of packed nibbles plus the 16-byte header, and 2 x 16
+// bytes of dS pieces.  The activation scales of its 32 rows go through a
+// wave-private LDS slice ([8][32] per super-block) and are read as 16-byte
+// broadcasts.  The partial tiles are summed through LDS in ascending wave
+// order, so the result does not depend on timing.
+struct SmallStage {
+  v4i a[8];
+  uint4 w[4], hdr;
+  v4i p01, p2;
+  float4 xs;
+};
+
+template <int SK>
+__global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) float s_x[SK][2][8 * 32];
+  __shared__ __attribute__((aligned(16))) float4 s_red[SK > 1 ? SK : 1][4][64];
+
+  const int lane = threadIdx.x & 63, kk = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 32;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int64_t nsb = K / 256;
+  const int64_t sb_begin = kk * nsb / SK, sb_end = (kk + 1) * nsb / SK;
+  int64_t m = m0 + l32, n = n0 + l32;
+  m = m < M ? m : M - 1;
+  n = n < N ? n : N - 1;
+  const int8_t* arow = qx + m * K + 16 * h;
+  const uint8_t* wrow = W + n * nsb * kQ4Bytes;
+  const uint16_t* prow = dsp + (m0 + l32) * nsb * 24;  // rows up to the padding (m0 + 31 < Mp)
+
+  auto load = [&](int64_t sb, SmallStage& st) {
+#pragma unroll
+    for (int b = 0; b < 8; b++) st.a[b] = *reinterpret_cast<const v4i*>(arow + 256 * sb + 32 * b);
+    const uint8_t* blk = wrow + sb * kQ4Bytes;
+    st.hdr = *reinterpret_cast<const uint4*>(blk);
+#pragma unroll
+    for (int c = 0; c < 4; c++) st.w[c] = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c + 16 * h);
+    st.p01 = *reinterpret_cast<const v4i*>(prow + sb * 24 + 8 * h);
+    st.p2 = *reinterpret_cast<const v4i*>(prow + sb * 24 + 16);
+    // activation scales of the 32 rows, 8 blocks: lane -> (block lane/8, rows 4*(lane%8)..+3)
+    st.xs = *reinterpret_cast<const float4*>(dxT + (8 * sb + (lane >> 3)) * Mp + m0 + 4 * (lane & 7));
+  };
+
+  v16i magic;
+#pragma unroll
+  for (int r = 0; r < 16; r++) magic[r] = kMagicBits;
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+
+  SmallStage cur, nxt;
+  if (sb_begin < sb_end) load(sb_begin, cur);
+  for (int64_t sb = sb_begin; sb < sb_end; sb++) {
+    if (sb + 1 < sb_end) load(sb + 1, nxt);
+    float* sx = s_x[kk][sb & 1];
+    *reinterpret_cast<float4*>(sx + 4 * lane) = cur.xs;  // [8][32]: block lane/8, rows 4*(lane%8)
+    const float d = half_to_float(cur.hdr.x & 0xFFFFu), dmin = half_to_float(cur.hdr.x >> 16);
+    const Q4Scales sc = unpack_q4_scales(cur.hdr.y, cur.hdr.z, cur.hdr.w);
+#pragma unroll
+    for (int jb = 0; jb < 8; jb++) {
+      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[jb], q4_codes(cur.w[jb >> 1], jb & 1),
+                                                           magic, 0, 0, 0);
+      const float dsc = d * static_cast<float>(sub_byte(sc.sc_lo, sc.sc_hi, jb));
+      const float cc = -kMagic * dsc;
+      float dxv[16];
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const float4 v = *reinterpret_cast<const float4*>(sx + jb * 32 + 8 * g + 4 * h);
+        dxv[4 * g] = v.x; dxv[4 * g + 1] = v.y; dxv[4 * g + 2] = v.z; dxv[4 * g + 3] = v.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float u = __builtin_fmaf(bits_to_float(D[r]), dsc, cc);  // fl(I*dsc)
+        acc[r] = __builtin_fmaf(u, dxv[r], acc[r]);
+      }
+    }
+    {  // min term of the super-block
+      const v8bf mb = mins_bf16(sc.m_lo, sc.m_hi);
+      const v8bf p01 = __builtin_bit_cast(v8bf, cur.p01);
+      const v8bf p2z = __builtin_bit_cast(v8bf, h ? v4i{0, 0, 0, 0} : cur.p2);
+      v16f T = {};
+      T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p01, mb, T, 0, 0, 0);
+      T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2z, mb, T, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[r] = __builtin_fmaf(T[r], -dmin, acc[r]);
+    }
+    if (sb + 1 < sb_end) cur = nxt;
+  }
+
+  const int64_t nn = n0 + l32;
+  if constexpr (SK > 1) {
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+      s_red[kk][g][lane] = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+    __syncthreads();
+    for (int g = kk; g < 4; g += SK) {
+      float4 s4 = s_red[0][g][lane];
+      for (int w = 1; w < SK; w++) {
+        const float4 v = s_red[w][g][lane];
+        s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
+      }
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      if (nn < N) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int64_t mm = m0 + acc_row(4 * g + q, h);
+          if (mm < M) y[mm * N + nn] = sv[q];
+        }
+      }
+    }
+  } else {
+    if (nn < N) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t mm = m0 + acc_row(r, h);
+        if (mm < M) y[mm * N + nn] = acc[r];
+      }
+    }
+  }
+}
+
+template <int SK>
+static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
+                         float* y, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((N + 31) / 32), static_cast<unsigned>((M + 31) / 32));
+  gemm_q4k_small_kernel<SK><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp,
+                                                                  M, N, K, y);
+}
+
+template <int TM, int TN, int WM, int WN, bool DPP, int NS>
 static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                        float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP><<<grid, dim3(64 * WM * WN), 0, stream>>>(
+  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS><<<grid, dim3(64 * WM * WN), 0, stream>>>(
       W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
 }
 
@@ -282,6 +459,25 @@ static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64
 
 hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream) {
-  qg::launch_lds<2, 2, 2, 4, false>(W, ws, M, N, K, y, stream);
+  // large grids: workgroups of 8 waves sharing 128x256 tiles through LDS;
+  // otherwise one 32x32 tile per wave with the K range split so that the chip
+  // gets about two waves per SIMD
+  constexpr int64_t kCUs = 256, kTargetWaves = 2048;
+  const int64_t nsb = K / 256;
+  if (((M + 127) / 128) * ((N + 255) / 256) >= kCUs) {
+    qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream);
+  } else if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs) {
+    qg::launch_lds<1, 1, 2, 4, false, 4>(W, ws, M, N, K, y, stream);
+  } else {
+    const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
+    if (tiles >= kTargetWaves || nsb < 2)
+      qg::launch_small<1>(W, ws, M, N, K, y, stream);
+    else if (tiles * 2 >= kTargetWaves || nsb < 4)
+      qg::launch_small<2>(W, ws, M, N, K, y, stream);
+    else if (tiles * 4 >= kTargetWaves || nsb < 8)
+      qg::launch_small<4>(W, ws, M, N, K, y, stream);
+    else
+      qg::launch_small<8>(W, ws, M, N, K, y, stream);
+  }
   return hipGetLastError();
 }
