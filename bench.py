@@ -9,10 +9,16 @@ activations, synthetic and seeded.  Each step runs the activation quantiser
 twice and the tiled int8-MFMA GEMM three times, with inputs resident in HBM.
 
 Printed: one JSON line with value = effective int8 TOPS of the step
-(2*M*N*K summed over the three projections / step time), prefill tok/s,
-the roofline of the dominant kernel (the tiled GEMM, timed per launch with HIP
-events on its stream), the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K)
-and the CPU oracle timed on the host.
+(2*M*N*K summed over the three projections / step time), prefill tok/s, the
+roofline of the dominant kernel (the GEMM kernel with the largest share of the
+step; its launches run back to back between two HIP events on its stream), the large-M headline
+projections (K=4096 -> N=24576 Q4_K and K=12288 -> N=4096 Q6_K at M=512), the
+M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K) and the CPU oracle timed on
+the host.
+
+--calib-copy-mib N additionally runs a plain elementwise copy kernel over
+N MiB (read N, write N) three times: the reference dispatch for scaling HBM
+byte counters taken with a profiler.
 """
 from __future__ import annotations
 
@@ -35,8 +41,10 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--lm-steps", type=int, default=50)
+    p.add_argument("--big-steps", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calib-copy-mib", type=int, default=0)
     return p.parse_args()
 
 
@@ -64,6 +72,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     # ---------------- workload: the small-model projection set, M = 512
     qkv, up, down = synth.CONFIGS[2]
     M = qkv.M
@@ -74,34 +85,26 @@ def main():
     ws_d = qg.alloc_workspace(M, down.K, dev)
     y = {g.name: torch.empty((M, g.N), dtype=torch.float32, device=dev) for g in (qkv, up, down)}
     step_ops = sum(g.ops for g in (qkv, up, down))
+    kname = {g.name: qg.qgemm_kernel_name(g.fmt, M, g.N, g.K, qg.QG_PATH_TILED)
+             for g in (qkv, up, down)}
 
-    gemm_events = []
-
-    def gemm(g, ws, record):
-        if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+    def gemm(g, ws):
         qg.qgemm_gemm_quantized(Wd[g.name], g.fmt, ws, M, g.N, g.K, y[g.name], stream,
                                 qg.QG_PATH_TILED)
-        if record:
-            e1.record(stream)
-            gemm_events.append((g.ops, e0, e1))
 
-    def step(record=False):
+    def step():
         qg.qgemm_quantize_workspace(x_hidden, M, qkv.K, ws_h, stream)
-        gemm(qkv, ws_h, record)
-        gemm(up, ws_h, record)
+        gemm(qkv, ws_h)
+        gemm(up, ws_h)
         qg.qgemm_quantize_workspace(x_down, M, down.K, ws_d, stream)
-        gemm(down, ws_d, record)
+        gemm(down, ws_d)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region 1: whole steps, no per-kernel events
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    t0, t1 = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
@@ -112,18 +115,55 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # timed region 2: the same steps with HIP events around every GEMM launch
-    gemm_events.clear()
-    for _ in range(args.steps):
-        step(record=True)
-    torch.cuda.synchronize()
-    g_ops = sum(o for o, _, _ in gemm_events)
-    g_ms = sum(a.elapsed_time(b) for _, a, b in gemm_events)
-    g_launches = len(gemm_events)
-    gemm_tops = g_ops / (g_ms * 1e-3) / 1e12
+    # timed region 2: per GEMM kernel, its launches of one step run back to back
+    # (same arguments, same stream) between two HIP events, repeated `steps`
+    # times: the average launch duration with no per-launch event in between
+    groups = {}
+    for g, ws in ((qkv, ws_h), (up, ws_h), (down, ws_d)):
+        groups.setdefault(kname[g.name], []).append((g, ws))
+    per_kernel = {}
+    for name, members in groups.items():
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.steps):
+            for g, ws in members:
+                gemm(g, ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_kernel[name] = {"ops": args.steps * sum(g.ops for g, _ in members),
+                            "ms": a.elapsed_time(b), "launches": args.steps * len(members)}
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
+    dk = per_kernel[dom]
+    dom_tops = dk["ops"] / (dk["ms"] * 1e-3) / 1e12
+    gemm_ms = sum(d["ms"] for d in per_kernel.values()) / args.steps
 
     value = step_ops / (ms_per_step * 1e-3) / 1e12
     tok_s = M / (ms_per_step * 1e-3)
+
+    # ---------------- large-M headline projections (one GEMM each, M = 512)
+    big = {}
+    for g in (synth.CONFIGS[4][0], synth.CONFIGS[4][1]):
+        Wb = to_dev(synth.make_weights(g))
+        xb = to_dev(synth.make_acts(g))
+        wsb = qg.alloc_workspace(g.M, g.K, dev)
+        yb = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
+        qg.qgemm_quantize_workspace(xb, g.M, g.K, wsb, stream)
+        for _ in range(5):
+            qg.qgemm_gemm_quantized(Wb, g.fmt, wsb, g.M, g.N, g.K, yb, stream)
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.big_steps):
+            qg.qgemm_gemm_quantized(Wb, g.fmt, wsb, g.M, g.N, g.K, yb, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / args.big_steps
+        tops = g.ops / (us * 1e-6) / 1e12
+        big[f"{g.name}"] = {"shape": f"M={g.M} K={g.K} N={g.N} "
+                                     f"{'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'}",
+                            "kernel": qg.qgemm_kernel_name(g.fmt, g.M, g.N, g.K),
+                            "avg_launch_us": round(us, 2), "tops": round(tops, 1),
+                            "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
+        del Wb, xb, wsb, yb
 
     # ---------------- LM head on the last token: M = 1, K = 4096 -> N = 152064, Q6_K
     lm = synth.CONFIGS[5][0]
@@ -134,25 +174,32 @@ def main():
     for _ in range(5):
         qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
     torch.cuda.synchronize()
-    ev = []
+    qg.qgemm_quantize_workspace(x_lm, 1, lm.K, ws_lm, stream)
+    a, b = ev(), ev()
+    a.record(stream)
     for _ in range(args.lm_steps):
-        qg.qgemm_quantize_workspace(x_lm, 1, lm.K, ws_lm, stream)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
         qg.qgemm_gemm_quantized(W_lm, lm.fmt, ws_lm, 1, lm.N, lm.K, y_lm, stream, qg.QG_PATH_SKINNY)
-        b.record(stream)
-        ev.append((a, b))
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
+    b.record(stream)
+    c0, c1 = ev(), ev()
     c0.record(stream)
     for _ in range(args.lm_steps):
         qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
     c1.record(stream)
     torch.cuda.synchronize()
-    lm_kernel_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    lm_kernel_us = 1e3 * a.elapsed_time(b) / args.lm_steps
     lm_call_us = 1e3 * c0.elapsed_time(c1) / args.lm_steps
     lm_gbs = lm.w_bytes / (lm_kernel_us * 1e-6) / 1e9
+    del W_lm
+
+    # ---------------- optional: plain copy kernel of known size (profiler counter scale)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- CPU oracle on the host (same step, whole workload, repeated)
     cpu = None
@@ -168,9 +215,9 @@ def main():
             t_cpu += time.perf_counter() - s0
             reps += 1
         cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-        cpu = {"value": round(step_ops * reps / t_cpu / 1e12, 6), "unit": "TOPS (int8 ops)",
+        cpu = {"value": round(step_ops * reps / t_cpu / 1e12, 6), "unit": "TOPS",
                "cores": cores, "kind": "oracle",
-               "sample": f"the whole step (qkv_gate, up_gate, down at M=512, activation "
+               "sample": f"the whole step (qkv_gate, up_gate, down at M=512; activation "
                          f"quantisation included) repeated {reps}x in {t_cpu:.1f} s",
                "tok_s": round(M * reps / t_cpu, 2)}
 
@@ -185,19 +232,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 x int8 -> int32, fp32 epilogue",
+        "dtype": "int8",
         "data": "synthetic (seeded N(0,0.02^2) weights packed to Q4_K, bf16 N(0,1) activations)",
         "config": {"workload": "small-model projection set, M=512: 1024->4096 + 1024->7168 "
                                "(shared hidden) + 3584->1024, Q4_K", "M": M,
                    "projections": [[g.K, g.N] for g in (qkv, up, down)]},
         "prefill_tok_s": round(tok_s, 1),
+        "gemm_ms_per_step": round(gemm_ms, 5),
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_q4k_kernel (tiled)",
-                     "achieved": round(gemm_tops, 3), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 5),
-                     "traffic": None, "launches": g_launches,
-                     "avg_launch_us": round(1e3 * g_ms / g_launches, 3)},
+        "roofline": {"bound": "mfma", "kernel": dom,
+                     "achieved": round(dom_tops, 3), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tops / PEAK_INT8_TOPS, 5),
+                     "traffic": None, "launches": dk["launches"],
+                     "avg_launch_us": round(1e3 * dk["ms"] / dk["launches"], 3),
+                     "ops_per_launch": dk["ops"] // dk["launches"]},
+        "gemm_kernels": {k: {"launches": d["launches"],
+                             "avg_launch_us": round(1e3 * d["ms"] / d["launches"], 3),
+                             "tops": round(d["ops"] / (d["ms"] * 1e-3) / 1e12, 2)}
+                         for k, d in per_kernel.items()},
+        "large_m": big,
         "lm_head": {"workload": "M=1, K=4096 -> N=152064, Q6_K (skinny path)",
+                    "kernel": qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K),
                     "weight_bytes": lm.w_bytes, "kernel_us": round(lm_kernel_us, 3),
                     "call_us": round(lm_call_us, 3), "gbps": round(lm_gbs, 1),
                     "frac_hbm": round(lm_gbs / PEAK_HBM_GBS, 4)},

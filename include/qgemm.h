@@ -120,6 +120,12 @@ int qgemm_gemm_quantized(const void *q_weights, int fmt, const void *workspace,
                          size_t workspace_bytes, int64_t M, int64_t N, int64_t K, float *y,
                          void *stream, int path);
 
+/* Name of the GPU kernel qgemm_gemm_quantized would launch for this problem
+ * and path (a static string, as a profiler lists the kernel; for benchmarks
+ * and profiles).  NULL when the arguments would be rejected.  Launches
+ * nothing and needs no GPU. */
+const char *qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path);
+
 /* Static message for a return code (never NULL). */
 const char *qgemm_strerror(int code);
 

@@ -23,7 +23,8 @@ QG_SKINNY_MAX_M = 8
 BLOCK_BYTES = {QG_Q4_K: 144, QG_Q6_K: 210}
 SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_lm_head",
            "qgemm_quantize_workspace", "qgemm_gemm_quantized",
-           "qgemm_strerror", "qgemm_quantize_act", "qgemm_dequant", "qgemm_block_partials")
+           "qgemm_strerror", "qgemm_kernel_name", "qgemm_quantize_act", "qgemm_dequant",
+           "qgemm_block_partials")
 
 
 class QgemmError(RuntimeError):
@@ -60,6 +61,8 @@ def load() -> ctypes.CDLL:
         lib.qgemm_quantize_workspace.restype = ci
         lib.qgemm_gemm_quantized.argtypes = [vp, ci, vp, sz, i64, i64, i64, vp, vp, ci]
         lib.qgemm_gemm_quantized.restype = ci
+        lib.qgemm_kernel_name.argtypes = [ci, i64, i64, i64, ci]
+        lib.qgemm_kernel_name.restype = ctypes.c_char_p
         lib.qgemm_strerror.argtypes = [ci]
         lib.qgemm_strerror.restype = ctypes.c_char_p
         lib.qgemm_quantize_act.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
@@ -109,6 +112,11 @@ def _check(code: int, fn: str) -> None:
 
 def qgemm_strerror(code: int) -> str:
     return load().qgemm_strerror(code).decode()
+
+
+def qgemm_kernel_name(fmt: int, M: int, N: int, K: int, path: int = QG_PATH_AUTO) -> str | None:
+    r = load().qgemm_kernel_name(fmt, M, N, K, path)
+    return None if r is None else r.decode()
 
 
 def qgemm_workspace_bytes(M: int, K: int) -> int:

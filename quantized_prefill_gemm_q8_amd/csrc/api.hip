@@ -166,6 +166,16 @@ int qgemm_lm_head(const void* q_weights, int fmt, const void* x_row, int x_dtype
                           stream, QG_PATH_AUTO);
 }
 
+const char* qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path) {
+  if (fmt != QG_Q4_K && fmt != QG_Q6_K) return NULL;
+  if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
+  if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return NULL;
+  if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return NULL;
+  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && M <= QG_SKINNY_MAX_M);
+  if (skinny) return qg_gemm_skinny_kernel_name(fmt, M);
+  return fmt == QG_Q4_K ? qg_gemm_q4k_kernel_name(M, N, K) : qg_gemm_q6k_kernel_name(M, N, K);
+}
+
 const char* qgemm_strerror(int code) {
   switch (code) {
     case QG_OK: return "success";

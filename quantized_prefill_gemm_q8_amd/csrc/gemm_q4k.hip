@@ -93,8 +93,8 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 // DPP: activation scales staged row-major and applied with the DPP-broadcast
 // epilogue; otherwise staged block-major ([8][BM], from dxT) and read as 16
 // per-element values per tile (four 16-byte broadcast reads).
-template <int TM, int TN, int WM, int WN, bool DPP, int NS>
-__global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_kernel(
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_lds_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
     int64_t N, int64_t K, float* __restrict__ y) {
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN + 3) / 4) void gemm_q4k_lds_
 
   auto issue_stage = [&](int64_t sb, int buf) {
     uint8_t* base = lds + buf * STAGE;
-#pragma unroll(LPT <= 6 ? LPT : 1)
+#pragma unroll((LPT <= 6 && OCC < 4) ? LPT : 1)
     for (int it = 0; it < LPT; it++) {
       const int q0 = wave * 64 + it * NT;  // region tests are uniform per wave
       if (q0 >= CH) {                      // padding load: same count on every wave
@@ -446,38 +446,61 @@ static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int
                                                                   M, N, K, y);
 }
 
-template <int TM, int TN, int WM, int WN, bool DPP, int NS>
+// OCC: waves per SIMD the register allocation must allow (launch bound)
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC = (WM * WN + 3) / 4>
 static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                        float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS><<<grid, dim3(64 * WM * WN), 0, stream>>>(
+  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS, OCC><<<grid, dim3(64 * WM * WN), 0, stream>>>(
       W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
 }
 
 }  // namespace qg
 
-hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
-                              int64_t K, float* y, hipStream_t stream) {
-  // large grids: workgroups of 8 waves sharing 128x256 tiles through LDS;
-  // otherwise one 32x32 tile per wave with the K range split so that the chip
-  // gets about two waves per SIMD
+namespace {
+
+// Kernel choice for a Q4_K problem: large grids get workgroups of 8 waves
+// sharing 128x256 (or 64x128) tiles through LDS; smaller ones one 32x32 tile
+// per wave with the K range split so that the chip gets about two waves per
+// SIMD.
+enum class Q4Pick { kLds128x256, kLds64x128, kSmall1, kSmall2, kSmall4, kSmall8 };
+
+Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256, kTargetWaves = 2048;
   const int64_t nsb = K / 256;
-  if (((M + 127) / 128) * ((N + 255) / 256) >= kCUs) {
-    qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream);
-  } else if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs) {
-    qg::launch_lds<1, 1, 2, 4, false, 4>(W, ws, M, N, K, y, stream);
-  } else {
-    const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
-    if (tiles >= kTargetWaves || nsb < 2)
-      qg::launch_small<1>(W, ws, M, N, K, y, stream);
-    else if (tiles * 2 >= kTargetWaves || nsb < 4)
-      qg::launch_small<2>(W, ws, M, N, K, y, stream);
-    else if (tiles * 4 >= kTargetWaves || nsb < 8)
-      qg::launch_small<4>(W, ws, M, N, K, y, stream);
-    else
-      qg::launch_small<8>(W, ws, M, N, K, y, stream);
+  if (((M + 127) / 128) * ((N + 255) / 256) >= kCUs) return Q4Pick::kLds128x256;
+  if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs) return Q4Pick::kLds64x128;
+  const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
+  if (tiles >= kTargetWaves || nsb < 2) return Q4Pick::kSmall1;
+  if (tiles * 2 >= kTargetWaves || nsb < 4) return Q4Pick::kSmall2;
+  if (tiles * 4 >= kTargetWaves || nsb < 8) return Q4Pick::kSmall4;
+  return Q4Pick::kSmall8;
+}
+
+}  // namespace
+
+const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K) {
+  switch (pick_q4k(M, N, K)) {
+    case Q4Pick::kLds128x256: return "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2>";
+    case Q4Pick::kLds64x128: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 4, 2>";
+    case Q4Pick::kSmall1: return "gemm_q4k_small_kernel<1>";
+    case Q4Pick::kSmall2: return "gemm_q4k_small_kernel<2>";
+    case Q4Pick::kSmall4: return "gemm_q4k_small_kernel<4>";
+    case Q4Pick::kSmall8: return "gemm_q4k_small_kernel<8>";
+  }
+  return "?";
+}
+
+hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream) {
+  switch (pick_q4k(M, N, K)) {
+    case Q4Pick::kLds128x256: qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds64x128: qg::launch_lds<1, 1, 2, 4, false, 4>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall1: qg::launch_small<1>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall2: qg::launch_small<2>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall4: qg::launch_small<4>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall8: qg::launch_small<8>(W, ws, M, N, K, y, stream); break;
   }
   return hipGetLastError();
 }

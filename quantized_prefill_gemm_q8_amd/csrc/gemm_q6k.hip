@@ -63,6 +63,8 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
 
 }  // namespace qg
 
+const char* qg_gemm_q6k_kernel_name(int64_t, int64_t, int64_t) { return "gemm_q6k_kernel"; }
+
 hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((N + 32 * qg::kQ6WN - 1) / (32 * qg::kQ6WN)),

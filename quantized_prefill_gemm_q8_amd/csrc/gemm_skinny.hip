@@ -138,6 +138,17 @@ static void launch_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int6
 
 }  // namespace qg
 
+const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M) {
+  static const char* const q4[8] = {"skinny_q4k_kernel<1>", "skinny_q4k_kernel<2>", "skinny_q4k_kernel<3>",
+                                    "skinny_q4k_kernel<4>", "skinny_q4k_kernel<5>", "skinny_q4k_kernel<6>",
+                                    "skinny_q4k_kernel<7>", "skinny_q4k_kernel<8>"};
+  static const char* const q6[8] = {"skinny_q6k_kernel<1>", "skinny_q6k_kernel<2>", "skinny_q6k_kernel<3>",
+                                    "skinny_q6k_kernel<4>", "skinny_q6k_kernel<5>", "skinny_q6k_kernel<6>",
+                                    "skinny_q6k_kernel<7>", "skinny_q6k_kernel<8>"};
+  if (M < 1 || M > 8) return "?";
+  return fmt == QG_Q4_K ? q4[M - 1] : q6[M - 1];
+}
+
 hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
                                  int64_t N, int64_t K, float* y, hipStream_t stream) {
   switch (M) {
