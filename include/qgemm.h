@@ -121,8 +121,9 @@ int qgemm_gemm_quantized(const void *q_weights, int fmt, const void *workspace,
                          void *stream, int path);
 
 /* Name of the GPU kernel qgemm_gemm_quantized would launch for this problem
- * and path (a static string, as a profiler lists the kernel; for benchmarks
- * and profiles).  NULL when the arguments would be rejected.  Launches
+ * and path, as a profiler lists it (template arguments included); for
+ * benchmarks and profiles.  The string stays valid until the next call from
+ * the same thread.  NULL when the arguments would be rejected.  Launches
  * nothing and needs no GPU. */
 const char *qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path);
 

@@ -3,164 +3,402 @@
 // prefill matmul + LM head on the last token only").  Every weight byte is read
 // once, so the kernel is bound by HBM bandwidth (the decode-GEMV yardstick of
 // issue #5305's merged ticket #5221, "decode GEMV at 223-504 GB/s vs llama.cpp
-// MMVQ 776-894").  Same arithmetic as the tiled kernel: int8 codes times int8
-// activation codes summed per sub-block in int32 (v_dot4_i32_i8), scales and
-// mins applied in fp32.
+// MMVQ 776-894", and the fraction-of-peak figures of issue #4220).  Same
+// arithmetic as the tiled kernels: int8 codes times int8 activation codes
+// summed per sub-block in int32 (v_dot4_i32_i8), scales and mins applied in
+// fp32.
 //
-// One wavefront per weight row n; lane t handles the 32-value blocks t, t+64, ...
-// of that row and the M activation rows; the per-lane fp32 partial sums are
-// reduced across the wavefront at the end.
+// Work split.  Four lanes share one 256-value super-block; each lane holds 64
+// of its values, read with three 16-byte loads:
+//   Q4_K  lane s (0..3): the 16-byte header (d, dmin, packed scales) and the
+//         32 code bytes qs[32s .. 32s+31], i.e. sub-blocks 2s (low nibbles)
+//         and 2s+1 (high nibbles).
+//   Q6_K  lane s = 2*half + lh: ql[64half + 16lh ..+16], ql[64half + 32 +
+//         16lh ..+16] and qh[32half + 16lh ..+16], i.e. the values
+//         128half + 32c + 16lh + i (c = 0..3, i < 16), which are the 16-value
+//         sub-blocks 8half + 2c + lh; plus the 8 scale bytes of its half and d.
+//         Q6_K blocks are 210 bytes, so these loads are only 2-byte aligned
+//         (gfx950 serves unaligned vector loads).
+// So a wavefront covers 16 super-blocks (4096 values) per step.  A row of nsb
+// super-blocks takes ceil(nsb/16) steps; when nsb divides 16, one step covers
+// R = 16/nsb whole rows.  Every wavefront streams a contiguous range of rows,
+// the loads of step t+1 in flight while step t is computed (two register
+// buffers used in turn).
+//
+// Activations.  When a row takes a single step, every lane works on the same
+// 64 activation values in every step, so it keeps their codes, block scales
+// and the -32 correction of the Q6_K codes in registers (XREG, for M <= 4).
+// Otherwise the activation rows are staged in LDS once per workgroup (XLDS)
+// or, when they do not fit, read from global memory where they stay L2-resident
+// (XGLB).
+//
+// Q6_K codes go to v_dot4_i32_i8 as the unsigned q6 in [0, 63] (below 128, so
+// also valid signed bytes) and the offset is applied through the activation
+// sum: sum (q6 - 32) x = sum q6 x - 32 sum x, with the dot chain started at
+// -32 sum x.
+#include <stdio.h>
+
 #include "common.h"
 
 namespace qg {
+
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
+  const u32x4_a2 v = *reinterpret_cast<const u32x4_a2*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int MR>
-__global__ __launch_bounds__(256) void skinny_q4k_kernel(const uint8_t* __restrict__ W,
-                                                         const int8_t* __restrict__ qx,
-                                                         const float* __restrict__ dx,
-                                                         const float* __restrict__ dS,
-                                                         int64_t N, int64_t K,
-                                                         float* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;  // whole wavefronts only
+// Raw bytes one lane loads for one super-block.
+struct SkRaw {
+  uint4 a, b, c;   // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
+  uint32_t s0, s1; // Q6_K: the 8 scale bytes of the lane's half
+  uint32_t dh;     // Q6_K: d (binary16 bits)
+};
+
+constexpr int kSkThreads = 256;
+constexpr int kSkMaxLds = 64 * 1024;
+enum { kXReg = 0, kXLds = 1, kXGlb = 2 };
+
+// sum over 16 int8 values
+__device__ __forceinline__ int sum16(const uint4& x) {
+  int s = dot4(0x01010101u, x.x, 0);
+  s = dot4(0x01010101u, x.y, s);
+  s = dot4(0x01010101u, x.z, s);
+  return dot4(0x01010101u, x.w, s);
+}
+
+// FMT: QG_Q4_K / QG_Q6_K.  MR: activation rows.  R: rows per wavefront step
+// (16/nsb when that divides, else 1).  XM: where the activations are read.
+template <int FMT, int MR, int R, int XM>
+__global__ __launch_bounds__(kSkThreads) void skinny_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ gdx,
+    const float* __restrict__ gdS, int64_t N, int64_t K, int64_t rows_per_wave,
+    float* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : kQ6Bytes;
+  constexpr int G = 64 / R;  // lanes per row within a step
   const int64_t nsb = K / 256, nb = K / 32;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kSkThreads / 64) + (threadIdx.x >> 6);
+
+  const int8_t* xs = qx;
+  const float* xd = gdx;
+  const float* xS = gdS;
+  if constexpr (XM == kXLds) {
+    int8_t* lq = reinterpret_cast<int8_t*>(smem);
+    float* ld = reinterpret_cast<float*>(smem + MR * K);
+    float* lS = ld + MR * nb;
+    const int64_t nq = MR * K / 16, nd = MR * nb / 4;
+    for (int64_t i = threadIdx.x; i < nq; i += kSkThreads)
+      reinterpret_cast<uint4*>(lq)[i] = reinterpret_cast<const uint4*>(qx)[i];
+    for (int64_t i = threadIdx.x; i < nd; i += kSkThreads) {
+      reinterpret_cast<float4*>(ld)[i] = reinterpret_cast<const float4*>(gdx)[i];
+      if (FMT == QG_Q4_K) reinterpret_cast<float4*>(lS)[i] = reinterpret_cast<const float4*>(gdS)[i];
+    }
+    __syncthreads();
+    xs = lq;
+    xd = ld;
+    xS = lS;
+  }
+
+  const int64_t row_begin = wave * rows_per_wave;
+  int64_t row_end = row_begin + rows_per_wave;
+  row_end = row_end < N ? row_end : N;
+  if (row_begin >= row_end) return;
+
+  const int grp = lane >> 2, s = lane & 3;
+  const int half = s >> 1, lh = s & 1;              // Q6_K lane roles
+  const int ro = grp / (16 / R);                    // row of this lane within a step
+  const int jb0 = R > 1 ? grp % (16 / R) : grp;     // super-block of this lane in a row's first step
+  const int64_t ipr = R > 1 ? 1 : (nsb + 15) / 16;  // steps per row
+  const int64_t nsteps = (row_end - row_begin + R - 1) / R * ipr;
+  const int64_t row_bytes = nsb * BB;
+  // lane offset inside a super-block of each of its loads
+  const uint32_t off_a = FMT == QG_Q4_K ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
+  const uint32_t off_b = FMT == QG_Q4_K ? 16u + 32u * s : static_cast<uint32_t>(64 * half + 32 + 16 * lh);
+  const uint32_t off_c = FMT == QG_Q4_K ? 32u + 32u * s : static_cast<uint32_t>(128 + 32 * half + 16 * lh);
+
+  // per-lane activation data for XREG (a lane's super-block never changes)
+  constexpr int XR = XM == kXReg ? MR : 1;
+  uint4 xr[XR][4];
+  float xdr[XR][4];
+  int xur[XR][4];
+  if constexpr (XM == kXReg) {
+    const int64_t jb = jb0 < nsb ? jb0 : nsb - 1;  // idle lanes (jb0 >= nsb) read valid data
+#pragma unroll
+    for (int m = 0; m < MR; m++) {
+      if (FMT == QG_Q4_K) {
+        const uint4* xv = reinterpret_cast<const uint4*>(qx + m * K + 256 * jb + 64 * s);
+#pragma unroll
+        for (int c = 0; c < 4; c++) xr[m][c] = xv[c];
+        const int64_t b0 = 8 * jb + 2 * s;
+        xdr[m][0] = gdx[m * nb + b0];
+        xdr[m][1] = gdx[m * nb + b0 + 1];
+        xdr[m][2] = gdS[m * nb + b0];
+        xdr[m][3] = gdS[m * nb + b0 + 1];
+      } else {
+        const int8_t* xp = qx + m * K + 256 * jb + 128 * half + 16 * lh;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          xr[m][c] = *reinterpret_cast<const uint4*>(xp + 32 * c);
+          xur[m][c] = -32 * sum16(xr[m][c]);
+          xdr[m][c] = gdx[m * nb + 8 * jb + 4 * half + c];
+        }
+      }
+    }
+  }
+
+  auto load = [&](int64_t rs, int64_t it, SkRaw& r) {
+    const int64_t n = row_begin + rs * R + ro, jb = jb0 + 16 * it;
+    if (n >= row_end || jb >= nsb) return;
+    const uint8_t* blk = W + n * row_bytes + jb * BB;
+    if (FMT == QG_Q4_K) {
+      r.a = *reinterpret_cast<const uint4*>(blk + off_a);
+      r.b = *reinterpret_cast<const uint4*>(blk + off_b);
+      r.c = *reinterpret_cast<const uint4*>(blk + off_c);
+    } else {
+      r.a = ld16_a2(blk + off_a);
+      r.b = ld16_a2(blk + off_b);
+      r.c = ld16_a2(blk + off_c);
+      const u32x2_a2 sc = *reinterpret_cast<const u32x2_a2*>(blk + 192 + 8 * half);
+      r.s0 = sc.x;
+      r.s1 = sc.y;
+      r.dh = *reinterpret_cast<const uint16_t*>(blk + 208);
+    }
+  };
+
   float acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; m++) acc[m] = 0.0f;
 
-  for (int64_t b = lane; b < nb; b += 64) {
-    const int64_t sb = b >> 3;
-    const int j = static_cast<int>(b & 7), c = j >> 1;
-    const uint8_t* blk = W + (n * nsb + sb) * kQ4Bytes;
-    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-    const Q4Scales s = unpack_q4_scales(hdr.y, hdr.z, hdr.w);
-    const float d = half_to_float(hdr.x & 0xFFFFu), dmin = half_to_float(hdr.x >> 16);
-    const float dsc = d * static_cast<float>(byte_of(j < 4 ? s.sc_lo : s.sc_hi, j & 3));
-    const float dmn = dmin * static_cast<float>(byte_of(j < 4 ? s.m_lo : s.m_hi, j & 3));
-    const uint4 r0 = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c);
-    const uint4 r1 = *reinterpret_cast<const uint4*>(blk + 32 + 32 * c);
-    const int sh = 4 * (j & 1);
-    const uint32_t w[8] = {(r0.x >> sh) & 0x0F0F0F0Fu, (r0.y >> sh) & 0x0F0F0F0Fu,
-                           (r0.z >> sh) & 0x0F0F0F0Fu, (r0.w >> sh) & 0x0F0F0F0Fu,
-                           (r1.x >> sh) & 0x0F0F0F0Fu, (r1.y >> sh) & 0x0F0F0F0Fu,
-                           (r1.z >> sh) & 0x0F0F0F0Fu, (r1.w >> sh) & 0x0F0F0F0Fu};
+  auto compute = [&](int64_t rs, int64_t it, const SkRaw& cur) {
+    const int64_t n = row_begin + rs * R + ro, jb = jb0 + 16 * it;
+    if (n < row_end && jb < nsb) {
+      if (FMT == QG_Q4_K) {
+        const float d = half_to_float(cur.a.x & 0xFFFFu), dmin = half_to_float(cur.a.x >> 16);
+        const Q4Scales sc = unpack_q4_scales(cur.a.y, cur.a.z, cur.a.w);
+        const uint32_t scw = s < 2 ? sc.sc_lo : sc.sc_hi, mw = s < 2 ? sc.m_lo : sc.m_hi;
+        const int bi = 2 * (s & 1);
+        const float dsc0 = d * static_cast<float>(byte_of(scw, bi));
+        const float dsc1 = d * static_cast<float>(byte_of(scw, bi + 1));
+        const float dm0 = dmin * static_cast<float>(byte_of(mw, bi));
+        const float dm1 = dmin * static_cast<float>(byte_of(mw, bi + 1));
+        const uint32_t w[8] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w, cur.c.x, cur.c.y, cur.c.z, cur.c.w};
+        uint32_t lo[8], hi[8];
 #pragma unroll
-    for (int m = 0; m < MR; m++) {
-      const uint4* xa = reinterpret_cast<const uint4*>(qx + m * K + 32 * b);
-      const uint4 a0 = xa[0], a1 = xa[1];
-      int I = dot4(w[0], a0.x, 0);
-      I = dot4(w[1], a0.y, I); I = dot4(w[2], a0.z, I); I = dot4(w[3], a0.w, I);
-      I = dot4(w[4], a1.x, I); I = dot4(w[5], a1.y, I); I = dot4(w[6], a1.z, I);
-      I = dot4(w[7], a1.w, I);
-      const float dxm = dx[m * nb + b], ds = dS[m * nb + b];
-      acc[m] = __builtin_fmaf(dsc * static_cast<float>(I), dxm, acc[m]);
-      acc[m] = __builtin_fmaf(-dmn, ds, acc[m]);
+        for (int i = 0; i < 8; i++) {
+          lo[i] = w[i] & 0x0F0F0F0Fu;
+          hi[i] = (w[i] >> 4) & 0x0F0F0F0Fu;
+        }
+        const int64_t b0 = 8 * jb + 2 * s;
+#pragma unroll
+        for (int m = 0; m < MR; m++) {
+          uint4 x0, x1, x2, x3;
+          float dx0, dx1, dS0, dS1;
+          if constexpr (XM == kXReg) {
+            x0 = xr[m][0]; x1 = xr[m][1]; x2 = xr[m][2]; x3 = xr[m][3];
+            dx0 = xdr[m][0]; dx1 = xdr[m][1]; dS0 = xdr[m][2]; dS1 = xdr[m][3];
+          } else {
+            const uint4* xv = reinterpret_cast<const uint4*>(xs + m * K + 256 * jb + 64 * s);
+            x0 = xv[0]; x1 = xv[1]; x2 = xv[2]; x3 = xv[3];
+            const float2 dxv = *reinterpret_cast<const float2*>(xd + m * nb + b0);
+            const float2 dSv = *reinterpret_cast<const float2*>(xS + m * nb + b0);
+            dx0 = dxv.x; dx1 = dxv.y; dS0 = dSv.x; dS1 = dSv.y;
+          }
+          int I0 = dot4(lo[0], x0.x, 0);
+          I0 = dot4(lo[1], x0.y, I0); I0 = dot4(lo[2], x0.z, I0); I0 = dot4(lo[3], x0.w, I0);
+          I0 = dot4(lo[4], x1.x, I0); I0 = dot4(lo[5], x1.y, I0); I0 = dot4(lo[6], x1.z, I0);
+          I0 = dot4(lo[7], x1.w, I0);
+          int I1 = dot4(hi[0], x2.x, 0);
+          I1 = dot4(hi[1], x2.y, I1); I1 = dot4(hi[2], x2.z, I1); I1 = dot4(hi[3], x2.w, I1);
+          I1 = dot4(hi[4], x3.x, I1); I1 = dot4(hi[5], x3.y, I1); I1 = dot4(hi[6], x3.z, I1);
+          I1 = dot4(hi[7], x3.w, I1);
+          float a = acc[m];
+          a = __builtin_fmaf(static_cast<float>(I0), dsc0 * dx0, a);
+          a = __builtin_fmaf(static_cast<float>(I1), dsc1 * dx1, a);
+          a = __builtin_fmaf(-dm0, dS0, a);
+          a = __builtin_fmaf(-dm1, dS1, a);
+          acc[m] = a;
+        }
+      } else {
+        const float d = half_to_float(cur.dh & 0xFFFFu);
+        float dsc[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const uint32_t sw = c < 2 ? cur.s0 : cur.s1;
+          dsc[c] = d * static_cast<float>(static_cast<int8_t>(byte_of(sw, (2 * c + lh) & 3)));
+        }
+        const uint32_t l0[4] = {cur.a.x, cur.a.y, cur.a.z, cur.a.w};
+        const uint32_t l1[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
+        const uint32_t hh[4] = {cur.c.x, cur.c.y, cur.c.z, cur.c.w};
+        uint32_t q[4][4];  // codes q6 in [0, 63], quarter c, dword i
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          q[0][i] = (l0[i] & 0x0F0F0F0Fu) | ((hh[i] << 4) & 0x30303030u);
+          q[1][i] = (l1[i] & 0x0F0F0F0Fu) | ((hh[i] << 2) & 0x30303030u);
+          q[2][i] = ((l0[i] >> 4) & 0x0F0F0F0Fu) | (hh[i] & 0x30303030u);
+          q[3][i] = ((l1[i] >> 4) & 0x0F0F0F0Fu) | ((hh[i] >> 2) & 0x30303030u);
+        }
+        const int64_t b0 = 8 * jb + 4 * half;
+#pragma unroll
+        for (int m = 0; m < MR; m++) {
+          float dxs[4];
+          if constexpr (XM != kXReg) {
+            const float4 dxv = *reinterpret_cast<const float4*>(xd + m * nb + b0);
+            dxs[0] = dxv.x; dxs[1] = dxv.y; dxs[2] = dxv.z; dxs[3] = dxv.w;
+          }
+          float a = acc[m];
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            uint4 xv;
+            int I;
+            float dxc;
+            if constexpr (XM == kXReg) {
+              xv = xr[m][c];
+              I = xur[m][c];
+              dxc = xdr[m][c];
+            } else {
+              xv = *reinterpret_cast<const uint4*>(xs + m * K + 256 * jb + 128 * half + 16 * lh + 32 * c);
+              I = -32 * sum16(xv);
+              dxc = dxs[c];
+            }
+            I = dot4(q[c][0], xv.x, I);
+            I = dot4(q[c][1], xv.y, I);
+            I = dot4(q[c][2], xv.z, I);
+            I = dot4(q[c][3], xv.w, I);
+            a = __builtin_fmaf(static_cast<float>(I), dsc[c] * dxc, a);
+          }
+          acc[m] = a;
+        }
+      }
     }
-  }
+    // end of a row (all its steps done): reduce over the row's lanes and store
+    if (it == ipr - 1) {
 #pragma unroll
-  for (int m = 0; m < MR; m++) {
-    const float v = wave_sum(acc[m]);
-    if (lane == 0) y[m * N + n] = v;
+      for (int m = 0; m < MR; m++) {
+        float v = acc[m];
+#pragma unroll
+        for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        acc[m] = 0.0f;
+        if ((lane & (G - 1)) == 0 && n < row_end) y[m * N + n] = v;
+      }
+    }
+  };
+
+  // two register buffers in turn: the loads of step t+1 are issued before
+  // step t is computed
+  auto advance = [&](int64_t& rs, int64_t& it) {
+    if (++it == ipr) {
+      it = 0;
+      ++rs;
+    }
+  };
+  SkRaw r0 = {}, r1 = {};
+  int64_t rs0 = 0, it0 = 0;
+  load(rs0, it0, r0);
+  for (int64_t t = 0; t < nsteps; t += 2) {
+    int64_t rs1 = rs0, it1 = it0;
+    advance(rs1, it1);
+    if (t + 1 < nsteps) load(rs1, it1, r1);
+    compute(rs0, it0, r0);
+    if (t + 1 >= nsteps) break;
+    rs0 = rs1;
+    it0 = it1;
+    advance(rs0, it0);
+    if (t + 2 < nsteps) load(rs0, it0, r0);
+    compute(rs1, it1, r1);
   }
 }
 
-template <int MR>
-__global__ __launch_bounds__(256) void skinny_q6k_kernel(const uint8_t* __restrict__ W,
-                                                         const int8_t* __restrict__ qx,
-                                                         const float* __restrict__ dx,
-                                                         int64_t N, int64_t K,
-                                                         float* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  const int64_t nsb = K / 256, nb = K / 32;
-  float acc[MR];
-#pragma unroll
-  for (int m = 0; m < MR; m++) acc[m] = 0.0f;
+// rows per wavefront step for K (16 / super-blocks per row when that divides)
+inline int skinny_rows_per_step(int64_t K) {
+  const int64_t nsb = K / 256;
+  return (nsb == 1 || nsb == 2 || nsb == 4 || nsb == 8) ? static_cast<int>(16 / nsb) : 1;
+}
 
-  for (int64_t b = lane; b < nb; b += 64) {
-    const int64_t sb = b >> 3;
-    const int jj = static_cast<int>(b & 7);  // 32-value slot in the block: values 32jj..32jj+31
-    const int half = jj >> 2, c = jj & 3;
-    const uint8_t* blk = W + (n * nsb + sb) * kQ6Bytes;
-    const uint8_t* pl = blk + 64 * half + 32 * (c & 1);
-    const uint8_t* ph = blk + 128 + 32 * half;
-    const int ls = 4 * (c >> 1), hs = 2 * c;
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const uint32_t lo = (load_u32_a2(pl + 4 * i) >> ls) & 0x0F0F0F0Fu;
-      const uint32_t hi = ((load_u32_a2(ph + 4 * i) >> hs) & 0x03030303u) << 4;
-      w[i] = q6_to_signed(lo | hi);
-    }
-    const float d = half_to_float(load_u16(blk + 208));
-    const float sa = d * static_cast<float>(static_cast<int8_t>(blk[192 + 2 * jj]));
-    const float sbv = d * static_cast<float>(static_cast<int8_t>(blk[193 + 2 * jj]));
-#pragma unroll
-    for (int m = 0; m < MR; m++) {
-      const uint4* xa = reinterpret_cast<const uint4*>(qx + m * K + 32 * b);
-      const uint4 a0 = xa[0], a1 = xa[1];
-      int Ia = dot4(w[0], a0.x, 0);
-      Ia = dot4(w[1], a0.y, Ia); Ia = dot4(w[2], a0.z, Ia); Ia = dot4(w[3], a0.w, Ia);
-      int Ib = dot4(w[4], a1.x, 0);
-      Ib = dot4(w[5], a1.y, Ib); Ib = dot4(w[6], a1.z, Ib); Ib = dot4(w[7], a1.w, Ib);
-      const float t = __builtin_fmaf(sa, static_cast<float>(Ia), sbv * static_cast<float>(Ib));
-      acc[m] = __builtin_fmaf(t, dx[m * nb + b], acc[m]);
-    }
+inline int64_t skinny_lds_bytes(int fmt, int64_t M, int64_t K) {
+  return fmt == QG_Q4_K ? M * K + 2 * M * (K / 32) * 4 : M * K + M * (K / 32) * 4;
+}
+
+inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
+  if (M <= 4 && K <= 4096) return kXReg;
+  return skinny_lds_bytes(fmt, M, K) <= kSkMaxLds ? kXLds : kXGlb;
+}
+
+template <int FMT, int MR, int R>
+static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
+                                  float* y, hipStream_t stream) {
+  // about eight workgroups (32 wavefronts) per CU, each wavefront a contiguous
+  // run of rows; a multiple of R rows per wavefront
+  constexpr int64_t kWaves = 256 * 32;
+  int64_t rpw = (N + kWaves - 1) / kWaves;
+  rpw = (rpw + R - 1) / R * R;
+  const int64_t waves = (N + rpw - 1) / rpw;
+  const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+  switch (skinny_xmode(FMT, MR, K)) {
+    case kXReg:
+      if constexpr (MR <= 4)
+        skinny_kernel<FMT, MR, R, kXReg><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
+                                                                               N, K, rpw, y);
+      break;
+    case kXLds:
+      skinny_kernel<FMT, MR, R, kXLds>
+          <<<grid, dim3(kSkThreads), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
+              W, ws.q, ws.dx, ws.dS, N, K, rpw, y);
+      break;
+    default:
+      skinny_kernel<FMT, MR, R, kXGlb><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N,
+                                                                             K, rpw, y);
   }
-#pragma unroll
-  for (int m = 0; m < MR; m++) {
-    const float v = wave_sum(acc[m]);
-    if (lane == 0) y[m * N + n] = v;
+  return hipGetLastError();
+}
+
+template <int FMT, int MR>
+static hipError_t launch_skinny(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
+                                float* y, hipStream_t stream) {
+  switch (K / 256) {
+    case 1: return launch_skinny_r<FMT, MR, 16>(W, ws, N, K, y, stream);
+    case 2: return launch_skinny_r<FMT, MR, 8>(W, ws, N, K, y, stream);
+    case 4: return launch_skinny_r<FMT, MR, 4>(W, ws, N, K, y, stream);
+    case 8: return launch_skinny_r<FMT, MR, 2>(W, ws, N, K, y, stream);
+    default: return launch_skinny_r<FMT, MR, 1>(W, ws, N, K, y, stream);
   }
 }
 
-template <int MR>
-static void launch_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t N,
-                          int64_t K, float* y, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((N + 3) / 4));
-  if (fmt == QG_Q4_K)
-    skinny_q4k_kernel<MR><<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
-  else
-    skinny_q6k_kernel<MR><<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dx, N, K, y);
+template <int FMT>
+static hipError_t launch_skinny_fmt(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                                    int64_t K, float* y, hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_skinny<FMT, 1>(W, ws, N, K, y, stream);
+    case 2: return launch_skinny<FMT, 2>(W, ws, N, K, y, stream);
+    case 3: return launch_skinny<FMT, 3>(W, ws, N, K, y, stream);
+    case 4: return launch_skinny<FMT, 4>(W, ws, N, K, y, stream);
+    case 5: return launch_skinny<FMT, 5>(W, ws, N, K, y, stream);
+    case 6: return launch_skinny<FMT, 6>(W, ws, N, K, y, stream);
+    case 7: return launch_skinny<FMT, 7>(W, ws, N, K, y, stream);
+    case 8: return launch_skinny<FMT, 8>(W, ws, N, K, y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qg
 
-const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M) {
-  static const char* const q4[8] = {"skinny_q4k_kernel<1>", "skinny_q4k_kernel<2>", "skinny_q4k_kernel<3>",
-                                    "skinny_q4k_kernel<4>", "skinny_q4k_kernel<5>", "skinny_q4k_kernel<6>",
-                                    "skinny_q4k_kernel<7>", "skinny_q4k_kernel<8>"};
-  static const char* const q6[8] = {"skinny_q6k_kernel<1>", "skinny_q6k_kernel<2>", "skinny_q6k_kernel<3>",
-                                    "skinny_q6k_kernel<4>", "skinny_q6k_kernel<5>", "skinny_q6k_kernel<6>",
-                                    "skinny_q6k_kernel<7>", "skinny_q6k_kernel<8>"};
-  if (M < 1 || M > 8) return "?";
-  return fmt == QG_Q4_K ? q4[M - 1] : q6[M - 1];
+const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t K) {
+  thread_local char name[64];
+  if (M < 1 || M > QG_SKINNY_MAX_M) return "?";
+  snprintf(name, sizeof name, "skinny_kernel<%d, %d, %d, %d>", fmt, static_cast<int>(M),
+           qg::skinny_rows_per_step(K), qg::skinny_xmode(fmt, M, K));
+  return name;
 }
 
 hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
                                  int64_t N, int64_t K, float* y, hipStream_t stream) {
-  switch (M) {
-    case 1: qg::launch_skinny<1>(W, fmt, ws, N, K, y, stream); break;
-    case 2: qg::launch_skinny<2>(W, fmt, ws, N, K, y, stream); break;
-    case 3: qg::launch_skinny<3>(W, fmt, ws, N, K, y, stream); break;
-    case 4: qg::launch_skinny<4>(W, fmt, ws, N, K, y, stream); break;
-    case 5: qg::launch_skinny<5>(W, fmt, ws, N, K, y, stream); break;
-    case 6: qg::launch_skinny<6>(W, fmt, ws, N, K, y, stream); break;
-    case 7: qg::launch_skinny<7>(W, fmt, ws, N, K, y, stream); break;
-    case 8: qg::launch_skinny<8>(W, fmt, ws, N, K, y, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return fmt == QG_Q4_K ? qg::launch_skinny_fmt<QG_Q4_K>(W, ws, M, N, K, y, stream)
+                        : qg::launch_skinny_fmt<QG_Q6_K>(W, ws, M, N, K, y, stream);
 }

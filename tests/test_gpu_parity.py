@@ -253,3 +253,20 @@ def test_full_size_sampled(g):
     tol = bound(x, rows, max_abs_w(g.fmt, W, g.N, g.K))
     r = check(y[np.ix_(rows, cols)], ref, tol, g.name)
     print(f"{g.name}: max err/tol {r:.2e}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
+@pytest.mark.parametrize("K", [256, 512, 1024, 2048, 2560, 4096, 4352, 8192, 12288])
+def test_skinny_all_row_splits(fmt, K):
+    """Skinny path over K values whose super-block counts select every work split
+    (several rows per wavefront step, one row per step, several steps per row,
+    partial last step) and over M rows that do and do not fit the LDS staging."""
+    N = 77
+    W = synth.pack(fmt, synth.normal(590 + K, (N, K), 0.0, 0.02))
+    wmax = max_abs_w(fmt, W, N, K)
+    for M in (1, 2, 5, 8):
+        x = synth.to_bf16_bits(synth.normal(591 + M, (M, K)))
+        ref = oracle.gemm(fmt, W, x, N)
+        tol = bound(x, np.arange(M), wmax)
+        check(gpu_prefill(W, fmt, x, N, qg.QG_PATH_SKINNY), ref, tol,
+              f"skinny M={M} N={N} K={K} {qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)}")
