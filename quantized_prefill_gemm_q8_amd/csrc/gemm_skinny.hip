@@ -18,10 +18,12 @@
 //         128half + 32c + 16lh + i (c = 0..3, i < 16), which are the 16-value
 //         sub-blocks 8half + 2c + lh; plus the 8 scale bytes of its half and d.
 //         Q6_K blocks are 210 bytes, so these loads are only 2-byte aligned
-//         (gfx950 serves unaligned vector loads).
+//         (gfx950 serves unaligned vector loads; realigning dword-aligned
+//         loads with v_alignbyte measured no faster).
 // So a wavefront covers 16 super-blocks (4096 values) per step.  A row of nsb
 // super-blocks takes ceil(nsb/16) steps; when nsb divides 16, one step covers
-// R = 16/nsb whole rows.  Every wavefront streams a contiguous range of rows,
+// R = 16/nsb whole rows.  Wavefronts take rows (or R-row groups) in turn, so
+// the grid streams one narrow band of the matrix at a time; each wavefront has
 // the loads of step t+1 in flight while step t is computed (two register
 // buffers used in turn).
 //
@@ -43,7 +45,6 @@
 namespace qg {
 
 typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
-typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
@@ -56,10 +57,11 @@ __device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
 
 // Raw bytes one lane loads for one super-block.
 struct SkRaw {
-  uint4 a, b, c;   // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
-  uint32_t s0, s1; // Q6_K: the 8 scale bytes of the lane's half
-  uint32_t dh;     // Q6_K: d (binary16 bits)
+  uint4 a, b, c;        // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
+  uint32_t s0, s1, dh;  // Q6_K: the 8 scale bytes of the lane's half, d (binary16)
 };
+
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 
 constexpr int kSkThreads = 256;
 constexpr int kSkMaxLds = 64 * 1024;
@@ -73,19 +75,39 @@ __device__ __forceinline__ int sum16(const uint4& x) {
   return dot4(0x01010101u, x.w, s);
 }
 
+// Sum of v over each aligned group of G lanes (G = 4, 8, 16, 32, 64) with DPP
+// moves; the sum ends in the group's last lane (for G <= 16 in all its lanes).
+// Steps: quad swaps, half-row and row mirrors, then the row broadcasts of
+// lane 15 and lane 31 into the following rows.
+template <int G>
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if (G >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if (G >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  if (G >= 32)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  if (G >= 64)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
 // FMT: QG_Q4_K / QG_Q6_K.  MR: activation rows.  R: rows per wavefront step
 // (16/nsb when that divides, else 1).  XM: where the activations are read.
 template <int FMT, int MR, int R, int XM>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ gdx,
-    const float* __restrict__ gdS, int64_t N, int64_t K, int64_t rows_per_wave,
-    float* __restrict__ y) {
+    const float* __restrict__ gdS, int64_t N, int64_t K, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : kQ6Bytes;
   constexpr int G = 64 / R;  // lanes per row within a step
   const int64_t nsb = K / 256, nb = K / 32;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kSkThreads / 64) + (threadIdx.x >> 6);
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kSkThreads / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int8_t* xs = qx;
   const float* xd = gdx;
@@ -107,17 +129,18 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     xS = lS;
   }
 
-  const int64_t row_begin = wave * rows_per_wave;
-  int64_t row_end = row_begin + rows_per_wave;
-  row_end = row_end < N ? row_end : N;
-  if (row_begin >= row_end) return;
+  // wavefront w takes rows w*R + k*stride (+ 0..R-1), k = 0, 1, ...: at any
+  // time the whole grid streams one narrow band of the weight matrix
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * (kSkThreads / 64) * R;
+  const int64_t row_begin = wave * R;
+  if (row_begin >= N) return;
 
   const int grp = lane >> 2, s = lane & 3;
   const int half = s >> 1, lh = s & 1;              // Q6_K lane roles
   const int ro = grp / (16 / R);                    // row of this lane within a step
   const int jb0 = R > 1 ? grp % (16 / R) : grp;     // super-block of this lane in a row's first step
   const int64_t ipr = R > 1 ? 1 : (nsb + 15) / 16;  // steps per row
-  const int64_t nsteps = (row_end - row_begin + R - 1) / R * ipr;
+  const int64_t nsteps = (N - row_begin + stride - 1) / stride * ipr;
   const int64_t row_bytes = nsb * BB;
   // lane offset inside a super-block of each of its loads
   const uint32_t off_a = FMT == QG_Q4_K ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
@@ -154,9 +177,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     }
   }
 
+  // Lanes past the row range or past the row's last super-block (partial last
+  // steps) load a clamped, valid block and their contribution is dropped, so
+  // the step code has no branches.
   auto load = [&](int64_t rs, int64_t it, SkRaw& r) {
-    const int64_t n = row_begin + rs * R + ro, jb = jb0 + 16 * it;
-    if (n >= row_end || jb >= nsb) return;
+    int64_t n = row_begin + rs * stride + ro, jb = jb0 + 16 * it;
+    n = n < N ? n : N - 1;
+    jb = jb < nsb ? jb : nsb - 1;
     const uint8_t* blk = W + n * row_bytes + jb * BB;
     if (FMT == QG_Q4_K) {
       r.a = *reinterpret_cast<const uint4*>(blk + off_a);
@@ -178,8 +205,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   for (int m = 0; m < MR; m++) acc[m] = 0.0f;
 
   auto compute = [&](int64_t rs, int64_t it, const SkRaw& cur) {
-    const int64_t n = row_begin + rs * R + ro, jb = jb0 + 16 * it;
-    if (n < row_end && jb < nsb) {
+    const int64_t n = row_begin + rs * stride + ro, jbr = jb0 + 16 * it;
+    const bool valid = n < N && jbr < nsb;
+    const int64_t jb = jbr < nsb ? jbr : nsb - 1;
+    {
       if (FMT == QG_Q4_K) {
         const float d = half_to_float(cur.a.x & 0xFFFFu), dmin = half_to_float(cur.a.x >> 16);
         const Q4Scales sc = unpack_q4_scales(cur.a.y, cur.a.z, cur.a.w);
@@ -224,14 +253,15 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
           a = __builtin_fmaf(static_cast<float>(I1), dsc1 * dx1, a);
           a = __builtin_fmaf(-dm0, dS0, a);
           a = __builtin_fmaf(-dm1, dS1, a);
-          acc[m] = a;
+          acc[m] = valid ? a : acc[m];
         }
       } else {
         const float d = half_to_float(cur.dh & 0xFFFFu);
+        const uint32_t s0 = cur.s0, s1 = cur.s1;
         float dsc[4];
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-          const uint32_t sw = c < 2 ? cur.s0 : cur.s1;
+          const uint32_t sw = c < 2 ? s0 : s1;
           dsc[c] = d * static_cast<float>(static_cast<int8_t>(byte_of(sw, (2 * c + lh) & 3)));
         }
         const uint32_t l0[4] = {cur.a.x, cur.a.y, cur.a.z, cur.a.w};
@@ -274,7 +304,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
             I = dot4(q[c][3], xv.w, I);
             a = __builtin_fmaf(static_cast<float>(I), dsc[c] * dxc, a);
           }
-          acc[m] = a;
+          acc[m] = valid ? a : acc[m];
         }
       }
     }
@@ -282,11 +312,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     if (it == ipr - 1) {
 #pragma unroll
       for (int m = 0; m < MR; m++) {
-        float v = acc[m];
-#pragma unroll
-        for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        const float v = group_sum_last<G>(acc[m]);
         acc[m] = 0.0f;
-        if ((lane & (G - 1)) == 0 && n < row_end) y[m * N + n] = v;
+        if ((lane & (G - 1)) == G - 1 && n < N) y[m * N + n] = v;
       }
     }
   };
@@ -299,19 +327,22 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       ++rs;
     }
   };
+  // The loads are issued unconditionally (past the last step they re-read a
+  // clamped, valid block), so the compiler's wait before each step counts
+  // exactly the next step's loads and leaves them in flight.
   SkRaw r0 = {}, r1 = {};
   int64_t rs0 = 0, it0 = 0;
   load(rs0, it0, r0);
   for (int64_t t = 0; t < nsteps; t += 2) {
     int64_t rs1 = rs0, it1 = it0;
     advance(rs1, it1);
-    if (t + 1 < nsteps) load(rs1, it1, r1);
+    load(rs1, it1, r1);
     compute(rs0, it0, r0);
     if (t + 1 >= nsteps) break;
     rs0 = rs1;
     it0 = it1;
     advance(rs0, it0);
-    if (t + 2 < nsteps) load(rs0, it0, r0);
+    load(rs0, it0, r0);
     compute(rs1, it1, r1);
   }
 }
@@ -334,27 +365,25 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
 template <int FMT, int MR, int R>
 static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                   float* y, hipStream_t stream) {
-  // about eight workgroups (32 wavefronts) per CU, each wavefront a contiguous
-  // run of rows; a multiple of R rows per wavefront
-  constexpr int64_t kWaves = 256 * 32;
-  int64_t rpw = (N + kWaves - 1) / kWaves;
-  rpw = (rpw + R - 1) / R * R;
-  const int64_t waves = (N + rpw - 1) / rpw;
+  // about four workgroups (16 wavefronts) per CU, all resident at once
+  constexpr int64_t kWaves = 256 * 16;
+  const int64_t row_groups = (N + R - 1) / R;
+  const int64_t waves = row_groups < kWaves ? row_groups : kWaves;
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
   switch (skinny_xmode(FMT, MR, K)) {
     case kXReg:
       if constexpr (MR <= 4)
         skinny_kernel<FMT, MR, R, kXReg><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
-                                                                               N, K, rpw, y);
+                                                                               N, K, y);
       break;
     case kXLds:
       skinny_kernel<FMT, MR, R, kXLds>
           <<<grid, dim3(kSkThreads), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
-              W, ws.q, ws.dx, ws.dS, N, K, rpw, y);
+              W, ws.q, ws.dx, ws.dS, N, K, y);
       break;
     default:
       skinny_kernel<FMT, MR, R, kXGlb><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N,
-                                                                             K, rpw, y);
+                                                                             K, y);
   }
   return hipGetLastError();
 }
