@@ -30,31 +30,10 @@
 // activation quantiser, so two K=16 bf16 MFMAs per tile and super-block give
 // sum_j m_j * dS_j to fp32 accuracy; one FMA per element then applies -dmin.
 #include "common.h"
+#include "lds_stage.h"
 #include "mfma_epilogue.h"
 
 namespace qg {
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// global_load_lds_dwordx4: 16 bytes per lane from global memory straight into
-// LDS; lane l writes lds_base + 16*l (lds_base is wave-uniform, passed in M0).
-// Issued from inline assembly on purpose: the compiler does not count these
-// loads, so it adds no wait for them before every LDS read (it cannot tell
-// the stage being filled from the one being read); the kernel waits for them
-// itself with an explicit vmcnt and a barrier.
-__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds_dst)));
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
-
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding and its LDS reads are done, then meet the workgroup barrier.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // The eight 6-bit mins of a super-block as bfloat16 integers (exact): two
 // dwords m[0..3], m[4..7] of bytes -> four dwords of bf16 pairs.

@@ -1,74 +1,234 @@
 // Tiled prefill GEMM for Q6_K weights on the int8 matrix cores (gfx950).
 //
-// Same scheme as the Q4_K kernel (fused decode in registers, int8 MFMA, fp32
-// scale epilogue with the magic-constant accumulator and the DPP-broadcast
-// activation scale), with Q6_K's 16-value sub-blocks: one
-// v_mfma_i32_32x32x16_i8 per sub-block, its int32 partial scaled by the
-// sub-block's d*sc, and the activation scale dx of the 32-value block holding
-// it.  Codes are fed to the matrix core as the signed bytes q6 - 32, so there
-// is no min term.
+// Same scheme as the Q4_K kernel (the fused "decode super-blocks in
+// registers, int8 tensor-core GEMM" of sparkinfer PR #464, section "Summary"),
+// with Q6_K's 16-value sub-blocks: one v_mfma_i32_32x32x16_i8 per sub-block,
+// its int32 partial scaled by the sub-block's d*sc, and the activation scale
+// dx of the 32-value block holding it.  Codes are fed to the matrix core as
+// the signed bytes q6 - 32, so there is no min term.
 //
 // Per y[m][n]: sum over 16-value sub-blocks s of dx[m][s/2] * d*sc[n][s] * I16.
 // d*sc has at most 19 significant bits (binary16 d times an int8), so
-// c = -12582912*d*sc is exact and fma(f, d*sc, c) = fl(I16 * d*sc).
+// c = -12582912*d*sc is exact and fma(f, d*sc, c) = fl(I16 * d*sc), with f the
+// accumulator started at the bit pattern of 12582912.0f.
+//
+// LDS pipeline (as the Q4_K kernel): WM x WN waves share super-block stages in
+// an NS-deep ring filled by global_load_lds_dwordx4; one stage holds
+//   A  [BM][256]  int8 activation codes, 16-byte chunks XOR-swizzled by row%16
+//   W  [BN][224]  the 210-byte blocks: bytes 0..207 as 13 chunks, then bytes
+//                 194..209 as a 14th chunk (so d sits at 222..223); the
+//                 blocks start 2-byte aligned in global memory
+//   DX [8][BM]    fp32 activation block scales, block-major (from dxT)
+// Each wave owns TM x TN tiles of 32x32 outputs.  Per 32-value block a lane
+// decodes the two sub-blocks' weight codes of its column from LDS (8 codes
+// each: low nibbles from ql, two high bits from qh) and reads the 16 row
+// scales its accumulator elements need.
 #include "common.h"
+#include "lds_stage.h"
 #include "mfma_epilogue.h"
 
 namespace qg {
 
-constexpr int kQ6WM = 2, kQ6WN = 2;
+constexpr int kQ6Row = 224;  // LDS bytes per staged Q6_K block
 
-__global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict__ W,
-                                                       const int8_t* __restrict__ qx,
-                                                       const float* __restrict__ dx, int64_t M,
-                                                       int64_t N, int64_t K, float* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int TM, int TN, int WM, int WN, int NS>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, int64_t M, int64_t N, int64_t K, float* __restrict__ y) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
+  constexpr int A_BYTES = BM * 256, W_BYTES = BN * kQ6Row, X_BYTES = BM * 32;
+  constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES;
+  constexpr int A_CH = A_BYTES / 16, W_CH = W_BYTES / 16, X_CH = X_BYTES / 16;
+  constexpr int CH = A_CH + W_CH + X_CH;
+  static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0,
+                "stage regions must be whole wave loads");
+  constexpr int LPT = (CH + NT - 1) / NT;  // loads per thread per stage
+  constexpr int JUNK = 1024;               // landing slot of the padding loads
+  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE + JUNK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 32 * kQ6WM + 32 * (wave / kQ6WN);
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 32 * kQ6WN + 32 * (wave % kQ6WN);
-  const int64_t n = n0 + l32, n_ld = n < N ? n : N - 1;
-  const int64_t m_a = m0 + l32 < M ? m0 + l32 : M - 1;
-  const int64_t nsb = K / 256, nb = K / 32;
-  const int8_t* arow = qx + m_a * K + 8 * h;
-  // rows beyond M read the workspace's padding rows (finite or not, they only
-  // reach discarded outputs)
-  const float* dxrow = dx + (m0 + dpp_scale_row(lane)) * nb;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
+  const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * BN;
+  const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
+  const int64_t nsb = K / 256;
+  const int64_t wrow_bytes = nsb * kQ6Bytes;
+
+  auto issue_stage = [&](int64_t sb, int buf) {
+    uint8_t* base = lds + buf * STAGE;
+#pragma unroll(LPT <= 8 ? LPT : 1)
+    for (int it = 0; it < LPT; it++) {
+      const int q0 = wave * 64 + it * NT;  // region tests are uniform per wave
+      if (q0 >= CH) {                      // padding load: same count on every wave
+        lds_dma16(qx, lds + NS * STAGE);
+        continue;
+      }
+      const int q = q0 + lane;
+      const void* src;
+      if (q0 < A_CH) {
+        const int row = q >> 4, pos = q & 15, c16 = pos ^ (row & 15);
+        int64_t m = m_cta + row;
+        m = m < M ? m : M - 1;
+        src = qx + m * K + sb * 256 + 16 * c16;
+      } else if (q0 < A_CH + W_CH) {
+        const int qq = q - A_CH, row = qq / 14, part = qq - 14 * row;
+        int64_t n = n_cta + row;
+        n = n < N ? n : N - 1;
+        src = W + n * wrow_bytes + sb * kQ6Bytes + (part < 13 ? 16 * part : 194);
+      } else {
+        const int qq = q - A_CH - W_CH;
+        const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
+        src = dxT + (8 * sb + jb) * Mp + m_cta + 4 * r4;
+      }
+      lds_dma16(src, base + 16 * q0);
+    }
+  };
 
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; r++) magic[r] = kMagicBits;
-  float acc[16];
+  float acc[TM][TN][16];
 #pragma unroll
-  for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  for (int64_t sb = 0; sb < nsb; sb++) {
-    const uint8_t* blk = W + (n_ld * nsb + sb) * kQ6Bytes;
-    const float d = half_to_float(load_u16(blk + 208));
-#pragma unroll 2
-    for (int s = 0; s < 16; s++) {
-      const long a = *reinterpret_cast<const long*>(arow + 256 * sb + 16 * s);
-      const v16i D = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, q6_codes(blk, s, h), magic, 0, 0, 0);
-      const float dsc = d * static_cast<float>(static_cast<int8_t>(blk[192 + s]));
-      epilogue_scale(acc, D, dsc, -kMagic * dsc, dxrow[8 * sb + (s >> 1)]);
-    }
-  }
-  if (n < N) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int64_t m = m0 + acc_row(r, h);
-      if (m < M) y[m * N + n] = acc[r];
+  for (int s0 = 0; s0 < NS - 1; s0++)
+    if (s0 < nsb) issue_stage(s0, s0);
+  for (int64_t sb = 0; sb < nsb; sb++) {
+    const int buf = static_cast<int>(sb % NS);
+    // stage sb has landed once at most the NS-2 later stages' loads are
+    // outstanding (near the end: all); after the barrier no wave still reads
+    // stage sb-1, whose buffer the next issue refills
+    if (sb + NS - 1 <= nsb) wait_vm_barrier<LPT * (NS - 2)>();
+    else wait_vm_barrier<0>();
+    if (sb + NS - 1 < nsb) issue_stage(sb + NS - 1, static_cast<int>((sb + NS - 1) % NS));
+
+    const uint8_t* sA = lds + buf * STAGE;
+    const uint8_t* sW = sA + A_BYTES;
+    const float* sX = reinterpret_cast<const float*>(sW + W_BYTES);
+
+    const uint8_t* wr[TN];
+    uint4 scv[TN];
+    float d[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      wr[j] = sW + (nl0 + 32 * j + l32) * kQ6Row;
+      scv[j] = *reinterpret_cast<const uint4*>(wr[j] + 192);
+      d[j] = half_to_float(*reinterpret_cast<const uint16_t*>(wr[j] + 222));
+    }
+
+#pragma unroll 2
+    for (int b = 0; b < 8; b++) {  // 32-value block of the super-block
+      const int half = b >> 2, c = b & 3;
+      // weight codes of the two sub-blocks s = 2b + e, this lane's 8 values
+      // 16e + 8h + i of quarter c: low nibbles ql[64half + 32(c&1) + 16e + 8h + i]
+      // (high nibble when c >= 2), top bits qh[32half + 16e + 8h + i] >> 2c
+      long bq[TN][2];
+      float dsc[TN][2], cc[TN][2];
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        const uint8_t* pl = wr[j] + 64 * half + 32 * (c & 1) + 8 * h;
+        const uint8_t* ph = wr[j] + 128 + 32 * half + 8 * h;
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+          const uint2 lo8 = *reinterpret_cast<const uint2*>(pl + 16 * e);
+          const uint2 hi8 = *reinterpret_cast<const uint2*>(ph + 16 * e);
+          const int ls = 4 * (c >> 1), hs = 2 * c;
+          const uint32_t w0 = q6_to_signed(((lo8.x >> ls) & 0x0F0F0F0Fu) | (((hi8.x >> hs) & 0x03030303u) << 4));
+          const uint32_t w1 = q6_to_signed(((lo8.y >> ls) & 0x0F0F0F0Fu) | (((hi8.y >> hs) & 0x03030303u) << 4));
+          bq[j][e] = static_cast<long>((static_cast<uint64_t>(w1) << 32) | w0);
+          const int s = 2 * b + e;
+          const uint32_t sw = s < 4 ? scv[j].x : s < 8 ? scv[j].y : s < 12 ? scv[j].z : scv[j].w;
+          dsc[j][e] = d[j] * static_cast<float>(static_cast<int8_t>(byte_of(sw, s & 3)));
+          cc[j][e] = -kMagic * dsc[j][e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const int row = ml0 + 32 * i + l32;
+        float dxv[16];
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const float4 v = *reinterpret_cast<const float4*>(sX + b * BM + ml0 + 32 * i + 8 * g + 4 * h);
+          dxv[4 * g] = v.x; dxv[4 * g + 1] = v.y; dxv[4 * g + 2] = v.z; dxv[4 * g + 3] = v.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+          const int s = 2 * b + e;
+          const long a = *reinterpret_cast<const long*>(sA + row * 256 + 16 * (s ^ (row & 15)) + 8 * h);
+#pragma unroll
+          for (int j = 0; j < TN; j++) {
+            const v16i D = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq[j][e], magic, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const float u = __builtin_fmaf(bits_to_float(D[r]), dsc[j][e], cc[j][e]);  // fl(I*dsc)
+              acc[i][j][r] = __builtin_fmaf(u, dxv[r], acc[i][j][r]);
+            }
+          }
+        }
+      }
     }
   }
+
+#pragma unroll
+  for (int j = 0; j < TN; j++) {
+    const int64_t n = n_cta + nl0 + 32 * j + l32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t m = m_cta + ml0 + 32 * i + acc_row(r, h);
+        if (m < M) y[m * N + n] = acc[i][j][r];
+      }
+  }
+}
+
+template <int TM, int TN, int WM, int WN, int NS>
+static void launch_q6k_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
+                           float* y, hipStream_t stream) {
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
+  gemm_q6k_lds_kernel<TM, TN, WM, WN, NS><<<grid, dim3(64 * WM * WN), 0, stream>>>(
+      W, ws.q, ws.dxT, ws.Mp, M, N, K, y);
+}
+
+// Kernel choice: the largest tile whose grid still covers every CU.
+enum class Q6Pick { k128x128, k128x64, k64x64 };
+
+inline Q6Pick pick_q6k(int64_t M, int64_t N) {
+  constexpr int64_t kCUs = 256;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= kCUs) return Q6Pick::k128x128;
+  if (((M + 127) / 128) * ((N + 63) / 64) >= kCUs) return Q6Pick::k128x64;
+  return Q6Pick::k64x64;
 }
 
 }  // namespace qg
 
-const char* qg_gemm_q6k_kernel_name(int64_t, int64_t, int64_t) { return "gemm_q6k_kernel"; }
+const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t) {
+  switch (qg::pick_q6k(M, N)) {
+    case qg::Q6Pick::k128x128: return "gemm_q6k_lds_kernel<2, 1, 2, 4, 2>";
+    case qg::Q6Pick::k128x64: return "gemm_q6k_lds_kernel<2, 1, 2, 2, 3>";
+    case qg::Q6Pick::k64x64: return "gemm_q6k_lds_kernel<1, 1, 2, 2, 4>";
+  }
+  return "?";
+}
 
 hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((N + 32 * qg::kQ6WN - 1) / (32 * qg::kQ6WN)),
-                  static_cast<unsigned>((M + 32 * qg::kQ6WM - 1) / (32 * qg::kQ6WM)));
-  qg::gemm_q6k_kernel<<<grid, dim3(256), 0, stream>>>(W, ws.q, ws.dx, M, N, K, y);
+  switch (qg::pick_q6k(M, N)) {
+    case qg::Q6Pick::k128x128: qg::launch_q6k_lds<2, 1, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k128x64: qg::launch_q6k_lds<2, 1, 2, 2, 3>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k64x64: qg::launch_q6k_lds<1, 1, 2, 2, 4>(W, ws, M, N, K, y, stream); break;
+  }
   return hipGetLastError();
 }
