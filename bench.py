@@ -19,6 +19,13 @@ the host.
 --calib-copy-mib N additionally runs a plain elementwise copy kernel over
 N MiB (read N, write N) three times: the reference dispatch for scaling HBM
 byte counters taken with a profiler.
+
+--pmc-summary FETCH_DB WRITE_DB OUT_JSON turns the databases of two
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of this script (with
+--calib-copy-mib) into per-kernel HBM bytes per dispatch, scaled by what the
+counters read for the copy kernel, stamped with a hash of the kernel sources;
+a later benchmark run reports them as `roofline.traffic` only while the
+sources still hash the same.
 """
 from __future__ import annotations
 
@@ -33,6 +40,84 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workload.json")
+CALIB_KERNEL = "neg_kernel"  # the copy kernel --calib-copy-mib launches
+
+
+def source_hash() -> str:
+    """sha256 over the library's kernel and header sources."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_prefill_gemm_q8_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files.append(os.path.join(ROOT, "include", "qgemm.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_kernel_name(name: str) -> str:
+    """'void qg::gemm_x<1, 2>(args)' -> 'gemm_x<1, 2>' (the form qgemm_kernel_name returns)."""
+    name = name.split("(")[0].strip()
+    if name.startswith("void "):
+        name = name[5:]
+    if name.startswith("qg::"):
+        name = name[4:]
+    return name
+
+
+def pmc_summary(fetch_db: str, write_db: str, out_json: str, calib_mib: int) -> None:
+    import sqlite3
+    per = {}
+    for db, counter in ((fetch_db, "FETCH_SIZE"), (write_db, "WRITE_SIZE")):
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, dispatch_id, counter_value from pmc_events "
+                           "where counter_name = ?", (counter,)).fetchall()
+        disp = {}
+        for name, did, v in rows:
+            key = (name, did)
+            disp[key] = disp.get(key, 0.0) + float(v)
+        for (name, _), v in disp.items():
+            d = per.setdefault(name, {}).setdefault(counter, [])
+            d.append(v)
+    calib = [n for n in per if CALIB_KERNEL in n]
+    if not calib:
+        raise SystemExit("no calibration copy kernel in the databases (run with --calib-copy-mib)")
+    cbytes = calib_mib * (1 << 20)
+    cf = per[calib[0]]
+    f_scale = cbytes / (sum(cf["FETCH_SIZE"]) / len(cf["FETCH_SIZE"]) * 1024.0)
+    w_scale = cbytes / (sum(cf["WRITE_SIZE"]) / len(cf["WRITE_SIZE"]) * 1024.0)
+    out = {"source_sha256": source_hash(), "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "calib_bytes": cbytes, "kernels": {}}
+    for name, d in per.items():
+        if "FETCH_SIZE" not in d or "WRITE_SIZE" not in d:
+            continue
+        fk = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
+        wk = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
+        out["kernels"][short_kernel_name(name)] = {
+            "dispatches": len(d["FETCH_SIZE"]), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+            "read_bytes": round(fk * 1024 * f_scale), "write_bytes": round(wk * 1024 * w_scale)}
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per dispatch of `kernel` from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k["read_bytes"] + k["write_bytes"]
 
 
 def parse():
@@ -45,11 +130,15 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
+    p.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_JSON"))
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, calib_mib=args.calib_copy_mib or 1024)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the kernel is shown at one GPU's share of the work).", file=sys.stderr)
@@ -243,7 +332,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dom,
                      "achieved": round(dom_tops, 3), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tops / PEAK_INT8_TOPS, 5),
-                     "traffic": None, "launches": dk["launches"],
+                     "traffic": traffic_for(dom), "launches": dk["launches"],
                      "avg_launch_us": round(1e3 * dk["ms"] / dk["launches"], 3),
                      "ops_per_launch": dk["ops"] // dk["launches"]},
         "gemm_kernels": {k: {"launches": d["launches"],

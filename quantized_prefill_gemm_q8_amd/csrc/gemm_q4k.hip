@@ -83,12 +83,9 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
   constexpr int A_BYTES = BM * 256, W_BYTES = BN * kQ4Bytes, X_BYTES = BM * 32, P_BYTES = BM * 48;
   constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES + P_BYTES;
   constexpr int A_CH = A_BYTES / 16, W_CH = W_BYTES / 16, X_CH = X_BYTES / 16, P_CH = P_BYTES / 16;
-  constexpr int CH = A_CH + W_CH + X_CH + P_CH;
   static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0 && P_CH % 64 == 0,
                 "stage regions must be whole wave loads");
-  constexpr int LPT = (CH + NT - 1) / NT;   // loads per thread per stage
   constexpr int JUNK = 1024;                // landing slot of the padding loads
-  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE + JUNK];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -102,42 +99,68 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
   const int64_t wrow_bytes = nsb * kQ4Bytes;
   const int drow = dpp_scale_row(lane);
 
-  auto issue_stage = [&](int64_t sb, int buf) {
-    uint8_t* base = lds + buf * STAGE;
-#pragma unroll((LPT <= 6 && OCC < 4) ? LPT : 1)
-    for (int it = 0; it < LPT; it++) {
-      const int q0 = wave * 64 + it * NT;  // region tests are uniform per wave
-      if (q0 >= CH) {                      // padding load: same count on every wave
-        lds_dma16(qx, lds + NS * STAGE);
-        continue;
-      }
-      const int q = q0 + lane;
-      const void* src;
-      if (q0 < A_CH) {
-        const int row = q >> 4, pos = q & 15, c16 = pos ^ (row & 15);
-        int64_t m = m_cta + row;
-        m = m < M ? m : M - 1;
-        src = qx + m * K + sb * 256 + 16 * c16;
-      } else if (q0 < A_CH + W_CH) {
-        const int qq = q - A_CH, row = qq / 9, part = qq - 9 * row;
-        int64_t n = n_cta + row;
-        n = n < N ? n : N - 1;
-        src = W + n * wrow_bytes + sb * kQ4Bytes + 16 * part;
-      } else if (q0 < A_CH + W_CH + X_CH) {
-        const int qq = q - A_CH - W_CH;
-        if (DPP) {
-          const int row = qq >> 1, half = qq & 1;
-          src = dx + (m_cta + row) * nb + 8 * sb + 4 * half;
-        } else {
-          const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
-          src = dxT + (8 * sb + jb) * Mp + m_cta + 4 * r4;
-        }
-      } else {
-        const int qq = q - A_CH - W_CH - X_CH, row = qq / 3, piece = qq - 3 * row;
-        src = dsp + ((m_cta + row) * nsb + sb) * 24 + 8 * piece;
-      }
-      lds_dma16(src, base + 16 * q0);
+  // Stage loads, region by region (A, W, DX, DSP).  A region of R_CH chunks
+  // is R_CH/64 wave-loads; wave w issues wave-loads w, w+NW, ... and every
+  // wave issues the same count per region (a wave-load past the region's end
+  // reads the region's first chunk into the junk slot), so a fixed vmcnt
+  // waits for a whole stage.  Each load reads base(region, sb) + voff: the
+  // base is a wave-uniform pointer advanced per super-block (SGPRs); voff is
+  // this lane's byte offset, computed once (tail rows and columns clamped to
+  // the last valid one).
+  constexpr int LA = (A_CH / 64 + NW - 1) / NW, LW = (W_CH / 64 + NW - 1) / NW;
+  constexpr int LX = (X_CH / 64 + NW - 1) / NW, LP = (P_CH / 64 + NW - 1) / NW;
+  uint32_t voff[LA + LW + LX + LP];
+#pragma unroll
+  for (int it = 0; it < LA; it++) {
+    const int q = (wave + it * NW) * 64 + lane;
+    const int row = q >> 4, c16 = (q & 15) ^ (row & 15);
+    const int64_t m = m_cta + row < M ? m_cta + row : M - 1;
+    voff[it] = (wave + it * NW) < A_CH / 64 ? static_cast<uint32_t>((m - m_cta) * K + 16 * c16) : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < LW; it++) {
+    const int qq = (wave + it * NW) * 64 + lane, row = qq / 9, part = qq - 9 * row;
+    const int64_t n = n_cta + row < N ? n_cta + row : N - 1;
+    voff[LA + it] = (wave + it * NW) < W_CH / 64 ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + 16 * part) : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < LX; it++) {
+    const int qq = (wave + it * NW) * 64 + lane;
+    uint32_t v;
+    if (DPP) {
+      const int row = qq >> 1, hf = qq & 1;
+      v = static_cast<uint32_t>((row * nb + 4 * hf) * 4);
+    } else {
+      const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
+      v = static_cast<uint32_t>((jb * Mp + 4 * r4) * 4);
     }
+    voff[LA + LW + it] = (wave + it * NW) < X_CH / 64 ? v : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < LP; it++) {
+    const int qq = (wave + it * NW) * 64 + lane, row = qq / 3, piece = qq - 3 * row;
+    voff[LA + LW + LX + it] = (wave + it * NW) < P_CH / 64 ? static_cast<uint32_t>(row * nsb * 48 + 16 * piece) : 0u;
+  }
+  constexpr int LPT = LA + LW + LX + LP;  // loads per thread per stage
+  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
+
+  auto issue_region = [&](const void* rbase, int first, int count, int nwl, int chunk0, uint8_t* sbase) {
+#pragma unroll
+    for (int it = 0; it < count; it++) {
+      const int wl = wave + it * NW;
+      lds_dma16_sv(rbase, voff[first + it],
+                   wl < nwl ? static_cast<const void*>(sbase + 16 * (chunk0 + 64 * wl))
+                            : static_cast<const void*>(lds + NS * STAGE));
+    }
+  };
+  auto issue_stage = [&](int64_t sb, int buf) {
+    uint8_t* sbase = lds + buf * STAGE;
+    issue_region(qx + m_cta * K + sb * 256, 0, LA, A_CH / 64, 0, sbase);
+    issue_region(W + n_cta * wrow_bytes + sb * kQ4Bytes, LA, LW, W_CH / 64, A_CH, sbase);
+    issue_region(DPP ? static_cast<const void*>(dx + m_cta * nb + 8 * sb)
+                     : static_cast<const void*>(dxT + 8 * sb * Mp + m_cta),
+                 LA + LW, LX, X_CH / 64, A_CH + W_CH, sbase);
+    issue_region(dsp + (m_cta * nsb + sb) * 24, LA + LW + LX, LP, P_CH / 64, A_CH + W_CH + X_CH, sbase);
   };
 
   v16i magic;
@@ -439,16 +462,18 @@ static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64
 
 namespace {
 
-// Kernel choice for a Q4_K problem: large grids get workgroups of 8 waves
-// sharing 128x256 (or 64x128) tiles through LDS; smaller ones one 32x32 tile
-// per wave with the K range split so that the chip gets about two waves per
-// SIMD.
+// Kernel choice for a Q4_K problem (measured on the workloads' shapes):
+// long prompts (M >= 2048) with enough 128x256 tiles to cover every CU take
+// workgroups of 8 waves x 2x2 tiles; otherwise, with enough 64x128 tiles,
+// workgroups of 8 waves x one tile at 4 waves per SIMD (two workgroups per
+// CU); smaller grids one 32x32 tile per wave with the K range split so that
+// the chip gets about two waves per SIMD.
 enum class Q4Pick { kLds128x256, kLds64x128, kSmall1, kSmall2, kSmall4, kSmall8 };
 
 Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256, kTargetWaves = 2048;
   const int64_t nsb = K / 256;
-  if (((M + 127) / 128) * ((N + 255) / 256) >= kCUs) return Q4Pick::kLds128x256;
+  if (M >= 2048 && ((M + 127) / 128) * ((N + 255) / 256) >= kCUs) return Q4Pick::kLds128x256;
   if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs) return Q4Pick::kLds64x128;
   const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
   if (tiles >= kTargetWaves || nsb < 2) return Q4Pick::kSmall1;
@@ -462,7 +487,7 @@ Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
 const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K) {
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256: return "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2>";
-    case Q4Pick::kLds64x128: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 4, 2>";
+    case Q4Pick::kLds64x128: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4>";
     case Q4Pick::kSmall1: return "gemm_q4k_small_kernel<1>";
     case Q4Pick::kSmall2: return "gemm_q4k_small_kernel<2>";
     case Q4Pick::kSmall4: return "gemm_q4k_small_kernel<4>";
@@ -475,7 +500,7 @@ hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M
                               int64_t K, float* y, hipStream_t stream) {
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256: qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream); break;
-    case Q4Pick::kLds64x128: qg::launch_lds<1, 1, 2, 4, false, 4>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds64x128: qg::launch_lds<1, 1, 2, 4, false, 2, 4>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall1: qg::launch_small<1>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall2: qg::launch_small<2>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall4: qg::launch_small<4>(W, ws, M, N, K, y, stream); break;

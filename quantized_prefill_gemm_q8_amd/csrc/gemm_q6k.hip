@@ -41,12 +41,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
   constexpr int A_BYTES = BM * 256, W_BYTES = BN * kQ6Row, X_BYTES = BM * 32;
   constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES;
   constexpr int A_CH = A_BYTES / 16, W_CH = W_BYTES / 16, X_CH = X_BYTES / 16;
-  constexpr int CH = A_CH + W_CH + X_CH;
   static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0,
                 "stage regions must be whole wave loads");
-  constexpr int LPT = (CH + NT - 1) / NT;  // loads per thread per stage
-  constexpr int JUNK = 1024;               // landing slot of the padding loads
-  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
+  constexpr int JUNK = 1024;  // landing slot of the padding loads
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE + JUNK];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -59,34 +56,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
   const int64_t nsb = K / 256;
   const int64_t wrow_bytes = nsb * kQ6Bytes;
 
-  auto issue_stage = [&](int64_t sb, int buf) {
-    uint8_t* base = lds + buf * STAGE;
-#pragma unroll(LPT <= 8 ? LPT : 1)
-    for (int it = 0; it < LPT; it++) {
-      const int q0 = wave * 64 + it * NT;  // region tests are uniform per wave
-      if (q0 >= CH) {                      // padding load: same count on every wave
-        lds_dma16(qx, lds + NS * STAGE);
-        continue;
-      }
-      const int q = q0 + lane;
-      const void* src;
-      if (q0 < A_CH) {
-        const int row = q >> 4, pos = q & 15, c16 = pos ^ (row & 15);
-        int64_t m = m_cta + row;
-        m = m < M ? m : M - 1;
-        src = qx + m * K + sb * 256 + 16 * c16;
-      } else if (q0 < A_CH + W_CH) {
-        const int qq = q - A_CH, row = qq / 14, part = qq - 14 * row;
-        int64_t n = n_cta + row;
-        n = n < N ? n : N - 1;
-        src = W + n * wrow_bytes + sb * kQ6Bytes + (part < 13 ? 16 * part : 194);
-      } else {
-        const int qq = q - A_CH - W_CH;
-        const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
-        src = dxT + (8 * sb + jb) * Mp + m_cta + 4 * r4;
-      }
-      lds_dma16(src, base + 16 * q0);
+  // Stage loads region by region (A, W, DX) with per-lane byte offsets
+  // computed once and wave-uniform bases advanced per super-block; every wave
+  // issues the same count per region (a wave-load past the region's end reads
+  // the region's first chunk into the junk slot), so a fixed vmcnt waits for
+  // a whole stage.  Tail rows and columns are clamped to the last valid one.
+  constexpr int LA = (A_CH / 64 + NW - 1) / NW, LW = (W_CH / 64 + NW - 1) / NW;
+  constexpr int LX = (X_CH / 64 + NW - 1) / NW;
+  constexpr int LPT = LA + LW + LX;  // loads per thread per stage
+  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
+  uint32_t voff[LPT];
+#pragma unroll
+  for (int it = 0; it < LA; it++) {
+    const int q = (wave + it * NW) * 64 + lane;
+    const int row = q >> 4, c16 = (q & 15) ^ (row & 15);
+    const int64_t m = m_cta + row < M ? m_cta + row : M - 1;
+    voff[it] = (wave + it * NW) < A_CH / 64 ? static_cast<uint32_t>((m - m_cta) * K + 16 * c16) : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < LW; it++) {
+    const int qq = (wave + it * NW) * 64 + lane, row = qq / 14, part = qq - 14 * row;
+    const int64_t n = n_cta + row < N ? n_cta + row : N - 1;
+    voff[LA + it] = (wave + it * NW) < W_CH / 64
+                        ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + (part < 13 ? 16 * part : 194))
+                        : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < LX; it++) {
+    const int qq = (wave + it * NW) * 64 + lane;
+    const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
+    voff[LA + LW + it] = (wave + it * NW) < X_CH / 64 ? static_cast<uint32_t>((jb * Mp + 4 * r4) * 4) : 0u;
+  }
+  auto issue_region = [&](const void* rbase, int first, int count, int nwl, int chunk0, uint8_t* sbase) {
+#pragma unroll
+    for (int it = 0; it < count; it++) {
+      const int wl = wave + it * NW;
+      lds_dma16_sv(rbase, voff[first + it],
+                   wl < nwl ? static_cast<const void*>(sbase + 16 * (chunk0 + 64 * wl))
+                            : static_cast<const void*>(lds + NS * STAGE));
     }
+  };
+  auto issue_stage = [&](int64_t sb, int buf) {
+    uint8_t* sbase = lds + buf * STAGE;
+    issue_region(qx + m_cta * K + sb * 256, 0, LA, A_CH / 64, 0, sbase);
+    issue_region(W + n_cta * wrow_bytes + sb * kQ6Bytes, LA, LW, W_CH / 64, A_CH, sbase);
+    issue_region(dxT + 8 * sb * Mp + m_cta, LA + LW, LX, X_CH / 64, A_CH + W_CH, sbase);
   };
 
   v16i magic;
@@ -202,13 +216,16 @@ static void launch_q6k_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, i
       W, ws.q, ws.dxT, ws.Mp, M, N, K, y);
 }
 
-// Kernel choice: the largest tile whose grid still covers every CU.
-enum class Q6Pick { k128x128, k128x64, k64x64 };
+// Kernel choice (measured on the workloads' shapes): long prompts (M >= 2048)
+// with enough 128x128 tiles take 8 waves x 2x1 tiles; otherwise 64x128 tiles
+// (8 waves x one tile) while they give at least half a workgroup per CU, else
+// 64x64 tiles (4 waves).
+enum class Q6Pick { k128x128, k64x128, k64x64 };
 
 inline Q6Pick pick_q6k(int64_t M, int64_t N) {
   constexpr int64_t kCUs = 256;
-  if (((M + 127) / 128) * ((N + 127) / 128) >= kCUs) return Q6Pick::k128x128;
-  if (((M + 127) / 128) * ((N + 63) / 64) >= kCUs) return Q6Pick::k128x64;
+  if (M >= 2048 && ((M + 127) / 128) * ((N + 127) / 128) >= kCUs) return Q6Pick::k128x128;
+  if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs / 2) return Q6Pick::k64x128;
   return Q6Pick::k64x64;
 }
 
@@ -217,8 +234,8 @@ inline Q6Pick pick_q6k(int64_t M, int64_t N) {
 const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t) {
   switch (qg::pick_q6k(M, N)) {
     case qg::Q6Pick::k128x128: return "gemm_q6k_lds_kernel<2, 1, 2, 4, 2>";
-    case qg::Q6Pick::k128x64: return "gemm_q6k_lds_kernel<2, 1, 2, 2, 3>";
-    case qg::Q6Pick::k64x64: return "gemm_q6k_lds_kernel<1, 1, 2, 2, 4>";
+    case qg::Q6Pick::k64x128: return "gemm_q6k_lds_kernel<1, 1, 2, 4, 2>";
+    case qg::Q6Pick::k64x64: return "gemm_q6k_lds_kernel<1, 1, 2, 2, 2>";
   }
   return "?";
 }
@@ -227,8 +244,8 @@ hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M
                               int64_t K, float* y, hipStream_t stream) {
   switch (qg::pick_q6k(M, N)) {
     case qg::Q6Pick::k128x128: qg::launch_q6k_lds<2, 1, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
-    case qg::Q6Pick::k128x64: qg::launch_q6k_lds<2, 1, 2, 2, 3>(W, ws, M, N, K, y, stream); break;
-    case qg::Q6Pick::k64x64: qg::launch_q6k_lds<1, 1, 2, 2, 4>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k64x128: qg::launch_q6k_lds<1, 1, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k64x64: qg::launch_q6k_lds<1, 1, 2, 2, 2>(W, ws, M, N, K, y, stream); break;
   }
   return hipGetLastError();
 }

@@ -20,6 +20,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) 
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
+// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane
+// 32-bit byte offset (the saddr form): address = base + voff.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t voff, const void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds_dst)));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(base)), "{m0}"(m0)
+               : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and its LDS reads are done, then meet the workgroup barrier.
 template <int N>
