@@ -125,8 +125,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--lm-steps", type=int, default=50)
-    p.add_argument("--big-steps", type=int, default=30)
+    p.add_argument("--lm-steps", type=int, default=50)    # 0: skip the LM head
+    p.add_argument("--big-steps", type=int, default=30)   # 0: skip the large-M GEMMs
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -231,7 +231,7 @@ def main():
 
     # ---------------- large-M headline projections (one GEMM each, M = 512)
     big = {}
-    for g in (synth.CONFIGS[4][0], synth.CONFIGS[4][1]):
+    for g in (synth.CONFIGS[4][0], synth.CONFIGS[4][1]) if args.big_steps > 0 else ():
         Wb = to_dev(synth.make_weights(g))
         xb = to_dev(synth.make_acts(g))
         wsb = qg.alloc_workspace(g.M, g.K, dev)
@@ -255,30 +255,38 @@ def main():
         del Wb, xb, wsb, yb
 
     # ---------------- LM head on the last token: M = 1, K = 4096 -> N = 152064, Q6_K
-    lm = synth.CONFIGS[5][0]
-    W_lm = to_dev(synth.make_weights(lm))
-    x_lm = to_dev(synth.make_acts(lm))[0]
-    ws_lm = qg.alloc_workspace(1, lm.K, dev)
-    y_lm = torch.empty(lm.N, dtype=torch.float32, device=dev)
-    for _ in range(5):
-        qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
-    torch.cuda.synchronize()
-    qg.qgemm_quantize_workspace(x_lm, 1, lm.K, ws_lm, stream)
-    a, b = ev(), ev()
-    a.record(stream)
-    for _ in range(args.lm_steps):
-        qg.qgemm_gemm_quantized(W_lm, lm.fmt, ws_lm, 1, lm.N, lm.K, y_lm, stream, qg.QG_PATH_SKINNY)
-    b.record(stream)
-    c0, c1 = ev(), ev()
-    c0.record(stream)
-    for _ in range(args.lm_steps):
-        qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    lm_kernel_us = 1e3 * a.elapsed_time(b) / args.lm_steps
-    lm_call_us = 1e3 * c0.elapsed_time(c1) / args.lm_steps
-    lm_gbs = lm.w_bytes / (lm_kernel_us * 1e-6) / 1e9
-    del W_lm
+    lm_out = None
+    if args.lm_steps > 0:
+        lm = synth.CONFIGS[5][0]
+        W_lm = to_dev(synth.make_weights(lm))
+        x_lm = to_dev(synth.make_acts(lm))[0]
+        ws_lm = qg.alloc_workspace(1, lm.K, dev)
+        y_lm = torch.empty(lm.N, dtype=torch.float32, device=dev)
+        for _ in range(5):
+            qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
+        torch.cuda.synchronize()
+        qg.qgemm_quantize_workspace(x_lm, 1, lm.K, ws_lm, stream)
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.lm_steps):
+            qg.qgemm_gemm_quantized(W_lm, lm.fmt, ws_lm, 1, lm.N, lm.K, y_lm, stream, qg.QG_PATH_SKINNY)
+        b.record(stream)
+        c0, c1 = ev(), ev()
+        c0.record(stream)
+        for _ in range(args.lm_steps):
+            qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        lm_kernel_us = 1e3 * a.elapsed_time(b) / args.lm_steps
+        lm_call_us = 1e3 * c0.elapsed_time(c1) / args.lm_steps
+        lm_gbs = lm.w_bytes / (lm_kernel_us * 1e-6) / 1e9
+        del W_lm
+        lm_out = {"workload": "M=1, K=4096 -> N=152064, Q6_K (skinny path)",
+                  "kernel": qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K),
+                  "weight_bytes": lm.w_bytes, "kernel_us": round(lm_kernel_us, 3),
+                  "call_us": round(lm_call_us, 3), "gbps": round(lm_gbs, 1),
+                  "frac_hbm": round(lm_gbs / PEAK_HBM_GBS, 4),
+                  "traffic": traffic_for(qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K))}
 
     # ---------------- optional: plain copy kernel of known size (profiler counter scale)
     if args.calib_copy_mib > 0:
@@ -340,11 +348,7 @@ def main():
                              "tops": round(d["ops"] / (d["ms"] * 1e-3) / 1e12, 2)}
                          for k, d in per_kernel.items()},
         "large_m": big,
-        "lm_head": {"workload": "M=1, K=4096 -> N=152064, Q6_K (skinny path)",
-                    "kernel": qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K),
-                    "weight_bytes": lm.w_bytes, "kernel_us": round(lm_kernel_us, 3),
-                    "call_us": round(lm_call_us, 3), "gbps": round(lm_gbs, 1),
-                    "frac_hbm": round(lm_gbs / PEAK_HBM_GBS, 4)},
+        "lm_head": lm_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
