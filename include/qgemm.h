@@ -67,8 +67,9 @@ enum {
     QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
 };
 
-/* Largest skinny-path batch: rows M <= QG_SKINNY_MAX_M go to the bandwidth-bound
- * skinny kernel under QG_PATH_AUTO, larger M to the tiled matrix-core kernel. */
+/* Largest skinny-path batch.  Under QG_PATH_AUTO, Q6_K problems with
+ * M <= QG_SKINNY_MAX_M rows and Q4_K problems with M <= 4 rows go to the
+ * bandwidth-bound skinny kernel, larger M to the tiled matrix-core kernels. */
 #define QG_SKINNY_MAX_M 8
 
 /* Workspace bytes needed by qgemm_prefill / qgemm_lm_head for M activation rows
@@ -88,7 +89,8 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t K);
  *   workspace : device scratch of at least qgemm_workspace_bytes(M, K) bytes,
  *               256-byte aligned; its contents are scratch on entry and exit.
  *   stream    : hipStream_t (NULL = default stream).
- * Dispatch: M <= QG_SKINNY_MAX_M -> skinny kernel, otherwise the tiled kernel. */
+ * Dispatch: the skinny kernel for M <= QG_SKINNY_MAX_M (Q6_K) or M <= 4 (Q4_K),
+ * otherwise the tiled kernels. */
 int qgemm_prefill(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
                   int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,
                   void *stream);

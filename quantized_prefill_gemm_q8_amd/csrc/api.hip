@@ -64,6 +64,11 @@ int check_common(const void* W, int fmt, int64_t N, int64_t K) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ELAUNCH; }
 
+// QG_PATH_AUTO: the skinny kernel for M <= 8 Q6_K rows and M <= 4 Q4_K rows
+// (measured: from 5 rows on, the Q4_K tiled kernels are faster, while the
+// Q6_K skinny kernel stays ahead up to 8 rows).
+bool auto_skinny(int fmt, int64_t M) { return M <= (fmt == QG_Q6_K ? QG_SKINNY_MAX_M : 4); }
+
 }  // namespace
 
 extern "C" {
@@ -124,7 +129,7 @@ int qgemm_gemm_quantized(const void* q_weights, int fmt, const void* workspace,
   rc = check_device();
   if (rc) return rc;
   const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
-  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && M <= QG_SKINNY_MAX_M);
+  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (skinny) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
@@ -171,7 +176,7 @@ const char* qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path
   if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
   if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return NULL;
   if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return NULL;
-  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && M <= QG_SKINNY_MAX_M);
+  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
   if (skinny) return qg_gemm_skinny_kernel_name(fmt, M, K);
   return fmt == QG_Q4_K ? qg_gemm_q4k_kernel_name(M, N, K) : qg_gemm_q6k_kernel_name(M, N, K);
 }

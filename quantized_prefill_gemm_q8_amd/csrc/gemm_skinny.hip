@@ -29,7 +29,7 @@
 //
 // Activations.  When a row takes a single step, every lane works on the same
 // 64 activation values in every step, so it keeps their codes, block scales
-// and the -32 correction of the Q6_K codes in registers (XREG, for M <= 4).
+// and the -32 correction of the Q6_K codes in registers (XREG).
 // Otherwise the activation rows are staged in LDS once per workgroup (XLDS)
 // or, when they do not fit, read from global memory where they stay L2-resident
 // (XGLB).
@@ -358,7 +358,7 @@ inline int64_t skinny_lds_bytes(int fmt, int64_t M, int64_t K) {
 }
 
 inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
-  if (M <= 4 && K <= 4096) return kXReg;
+  if (K <= 4096) return kXReg;
   return skinny_lds_bytes(fmt, M, K) <= kSkMaxLds ? kXLds : kXGlb;
 }
 
@@ -372,9 +372,8 @@ static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
   switch (skinny_xmode(FMT, MR, K)) {
     case kXReg:
-      if constexpr (MR <= 4)
-        skinny_kernel<FMT, MR, R, kXReg><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
-                                                                               N, K, y);
+      skinny_kernel<FMT, MR, R, kXReg><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
+                                                                             N, K, y);
       break;
     case kXLds:
       skinny_kernel<FMT, MR, R, kXLds>

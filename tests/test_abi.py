@@ -98,3 +98,33 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 256, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qg.prefill(W, qg.QG_Q4_K, x, 8, workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_kernel_name_dispatch_rule():
+    """Host dispatch (no GPU): which kernel each path and shape selects."""
+    kn = qg.qgemm_kernel_name
+    Q4, Q6, AUTO, TILED, SKINNY = qg.QG_Q4_K, qg.QG_Q6_K, qg.QG_PATH_AUTO, qg.QG_PATH_TILED, qg.QG_PATH_SKINNY
+    # skinny below the measured crossover: Q4_K up to 4 rows, Q6_K up to 8
+    assert kn(Q4, 4, 4096, 4096, AUTO).startswith("skinny_kernel<0, 4,")
+    assert kn(Q4, 5, 4096, 4096, AUTO).startswith("gemm_q4k_")
+    assert kn(Q6, 8, 152064, 4096, AUTO).startswith("skinny_kernel<1, 8,")
+    assert kn(Q6, 9, 152064, 4096, AUTO).startswith("gemm_q6k_")
+    assert kn(Q4, 8, 4096, 4096, SKINNY).startswith("skinny_kernel<0, 8,")
+    assert kn(Q4, 1, 4096, 4096, TILED).startswith("gemm_q4k_")
+    # skinny work split: rows per step R = 16 / (K/256) when that divides, else 1;
+    # activations in registers up to K = 4096, then LDS, then L2
+    assert kn(Q6, 1, 152064, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0>"
+    assert kn(Q4, 2, 100, 1024, AUTO) == "skinny_kernel<0, 2, 4, 0>"
+    assert kn(Q4, 1, 100, 2560, AUTO) == "skinny_kernel<0, 1, 1, 0>"
+    assert kn(Q6, 8, 100, 4352, AUTO) == "skinny_kernel<1, 8, 1, 1>"
+    assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2>"
+    # tiled tile choice by grid size
+    assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2>"
+    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4>"
+    assert kn(Q4, 64, 1024, 1024, AUTO).startswith("gemm_q4k_small_kernel<")
+    assert kn(Q6, 8192, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<2, 1, 2, 4, 2>"
+    # arguments the entry points would reject
+    assert kn(2, 8, 8, 256, AUTO) is None
+    assert kn(Q4, 8, 8, 300, AUTO) is None
+    assert kn(Q4, 9, 8, 256, SKINNY) is None
+    assert kn(Q4, 0, 8, 256, AUTO) is None
