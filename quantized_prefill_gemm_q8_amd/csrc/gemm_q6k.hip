@@ -8,9 +8,15 @@
 // the signed bytes q6 - 32, so there is no min term.
 //
 // Per y[m][n]: sum over 16-value sub-blocks s of dx[m][s/2] * d*sc[n][s] * I16.
-// d*sc has at most 19 significant bits (binary16 d times an int8), so
-// c = -12582912*d*sc is exact and fma(f, d*sc, c) = fl(I16 * d*sc), with f the
-// accumulator started at the bit pattern of 12582912.0f.
+// The accumulator starts at the bit pattern of M = 12582912.0f, so its int32
+// result reads as the float f = M + I16.  The two sub-blocks a, b of one
+// 32-value activation block share dx and are combined in two fmas:
+// p = fma(f_a, dsc_a, -M*(dsc_a + dsc_b)) = I_a*dsc_a - M*dsc_b (the constant
+// is exact: d*(sc_a + sc_b) has at most 20 significant bits), then
+// t = fma(f_b, dsc_b, p) = I_a*dsc_a + I_b*dsc_b, and acc += t*dx.  p carries
+// one rounding at the magnitude of M*dsc_b, i.e. an error below half a unit of
+// I_b*dsc_b per block: far inside the output tolerance, and zero whenever the
+// products are integers below 2^24 (unit scales).
 //
 // LDS pipeline (as the Q4_K kernel): WM x WN waves share super-block stages in
 // an NS-deep ring filled by global_load_lds_dwordx4; one stage holds
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
       // 16e + 8h + i of quarter c: low nibbles ql[64half + 32(c&1) + 16e + 8h + i]
       // (high nibble when c >= 2), top bits qh[32half + 16e + 8h + i] >> 2c
       long bq[TN][2];
-      float dsc[TN][2], cc[TN][2];
+      float dsc[TN][2], cc[TN][1];
 #pragma unroll
       for (int j = 0; j < TN; j++) {
         const uint8_t* pl = wr[j] + 64 * half + 32 * (c & 1) + 8 * h;
@@ -163,8 +169,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
           const int s = 2 * b + e;
           const uint32_t sw = s < 4 ? scv[j].x : s < 8 ? scv[j].y : s < 12 ? scv[j].z : scv[j].w;
           dsc[j][e] = d[j] * static_cast<float>(static_cast<int8_t>(byte_of(sw, s & 3)));
-          cc[j][e] = -kMagic * dsc[j][e];
         }
+        // exact: d*(sc0 + sc1) has at most 20 significant bits
+        cc[j][0] = -kMagic * (dsc[j][0] + dsc[j][1]);
       }
 #pragma unroll
       for (int i = 0; i < TM; i++) {
@@ -175,18 +182,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
           const float4 v = *reinterpret_cast<const float4*>(sX + b * BM + ml0 + 32 * i + 8 * g + 4 * h);
           dxv[4 * g] = v.x; dxv[4 * g + 1] = v.y; dxv[4 * g + 2] = v.z; dxv[4 * g + 3] = v.w;
         }
+        long a[2];
 #pragma unroll
         for (int e = 0; e < 2; e++) {
           const int s = 2 * b + e;
-          const long a = *reinterpret_cast<const long*>(sA + row * 256 + 16 * (s ^ (row & 15)) + 8 * h);
+          a[e] = *reinterpret_cast<const long*>(sA + row * 256 + 16 * (s ^ (row & 15)) + 8 * h);
+        }
 #pragma unroll
-          for (int j = 0; j < TN; j++) {
-            const v16i D = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq[j][e], magic, 0, 0, 0);
+        for (int j = 0; j < TN; j++) {
+          const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[0], bq[j][0], magic, 0, 0, 0);
+          const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[1], bq[j][1], magic, 0, 0, 0);
+          // t = I0*dsc0 + I1*dsc1 in two fmas: p = f0*dsc0 - M*(dsc0 + dsc1)
+          // = I0*dsc0 - M*dsc1 (one rounding, at the scale of M*dsc1), then
+          // t = f1*dsc1 + p; acc += t*dx
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-              const float u = __builtin_fmaf(bits_to_float(D[r]), dsc[j][e], cc[j][e]);  // fl(I*dsc)
-              acc[i][j][r] = __builtin_fmaf(u, dxv[r], acc[i][j][r]);
-            }
+          for (int r = 0; r < 16; r++) {
+            const float p = __builtin_fmaf(bits_to_float(D0[r]), dsc[j][0], cc[j][0]);
+            const float t = __builtin_fmaf(bits_to_float(D1[r]), dsc[j][1], p);
+            acc[i][j][r] = __builtin_fmaf(t, dxv[r], acc[i][j][r]);
           }
         }
       }
@@ -216,15 +229,15 @@ static void launch_q6k_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, i
       W, ws.q, ws.dxT, ws.Mp, M, N, K, y);
 }
 
-// Kernel choice (measured on the workloads' shapes): long prompts (M >= 2048)
-// with enough 128x128 tiles take 8 waves x 2x1 tiles; otherwise 64x128 tiles
+// Kernel choice (measured on the workloads' shapes): with at least two
+// 128x128 tiles per CU, 8 waves x 2x1 tiles; otherwise 64x128 tiles
 // (8 waves x one tile) while they give at least half a workgroup per CU, else
 // 64x64 tiles (4 waves).
 enum class Q6Pick { k128x128, k64x128, k64x64 };
 
 inline Q6Pick pick_q6k(int64_t M, int64_t N) {
   constexpr int64_t kCUs = 256;
-  if (M >= 2048 && ((M + 127) / 128) * ((N + 127) / 128) >= kCUs) return Q6Pick::k128x128;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= 2 * kCUs) return Q6Pick::k128x128;
   if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs / 2) return Q6Pick::k64x128;
   return Q6Pick::k64x64;
 }
