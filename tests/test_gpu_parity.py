@@ -270,3 +270,30 @@ def test_skinny_all_row_splits(fmt, K):
         tol = bound(x, np.arange(M), wmax)
         check(gpu_prefill(W, fmt, x, N, qg.QG_PATH_SKINNY), ref, tol,
               f"skinny M={M} N={N} K={K} {qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)}")
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    (qg.QG_Q4_K, 2049, 16480, 1024),   # 128x256 tiles, ragged M and N
+    (qg.QG_Q4_K, 577, 8240, 768),      # 64x128 tiles at 4 waves/SIMD, ragged
+    (qg.QG_Q6_K, 1100, 8300, 1280),    # 128x128 tiles, ragged
+    (qg.QG_Q6_K, 300, 8300, 512),      # 64x128 tiles, ragged
+    (qg.QG_Q6_K, 70, 300, 768),        # 64x64 tiles, ragged
+    (qg.QG_Q4_K, 65, 230, 2048),       # one 32x32 tile per wave, K split over 8 waves
+    (qg.QG_Q4_K, 100, 200, 512),       # K split over 2 waves
+])
+def test_tiled_configs_ragged(fmt, M, N, K):
+    """Every tiled kernel configuration the dispatcher can pick, on shapes whose
+    M and N are not multiples of the tile: sampled rows and columns, always
+    including the last row and column and the tile edges around them."""
+    W = synth.pack(fmt, synth.normal(600 + M, (N, K), 0.0, 0.02))
+    x = synth.to_bf16_bits(synth.normal(601 + N, (M, K)))
+    name = qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_TILED)
+    y = gpu_prefill(W, fmt, x, N, qg.QG_PATH_TILED)
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, 63, 64, 127, 128, M - 2, M - 1], rng.integers(0, M, 8)]))
+    rows = rows[rows < M]
+    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N - 33, N - 2, N - 1], rng.integers(0, N, 64)]))
+    cols = cols[cols < N]
+    ref = oracle.gemm(fmt, W, x, N, rows=rows, cols=cols)
+    tol = bound(x, rows, max_abs_w(fmt, W, N, K))
+    check(y[np.ix_(rows, cols)], ref, tol, f"{name} M={M} N={N} K={K}")
