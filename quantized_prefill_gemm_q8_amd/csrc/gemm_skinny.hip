@@ -16,10 +16,12 @@
 //   Q6_K  lane s = 2*half + lh: ql[64half + 16lh ..+16], ql[64half + 32 +
 //         16lh ..+16] and qh[32half + 16lh ..+16], i.e. the values
 //         128half + 32c + 16lh + i (c = 0..3, i < 16), which are the 16-value
-//         sub-blocks 8half + 2c + lh; plus the 8 scale bytes of its half and d.
-//         Q6_K blocks are 210 bytes, so these loads are only 2-byte aligned
-//         (gfx950 serves unaligned vector loads; realigning dword-aligned
-//         loads with v_alignbyte measured no faster).
+//         sub-blocks 8half + 2c + lh; plus one 8-byte load of the scales / d
+//         region, the four lanes' pieces exchanged with quad DPP moves (a
+//         separate 2-byte load of d measured ~5% slower).  Q6_K blocks are
+//         210 bytes, so these loads are only 2-byte aligned (gfx950 serves
+//         unaligned vector loads; realigning dword-aligned loads with
+//         v_alignbyte measured no faster).
 // So a wavefront covers 16 super-blocks (4096 values) per step.  A row of nsb
 // super-blocks takes ceil(nsb/16) steps; when nsb divides 16, one step covers
 // R = 16/nsb whole rows.  Wavefronts take rows (or R-row groups) in turn, so
@@ -57,8 +59,8 @@ __device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
 
 // Raw bytes one lane loads for one super-block.
 struct SkRaw {
-  uint4 a, b, c;        // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
-  uint32_t s0, s1, dh;  // Q6_K: the 8 scale bytes of the lane's half, d (binary16)
+  uint4 a, b, c;    // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
+  uint32_t s0, s1;  // Q6_K: 8 bytes of the scales / d region (see the load)
 };
 
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
@@ -193,10 +195,12 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       r.a = ld16_a2(blk + off_a);
       r.b = ld16_a2(blk + off_b);
       r.c = ld16_a2(blk + off_c);
-      const u32x2_a2 sc = *reinterpret_cast<const u32x2_a2*>(blk + 192 + 8 * half);
-      r.s0 = sc.x;
-      r.s1 = sc.y;
-      r.dh = *reinterpret_cast<const uint16_t*>(blk + 208);
+      // one 8-byte load per lane covers the 18 bytes of scales and d between
+      // the four lanes of the block: s = 0, 1, 2 read bytes 192, 196, 200
+      // (+8), s = 3 reads bytes 202..209 (scales 10..15 and d)
+      const u32x2_a2 e = *reinterpret_cast<const u32x2_a2*>(blk + (s == 3 ? 202 : 192 + 4 * s));
+      r.s0 = e.x;
+      r.s1 = e.y;
     }
   };
 
@@ -256,8 +260,17 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
           acc[m] = valid ? a : acc[m];
         }
       } else {
-        const float d = half_to_float(cur.dh & 0xFFFFu);
-        const uint32_t s0 = cur.s0, s1 = cur.s1;
+        // scales sc[8half .. 8half+7] as two dwords and d, from the quad's
+        // loads: lane 1 takes sc[0..3] from lane 0, lane 3 sc[8..11] from
+        // lane 2 and realigns sc[12..15] from its own bytes 202..209; d is
+        // the top half of lane 3's second dword
+        const uint32_t nb0 = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(cur.s0), 0xA0, 0xF, 0xF, false));
+        const uint32_t dq = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(cur.s1), 0xFF, 0xF, 0xF, false));
+        const float d = half_to_float(dq >> 16);
+        const uint32_t s0 = (s & 1) ? nb0 : cur.s0;
+        const uint32_t s1 = s == 1 ? cur.s0 : s == 3 ? __builtin_amdgcn_alignbyte(cur.s1, cur.s0, 2) : cur.s1;
         float dsc[4];
 #pragma unroll
         for (int c = 0; c < 4; c++) {
