@@ -13,8 +13,9 @@ Printed: one JSON line with value = effective int8 TOPS of the step
 roofline of the dominant kernel (the GEMM kernel with the largest share of the
 step; its launches run back to back between two HIP events on its stream), the large-M headline
 projections (K=4096 -> N=24576 Q4_K and K=12288 -> N=4096 Q6_K at M=512), the
-M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K) and the CPU oracle timed on
-the host.
+decode-sized GEMV (M = 1 and 8) over every projection shape of the workloads,
+the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K) and the CPU oracle timed
+on the host.
 
 --calib-copy-mib N additionally runs a plain elementwise copy kernel over
 N MiB (read N, write N) three times: the reference dispatch for scaling HBM
@@ -127,6 +128,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--lm-steps", type=int, default=50)    # 0: skip the LM head
     p.add_argument("--big-steps", type=int, default=30)   # 0: skip the large-M GEMMs
+    p.add_argument("--gemv-steps", type=int, default=20)  # 0: skip the decode GEMV table
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -254,6 +256,38 @@ def main():
                             "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
         del Wb, xb, wsb, yb
 
+    # ---------------- decode-sized GEMV over every projection shape of the workloads
+    # (M = 1 and M = 8 rows; weight bytes / kernel time against 8 TB/s)
+    gemv = {}
+    seen = set()
+    for cfg in (2, 3, 4) if args.gemv_steps > 0 else ():
+        for g in synth.CONFIGS[cfg]:
+            key = (g.K, g.N, g.fmt)
+            if key in seen:
+                continue
+            seen.add(key)
+            Wg = to_dev(synth.make_weights(g))
+            xg = to_dev(synth.make_acts(g, rows=8))
+            for Mg in (1, 8):
+                wsg = qg.alloc_workspace(Mg, g.K, dev)
+                yg = torch.empty((Mg, g.N), dtype=torch.float32, device=dev)
+                qg.qgemm_quantize_workspace(xg[:Mg].contiguous(), Mg, g.K, wsg, stream)
+                for _ in range(3):
+                    qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
+                a, b = ev(), ev()
+                a.record(stream)
+                for _ in range(args.gemv_steps):
+                    qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = 1e3 * a.elapsed_time(b) / args.gemv_steps
+                gbs = g.w_bytes / (us * 1e-6) / 1e9
+                gemv[f"K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'} M={Mg}"] = {
+                    "kernel": qg.qgemm_kernel_name(g.fmt, Mg, g.N, g.K),
+                    "weight_bytes": g.w_bytes, "avg_launch_us": round(us, 2),
+                    "gbps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+            del Wg, xg
+
     # ---------------- LM head on the last token: M = 1, K = 4096 -> N = 152064, Q6_K
     lm_out = None
     if args.lm_steps > 0:
@@ -348,6 +382,7 @@ def main():
                              "tops": round(d["ops"] / (d["ms"] * 1e-3) / 1e12, 2)}
                          for k, d in per_kernel.items()},
         "large_m": big,
+        "decode_gemv": gemv,
         "lm_head": lm_out,
         "cpu_baseline": cpu,
     }
