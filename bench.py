@@ -133,13 +133,57 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
     p.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_JSON"))
+    p.add_argument("--single", metavar="WORKLOAD",
+                   help="time one workload GEMM only (e.g. c4_gate_up_M512) and print its line")
     return p.parse_args()
+
+
+def run_single(name: str, steps: int) -> None:
+    """Quantise once, then time `steps` back-to-back launches of one workload GEMM."""
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import synth
+    import quantized_prefill_gemm_q8_amd as qg
+    allg = {f"c{c}_{g.name}": g for c in synth.CONFIGS for g in synth.CONFIGS[c]}
+    if name not in allg:
+        raise SystemExit(f"unknown workload {name}; one of: {', '.join(sorted(allg))}")
+    g = allg[name]
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(synth.make_weights(g)).to(dev)
+    xb = synth.make_acts(g)
+    x = torch.from_numpy(xb.view(np.int16) if xb.dtype == np.uint16 else xb).to(dev)
+    if xb.dtype == np.uint16:
+        x = x.view(torch.bfloat16)
+    ws = qg.alloc_workspace(g.M, g.K, dev)
+    y = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
+    qg.qgemm_quantize_workspace(x, g.M, g.K, ws)
+    for _ in range(3):
+        qg.qgemm_gemm_quantized(W, g.fmt, ws, g.M, g.N, g.K, y)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        qg.qgemm_gemm_quantized(W, g.fmt, ws, g.M, g.N, g.K, y)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    print(json.dumps({"workload": name, "shape": [g.M, g.K, g.N], "fmt": "Q4_K" if g.fmt == 0 else "Q6_K",
+                      "kernel": qg.qgemm_kernel_name(g.fmt, g.M, g.N, g.K), "avg_launch_us": round(us, 3),
+                      "tops": round(g.ops / (us * 1e-6) / 1e12, 2),
+                      "gbps_weights": round(g.w_bytes / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, calib_mib=args.calib_copy_mib or 1024)
+        return
+    if args.single:
+        run_single(args.single, max(1, min(args.steps, 50)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
