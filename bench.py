@@ -8,10 +8,17 @@ K=3584 -> N=1024; all Q4_K weights (N(0, 0.02^2) packed), bf16 N(0,1)
 activations, synthetic and seeded.  Each step runs the activation quantiser
 twice and the tiled int8-MFMA GEMM three times, with inputs resident in HBM.
 
+Timing: library calls are issued back to back on one stream between two HIP
+events on that stream.  The step and the long GEMMs are issued eagerly, one
+call at a time (the host stays ahead of the GPU there; the step replayed from a
+captured HIP graph is reported next to it); the decode-sized GEMVs and the LM
+head, whose kernels are short enough for the host's per-call cost to pace an
+eager loop, are captured once as a HIP graph and replayed.
+
 Printed: one JSON line with value = effective int8 TOPS of the step
 (2*M*N*K summed over the three projections / step time), prefill tok/s, the
 roofline of the dominant kernel (the GEMM kernel with the largest share of the
-step; its launches run back to back between two HIP events on its stream), the large-M headline
+step; its launches run back to back), the large-M headline
 projections (K=4096 -> N=24576 Q4_K and K=12288 -> N=4096 Q6_K at M=512), the
 decode-sized GEMV (M = 1 and 8) over every projection shape of the workloads,
 the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K) and the CPU oracle timed
@@ -200,7 +207,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    # every timed launch goes to one non-default stream: HIP graphs are captured
+    # on it and replayed on it, and the timing events are recorded on it
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -209,6 +219,30 @@ def main():
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
+
+    def capture(fn, n):
+        """A HIP graph of n back-to-back calls fn() on `stream` (the library's
+        launches are recorded, not run; nothing is allocated inside)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                fn()
+        return g
+
+    def time_replays(g, replays):
+        """ms for `replays` back-to-back replays of g, between two events on `stream`."""
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(replays):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def per_graph(total):
+        """calls per captured graph and replays for `total` timed calls"""
+        n = min(total, 50)
+        return n, max(1, (total + n - 1) // n)
 
     # ---------------- workload: the small-model projection set, M = 512
     qkv, up, down = synth.CONFIGS[2]
@@ -238,7 +272,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region 1: whole steps, no per-kernel events
+    # timed region 1: whole steps, issued eagerly, no per-kernel events
     t0, t1 = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -249,6 +283,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    # the same steps replayed from a captured HIP graph (for reference)
+    per, replays = per_graph(args.steps)
+    g_step = capture(step, per)
+    time_replays(g_step, 1)
+    graph_ms_per_step = time_replays(g_step, replays) / (per * replays)
+    del g_step
 
     # timed region 2: per GEMM kernel, its launches of one step run back to back
     # (same arguments, same stream) between two HIP events, repeated `steps`
@@ -283,6 +323,7 @@ def main():
         wsb = qg.alloc_workspace(g.M, g.K, dev)
         yb = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
         qg.qgemm_quantize_workspace(xb, g.M, g.K, wsb, stream)
+
         for _ in range(5):
             qg.qgemm_gemm_quantized(Wb, g.fmt, wsb, g.M, g.N, g.K, yb, stream)
         a, b = ev(), ev()
@@ -316,15 +357,16 @@ def main():
                 wsg = qg.alloc_workspace(Mg, g.K, dev)
                 yg = torch.empty((Mg, g.N), dtype=torch.float32, device=dev)
                 qg.qgemm_quantize_workspace(xg[:Mg].contiguous(), Mg, g.K, wsg, stream)
+
+                def gemv_call(g=g, Wg=Wg, wsg=wsg, yg=yg, Mg=Mg):
+                    qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
                 for _ in range(3):
-                    qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
-                a, b = ev(), ev()
-                a.record(stream)
-                for _ in range(args.gemv_steps):
-                    qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
-                b.record(stream)
-                torch.cuda.synchronize()
-                us = 1e3 * a.elapsed_time(b) / args.gemv_steps
+                    gemv_call()
+                n, r = per_graph(args.gemv_steps)
+                gg = capture(gemv_call, n)
+                time_replays(gg, 1)
+                us = 1e3 * time_replays(gg, r) / (n * r)
+                del gg
                 gbs = g.w_bytes / (us * 1e-6) / 1e9
                 gemv[f"K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'} M={Mg}"] = {
                     "kernel": qg.qgemm_kernel_name(g.fmt, Mg, g.N, g.K),
@@ -340,23 +382,23 @@ def main():
         x_lm = to_dev(synth.make_acts(lm))[0]
         ws_lm = qg.alloc_workspace(1, lm.K, dev)
         y_lm = torch.empty(lm.N, dtype=torch.float32, device=dev)
-        for _ in range(5):
+        def lm_call():
             qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
+
+        def lm_gemm():
+            qg.qgemm_gemm_quantized(W_lm, lm.fmt, ws_lm, 1, lm.N, lm.K, y_lm, stream,
+                                    qg.QG_PATH_SKINNY)
+        for _ in range(5):
+            lm_call()
         torch.cuda.synchronize()
         qg.qgemm_quantize_workspace(x_lm, 1, lm.K, ws_lm, stream)
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(args.lm_steps):
-            qg.qgemm_gemm_quantized(W_lm, lm.fmt, ws_lm, 1, lm.N, lm.K, y_lm, stream, qg.QG_PATH_SKINNY)
-        b.record(stream)
-        c0, c1 = ev(), ev()
-        c0.record(stream)
-        for _ in range(args.lm_steps):
-            qg.qgemm_lm_head(W_lm, lm.fmt, x_lm, lm.N, lm.K, y_lm, ws_lm, stream)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        lm_kernel_us = 1e3 * a.elapsed_time(b) / args.lm_steps
-        lm_call_us = 1e3 * c0.elapsed_time(c1) / args.lm_steps
+        n, r = per_graph(args.lm_steps)
+        ga, gc = capture(lm_gemm, n), capture(lm_call, n)
+        time_replays(ga, 1)
+        lm_kernel_us = 1e3 * time_replays(ga, r) / (n * r)
+        time_replays(gc, 1)
+        lm_call_us = 1e3 * time_replays(gc, r) / (n * r)
+        del ga, gc
         lm_gbs = lm.w_bytes / (lm_kernel_us * 1e-6) / 1e9
         del W_lm
         lm_out = {"workload": "M=1, K=4096 -> N=152064, Q6_K (skinny path)",
@@ -404,6 +446,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "graph_ms_per_step": round(graph_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -53,9 +53,13 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 
 // ---------------------------------------------------------------- LDS-staged kernel
 //
-// WM x WN waves share super-block stages in LDS; each wave owns TM x TN tiles
-// of 32x32 outputs.  One stage (256 values of K) holds, for the BM activation
-// rows and BN weight rows of the workgroup:
+// KS groups of WM x WN waves; the waves of a group share super-block stages in
+// LDS and each owns TM x TN tiles of 32x32 outputs.  The KS groups of a
+// workgroup compute the same BM x BN output block over disjoint super-block
+// ranges of K (a split of the reduction for grids with few output blocks) and
+// are summed through LDS at the end in group order, so the result does not
+// depend on timing.  One stage (256 values of K) holds, for the BM activation
+// rows and BN weight rows of the block:
 //   A   [BM][256]  int8 codes; each row's sixteen 16-byte chunks are XOR-
 //                  swizzled by (row % 16) so that 16 lanes reading 16 rows at
 //                  the same column hit 16 different bank groups
@@ -64,32 +68,37 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 //   DX  [BM][8]    fp32 activation block scales
 //   DSP [BM][3][8] bfloat16 pieces of dS
 // Stages are filled by global_load_lds_dwordx4 (global memory straight into
-// LDS) in an NS-deep ring: while super-block sb is computed, the loads of the
-// next NS-1 super-blocks are in flight; one workgroup barrier per stage.
-// Every wave issues the same number of loads per stage (the last ones of the
-// short waves land in a junk slot), so a fixed vmcnt waits for exactly one
-// stage.
+// LDS) in an NS-deep ring per group: while super-block sb is computed, the
+// loads of the next NS-1 super-blocks are in flight; one workgroup barrier per
+// stage.  Each region is a whole number of wave-loads (64 chunks of 16 bytes);
+// the lanes of a region's last wave-load that fall past its end re-read the
+// region's first chunk into the region's padding.  Every wave issues the same
+// number of loads per stage (the extra ones of the short waves repeat one of
+// the region's wave-loads, writing the same bytes to the same place), so a
+// fixed vmcnt waits for exactly one stage.
 // DPP: activation scales staged row-major and applied with the DPP-broadcast
 // epilogue; otherwise staged block-major ([8][BM], from dxT) and read as 16
 // per-element values per tile (four 16-byte broadcast reads).
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_lds_kernel(
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_lds_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
     int64_t N, int64_t K, float* __restrict__ y) {
-  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int NW = WM * WN;  // waves per group
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
-  constexpr int A_BYTES = BM * 256, W_BYTES = BN * kQ4Bytes, X_BYTES = BM * 32, P_BYTES = BM * 48;
+  constexpr int A_CH = BM * 256 / 16, W_CH = BN * kQ4Bytes / 16, X_CH = BM * 32 / 16, P_CH = BM * 48 / 16;
+  // wave-loads per region and region sizes in LDS (whole wave-loads)
+  constexpr int A_WL = (A_CH + 63) / 64, W_WL = (W_CH + 63) / 64, X_WL = (X_CH + 63) / 64, P_WL = (P_CH + 63) / 64;
+  constexpr int A_BYTES = A_WL * 1024, W_BYTES = W_WL * 1024, X_BYTES = X_WL * 1024, P_BYTES = P_WL * 1024;
   constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES + P_BYTES;
-  constexpr int A_CH = A_BYTES / 16, W_CH = W_BYTES / 16, X_CH = X_BYTES / 16, P_CH = P_BYTES / 16;
-  static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0 && P_CH % 64 == 0,
-                "stage regions must be whole wave loads");
-  constexpr int JUNK = 1024;                // landing slot of the padding loads
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE + JUNK];
+  static_assert(KS * NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(KS == 1 || (KS - 1) * NW * TM * TN * 4096 <= KS * NS * STAGE, "reduction space");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KS * NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / NW, wave = wave_all - grp * NW;  // K-group, wave within the group
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
@@ -98,34 +107,37 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
   const int64_t nsb = K / 256, nb = K / 32;
   const int64_t wrow_bytes = nsb * kQ4Bytes;
   const int drow = dpp_scale_row(lane);
+  uint8_t* const glds = lds + grp * NS * STAGE;  // this group's ring
+  // this group's super-blocks: sb0 .. sb0 + cnt - 1 (the launcher keeps KS <= nsb)
+  const int64_t sb0 = grp * nsb / KS, cnt = (grp + 1) * nsb / KS - sb0;
+  const int64_t iters = (nsb + KS - 1) / KS;  // the longest group's count
 
-  // Stage loads, region by region (A, W, DX, DSP).  A region of R_CH chunks
-  // is R_CH/64 wave-loads; wave w issues wave-loads w, w+NW, ... and every
-  // wave issues the same count per region (a wave-load past the region's end
-  // reads the region's first chunk into the junk slot), so a fixed vmcnt
-  // waits for a whole stage.  Each load reads base(region, sb) + voff: the
-  // base is a wave-uniform pointer advanced per super-block (SGPRs); voff is
-  // this lane's byte offset, computed once (tail rows and columns clamped to
-  // the last valid one).
-  constexpr int LA = (A_CH / 64 + NW - 1) / NW, LW = (W_CH / 64 + NW - 1) / NW;
-  constexpr int LX = (X_CH / 64 + NW - 1) / NW, LP = (P_CH / 64 + NW - 1) / NW;
+  // Stage loads, region by region (A, W, DX, DSP).  A region of R_WL wave-
+  // loads is issued by the group's waves round robin: wave w issues wave-loads
+  // w, w+NW, ... (taken modulo R_WL, so that every wave issues the same count
+  // per region).  Each load reads base(region, sb) + voff: the base is a
+  // wave-uniform pointer advanced per super-block (SGPRs); voff is this lane's
+  // byte offset, computed once (tail rows and columns clamped to the last valid
+  // one, lanes past the region's end to offset 0).
+  constexpr int LA = (A_WL + NW - 1) / NW, LW = (W_WL + NW - 1) / NW;
+  constexpr int LX = (X_WL + NW - 1) / NW, LP = (P_WL + NW - 1) / NW;
   uint32_t voff[LA + LW + LX + LP];
 #pragma unroll
   for (int it = 0; it < LA; it++) {
-    const int q = (wave + it * NW) * 64 + lane;
+    const int q = ((wave + it * NW) % A_WL) * 64 + lane;
     const int row = q >> 4, c16 = (q & 15) ^ (row & 15);
     const int64_t m = m_cta + row < M ? m_cta + row : M - 1;
-    voff[it] = (wave + it * NW) < A_CH / 64 ? static_cast<uint32_t>((m - m_cta) * K + 16 * c16) : 0u;
+    voff[it] = q < A_CH ? static_cast<uint32_t>((m - m_cta) * K + 16 * c16) : 0u;
   }
 #pragma unroll
   for (int it = 0; it < LW; it++) {
-    const int qq = (wave + it * NW) * 64 + lane, row = qq / 9, part = qq - 9 * row;
+    const int qq = ((wave + it * NW) % W_WL) * 64 + lane, row = qq / 9, part = qq - 9 * row;
     const int64_t n = n_cta + row < N ? n_cta + row : N - 1;
-    voff[LA + it] = (wave + it * NW) < W_CH / 64 ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + 16 * part) : 0u;
+    voff[LA + it] = qq < W_CH ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + 16 * part) : 0u;
   }
 #pragma unroll
   for (int it = 0; it < LX; it++) {
-    const int qq = (wave + it * NW) * 64 + lane;
+    const int qq = ((wave + it * NW) % X_WL) * 64 + lane;
     uint32_t v;
     if (DPP) {
       const int row = qq >> 1, hf = qq & 1;
@@ -134,33 +146,32 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
       const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
       v = static_cast<uint32_t>((jb * Mp + 4 * r4) * 4);
     }
-    voff[LA + LW + it] = (wave + it * NW) < X_CH / 64 ? v : 0u;
+    voff[LA + LW + it] = qq < X_CH ? v : 0u;
   }
 #pragma unroll
   for (int it = 0; it < LP; it++) {
-    const int qq = (wave + it * NW) * 64 + lane, row = qq / 3, piece = qq - 3 * row;
-    voff[LA + LW + LX + it] = (wave + it * NW) < P_CH / 64 ? static_cast<uint32_t>(row * nsb * 48 + 16 * piece) : 0u;
+    const int qq = ((wave + it * NW) % P_WL) * 64 + lane, row = qq / 3, piece = qq - 3 * row;
+    voff[LA + LW + LX + it] = qq < P_CH ? static_cast<uint32_t>(row * nsb * 48 + 16 * piece) : 0u;
   }
   constexpr int LPT = LA + LW + LX + LP;  // loads per thread per stage
   static_assert(LPT * (NS - 1) < 64, "vmcnt range");
 
-  auto issue_region = [&](const void* rbase, int first, int count, int nwl, int chunk0, uint8_t* sbase) {
+  auto issue_region = [&](const void* rbase, int first, int count, int nwl, int off, uint8_t* sbase) {
 #pragma unroll
     for (int it = 0; it < count; it++) {
-      const int wl = wave + it * NW;
-      lds_dma16_sv(rbase, voff[first + it],
-                   wl < nwl ? static_cast<const void*>(sbase + 16 * (chunk0 + 64 * wl))
-                            : static_cast<const void*>(lds + NS * STAGE));
+      const int wl = (wave + it * NW) % nwl;
+      lds_dma16_sv(rbase, voff[first + it], sbase + off + 1024 * wl);
     }
   };
-  auto issue_stage = [&](int64_t sb, int buf) {
-    uint8_t* sbase = lds + buf * STAGE;
-    issue_region(qx + m_cta * K + sb * 256, 0, LA, A_CH / 64, 0, sbase);
-    issue_region(W + n_cta * wrow_bytes + sb * kQ4Bytes, LA, LW, W_CH / 64, A_CH, sbase);
+  auto issue_stage = [&](int64_t s, int buf) {
+    const int64_t sb = sb0 + (s < cnt ? s : cnt - 1);  // past the group's range: reload its last
+    uint8_t* sbase = glds + buf * STAGE;
+    issue_region(qx + m_cta * K + sb * 256, 0, LA, A_WL, 0, sbase);
+    issue_region(W + n_cta * wrow_bytes + sb * kQ4Bytes, LA, LW, W_WL, A_BYTES, sbase);
     issue_region(DPP ? static_cast<const void*>(dx + m_cta * nb + 8 * sb)
                      : static_cast<const void*>(dxT + 8 * sb * Mp + m_cta),
-                 LA + LW, LX, X_CH / 64, A_CH + W_CH, sbase);
-    issue_region(dsp + (m_cta * nsb + sb) * 24, LA + LW + LX, LP, P_CH / 64, A_CH + W_CH + X_CH, sbase);
+                 LA + LW, LX, X_WL, A_BYTES + W_BYTES, sbase);
+    issue_region(dsp + (m_cta * nsb + sb) * 24, LA + LW + LX, LP, P_WL, A_BYTES + W_BYTES + X_BYTES, sbase);
   };
 
   v16i magic;
@@ -176,18 +187,19 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
 
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; s0++)
-    if (s0 < nsb) issue_stage(s0, s0);
-  for (int64_t sb = 0; sb < nsb; sb++) {
-    const int buf = static_cast<int>(sb % NS);
-    // This wave's loads of stage sb have landed once at most the loads of the
+    if (s0 < iters) issue_stage(s0, s0);
+  for (int64_t s = 0; s < iters; s++) {
+    const int buf = static_cast<int>(s % NS);
+    // This wave's loads of stage s have landed once at most the loads of the
     // NS-2 later stages are outstanding (near the end fewer are: wait for
     // all); after the barrier every wave's have, and no wave still reads
-    // stage sb-1, whose buffer the next issue refills.
-    if (sb + NS - 1 <= nsb) wait_vm_barrier<LPT * (NS - 2)>();
+    // stage s-1, whose buffer the next issue refills.
+    if (s + NS - 1 <= iters) wait_vm_barrier<LPT * (NS - 2)>();
     else wait_vm_barrier<0>();
-    if (sb + NS - 1 < nsb) issue_stage(sb + NS - 1, static_cast<int>((sb + NS - 1) % NS));
+    if (s + NS - 1 < iters) issue_stage(s + NS - 1, static_cast<int>((s + NS - 1) % NS));
+    if (KS > 1 && s >= cnt) continue;  // a shorter group idles through the last step
 
-    const uint8_t* sA = lds + buf * STAGE;
+    const uint8_t* sA = glds + buf * STAGE;
     const uint8_t* sW = sA + A_BYTES;
     const float* sX = reinterpret_cast<const float*>(sW + W_BYTES);
     const uint8_t* sP = sW + W_BYTES + X_BYTES;
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
       }
     }
 
-#pragma unroll(NW >= 12 ? 1 : 4)
+#pragma unroll(NW * KS >= 12 ? 1 : 4)
     for (int c = 0; c < 4; c++) {
       uint4 wraw[TN];
 #pragma unroll
@@ -293,6 +305,40 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
         for (int r = 0; r < 16; r++) acc[i][j][r] = __builtin_fmaf(T[r], nd, acc[i][j][r]);
       }
     }
+  }
+
+  if constexpr (KS > 1) {
+    // Sum the groups' partial blocks in group order: groups 1..KS-1 leave
+    // theirs in LDS (the stage ring is free once every wave has passed this
+    // barrier), group 0 adds them to its own and stores.
+    float4* red = reinterpret_cast<float4*>(lds);  // [KS-1][NW][TM*TN*4][64]
+    __syncthreads();
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            red[((((grp - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; g++)
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const float4 v = red[((((g - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane];
+            acc[i][j][4 * q] += v.x;
+            acc[i][j][4 * q + 1] += v.y;
+            acc[i][j][4 * q + 2] += v.z;
+            acc[i][j][4 * q + 3] += v.w;
+          }
   }
 
 #pragma unroll
@@ -448,13 +494,14 @@ static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int
                                                                   M, N, K, y);
 }
 
-// OCC: waves per SIMD the register allocation must allow (launch bound)
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC = (WM * WN + 3) / 4>
+// OCC: waves per SIMD the register allocation must allow (launch bound);
+// KS: K-groups per workgroup (at most the number of super-blocks)
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC = (WM * WN + 3) / 4, int KS = 1>
 static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                        float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS, OCC><<<grid, dim3(64 * WM * WN), 0, stream>>>(
+  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
       W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
 }
 
@@ -464,17 +511,24 @@ namespace {
 
 // Kernel choice for a Q4_K problem (measured on the workloads' shapes):
 // long prompts (M >= 2048) with enough 128x256 tiles to cover every CU take
-// workgroups of 8 waves x 2x2 tiles; otherwise, with enough 64x128 tiles,
+// workgroups of 8 waves x 2x2 tiles; otherwise, with enough 64x128 blocks,
 // workgroups of 8 waves x one tile at 4 waves per SIMD (two workgroups per
-// CU); smaller grids one 32x32 tile per wave with the K range split so that
-// the chip gets about two waves per SIMD.
-enum class Q4Pick { kLds128x256, kLds64x128, kSmall1, kSmall2, kSmall4, kSmall8 };
+// CU).  Grids with fewer output blocks split K inside the workgroup: 64x128
+// blocks with two K-groups (16 waves) when there are at least half as many
+// blocks as CUs, else 32x64 blocks with four K-groups (8 waves) when those
+// cover the CUs (both only where the rows fill most of the block).  Smaller
+// grids take one 32x32 tile per wave with the K range split so that the chip
+// gets about two waves per SIMD.
+enum class Q4Pick { kLds128x256, kLds64x128, kLds64x128K2, kLds32x64K4, kSmall1, kSmall2, kSmall4, kSmall8 };
 
 Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256, kTargetWaves = 2048;
   const int64_t nsb = K / 256;
   if (M >= 2048 && ((M + 127) / 128) * ((N + 255) / 256) >= kCUs) return Q4Pick::kLds128x256;
-  if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs) return Q4Pick::kLds64x128;
+  const int64_t blocks64x128 = ((M + 63) / 64) * ((N + 127) / 128);
+  if (blocks64x128 >= kCUs) return Q4Pick::kLds64x128;
+  if (M >= 48 && blocks64x128 * 2 >= kCUs && nsb >= 4) return Q4Pick::kLds64x128K2;
+  if (M >= 24 && ((M + 31) / 32) * ((N + 63) / 64) >= kCUs && nsb >= 8) return Q4Pick::kLds32x64K4;
   const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
   if (tiles >= kTargetWaves || nsb < 2) return Q4Pick::kSmall1;
   if (tiles * 2 >= kTargetWaves || nsb < 4) return Q4Pick::kSmall2;
@@ -486,8 +540,10 @@ Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
 
 const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K) {
   switch (pick_q4k(M, N, K)) {
-    case Q4Pick::kLds128x256: return "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2>";
-    case Q4Pick::kLds64x128: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4>";
+    case Q4Pick::kLds128x256: return "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1>";
+    case Q4Pick::kLds64x128: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1>";
+    case Q4Pick::kLds64x128K2: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>";
+    case Q4Pick::kLds32x64K4: return "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>";
     case Q4Pick::kSmall1: return "gemm_q4k_small_kernel<1>";
     case Q4Pick::kSmall2: return "gemm_q4k_small_kernel<2>";
     case Q4Pick::kSmall4: return "gemm_q4k_small_kernel<4>";
@@ -501,6 +557,8 @@ hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256: qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kLds64x128: qg::launch_lds<1, 1, 2, 4, false, 2, 4>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds64x128K2: qg::launch_lds<1, 1, 2, 4, false, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds32x64K4: qg::launch_lds<1, 1, 1, 2, false, 2, 2, 4>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall1: qg::launch_small<1>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall2: qg::launch_small<2>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall4: qg::launch_small<4>(W, ws, M, N, K, y, stream); break;

@@ -119,9 +119,15 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 8, 100, 4352, AUTO) == "skinny_kernel<1, 8, 1, 1>"
     assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2>"
     # tiled tile choice by grid size
-    assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2>"
-    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4>"
+    assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1>"
+    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1>"
     assert kn(Q4, 64, 1024, 1024, AUTO).startswith("gemm_q4k_small_kernel<")
+    # few output blocks: K split inside the workgroup
+    assert kn(Q4, 512, 2560, 9728, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>"
+    assert kn(Q4, 512, 1024, 3584, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>"
+    assert kn(Q4, 330, 2700, 1280, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>"
+    assert kn(Q4, 170, 2800, 2816, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>"
+    assert kn(Q4, 512, 1024, 1792, AUTO).startswith("gemm_q4k_small_kernel<")   # too few super-blocks
     assert kn(Q6, 8192, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<2, 1, 2, 4, 2>"
     # arguments the entry points would reject
     assert kn(2, 8, 8, 256, AUTO) is None
