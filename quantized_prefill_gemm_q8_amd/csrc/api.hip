@@ -177,7 +177,7 @@ const char* qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path
   if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return NULL;
   if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return NULL;
   const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
-  if (skinny) return qg_gemm_skinny_kernel_name(fmt, M, K);
+  if (skinny) return qg_gemm_skinny_kernel_name(fmt, M, N, K);
   return fmt == QG_Q4_K ? qg_gemm_q4k_kernel_name(M, N, K) : qg_gemm_q6k_kernel_name(M, N, K);
 }
 

@@ -120,7 +120,7 @@ hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& w
 // the kernel names a profiler reports).
 const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K);
 const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t K);
-const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t K);
+const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t qg_launch_dequant(const uint8_t* W, int fmt, int64_t N, int64_t K, float* w,
                              hipStream_t stream);
 hipError_t qg_launch_block_partials(const uint8_t* W, int fmt, const int8_t* qx, int64_t M,

@@ -22,6 +22,8 @@
 //         210 bytes, so these loads are only 2-byte aligned (gfx950 serves
 //         unaligned vector loads; realigning dword-aligned loads with
 //         v_alignbyte measured no faster).
+// Q6_K matrices whose steps start on 16-byte boundaries are instead loaded
+// whole-line (see CO at the kernel) and the same fields read back from LDS.
 // So a wavefront covers 16 super-blocks (4096 values) per step.  A row of nsb
 // super-blocks takes ceil(nsb/16) steps; when nsb divides 16, one step covers
 // R = 16/nsb whole rows.  Wavefronts take rows (or R-row groups) in turn, so
@@ -43,6 +45,7 @@
 #include <stdio.h>
 
 #include "common.h"
+#include "lds_stage.h"
 
 namespace qg {
 
@@ -57,10 +60,11 @@ __device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Raw bytes one lane loads for one super-block.
+// Raw bytes one lane loads for one step.
 struct SkRaw {
   uint4 a, b, c;    // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
   uint32_t s0, s1;  // Q6_K: 8 bytes of the scales / d region (see the load)
+  uint4 e;          // Q6_K, coalesced loads: a, b, c, e are the step's chunks l, l+64, l+128, l+192
 };
 
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
@@ -68,6 +72,7 @@ typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 constexpr int kSkThreads = 256;
 constexpr int kSkMaxLds = 64 * 1024;
 enum { kXReg = 0, kXLds = 1, kXGlb = 2 };
+enum { kCoNone = 0, kCoReg = 1, kCoDma = 2 };
 
 // sum over 16 int8 values
 __device__ __forceinline__ int sum16(const uint4& x) {
@@ -99,11 +104,23 @@ __device__ __forceinline__ float group_sum_last(float v) {
 
 // FMT: QG_Q4_K / QG_Q6_K.  MR: activation rows.  R: rows per wavefront step
 // (16/nsb when that divides, else 1).  XM: where the activations are read.
-template <int FMT, int MR, int R, int XM>
+// CO (Q6_K only): coalesced loads.  A step's sixteen super-blocks are 3360
+// contiguous bytes; when every step starts 16-byte aligned and the matrix ends
+// on a 16-byte boundary, lane l loads the step's aligned chunks l, l+64, l+128
+// and l+192 (whole cache lines per load instead of 16-byte fields scattered at
+// 2-byte alignment) into the wavefront's own 4 KB of LDS, and every lane reads
+// its fields back from there.  kCoReg: the chunks go through registers (two
+// register buffers, as the field loads); kCoDma: global_load_lds_dwordx4 puts
+// them straight into two LDS buffers (no registers held; used for one or two
+// activation rows, where it measured fastest).
+template <int FMT, int MR, int R, int XM, int CO>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ gdx,
     const float* __restrict__ gdS, int64_t N, int64_t K, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  static_assert(CO == kCoNone || FMT == QG_Q6_K, "coalesced loads are for Q6_K");
+  constexpr int NBUF = CO == kCoDma ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t rowbuf[CO ? kSkThreads / 64 : 1][NBUF][CO ? 4096 : 16];
   constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : kQ6Bytes;
   constexpr int G = 64 / R;  // lanes per row within a step
   const int64_t nsb = K / 256, nb = K / 32;
@@ -144,6 +161,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   const int64_t ipr = R > 1 ? 1 : (nsb + 15) / 16;  // steps per row
   const int64_t nsteps = (N - row_begin + stride - 1) / stride * ipr;
   const int64_t row_bytes = nsb * BB;
+  const int64_t last_chunk = N * row_bytes / 16 - 1;  // CO: the matrix is a whole number of chunks
+  uint8_t* const lrow0 = rowbuf[CO ? threadIdx.x >> 6 : 0][0];
+  uint8_t* const lrow1 = rowbuf[CO ? threadIdx.x >> 6 : 0][NBUF - 1];
   // lane offset inside a super-block of each of its loads
   const uint32_t off_a = FMT == QG_Q4_K ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
   const uint32_t off_b = FMT == QG_Q4_K ? 16u + 32u * s : static_cast<uint32_t>(64 * half + 32 + 16 * lh);
@@ -183,24 +203,43 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   // steps) load a clamped, valid block and their contribution is dropped, so
   // the step code has no branches.
   auto load = [&](int64_t rs, int64_t it, SkRaw& r) {
-    int64_t n = row_begin + rs * stride + ro, jb = jb0 + 16 * it;
-    n = n < N ? n : N - 1;
-    jb = jb < nsb ? jb : nsb - 1;
-    const uint8_t* blk = W + n * row_bytes + jb * BB;
-    if (FMT == QG_Q4_K) {
-      r.a = *reinterpret_cast<const uint4*>(blk + off_a);
-      r.b = *reinterpret_cast<const uint4*>(blk + off_b);
-      r.c = *reinterpret_cast<const uint4*>(blk + off_c);
+    if constexpr (CO) {
+      // chunk index of the step's first byte: row (row_begin + rs*stride),
+      // super-block 16*it; chunks past the matrix re-read its last chunk
+      const int64_t c0 = ((row_begin + rs * stride) * row_bytes + 16 * it * BB) / 16 + lane;
+      const uint4* wc = reinterpret_cast<const uint4*>(W);
+      if constexpr (CO == kCoDma) {
+        // into the LDS buffer of this register set (its index rides in s0)
+        uint8_t* lb = r.s0 ? lrow1 : lrow0;
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          lds_dma16(wc + (c0 + 64 * k < last_chunk ? c0 + 64 * k : last_chunk), lb + 1024 * k);
+      } else {
+        r.a = wc[c0 < last_chunk ? c0 : last_chunk];
+        r.b = wc[c0 + 64 < last_chunk ? c0 + 64 : last_chunk];
+        r.c = wc[c0 + 128 < last_chunk ? c0 + 128 : last_chunk];
+        r.e = wc[c0 + 192 < last_chunk ? c0 + 192 : last_chunk];
+      }
     } else {
-      r.a = ld16_a2(blk + off_a);
-      r.b = ld16_a2(blk + off_b);
-      r.c = ld16_a2(blk + off_c);
-      // one 8-byte load per lane covers the 18 bytes of scales and d between
-      // the four lanes of the block: s = 0, 1, 2 read bytes 192, 196, 200
-      // (+8), s = 3 reads bytes 202..209 (scales 10..15 and d)
-      const u32x2_a2 e = *reinterpret_cast<const u32x2_a2*>(blk + (s == 3 ? 202 : 192 + 4 * s));
-      r.s0 = e.x;
-      r.s1 = e.y;
+      int64_t n = row_begin + rs * stride + ro, jb = jb0 + 16 * it;
+      n = n < N ? n : N - 1;
+      jb = jb < nsb ? jb : nsb - 1;
+      const uint8_t* blk = W + n * row_bytes + jb * BB;
+      if (FMT == QG_Q4_K) {
+        r.a = *reinterpret_cast<const uint4*>(blk + off_a);
+        r.b = *reinterpret_cast<const uint4*>(blk + off_b);
+        r.c = *reinterpret_cast<const uint4*>(blk + off_c);
+      } else {
+        r.a = ld16_a2(blk + off_a);
+        r.b = ld16_a2(blk + off_b);
+        r.c = ld16_a2(blk + off_c);
+        // one 8-byte load per lane covers the 18 bytes of scales and d between
+        // the four lanes of the block: s = 0, 1, 2 read bytes 192, 196, 200
+        // (+8), s = 3 reads bytes 202..209 (scales 10..15 and d)
+        const u32x2_a2 e = *reinterpret_cast<const u32x2_a2*>(blk + (s == 3 ? 202 : 192 + 4 * s));
+        r.s0 = e.x;
+        r.s1 = e.y;
+      }
     }
   };
 
@@ -208,21 +247,53 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
 #pragma unroll
   for (int m = 0; m < MR; m++) acc[m] = 0.0f;
 
-  auto compute = [&](int64_t rs, int64_t it, const SkRaw& cur) {
+  auto compute = [&](int64_t rs, int64_t it, const SkRaw raw) {
     const int64_t n = row_begin + rs * stride + ro, jbr = jb0 + 16 * it;
     const bool valid = n < N && jbr < nsb;
     const int64_t jb = jbr < nsb ? jbr : nsb - 1;
+    uint4 fa, fb, fc;  // this lane's fields (see SkRaw)
+    uint32_t fs0, fs1;
+    if constexpr (CO) {
+      // through this wavefront's LDS row buffer: the step's chunks in, this
+      // lane's fields (block grp of the step, 2-byte aligned) out
+      const uint8_t* bp;
+      if constexpr (CO == kCoDma) {
+        // this step's four loads have landed once at most the next step's
+        // four are outstanding (same-type loads complete in order; a pending
+        // output store only makes the wait longer)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        bp = (raw.s0 ? lrow1 : lrow0) + grp * BB;
+      } else {
+        *reinterpret_cast<uint4*>(lrow0 + 16 * lane) = raw.a;
+        *reinterpret_cast<uint4*>(lrow0 + 16 * (lane + 64)) = raw.b;
+        *reinterpret_cast<uint4*>(lrow0 + 16 * (lane + 128)) = raw.c;
+        *reinterpret_cast<uint4*>(lrow0 + 16 * (lane + 192)) = raw.e;
+        bp = lrow0 + grp * BB;
+      }
+      fa = ld16_a2(bp + off_a);
+      fb = ld16_a2(bp + off_b);
+      fc = ld16_a2(bp + off_c);
+      const u32x2_a2 e = *reinterpret_cast<const u32x2_a2*>(bp + (s == 3 ? 202 : 192 + 4 * s));
+      fs0 = e.x;
+      fs1 = e.y;
+    } else {
+      fa = raw.a;
+      fb = raw.b;
+      fc = raw.c;
+      fs0 = raw.s0;
+      fs1 = raw.s1;
+    }
     {
       if (FMT == QG_Q4_K) {
-        const float d = half_to_float(cur.a.x & 0xFFFFu), dmin = half_to_float(cur.a.x >> 16);
-        const Q4Scales sc = unpack_q4_scales(cur.a.y, cur.a.z, cur.a.w);
+        const float d = half_to_float(fa.x & 0xFFFFu), dmin = half_to_float(fa.x >> 16);
+        const Q4Scales sc = unpack_q4_scales(fa.y, fa.z, fa.w);
         const uint32_t scw = s < 2 ? sc.sc_lo : sc.sc_hi, mw = s < 2 ? sc.m_lo : sc.m_hi;
         const int bi = 2 * (s & 1);
         const float dsc0 = d * static_cast<float>(byte_of(scw, bi));
         const float dsc1 = d * static_cast<float>(byte_of(scw, bi + 1));
         const float dm0 = dmin * static_cast<float>(byte_of(mw, bi));
         const float dm1 = dmin * static_cast<float>(byte_of(mw, bi + 1));
-        const uint32_t w[8] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w, cur.c.x, cur.c.y, cur.c.z, cur.c.w};
+        const uint32_t w[8] = {fb.x, fb.y, fb.z, fb.w, fc.x, fc.y, fc.z, fc.w};
         uint32_t lo[8], hi[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -265,21 +336,21 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
         // lane 2 and realigns sc[12..15] from its own bytes 202..209; d is
         // the top half of lane 3's second dword
         const uint32_t nb0 = static_cast<uint32_t>(
-            __builtin_amdgcn_update_dpp(0, static_cast<int>(cur.s0), 0xA0, 0xF, 0xF, false));
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(fs0), 0xA0, 0xF, 0xF, false));
         const uint32_t dq = static_cast<uint32_t>(
-            __builtin_amdgcn_update_dpp(0, static_cast<int>(cur.s1), 0xFF, 0xF, 0xF, false));
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(fs1), 0xFF, 0xF, 0xF, false));
         const float d = half_to_float(dq >> 16);
-        const uint32_t s0 = (s & 1) ? nb0 : cur.s0;
-        const uint32_t s1 = s == 1 ? cur.s0 : s == 3 ? __builtin_amdgcn_alignbyte(cur.s1, cur.s0, 2) : cur.s1;
+        const uint32_t s0 = (s & 1) ? nb0 : fs0;
+        const uint32_t s1 = s == 1 ? fs0 : s == 3 ? __builtin_amdgcn_alignbyte(fs1, fs0, 2) : fs1;
         float dsc[4];
 #pragma unroll
         for (int c = 0; c < 4; c++) {
           const uint32_t sw = c < 2 ? s0 : s1;
           dsc[c] = d * static_cast<float>(static_cast<int8_t>(byte_of(sw, (2 * c + lh) & 3)));
         }
-        const uint32_t l0[4] = {cur.a.x, cur.a.y, cur.a.z, cur.a.w};
-        const uint32_t l1[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
-        const uint32_t hh[4] = {cur.c.x, cur.c.y, cur.c.z, cur.c.w};
+        const uint32_t l0[4] = {fa.x, fa.y, fa.z, fa.w};
+        const uint32_t l1[4] = {fb.x, fb.y, fb.z, fb.w};
+        const uint32_t hh[4] = {fc.x, fc.y, fc.z, fc.w};
         uint32_t q[4][4];  // codes q6 in [0, 63], quarter c, dword i
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -344,6 +415,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   // clamped, valid block), so the compiler's wait before each step counts
   // exactly the next step's loads and leaves them in flight.
   SkRaw r0 = {}, r1 = {};
+  if constexpr (CO == kCoDma) r1.s0 = 1;  // LDS buffer of each register set
   int64_t rs0 = 0, it0 = 0;
   load(rs0, it0, r0);
   for (int64_t t = 0; t < nsteps; t += 2) {
@@ -375,9 +447,20 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
   return skinny_lds_bytes(fmt, M, K) <= kSkMaxLds ? kXLds : kXGlb;
 }
 
-template <int FMT, int MR, int R>
-static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
-                                  float* y, hipStream_t stream) {
+// Q6_K coalesced loads (CO) where every step starts on a 16-byte boundary
+// (several rows per step, or rows of a multiple of 8 super-blocks) and the
+// matrix is a whole number of 16-byte chunks: straight into LDS for up to two
+// activation rows, through registers above
+inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int64_t nsb = K / 256;
+  if (fmt != QG_Q6_K || !(skinny_rows_per_step(K) > 1 || nsb % 8 == 0) || (N * nsb) % 8 != 0)
+    return kCoNone;
+  return M <= 2 ? kCoDma : kCoReg;
+}
+
+template <int FMT, int MR, int R, int CO>
+static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
+                                   float* y, hipStream_t stream) {
   // about four workgroups (16 wavefronts) per CU, all resident at once
   constexpr int64_t kWaves = 256 * 16;
   const int64_t row_groups = (N + R - 1) / R;
@@ -385,19 +468,32 @@ static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
   switch (skinny_xmode(FMT, MR, K)) {
     case kXReg:
-      skinny_kernel<FMT, MR, R, kXReg><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
-                                                                             N, K, y);
+      skinny_kernel<FMT, MR, R, kXReg, CO><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
+                                                                                 N, K, y);
       break;
     case kXLds:
-      skinny_kernel<FMT, MR, R, kXLds>
+      skinny_kernel<FMT, MR, R, kXLds, CO>
           <<<grid, dim3(kSkThreads), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
               W, ws.q, ws.dx, ws.dS, N, K, y);
       break;
     default:
-      skinny_kernel<FMT, MR, R, kXGlb><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N,
-                                                                             K, y);
+      skinny_kernel<FMT, MR, R, kXGlb, CO><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
+                                                                                 N, K, y);
   }
   return hipGetLastError();
+}
+
+template <int FMT, int MR, int R>
+static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
+                                  float* y, hipStream_t stream) {
+  if constexpr (FMT == QG_Q6_K) {
+    switch (skinny_coalesced(FMT, MR, N, K)) {
+      case kCoDma: return launch_skinny_rc<FMT, MR, R, kCoDma>(W, ws, N, K, y, stream);
+      case kCoReg: return launch_skinny_rc<FMT, MR, R, kCoReg>(W, ws, N, K, y, stream);
+      default: break;
+    }
+  }
+  return launch_skinny_rc<FMT, MR, R, kCoNone>(W, ws, N, K, y, stream);
 }
 
 template <int FMT, int MR>
@@ -430,11 +526,12 @@ static hipError_t launch_skinny_fmt(const uint8_t* W, const QgWorkspace& ws, int
 
 }  // namespace qg
 
-const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t K) {
+const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   thread_local char name[64];
   if (M < 1 || M > QG_SKINNY_MAX_M) return "?";
-  snprintf(name, sizeof name, "skinny_kernel<%d, %d, %d, %d>", fmt, static_cast<int>(M),
-           qg::skinny_rows_per_step(K), qg::skinny_xmode(fmt, M, K));
+  snprintf(name, sizeof name, "skinny_kernel<%d, %d, %d, %d, %d>", fmt, static_cast<int>(M),
+           qg::skinny_rows_per_step(K), qg::skinny_xmode(fmt, M, K),
+           qg::skinny_coalesced(fmt, M, N, K));
   return name;
 }
 

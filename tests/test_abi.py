@@ -113,11 +113,21 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 1, 4096, 4096, TILED).startswith("gemm_q4k_")
     # skinny work split: rows per step R = 16 / (K/256) when that divides, else 1;
     # activations in registers up to K = 4096, then LDS, then L2
-    assert kn(Q6, 1, 152064, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0>"
-    assert kn(Q4, 2, 100, 1024, AUTO) == "skinny_kernel<0, 2, 4, 0>"
-    assert kn(Q4, 1, 100, 2560, AUTO) == "skinny_kernel<0, 1, 1, 0>"
-    assert kn(Q6, 8, 100, 4352, AUTO) == "skinny_kernel<1, 8, 1, 1>"
-    assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2>"
+    assert kn(Q6, 1, 152064, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
+    assert kn(Q4, 2, 100, 1024, AUTO) == "skinny_kernel<0, 2, 4, 0, 0>"
+    assert kn(Q4, 1, 100, 2560, AUTO) == "skinny_kernel<0, 1, 1, 0, 0>"
+    assert kn(Q6, 8, 100, 4352, AUTO) == "skinny_kernel<1, 8, 1, 1, 0>"
+    assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2, 0>"
+    # Q6_K coalesced loads (last parameter: 2 straight into LDS for M <= 2,
+    # 1 through registers above, 0 field loads) need aligned steps (several
+    # rows per step, or rows of a multiple of 8 super-blocks) and a matrix of
+    # whole 16-byte chunks
+    assert kn(Q6, 1, 4096, 12288, AUTO) == "skinny_kernel<1, 1, 1, 1, 2>"
+    assert kn(Q6, 1, 77, 1024, AUTO) == "skinny_kernel<1, 1, 4, 0, 0>"    # 77*4 % 8 != 0
+    assert kn(Q6, 2, 78, 1024, AUTO) == "skinny_kernel<1, 2, 4, 0, 2>"
+    assert kn(Q6, 1, 80, 2560, AUTO) == "skinny_kernel<1, 1, 1, 0, 0>"    # 10 super-blocks a row
+    assert kn(Q6, 3, 81, 6144, AUTO) == "skinny_kernel<1, 3, 1, 1, 1>"    # 24 super-blocks a row
+    assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1>"
     # tiled tile choice by grid size
     assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1>"
     assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1>"

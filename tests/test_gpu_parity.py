@@ -256,12 +256,15 @@ def test_full_size_sampled(g):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
-@pytest.mark.parametrize("K", [256, 512, 1024, 2048, 2560, 4096, 4352, 8192, 12288])
-def test_skinny_all_row_splits(fmt, K):
+@pytest.mark.parametrize("K", [256, 512, 1024, 2048, 2560, 4096, 4352, 6144, 8192, 12288])
+@pytest.mark.parametrize("N", [77, 80])
+def test_skinny_all_row_splits(fmt, K, N):
     """Skinny path over K values whose super-block counts select every work split
     (several rows per wavefront step, one row per step, several steps per row,
-    partial last step) and over M rows that do and do not fit the LDS staging."""
-    N = 77
+    partial last step) and over M rows that do and do not fit the LDS staging;
+    N = 80 makes every Q6_K matrix a whole number of 16-byte chunks, so the
+    coalesced loads run wherever the steps are aligned (N = 77 only for K a
+    multiple of 2048)."""
     W = synth.pack(fmt, synth.normal(590 + K, (N, K), 0.0, 0.02))
     wmax = max_abs_w(fmt, W, N, K)
     for M in (1, 2, 5, 8):
