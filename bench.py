@@ -135,7 +135,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--lm-steps", type=int, default=50)    # 0: skip the LM head
     p.add_argument("--big-steps", type=int, default=30)   # 0: skip the large-M GEMMs
-    p.add_argument("--gemv-steps", type=int, default=20)  # 0: skip the decode GEMV table
+    p.add_argument("--gemv-steps", type=int, default=200)  # 0: skip the decode GEMV table
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -388,7 +388,9 @@ def main():
         def lm_gemm():
             qg.qgemm_gemm_quantized(W_lm, lm.fmt, ws_lm, 1, lm.N, lm.K, y_lm, stream,
                                     qg.QG_PATH_SKINNY)
-        for _ in range(5):
+        # warm-up long enough (about 20 ms) for clocks to settle after the
+        # lighter work before it
+        for _ in range(200):
             lm_call()
         torch.cuda.synchronize()
         qg.qgemm_quantize_workspace(x_lm, 1, lm.K, ws_lm, stream)

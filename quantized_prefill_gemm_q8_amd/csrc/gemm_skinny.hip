@@ -448,12 +448,14 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
 }
 
 // Q6_K coalesced loads (CO) where every step starts on a 16-byte boundary
-// (several rows per step, or rows of a multiple of 8 super-blocks) and the
-// matrix is a whole number of 16-byte chunks: straight into LDS for up to two
+// (several rows per step, or rows of a multiple of 8 super-blocks), the matrix
+// is a whole number of 16-byte chunks and the activations sit in registers
+// (with them in LDS or L2, measured slower): straight into LDS for up to two
 // activation rows, through registers above
 inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
   const int64_t nsb = K / 256;
-  if (fmt != QG_Q6_K || !(skinny_rows_per_step(K) > 1 || nsb % 8 == 0) || (N * nsb) % 8 != 0)
+  if (fmt != QG_Q6_K || !(skinny_rows_per_step(K) > 1 || nsb % 8 == 0) || (N * nsb) % 8 != 0 ||
+      skinny_xmode(fmt, M, K) != kXReg)
     return kCoNone;
   return M <= 2 ? kCoDma : kCoReg;
 }
@@ -461,10 +463,14 @@ inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
 template <int FMT, int MR, int R, int CO>
 static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                    float* y, hipStream_t stream) {
-  // about four workgroups (16 wavefronts) per CU, all resident at once
+  // at most four workgroups (16 wavefronts) per CU, all resident at once; as
+  // few wavefronts as keep the same number of row groups per wavefront, so
+  // that the last rows are shared out evenly instead of a few wavefronts
+  // taking one more step than the rest
   constexpr int64_t kWaves = 256 * 16;
   const int64_t row_groups = (N + R - 1) / R;
-  const int64_t waves = row_groups < kWaves ? row_groups : kWaves;
+  const int64_t per_wave = (row_groups + kWaves - 1) / kWaves;
+  const int64_t waves = ((row_groups + per_wave - 1) / per_wave + 3) / 4 * 4;
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
   switch (skinny_xmode(FMT, MR, K)) {
     case kXReg:

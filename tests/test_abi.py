@@ -120,13 +120,14 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2, 0>"
     # Q6_K coalesced loads (last parameter: 2 straight into LDS for M <= 2,
     # 1 through registers above, 0 field loads) need aligned steps (several
-    # rows per step, or rows of a multiple of 8 super-blocks) and a matrix of
-    # whole 16-byte chunks
-    assert kn(Q6, 1, 4096, 12288, AUTO) == "skinny_kernel<1, 1, 1, 1, 2>"
+    # rows per step, or rows of a multiple of 8 super-blocks), a matrix of
+    # whole 16-byte chunks and the activations in registers (K <= 4096)
+    assert kn(Q6, 1, 4096, 12288, AUTO) == "skinny_kernel<1, 1, 1, 1, 0>"
     assert kn(Q6, 1, 77, 1024, AUTO) == "skinny_kernel<1, 1, 4, 0, 0>"    # 77*4 % 8 != 0
     assert kn(Q6, 2, 78, 1024, AUTO) == "skinny_kernel<1, 2, 4, 0, 2>"
     assert kn(Q6, 1, 80, 2560, AUTO) == "skinny_kernel<1, 1, 1, 0, 0>"    # 10 super-blocks a row
-    assert kn(Q6, 3, 81, 6144, AUTO) == "skinny_kernel<1, 3, 1, 1, 1>"    # 24 super-blocks a row
+    assert kn(Q6, 3, 81, 2048, AUTO) == "skinny_kernel<1, 3, 2, 0, 1>"
+    assert kn(Q6, 1, 80, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
     assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1>"
     # tiled tile choice by grid size
     assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1>"

@@ -263,8 +263,8 @@ def test_skinny_all_row_splits(fmt, K, N):
     (several rows per wavefront step, one row per step, several steps per row,
     partial last step) and over M rows that do and do not fit the LDS staging;
     N = 80 makes every Q6_K matrix a whole number of 16-byte chunks, so the
-    coalesced loads run wherever the steps are aligned (N = 77 only for K a
-    multiple of 2048)."""
+    coalesced loads run wherever the steps are aligned and K <= 4096 (N = 77
+    only for K = 2048 and 4096)."""
     W = synth.pack(fmt, synth.normal(590 + K, (N, K), 0.0, 0.02))
     wmax = max_abs_w(fmt, W, N, K)
     for M in (1, 2, 5, 8):
