@@ -19,7 +19,8 @@
 // products are integers below 2^24 (unit scales).
 //
 // LDS pipeline (as the Q4_K kernel): WM x WN waves share super-block stages in
-// an NS-deep ring filled by global_load_lds_dwordx4; one stage holds
+// an NS-deep ring (per K-group) filled by global_load_lds_dwordx4; one stage
+// holds
 //   A  [BM][256]  int8 activation codes, 16-byte chunks XOR-swizzled by row%16
 //   W  [BN][224]  the 210-byte blocks: bytes 0..207 as 13 chunks, then bytes
 //                 194..209 as a 14th chunk (so d sits at 222..223); the
@@ -37,23 +38,31 @@ namespace qg {
 
 constexpr int kQ6Row = 224;  // LDS bytes per staged Q6_K block
 
-template <int TM, int TN, int WM, int WN, int NS>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
+// KS groups of WM x WN waves compute the same BM x BN output block over
+// disjoint super-block ranges of K and are summed through LDS in group order
+// at the end (grids with few output blocks).  NS = 1: one stage buffer per
+// group, loaded, waited for and computed in turn (two barriers per stage; the
+// overlap comes from the other workgroups on the CU, which the halved LDS
+// footprint lets in).  Regions are padded to whole wave-loads; the extra loads
+// of short waves repeat one of the region's wave-loads.
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q6k_lds_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
     int64_t Mp, int64_t M, int64_t N, int64_t K, float* __restrict__ y) {
-  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int NW = WM * WN;  // waves per group
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
-  constexpr int A_BYTES = BM * 256, W_BYTES = BN * kQ6Row, X_BYTES = BM * 32;
+  constexpr int A_CH = BM * 256 / 16, W_CH = BN * kQ6Row / 16, X_CH = BM * 32 / 16;
+  constexpr int A_WL = (A_CH + 63) / 64, W_WL = (W_CH + 63) / 64, X_WL = (X_CH + 63) / 64;
+  constexpr int A_BYTES = A_WL * 1024, W_BYTES = W_WL * 1024, X_BYTES = X_WL * 1024;
   constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES;
-  constexpr int A_CH = A_BYTES / 16, W_CH = W_BYTES / 16, X_CH = X_BYTES / 16;
-  static_assert(A_CH % 64 == 0 && W_CH % 64 == 0 && X_CH % 64 == 0,
-                "stage regions must be whole wave loads");
-  constexpr int JUNK = 1024;  // landing slot of the padding loads
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE + JUNK];
+  static_assert(KS * NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(KS == 1 || (KS - 1) * NW * TM * TN * 4096 <= KS * NS * STAGE, "reduction space");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KS * NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / NW, wave = wave_all - grp * NW;  // K-group, wave within the group
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
@@ -61,52 +70,55 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
   const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
   const int64_t nsb = K / 256;
   const int64_t wrow_bytes = nsb * kQ6Bytes;
+  uint8_t* const glds = lds + grp * NS * STAGE;  // this group's ring
+  // this group's super-blocks: sb0 .. sb0 + cnt - 1 (the launcher keeps KS <= nsb)
+  const int64_t sb0 = grp * nsb / KS, cnt = (grp + 1) * nsb / KS - sb0;
+  const int64_t iters = (nsb + KS - 1) / KS;  // the longest group's count
 
   // Stage loads region by region (A, W, DX) with per-lane byte offsets
-  // computed once and wave-uniform bases advanced per super-block; every wave
-  // issues the same count per region (a wave-load past the region's end reads
-  // the region's first chunk into the junk slot), so a fixed vmcnt waits for
-  // a whole stage.  Tail rows and columns are clamped to the last valid one.
-  constexpr int LA = (A_CH / 64 + NW - 1) / NW, LW = (W_CH / 64 + NW - 1) / NW;
-  constexpr int LX = (X_CH / 64 + NW - 1) / NW;
+  // computed once and wave-uniform bases advanced per super-block; the group's
+  // waves issue a region's wave-loads round robin, modulo the region's count,
+  // so that every wave issues the same number per stage and a fixed vmcnt
+  // waits for a whole stage.  Tail rows and columns are clamped to the last
+  // valid one, lanes past a region's end read its first chunk into its padding.
+  constexpr int LA = (A_WL + NW - 1) / NW, LW = (W_WL + NW - 1) / NW;
+  constexpr int LX = (X_WL + NW - 1) / NW;
   constexpr int LPT = LA + LW + LX;  // loads per thread per stage
-  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
+  static_assert(NS == 1 || LPT * (NS - 1) < 64, "vmcnt range");
   uint32_t voff[LPT];
 #pragma unroll
   for (int it = 0; it < LA; it++) {
-    const int q = (wave + it * NW) * 64 + lane;
+    const int q = ((wave + it * NW) % A_WL) * 64 + lane;
     const int row = q >> 4, c16 = (q & 15) ^ (row & 15);
     const int64_t m = m_cta + row < M ? m_cta + row : M - 1;
-    voff[it] = (wave + it * NW) < A_CH / 64 ? static_cast<uint32_t>((m - m_cta) * K + 16 * c16) : 0u;
+    voff[it] = q < A_CH ? static_cast<uint32_t>((m - m_cta) * K + 16 * c16) : 0u;
   }
 #pragma unroll
   for (int it = 0; it < LW; it++) {
-    const int qq = (wave + it * NW) * 64 + lane, row = qq / 14, part = qq - 14 * row;
+    const int qq = ((wave + it * NW) % W_WL) * 64 + lane, row = qq / 14, part = qq - 14 * row;
     const int64_t n = n_cta + row < N ? n_cta + row : N - 1;
-    voff[LA + it] = (wave + it * NW) < W_CH / 64
-                        ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + (part < 13 ? 16 * part : 194))
-                        : 0u;
+    voff[LA + it] = qq < W_CH ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + (part < 13 ? 16 * part : 194))
+                              : 0u;
   }
 #pragma unroll
   for (int it = 0; it < LX; it++) {
-    const int qq = (wave + it * NW) * 64 + lane;
+    const int qq = ((wave + it * NW) % X_WL) * 64 + lane;
     const int jb = qq / (BM / 4), r4 = qq - jb * (BM / 4);
-    voff[LA + LW + it] = (wave + it * NW) < X_CH / 64 ? static_cast<uint32_t>((jb * Mp + 4 * r4) * 4) : 0u;
+    voff[LA + LW + it] = qq < X_CH ? static_cast<uint32_t>((jb * Mp + 4 * r4) * 4) : 0u;
   }
-  auto issue_region = [&](const void* rbase, int first, int count, int nwl, int chunk0, uint8_t* sbase) {
+  auto issue_region = [&](const void* rbase, int first, int count, int nwl, int off, uint8_t* sbase) {
 #pragma unroll
     for (int it = 0; it < count; it++) {
-      const int wl = wave + it * NW;
-      lds_dma16_sv(rbase, voff[first + it],
-                   wl < nwl ? static_cast<const void*>(sbase + 16 * (chunk0 + 64 * wl))
-                            : static_cast<const void*>(lds + NS * STAGE));
+      const int wl = (wave + it * NW) % nwl;
+      lds_dma16_sv(rbase, voff[first + it], sbase + off + 1024 * wl);
     }
   };
-  auto issue_stage = [&](int64_t sb, int buf) {
-    uint8_t* sbase = lds + buf * STAGE;
-    issue_region(qx + m_cta * K + sb * 256, 0, LA, A_CH / 64, 0, sbase);
-    issue_region(W + n_cta * wrow_bytes + sb * kQ6Bytes, LA, LW, W_CH / 64, A_CH, sbase);
-    issue_region(dxT + 8 * sb * Mp + m_cta, LA + LW, LX, X_CH / 64, A_CH + W_CH, sbase);
+  auto issue_stage = [&](int64_t s, int buf) {
+    const int64_t sb = sb0 + (s < cnt ? s : cnt - 1);  // past the group's range: reload its last
+    uint8_t* sbase = glds + buf * STAGE;
+    issue_region(qx + m_cta * K + sb * 256, 0, LA, A_WL, 0, sbase);
+    issue_region(W + n_cta * wrow_bytes + sb * kQ6Bytes, LA, LW, W_WL, A_BYTES, sbase);
+    issue_region(dxT + 8 * sb * Mp + m_cta, LA + LW, LX, X_WL, A_BYTES + W_BYTES, sbase);
   };
 
   v16i magic;
@@ -120,22 +132,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
+  if constexpr (NS > 1) {
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; s0++)
-    if (s0 < nsb) issue_stage(s0, s0);
-  for (int64_t sb = 0; sb < nsb; sb++) {
-    const int buf = static_cast<int>(sb % NS);
-    // stage sb has landed once at most the NS-2 later stages' loads are
-    // outstanding (near the end: all); after the barrier no wave still reads
-    // stage sb-1, whose buffer the next issue refills
-    if (sb + NS - 1 <= nsb) wait_vm_barrier<LPT * (NS - 2)>();
-    else wait_vm_barrier<0>();
-    if (sb + NS - 1 < nsb) issue_stage(sb + NS - 1, static_cast<int>((sb + NS - 1) % NS));
+    for (int s0 = 0; s0 < NS - 1; s0++)
+      if (s0 < iters) issue_stage(s0, s0);
+  }
+  for (int64_t s = 0; s < iters; s++) {
+    const int buf = NS > 1 ? static_cast<int>(s % NS) : 0;
+    if constexpr (NS == 1) {
+      // no wave still reads the previous stage once all have met here
+      if (s > 0) wait_lgkm_barrier();
+      issue_stage(s, 0);
+      wait_vm_barrier<0>();
+    } else {
+      // stage s has landed once at most the NS-2 later stages' loads are
+      // outstanding (near the end: all); after the barrier no wave still
+      // reads stage s-1, whose buffer the next issue refills
+      if (s + NS - 1 <= iters) wait_vm_barrier<LPT * (NS - 2)>();
+      else wait_vm_barrier<0>();
+      if (s + NS - 1 < iters) issue_stage(s + NS - 1, static_cast<int>((s + NS - 1) % NS));
+    }
+    if (KS > 1 && s >= cnt) continue;  // a shorter group idles through the last step
 
-    const uint8_t* sA = lds + buf * STAGE;
+    const uint8_t* sA = glds + buf * STAGE;
     const uint8_t* sW = sA + A_BYTES;
     const float* sX = reinterpret_cast<const float*>(sW + W_BYTES);
-
     const uint8_t* wr[TN];
     uint4 scv[TN];
     float d[TN];
@@ -206,6 +227,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
     }
   }
 
+  if constexpr (KS > 1) {
+    // groups 1..KS-1 leave their partial blocks in LDS, group 0 adds them in order
+    float4* red = reinterpret_cast<float4*>(lds);  // [KS-1][NW][TM*TN*4][64]
+    __syncthreads();
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            red[((((grp - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; g++)
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const float4 v = red[((((g - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane];
+            acc[i][j][4 * q] += v.x;
+            acc[i][j][4 * q + 1] += v.y;
+            acc[i][j][4 * q + 2] += v.z;
+            acc[i][j][4 * q + 3] += v.w;
+          }
+  }
+
 #pragma unroll
   for (int j = 0; j < TN; j++) {
     const int64_t n = n_cta + nl0 + 32 * j + l32;
@@ -220,45 +273,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q6k_lds_kernel(
   }
 }
 
-template <int TM, int TN, int WM, int WN, int NS>
+// OCC: waves per SIMD the register allocation must allow; KS: K-groups per
+// workgroup (at most the number of super-blocks)
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
 static void launch_q6k_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                            float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_q6k_lds_kernel<TM, TN, WM, WN, NS><<<grid, dim3(64 * WM * WN), 0, stream>>>(
+  gemm_q6k_lds_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
       W, ws.q, ws.dxT, ws.Mp, M, N, K, y);
 }
 
 // Kernel choice (measured on the workloads' shapes): with at least two
-// 128x128 tiles per CU, 8 waves x 2x1 tiles; otherwise 64x128 tiles
-// (8 waves x one tile) while they give at least half a workgroup per CU, else
-// 64x64 tiles (4 waves).
-enum class Q6Pick { k128x128, k64x128, k64x64 };
+// 128x128 tiles per CU, 8 waves x 2x1 tiles; otherwise 64x128 tiles (8 waves x
+// one tile) while they give two workgroups per CU; smaller grids take 64x64
+// blocks with two K-groups of 4 waves and one stage buffer each (two such
+// workgroups per CU, 4 waves per SIMD; measured about 8% ahead of 64x128 tiles
+// at M = 512), or 4 waves with two stage buffers when K is one super-block.
+enum class Q6Pick { k128x128, k64x128, k64x64K2, k64x64 };
 
-inline Q6Pick pick_q6k(int64_t M, int64_t N) {
+inline Q6Pick pick_q6k(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256;
   if (((M + 127) / 128) * ((N + 127) / 128) >= 2 * kCUs) return Q6Pick::k128x128;
-  if (((M + 63) / 64) * ((N + 127) / 128) >= kCUs / 2) return Q6Pick::k64x128;
-  return Q6Pick::k64x64;
+  if (((M + 63) / 64) * ((N + 127) / 128) >= 2 * kCUs) return Q6Pick::k64x128;
+  return K >= 512 ? Q6Pick::k64x64K2 : Q6Pick::k64x64;
 }
 
 }  // namespace qg
 
-const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t) {
-  switch (qg::pick_q6k(M, N)) {
-    case qg::Q6Pick::k128x128: return "gemm_q6k_lds_kernel<2, 1, 2, 4, 2>";
-    case qg::Q6Pick::k64x128: return "gemm_q6k_lds_kernel<1, 1, 2, 4, 2>";
-    case qg::Q6Pick::k64x64: return "gemm_q6k_lds_kernel<1, 1, 2, 2, 2>";
+const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t K) {
+  switch (qg::pick_q6k(M, N, K)) {
+    case qg::Q6Pick::k128x128: return "gemm_q6k_lds_kernel<2, 1, 2, 4, 2, 2, 1>";
+    case qg::Q6Pick::k64x128: return "gemm_q6k_lds_kernel<1, 1, 2, 4, 2, 2, 1>";
+    case qg::Q6Pick::k64x64K2: return "gemm_q6k_lds_kernel<1, 1, 2, 2, 1, 4, 2>";
+    case qg::Q6Pick::k64x64: return "gemm_q6k_lds_kernel<1, 1, 2, 2, 2, 1, 1>";
   }
   return "?";
 }
 
 hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream) {
-  switch (qg::pick_q6k(M, N)) {
-    case qg::Q6Pick::k128x128: qg::launch_q6k_lds<2, 1, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
-    case qg::Q6Pick::k64x128: qg::launch_q6k_lds<1, 1, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
-    case qg::Q6Pick::k64x64: qg::launch_q6k_lds<1, 1, 2, 2, 2>(W, ws, M, N, K, y, stream); break;
+  switch (qg::pick_q6k(M, N, K)) {
+    case qg::Q6Pick::k128x128: qg::launch_q6k_lds<2, 1, 2, 4, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k64x128: qg::launch_q6k_lds<1, 1, 2, 4, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k64x64K2: qg::launch_q6k_lds<1, 1, 2, 2, 1, 4, 2>(W, ws, M, N, K, y, stream); break;
+    case qg::Q6Pick::k64x64: qg::launch_q6k_lds<1, 1, 2, 2, 2, 1, 1>(W, ws, M, N, K, y, stream); break;
   }
   return hipGetLastError();
 }

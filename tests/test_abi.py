@@ -139,7 +139,10 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 330, 2700, 1280, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>"
     assert kn(Q4, 170, 2800, 2816, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>"
     assert kn(Q4, 512, 1024, 1792, AUTO).startswith("gemm_q4k_small_kernel<")   # too few super-blocks
-    assert kn(Q6, 8192, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<2, 1, 2, 4, 2>"
+    assert kn(Q6, 8192, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<2, 1, 2, 4, 2, 2, 1>"
+    assert kn(Q6, 1536, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
+    assert kn(Q6, 512, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<1, 1, 2, 2, 1, 4, 2>"
+    assert kn(Q6, 70, 300, 256, AUTO) == "gemm_q6k_lds_kernel<1, 1, 2, 2, 2, 1, 1>"
     # arguments the entry points would reject
     assert kn(2, 8, 8, 256, AUTO) is None
     assert kn(Q4, 8, 8, 300, AUTO) is None

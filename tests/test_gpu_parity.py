@@ -281,8 +281,10 @@ def test_skinny_all_row_splits(fmt, K, N):
     (qg.QG_Q4_K, 330, 2700, 1280),     # 64x128 blocks, K split over 2 groups (2 + 3 super-blocks)
     (qg.QG_Q4_K, 170, 2800, 2816),     # 32x64 blocks, K split over 4 groups (2 + 3 + 3 + 3)
     (qg.QG_Q6_K, 1100, 8300, 1280),    # 128x128 tiles, ragged
-    (qg.QG_Q6_K, 300, 8300, 512),      # 64x128 tiles, ragged
-    (qg.QG_Q6_K, 70, 300, 768),        # 64x64 tiles, ragged
+    (qg.QG_Q6_K, 600, 8300, 512),      # 64x128 tiles, ragged
+    (qg.QG_Q6_K, 300, 8300, 512),      # 64x64 blocks, K split over 2 groups of one stage buffer
+    (qg.QG_Q6_K, 70, 300, 768),        # the same, 1 + 2 super-blocks
+    (qg.QG_Q6_K, 70, 300, 256),        # 64x64 tiles, one super-block
     (qg.QG_Q4_K, 65, 230, 2048),       # one 32x32 tile per wave, K split over 8 waves
     (qg.QG_Q4_K, 100, 200, 512),       # K split over 2 waves
 ])
