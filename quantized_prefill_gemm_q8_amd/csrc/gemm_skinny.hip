@@ -205,20 +205,26 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   auto load = [&](int64_t rs, int64_t it, SkRaw& r) {
     if constexpr (CO) {
       // chunk index of the step's first byte: row (row_begin + rs*stride),
-      // super-block 16*it; chunks past the matrix re-read its last chunk
-      const int64_t c0 = ((row_begin + rs * stride) * row_bytes + 16 * it * BB) / 16 + lane;
+      // super-block 16*it; the step's 210 chunks end at c_end, the lanes past
+      // it (fourth load) re-read that chunk, and chunks past the matrix its last
+      const int64_t cs = ((row_begin + rs * stride) * row_bytes + 16 * it * BB) / 16;
+      const int64_t c_end = cs + 16 * BB / 16 - 1 < last_chunk ? cs + 16 * BB / 16 - 1 : last_chunk;
+      const int64_t c0 = cs + lane;
       const uint4* wc = reinterpret_cast<const uint4*>(W);
+      auto chunk = [&](int k) {
+        const int64_t c = c0 + 64 * k;
+        return wc + (c < c_end ? c : c_end);
+      };
       if constexpr (CO == kCoDma) {
         // into the LDS buffer of this register set (its index rides in s0)
         uint8_t* lb = r.s0 ? lrow1 : lrow0;
 #pragma unroll
-        for (int k = 0; k < 4; k++)
-          lds_dma16(wc + (c0 + 64 * k < last_chunk ? c0 + 64 * k : last_chunk), lb + 1024 * k);
+        for (int k = 0; k < 4; k++) lds_dma16(chunk(k), lb + 1024 * k);
       } else {
-        r.a = wc[c0 < last_chunk ? c0 : last_chunk];
-        r.b = wc[c0 + 64 < last_chunk ? c0 + 64 : last_chunk];
-        r.c = wc[c0 + 128 < last_chunk ? c0 + 128 : last_chunk];
-        r.e = wc[c0 + 192 < last_chunk ? c0 + 192 : last_chunk];
+        r.a = *chunk(0);
+        r.b = *chunk(1);
+        r.c = *chunk(2);
+        r.e = *chunk(3);
       }
     } else {
       int64_t n = row_begin + rs * stride + ro, jb = jb0 + 16 * it;
