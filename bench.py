@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
+COLD_BYTES = 600 * 1000 ** 2  # weight footprint that defeats the 256 MB MALL (cold-cache GEMV)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workload.json")
 CALIB_KERNEL = "neg_kernel"  # the copy kernel --calib-copy-mib launches
 
@@ -136,6 +137,7 @@ def parse():
     p.add_argument("--lm-steps", type=int, default=50)    # 0: skip the LM head
     p.add_argument("--big-steps", type=int, default=30)   # 0: skip the large-M GEMMs
     p.add_argument("--gemv-steps", type=int, default=200)  # 0: skip the decode GEMV table
+    p.add_argument("--set-steps", type=int, default=10)   # 0: skip the config 3/4 projection sets
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -283,6 +285,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    # per-step distribution: the same steps with an event pair around each
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+
+    def pct(xs, q):
+        return xs[min(len(xs) - 1, int(q * len(xs)))]
     # the same steps replayed from a captured HIP graph (for reference)
     per, replays = per_graph(args.steps)
     g_step = capture(step, per)
@@ -341,6 +354,47 @@ def main():
                             "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
         del Wb, xb, wsb, yb
 
+    # ---------------- one layer's projection set of the mid-size and long-prompt
+    # configurations at each prompt length: quantise each input, run each GEMM
+    # (the weights of a configuration do not depend on M); prefill tok/s per layer
+    sets = {}
+    for cfg in (3, 4) if args.set_steps > 0 else ():
+        gs = synth.CONFIGS[cfg]
+        Ws = {}
+        for Mset in sorted({g.M for g in gs}):
+            members = [g for g in gs if g.M == Mset]
+            bufs = []
+            for g in members:
+                key = (g.K, g.N, g.fmt)
+                if key not in Ws:
+                    Ws[key] = to_dev(synth.make_weights(g))
+                xs = to_dev(synth.make_acts(g))
+                wss = qg.alloc_workspace(g.M, g.K, dev)
+                ys = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
+                bufs.append((g, Ws[key], xs, wss, ys))
+
+            def set_step(bufs=bufs):
+                for g, Wm, xs, wss, ys in bufs:
+                    qg.qgemm_quantize_workspace(xs, g.M, g.K, wss, stream)
+                    qg.qgemm_gemm_quantized(Wm, g.fmt, wss, g.M, g.N, g.K, ys, stream)
+            for _ in range(2):
+                set_step()
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(args.set_steps):
+                set_step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.set_steps
+            ops = sum(g.ops for g in members)
+            sets[f"config{cfg}_M{Mset}"] = {
+                "projections": [f"{g.K}->{g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'}" for g in members],
+                "ms_per_layer": round(ms, 4), "prefill_tok_s": round(Mset / (ms * 1e-3), 1),
+                "tops": round(ops / (ms * 1e-3) / 1e12, 2)}
+            del bufs
+        del Ws
+    torch.cuda.empty_cache()
+
     # ---------------- decode-sized GEMV over every projection shape of the workloads
     # (M = 1 and M = 8 rows; weight bytes / kernel time against 8 TB/s)
     gemv = {}
@@ -367,11 +421,27 @@ def main():
                 time_replays(gg, 1)
                 us = 1e3 * time_replays(gg, r) / (n * r)
                 del gg
+                # cold: launches rotate through copies of W whose footprint exceeds
+                # twice the 256 MB MALL, so every launch streams its weights from HBM
+                copies = [Wg] + [Wg.clone() for _ in range(max(1, -(-COLD_BYTES // g.w_bytes)) - 1)]
+                ring = iter(range(1 << 30))
+
+                def gemv_cold(g=g, wsg=wsg, yg=yg, Mg=Mg, copies=copies, ring=ring):
+                    qg.qgemm_gemm_quantized(copies[next(ring) % len(copies)], g.fmt, wsg, Mg, g.N, g.K,
+                                            yg, stream)
+                nc = max(n, len(copies))
+                gc = capture(gemv_cold, nc)
+                time_replays(gc, 1)
+                us_cold = 1e3 * time_replays(gc, r) / (nc * r)
+                del gc, copies
                 gbs = g.w_bytes / (us * 1e-6) / 1e9
+                gbs_cold = g.w_bytes / (us_cold * 1e-6) / 1e9
                 gemv[f"K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'} M={Mg}"] = {
                     "kernel": qg.qgemm_kernel_name(g.fmt, Mg, g.N, g.K),
                     "weight_bytes": g.w_bytes, "avg_launch_us": round(us, 2),
-                    "gbps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+                    "gbps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                    "cold_avg_launch_us": round(us_cold, 2), "cold_gbps": round(gbs_cold, 1),
+                    "cold_frac_hbm": round(gbs_cold / PEAK_HBM_GBS, 4)}
             del Wg, xg
 
     # ---------------- LM head on the last token: M = 1, K = 4096 -> N = 152064, Q6_K
@@ -470,7 +540,10 @@ def main():
                              "avg_launch_us": round(1e3 * d["ms"] / d["launches"], 3),
                              "tops": round(d["ops"] / (d["ms"] * 1e-3) / 1e12, 2)}
                          for k, d in per_kernel.items()},
+        "step_ms_p10_p50_p90": [round(pct(step_ms, 0.1), 5), round(pct(step_ms, 0.5), 5),
+                                round(pct(step_ms, 0.9), 5)],
         "large_m": big,
+        "projection_sets": sets,
         "decode_gemv": gemv,
         "lm_head": lm_out,
         "cpu_baseline": cpu,
