@@ -214,6 +214,9 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
       d[j] = half_to_float(hdr.x & 0xFFFFu);
       dmin[j] = half_to_float(hdr.x >> 16);
       sc[j] = unpack_q4_scales(hdr.y, hdr.z, hdr.w);
+      // keep the masked scale bytes as values, so that each scale converts
+      // with one v_cvt_f32_ubyteN instead of a field extract and a convert
+      asm volatile("" : "+v"(sc[j].sc_lo), "+v"(sc[j].sc_hi));
     }
     float dxr[TM][8];
     if (DPP) {
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int64_t m = m_cta + ml0 + 32 * i + acc_row(r, h);
-        if (m < M) y[m * N + n] = acc[i][j][r];
+        if (m < M) store_out(y + m * N + n, acc[i][j][r]);
       }
   }
 }
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           const int64_t mm = m0 + acc_row(4 * g + q, h);
-          if (mm < M) y[mm * N + nn] = sv[q];
+          if (mm < M) store_out(y + mm * N + nn, sv[q]);
         }
       }
     }
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int64_t mm = m0 + acc_row(r, h);
-        if (mm < M) y[mm * N + nn] = acc[r];
+        if (mm < M) store_out(y + mm * N + nn, acc[r]);
       }
     }
   }

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int64_t m = m_cta + ml0 + 32 * i + acc_row(r, h);
-        if (m < M) y[m * N + n] = acc[i][j][r];
+        if (m < M) store_out(y + m * N + n, acc[i][j][r]);
       }
   }
 }
