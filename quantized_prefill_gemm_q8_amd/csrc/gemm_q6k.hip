@@ -5,7 +5,9 @@
 // with Q6_K's 16-value sub-blocks: one v_mfma_i32_32x32x16_i8 per sub-block,
 // its int32 partial scaled by the sub-block's d*sc, and the activation scale
 // dx of the 32-value block holding it.  Codes are fed to the matrix core as
-// the signed bytes q6 - 32, so there is no min term.
+// the signed bytes 4*(q6 - 32) (the six code bits in the top of the byte,
+// which takes four instructions per four codes to build), and d*sc/4 scales
+// the products, so there is no min term.
 //
 // Per y[m][n]: sum over 16-value sub-blocks s of dx[m][s/2] * d*sc[n][s] * I16.
 // The accumulator starts at the bit pattern of M = 12582912.0f, so its int32
@@ -184,12 +186,21 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
           const uint2 lo8 = *reinterpret_cast<const uint2*>(pl + 16 * e);
           const uint2 hi8 = *reinterpret_cast<const uint2*>(ph + 16 * e);
           const int ls = 4 * (c >> 1), hs = 2 * c;
-          const uint32_t w0 = q6_to_signed(((lo8.x >> ls) & 0x0F0F0F0Fu) | (((hi8.x >> hs) & 0x03030303u) << 4));
-          const uint32_t w1 = q6_to_signed(((lo8.y >> ls) & 0x0F0F0F0Fu) | (((hi8.y >> hs) & 0x03030303u) << 4));
+          // each byte becomes 4*(q6 - 32) as a signed byte: the nibble in bits
+          // 2..5 (a rotate brings either half there), the two high bits in
+          // bits 6..7 with the top one flipped (XOR 0xAA.. flips the top bit of
+          // every 2-bit field of qh); the factor 4 comes out of dsc below
+          auto code4 = [&](uint32_t l, uint32_t hq) {
+            const uint32_t lo = __builtin_amdgcn_alignbit(l, l, static_cast<uint32_t>(ls + 30) & 31u) & 0x3C3C3C3Cu;
+            return (((hq ^ 0xAAAAAAAAu) << (6 - hs)) & 0xC0C0C0C0u) | lo;
+          };
+          const uint32_t w0 = code4(lo8.x, hi8.x);
+          const uint32_t w1 = code4(lo8.y, hi8.y);
           bq[j][e] = static_cast<long>((static_cast<uint64_t>(w1) << 32) | w0);
           const int s = 2 * b + e;
           const uint32_t sw = s < 4 ? scv[j].x : s < 8 ? scv[j].y : s < 12 ? scv[j].z : scv[j].w;
-          dsc[j][e] = d[j] * static_cast<float>(static_cast<int8_t>(byte_of(sw, s & 3)));
+          // d*sc/4 (exact): the products carry the codes' factor 4
+          dsc[j][e] = 0.25f * d[j] * static_cast<float>(static_cast<int8_t>(byte_of(sw, s & 3)));
         }
         // exact: d*(sc0 + sc1) has at most 20 significant bits
         cc[j][0] = -kMagic * (dsc[j][0] + dsc[j][1]);
