@@ -20,11 +20,11 @@
 //     its int32 result reads as the float 12582912 + I, and fma(f, dsc, c) is
 //     exactly fl(I * dsc).
 //   * The activation scale dx differs per output row, i.e. per accumulator
-//     element.  Instead of one register per element, every lane holds the
-//     scale of one row and the accumulate is v_fmac_f32 with a DPP
-//     row_newbcast operand: element r of every 16-lane DPP row reads the value
-//     held by lane r of that row, which is arranged to be the scale of
-//     element r's output row.
+//     element: the kernels read the 16 scales of a tile's rows for each block
+//     from LDS as four 16-byte broadcasts (staged block-major, [8][BM]) and
+//     accumulate acc = fma(u, dx, acc).  (The DPP=true variant instead keeps
+//     one row's scale per lane and accumulates with v_fmac_f32 and a DPP
+//     row_newbcast operand; it issues more slowly and is not dispatched.)
 // Min term -- on the matrix core: the mins m are 6-bit integers (exact in
 // bfloat16) and dS = dx*S is split exactly into three bfloat16 pieces by the
 // activation quantiser, so two K=16 bf16 MFMAs per tile and super-block give
