@@ -56,6 +56,14 @@ def _bind(path: str):
     lib.oracle_block_partials.restype = None
     lib.oracle_gemm.argtypes = [ci, vp, vp, ci, i64, i64, i64, vp, i64, vp, i64, vp]
     lib.oracle_gemm.restype = ci
+    lib.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_f16.restype = ctypes.c_uint16
+    lib.oracle_x_to_f16.argtypes = [vp, ci, i64, i64, vp]
+    lib.oracle_x_to_f16.restype = None
+    lib.oracle_dequant_f16.argtypes = [ci, vp, i64, i64, vp]
+    lib.oracle_dequant_f16.restype = None
+    lib.oracle_gemm_deq_f16.argtypes = [ci, vp, vp, ci, i64, i64, i64, vp, i64, vp, i64, vp, vp]
+    lib.oracle_gemm_deq_f16.restype = ci
     return lib
 
 
@@ -167,6 +175,52 @@ def gemm(fmt: int, W: np.ndarray, x: np.ndarray, N: int, rows=None, cols=None) -
     if rc != 0:
         raise MemoryError("oracle_gemm: allocation failed")
     return y
+
+
+def f64_to_f16(v: float) -> int:
+    """binary16 bits of the value nearest to v (ties to even)."""
+    return int(_load().oracle_f64_to_f16(float(v)))
+
+
+def x_to_f16(x: np.ndarray) -> np.ndarray:
+    """x [M, K] float32 or bf16 bits -> binary16 bits [M, K] (uint16)."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    out = np.empty((M, K), np.uint16)
+    _load().oracle_x_to_f16(_p(x), _x_dtype(x), M, K, _p(out))
+    return out
+
+
+def dequant_f16(fmt: int, W: np.ndarray, N: int, K: int) -> np.ndarray:
+    """binary16 weights [N, K] (uint16 bits) of the dequantise-to-fp16 branch."""
+    W = np.ascontiguousarray(W, np.uint8)
+    assert W.size == N * K // 256 * BLOCK_BYTES[fmt]
+    out = np.empty((N, K), np.uint16)
+    _load().oracle_dequant_f16(fmt, _p(W), N, K, _p(out))
+    return out
+
+
+def gemm_deq_f16(fmt: int, W: np.ndarray, x: np.ndarray, N: int, rows=None, cols=None):
+    """(y, yabs) [len(rows), len(cols)] in fp64 for the dequantise-to-fp16 branch:
+    y = x16 . w16^T and yabs = sum_k |x16 * w16|."""
+    W = np.ascontiguousarray(W, np.uint8)
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    assert K % 256 == 0 and W.size == N * K // 256 * BLOCK_BYTES[fmt]
+    r = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    y = np.empty((nr, nc), np.float64)
+    ya = np.empty((nr, nc), np.float64)
+    if nr == 0 or nc == 0:
+        return y, ya
+    rc = _load().oracle_gemm_deq_f16(fmt, _p(W), _p(x), _x_dtype(x), M, N, K,
+                                     None if r is None else _p(r), nr,
+                                     None if c is None else _p(c), nc, _p(y), _p(ya))
+    if rc != 0:
+        raise MemoryError("oracle_gemm_deq_f16: allocation failed")
+    return y, ya
 
 
 class Oracle:

@@ -318,3 +318,165 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
     free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw);
     return 0;
 }
+
+/* ============================================================================
+ * The other design branch: dequantise the weights to 16-bit floats and run a
+ * float GEMM on them.  aprender issue #5475 ("apr serve / apr run: Qwen3.5 on
+ * CPU prefills one token at a time ..."), section "Ask", item 1, names it as
+ * the alternative to the fused Q4_K x int8 kernel (there: dequantise a tile to
+ * F32 and call the GEMM); aprender issue #4220 ("CRUX parity spike ..."),
+ * section "Readings", has the serving path hold the prefill weights as a
+ * dense fp16 copy.  On the matrix cores a float GEMM takes 16-bit operands,
+ * so this branch dequantises to IEEE binary16 (11 significant bits, against
+ * bfloat16's 8).  The pages fix no rounding; the reading taken here rounds
+ * each step once, to nearest with ties to even:
+ *   x16  = f16(x)                         (x as its fp32 value; bf16 widens exactly)
+ *   Q4_K: dsc = f16(d*sc[j]), dmn = f16(dmin*m[j]), w16 = f16(dsc*q - dmn)
+ *   Q6_K: dsc = f16(d*sc[s]),                       w16 = f16(dsc*(q6 - 32))
+ *   y[m][n] = sum_k x16[m][k] * w16[n][k]   (exact products, fp64 sum)
+ * where f16(v) is the binary16 value nearest to the exact real v (ties to the
+ * even significand, magnitudes from 65520 up to infinity).  Every f16() here is
+ * applied to an exactly known value, so there is one rounding per step.
+ * ========================================================================== */
+
+/* binary16 bits of the value nearest to D * 2^e (D an exact integer). */
+static uint16_t f16_round_scaled(int64_t D, int e) {
+    uint16_t sign = 0;
+    if (D < 0) { sign = 0x8000; D = -D; }
+    if (D == 0) return sign;
+    /* normalise: D < 2^62 so that shifting left stays exact */
+    while (D >= ((int64_t)1 << 62)) {            /* keep a sticky bit while halving */
+        int64_t lost = D & 1;
+        D = (D >> 1) | lost;
+        e += 1;
+    }
+    int top = 63 - __builtin_clzll((unsigned long long)D);   /* value in [2^(top+e), 2^(top+e+1)) */
+    int ev = top + e;                                         /* exponent of the leading bit */
+    int qe = ev - 10 < -24 ? -24 : ev - 10;                   /* exponent of one unit in the last place */
+    int64_t r;
+    if (qe <= e) {
+        r = D << (e - qe);                                    /* exact: no bits below the quantum */
+    } else {
+        int sh = qe - e;
+        if (sh > 62) return sign;                             /* far below half the smallest subnormal */
+        int64_t keep = D >> sh, rem = D - (keep << sh), half = (int64_t)1 << (sh - 1);
+        r = keep + ((rem > half || (rem == half && (keep & 1))) ? 1 : 0);
+    }
+    /* r counts quanta of 2^qe; for normals r is in [1024, 2048] */
+    if (qe == -24 && r < 1024) return (uint16_t)(sign | r);   /* subnormal */
+    if (r == 2048) { r = 1024; qe += 1; }
+    if (qe - (-24) > 29) return (uint16_t)(sign | 0x7C00);    /* past the largest finite value */
+    int ebits = qe + 25;                                      /* biased exponent: value = r * 2^qe */
+    if (ebits >= 31) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (ebits << 10) | (r - 1024));
+}
+
+/* binary16 bits of the value nearest to the finite double v. */
+uint16_t oracle_f64_to_f16(double v) {
+    if (v != v) return 0x7E00;
+    if (v == INFINITY) return 0x7C00;
+    if (v == -INFINITY) return 0xFC00;
+    if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+    int e;
+    double fr = frexp(v, &e);                 /* v = fr * 2^e, 0.5 <= |fr| < 1 */
+    int64_t D = (int64_t)ldexp(fr, 53);       /* exact: 53 significant bits */
+    return f16_round_scaled(D, e - 53);
+}
+
+/* A binary16 value as an exact integer significand and exponent: v = sig * 2^ex. */
+static void f16_split(uint16_t h, int64_t *sig, int *ex) {
+    int s = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    int64_t m = e == 0 ? f : (f | 0x400);
+    *sig = s ? -m : m;
+    *ex = e == 0 ? -24 : e - 25;
+}
+
+/* x [M x K] (fp32 or bf16) -> binary16 bits. */
+void oracle_x_to_f16(const void *x, int x_dtype, int64_t M, int64_t K, uint16_t *x16) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * K; i++) x16[i] = oracle_f64_to_f16((double)load_x(x, x_dtype, i));
+}
+
+/* The binary16 weights w16 [N x K] of the rounding chain above. */
+void oracle_dequant_f16(int fmt, const uint8_t *W, int64_t N, int64_t K, uint16_t *w16) {
+    int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N * nb; i++) {
+        uint8_t q[256];
+        uint16_t *o = w16 + i * 256;
+        if (fmt == ORACLE_Q4_K) {
+            uint8_t sc[8], m[8];
+            double d, dmin;
+            decode_q4k_block(W + i * 144, q, sc, m, &d, &dmin);
+            for (int j = 0; j < 8; j++) {
+                int64_t a, b;
+                int ea, eb;
+                f16_split(oracle_f64_to_f16(d * sc[j]), &a, &ea);     /* d*sc is exact in fp64 */
+                f16_split(oracle_f64_to_f16(dmin * m[j]), &b, &eb);
+                int e0 = ea < eb ? ea : eb;
+                for (int t = 0; t < 32; t++) {
+                    /* dsc*q - dmn exactly, as an integer times 2^e0 (< 2^60) */
+                    int64_t D = ((a * q[32 * j + t]) << (ea - e0)) - (b << (eb - e0));
+                    o[32 * j + t] = f16_round_scaled(D, e0);
+                }
+            }
+        } else {
+            int8_t sc[16];
+            double d;
+            decode_q6k_block(W + i * 210, q, sc, &d);
+            for (int s = 0; s < 16; s++) {
+                int64_t a;
+                int ea;
+                f16_split(oracle_f64_to_f16(d * sc[s]), &a, &ea);
+                for (int t = 0; t < 16; t++)
+                    o[16 * s + t] = f16_round_scaled(a * ((int64_t)q[16 * s + t] - 32), ea);
+            }
+        }
+    }
+}
+
+/* y [nrows x ncols] = x16 . w16^T in fp64 over the selected rows / columns
+ * (all when rows / cols is NULL), plus yabs = sum_k |x16*w16| (the scale of the
+ * fp32 summation error the GPU is allowed).  Returns 0, or -1 on allocation
+ * failure. */
+int oracle_gemm_deq_f16(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M,
+                        int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                        const int64_t *cols, int64_t ncols, double *y, double *yabs) {
+    if (!rows) nrows = M;
+    if (!cols) ncols = N;
+    int64_t bbytes = fmt == ORACLE_Q4_K ? 144 : 210, nsb = K / 256;
+    double *xd = malloc(sizeof(double) * (size_t)(nrows * K));
+    double *wd = malloc(sizeof(double) * (size_t)(ncols * K));
+    uint16_t *tmp = malloc(sizeof(uint16_t) * (size_t)K);
+    if (!xd || !wd || !tmp) { free(xd); free(wd); free(tmp); return -1; }
+    free(tmp);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; i++) {
+        int64_t r = rows ? rows[i] : i;
+        for (int64_t k = 0; k < K; k++)
+            xd[i * K + k] = oracle_half_to_double(oracle_f64_to_f16((double)load_x(x, x_dtype, r * K + k)));
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        uint16_t w16[256];
+        for (int64_t sb = 0; sb < nsb; sb++) {
+            oracle_dequant_f16(fmt, W + (n * nsb + sb) * bbytes, 1, 256, w16);
+            for (int v = 0; v < 256; v++) wd[j * K + 256 * sb + v] = oracle_half_to_double(w16[v]);
+        }
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < nrows; i++)
+        for (int64_t j = 0; j < ncols; j++) {
+            double acc = 0.0, aabs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = xd[i * K + k] * wd[j * K + k];   /* exact: 11 x 11 significant bits */
+                acc += p;
+                aabs += fabs(p);
+            }
+            y[i * ncols + j] = acc;
+            if (yabs) yabs[i * ncols + j] = aabs;
+        }
+    free(xd); free(wd);
+    return 0;
+}

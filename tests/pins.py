@@ -16,7 +16,11 @@ mathematics fix:
   * the textbook special case (unit scales, zero mins, integer activations
     whose blocks all reach +-127) where the result is a plain integer matmul,
   * closed-form sums of the worked examples under an all-ones activation row,
-  * invariants (row / column selection, exact power-of-two scaling of x).
+  * invariants (row / column selection, exact power-of-two scaling of x),
+  * for the dequantise-to-fp16 branch: binary16 rounding against numpy's and
+    CPython's own conversions, the worked examples (binary16-exact), the
+    rounding chain rebuilt from numpy conversions, brute force and the
+    textbook integer case.
 
 The mutation tests plant plausible mistakes in a copy of oracle.c and require
 that at least one of these functions fails for each.
@@ -374,8 +378,119 @@ def pin_gemm_semantic_bound(orc):
         assert np.all(np.abs(y - exact) <= bound + 1e-12)
 
 
+# ------------------------------------------------- dequantise-to-fp16 branch
+
+def _np_f16(v) -> np.ndarray:
+    """binary16 bits of float64 values, rounded by numpy's own conversion."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, np.float64).astype(np.float16).view(np.uint16)
+
+
+def pin_f16_rounding(orc):
+    """Round-to-nearest-even binary16 from double, against numpy's conversion and
+    CPython's struct 'e' packing (two independent implementations)."""
+    import struct
+    rng = np.random.default_rng(7)
+    quanta = 2.0 ** rng.integers(-34, 6, 4000)
+    vals = [rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 5, 4000),
+            (rng.integers(0, 2048, 4000) + 0.5) * quanta,                    # exact ties
+            (rng.integers(0, 2048, 4000) + 0.5) * quanta * (1 + 2.0 ** -40),  # just above a tie
+            (rng.integers(0, 2048, 4000) + 0.5) * quanta * (1 - 2.0 ** -40),  # just below a tie
+            np.array([0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -26,
+                      65504.0, 65519.99, 65520.0, -65520.0, 1e30, -1e-30, 1 + 2.0 ** -11 + 2.0 ** -40])]
+    v = np.concatenate(vals)
+    got = np.array([orc.f64_to_f16(t) for t in v], np.uint16)
+    assert np.array_equal(got, _np_f16(v)), v[got != _np_f16(v)][:5]
+    for t in v[np.abs(v) < 65520][:3000]:
+        assert orc.f64_to_f16(t) == struct.unpack("<H", struct.pack("<e", t))[0], t
+
+
+def pin_f16_activations(orc):
+    x = _acts(61, 3, 512, scale=3.0)
+    x[0, :7] = [0.0, -0.0, 1e-9, -7e-6, 65519.0, 6e-5, -2.5]
+    assert np.array_equal(orc.x_to_f16(x), _np_f16(x.astype(np.float64)))
+    b = synth.to_bf16_bits(x)
+    assert np.array_equal(orc.x_to_f16(b), _np_f16(synth.bf16_bits_to_f32(b).astype(np.float64)))
+
+
+def _np_dequant_f16(orc, fmt, W, N, K):
+    """The fp16 rounding chain written with numpy conversions, on fields decoded
+    by the (separately pinned) block decoders.  A zero weight is compared as +0
+    (its sign is not part of the method)."""
+    if fmt == Q4_K:
+        q, sc, m, d, dmin = orc.decode_q4k(W, N, K)
+        d32 = np.repeat(d, 8, axis=1)
+        dm32 = np.repeat(dmin, 8, axis=1)
+        dsc = _np_f16(d32 * sc).view(np.float16).astype(np.float64)
+        dmn = _np_f16(dm32 * m).view(np.float16).astype(np.float64)
+        exact = np.repeat(dsc, 32, axis=1) * q - np.repeat(dmn, 32, axis=1)
+    else:
+        q6, sc, d = orc.decode_q6k(W, N, K)
+        dsc = _np_f16(np.repeat(d, 16, axis=1) * sc).view(np.float16).astype(np.float64)
+        exact = np.repeat(dsc, 16, axis=1) * (q6.astype(np.float64) - 32)
+    return _np_f16(exact + 0.0)
+
+
+def pin_f16_dequant_worked_examples(orc):
+    blk4, fx4 = q4k_example_block()
+    w4 = orc.dequant_f16(Q4_K, blk4, 1, 256).view(np.float16).astype(np.float64)
+    assert w4.sum() == float(fx4["sum_w"])                     # every value is binary16-exact
+    assert w4.min() == float(fx4["min_w"]) and w4.max() == float(fx4["max_w"])
+    blk6, fx6 = q6k_example_block()
+    w6 = orc.dequant_f16(Q6_K, blk6, 1, 256).view(np.float16).astype(np.float64)
+    assert w6.sum() == float(fx6["sum_w"])
+
+
+def pin_f16_dequant_rounding(orc):
+    for fmt in (Q4_K, Q6_K):
+        # exponents up to 23: every d*sc stays below 65504, so the rounded
+        # sub-block scales are finite (scales that overflow are outside the domain)
+        for seed, (emin, emax) in ((3, (1, 23)), (4, (10, 20)), (5, (1, 6))):
+            N, K = 9, 512
+            W = synth.random_blocks(fmt, N, K, seed=700 + seed, emin=emin, emax=emax)
+            assert np.array_equal(orc.dequant_f16(fmt, W, N, K), _np_dequant_f16(orc, fmt, W, N, K))
+    # a hand-built case: d = 1 + 2^-10 and sc = 3 give d*sc = 3 + 3*2^-10, a binary16 tie
+    # between 3 + 2^-9 and 3 + 2^-8 that goes to the even 3 + 2^-8
+    blk = np.zeros(144, np.uint8)
+    blk[0:2] = (0x01, 0x3C)
+    blk[4] = 3
+    blk[16] = 0x01                                                # q[0] = 1
+    w = orc.dequant_f16(Q4_K, blk, 1, 256).view(np.float16).astype(np.float64)
+    assert w[0, 0] == 3 + 2.0 ** -8 and w[0, 1] == 0.0
+
+
+def pin_f16_gemm_bruteforce(orc):
+    for fmt in (Q4_K, Q6_K):
+        for (M, N, K, seed) in ((1, 1, 256, 1), (3, 5, 512, 2), (4, 7, 768, 3)):
+            W = synth.random_blocks(fmt, N, K, seed=800 + seed, emin=5, emax=18)
+            x = _acts(900 + seed, M, K)
+            for xin in (x, synth.to_bf16_bits(x)):
+                y, ya = orc.gemm_deq_f16(fmt, W, xin, N)
+                xf = x.astype(np.float64) if xin.dtype == np.float32 else \
+                    synth.bf16_bits_to_f32(xin).astype(np.float64)
+                x16 = _np_f16(xf).view(np.float16).astype(np.float64)
+                w16 = _np_dequant_f16(orc, fmt, W, N, K).view(np.float16).astype(np.float64)
+                ref, refabs = x16 @ w16.T, np.abs(x16) @ np.abs(w16).T
+                assert np.all(np.abs(y - ref) <= 1e-12 * refabs + 1e-300)
+                assert np.allclose(ya, refabs, rtol=1e-12, atol=0)
+
+
+def pin_f16_gemm_textbook(orc):
+    for fmt in (Q4_K, Q6_K):
+        M, N, K = 5, 6, 512
+        W, wv = _textbook_blocks(fmt, N, K, seed=29 + fmt)
+        xi = _integer_acts(M, K, seed=39 + fmt)
+        y, _ = orc.gemm_deq_f16(fmt, W, xi.astype(np.float32), N)
+        assert np.array_equal(y, (xi @ wv.T).astype(np.float64))
+        rows, cols = np.array([4, 1]), np.array([5, 0, 0])
+        ys, _ = orc.gemm_deq_f16(fmt, W, xi.astype(np.float32), N, rows=rows, cols=cols)
+        assert np.array_equal(ys, y[np.ix_(rows, cols)])
+
+
 ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bit_probe,
             pin_q6k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
             pin_quant_symmetry_and_scaling, pin_quant_integer_blocks, pin_quant_bf16_matches_f32,
             pin_gemm_bruteforce, pin_gemm_textbook, pin_gemm_worked_examples,
-            pin_gemm_selection_and_scaling, pin_gemm_semantic_bound]
+            pin_gemm_selection_and_scaling, pin_gemm_semantic_bound,
+            pin_f16_rounding, pin_f16_activations, pin_f16_dequant_worked_examples,
+            pin_f16_dequant_rounding, pin_f16_gemm_bruteforce, pin_f16_gemm_textbook]

@@ -75,6 +75,27 @@ MUTANTS = [
     ("partials_offset_dropped",
      "acc += ((int32_t)qw[n * K + b * L + t] - off) * (int32_t)qx[mi * K + b * L + t];",
      "acc += ((int32_t)qw[n * K + b * L + t]) * (int32_t)qx[mi * K + b * L + t];"),
+    ("f16_ties_away_from_zero",
+     "r = keep + ((rem > half || (rem == half && (keep & 1))) ? 1 : 0);",
+     "r = keep + ((rem >= half) ? 1 : 0);"),
+    ("f16_no_subnormal_floor",
+     "int qe = ev - 10 < -24 ? -24 : ev - 10;",
+     "int qe = ev - 10;"),
+    ("f16_exponent_bias",
+     "int ebits = qe + 25;",
+     "int ebits = qe + 24;"),
+    ("deq_f16_min_sign",
+     "int64_t D = ((a * q[32 * j + t]) << (ea - e0)) - (b << (eb - e0));",
+     "int64_t D = ((a * q[32 * j + t]) << (ea - e0)) + (b << (eb - e0));"),
+    ("deq_f16_neighbour_scale",
+     "f16_split(oracle_f64_to_f16(d * sc[j]), &a, &ea);     /* d*sc is exact in fp64 */",
+     "f16_split(oracle_f64_to_f16(d * sc[j ^ 1]), &a, &ea);"),
+    ("deq_f16_q6_offset_dropped",
+     "o[16 * s + t] = f16_round_scaled(a * ((int64_t)q[16 * s + t] - 32), ea);",
+     "o[16 * s + t] = f16_round_scaled(a * ((int64_t)q[16 * s + t]), ea);"),
+    ("gemm_f16_abs_sum_signed",
+     "aabs += fabs(p);",
+     "aabs += p;"),
 ]
 
 
