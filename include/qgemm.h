@@ -153,6 +153,47 @@ int qgemm_dequant(const void *q_weights, int fmt, int64_t N, int64_t K, float *w
 int qgemm_block_partials(const void *q_weights, int fmt, const int8_t *qx, int64_t M, int64_t N,
                          int64_t K, int32_t *out, void *stream);
 
+/* ---- the other design branch: dequantise to binary16, float matrix-core GEMM ----
+ *
+ * aprender issue #5475 ("apr serve / apr run: Qwen3.5 on CPU prefills one token
+ * at a time ..."), section "Ask", item 1, names two kernels for the batched
+ * quantised matmul: dequantise a weight tile and call a float GEMM, or the
+ * row-batched fused Q4_K x int8 kernel above.  These entry points are the first
+ * branch, built to measure it beside the second; they compute a different
+ * (fp16-rounded) result, not the int8 method's.  Each step rounds once, to
+ * nearest even:
+ *   x16 = f16(x)  (x as its fp32 value; bf16 widens exactly)
+ *   per sub-block j: dsc = f16(d*sc[j]), dmn = f16(dmin*m[j]); w16 = f16(dsc*q - dmn)
+ *   y[m][n] = sum_k x16[m][k] * w16[n][k], accumulated in fp32 on the matrix cores.
+ * Activations of magnitude 65520 and above become infinite in binary16, and
+ * weights whose d*sc or dmin*m reach 65520 are outside the domain (results
+ * unspecified).  Q4_K only (QG_EFMT otherwise). */
+
+/* Workspace bytes for qgemm_prefill_deq_f16: the binary16 copy of x (M*K*2,
+ * rounded up to 256).  0 when M < 1, K < 256, K % 256 != 0 or on overflow. */
+size_t qgemm_deq_f16_workspace_bytes(int64_t M, int64_t K);
+
+/* y[m][n] = sum_k x16[m][k] * w16[n][k] as above.  Arguments, alignment,
+ * ownership and error codes as qgemm_prefill, with workspace sized by
+ * qgemm_deq_f16_workspace_bytes.  Two launches: x -> binary16 into the
+ * workspace, then the GEMM, which dequantises each weight tile in registers. */
+int qgemm_prefill_deq_f16(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
+                          int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Name of the GEMM kernel qgemm_prefill_deq_f16 launches (as a profiler lists
+ * it), or NULL for arguments it would reject.  Needs no GPU. */
+const char *qgemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* Test hooks of this branch.  qgemm_to_f16: x [M][K] -> binary16 bits x16 [M][K]
+ * (K % 8 == 0; x and x16 16-byte aligned).  qgemm_dequant_f16: every weight of
+ * W [N][K] as binary16 bits w16 [N][K] (16-byte aligned), through the GEMM's own
+ * decoder for Q4_K; for Q6_K: dsc = f16(d*sc[s]), w16 = f16(dsc*(q6 - 32)).
+ * A zero weight may be returned as -0. */
+int qgemm_to_f16(const void *x, int x_dtype, int64_t M, int64_t K, uint16_t *x16, void *stream);
+int qgemm_dequant_f16(const void *q_weights, int fmt, int64_t N, int64_t K, uint16_t *w16,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

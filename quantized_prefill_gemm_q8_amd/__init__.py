@@ -24,7 +24,8 @@ BLOCK_BYTES = {QG_Q4_K: 144, QG_Q6_K: 210}
 SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_lm_head",
            "qgemm_quantize_workspace", "qgemm_gemm_quantized",
            "qgemm_strerror", "qgemm_kernel_name", "qgemm_quantize_act", "qgemm_dequant",
-           "qgemm_block_partials")
+           "qgemm_block_partials", "qgemm_deq_f16_workspace_bytes", "qgemm_prefill_deq_f16",
+           "qgemm_deq_f16_kernel_name", "qgemm_to_f16", "qgemm_dequant_f16")
 
 
 class QgemmError(RuntimeError):
@@ -71,6 +72,16 @@ def load() -> ctypes.CDLL:
         lib.qgemm_dequant.restype = ci
         lib.qgemm_block_partials.argtypes = [vp, ci, vp, i64, i64, i64, vp, vp]
         lib.qgemm_block_partials.restype = ci
+        lib.qgemm_deq_f16_workspace_bytes.argtypes = [i64, i64]
+        lib.qgemm_deq_f16_workspace_bytes.restype = sz
+        lib.qgemm_prefill_deq_f16.argtypes = [vp, ci, vp, ci, i64, i64, i64, vp, vp, sz, vp]
+        lib.qgemm_prefill_deq_f16.restype = ci
+        lib.qgemm_deq_f16_kernel_name.argtypes = [ci, i64, i64, i64]
+        lib.qgemm_deq_f16_kernel_name.restype = ctypes.c_char_p
+        lib.qgemm_to_f16.argtypes = [vp, ci, i64, i64, vp, vp]
+        lib.qgemm_to_f16.restype = ci
+        lib.qgemm_dequant_f16.argtypes = [vp, ci, i64, i64, vp, vp]
+        lib.qgemm_dequant_f16.restype = ci
         _lib = lib
     return _lib
 
@@ -162,6 +173,34 @@ def qgemm_dequant(q_weights, fmt, N, K, w, stream=None):
 def qgemm_block_partials(q_weights, fmt, qx, M, N, K, out, stream=None):
     _check(load().qgemm_block_partials(_ptr(q_weights), fmt, _ptr(qx), M, N, K, _ptr(out),
                                        _stream(stream)), "qgemm_block_partials")
+
+
+# ---- the dequantise-to-fp16 branch (measured beside the int8 method) ----
+
+def qgemm_deq_f16_workspace_bytes(M: int, K: int) -> int:
+    return int(load().qgemm_deq_f16_workspace_bytes(M, K))
+
+
+def qgemm_prefill_deq_f16(q_weights, fmt, x, M, N, K, y, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_prefill_deq_f16(_ptr(q_weights), fmt, _ptr(x), _dtype_code(x), M, N, K,
+                                        _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
+           "qgemm_prefill_deq_f16")
+
+
+def qgemm_deq_f16_kernel_name(fmt: int, M: int, N: int, K: int) -> str | None:
+    r = load().qgemm_deq_f16_kernel_name(fmt, M, N, K)
+    return None if r is None else r.decode()
+
+
+def qgemm_to_f16(x, M, K, x16, stream=None):
+    _check(load().qgemm_to_f16(_ptr(x), _dtype_code(x), M, K, _ptr(x16), _stream(stream)),
+           "qgemm_to_f16")
+
+
+def qgemm_dequant_f16(q_weights, fmt, N, K, w16, stream=None):
+    _check(load().qgemm_dequant_f16(_ptr(q_weights), fmt, N, K, _ptr(w16), _stream(stream)),
+           "qgemm_dequant_f16")
 
 
 # ---- plumbing helpers: device buffers for callers that do not manage their own ----

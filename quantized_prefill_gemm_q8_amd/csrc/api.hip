@@ -230,4 +230,59 @@ int qgemm_block_partials(const void* q_weights, int fmt, const int8_t* qx, int64
                                                 M, N, K, out, static_cast<hipStream_t>(stream)));
 }
 
+// ---- the dequantise-to-fp16 branch ----
+
+size_t qgemm_deq_f16_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 256 || K % 256 != 0 || M > (INT64_C(1) << 39) / K) return 0;  // 2*M*K <= 2^40
+  return static_cast<size_t>((M * K * 2 + 255) / 256 * 256);
+}
+
+int qgemm_to_f16(const void* x, int x_dtype, int64_t M, int64_t K, uint16_t* x16, void* stream) {
+  if (!x || !x16 || M < 1 || K < 8 || K % 8 != 0) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / K) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  if (!aligned(x, 16) || !aligned(x16, 16)) return QG_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_to_f16(x, x_dtype, M, K, x16, static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_dequant_f16(const void* q_weights, int fmt, int64_t N, int64_t K, uint16_t* w16,
+                      void* stream) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (!w16) return QG_EINVAL;
+  if (!aligned(w16, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_dequant_f16(static_cast<const uint8_t*>(q_weights), fmt, N, K, w16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_prefill_deq_f16(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M,
+                          int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (fmt != QG_Q4_K) return QG_EFMT;
+  if (!x || !y || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  const size_t need = qgemm_deq_f16_workspace_bytes(M, K);
+  if (need == 0 || M > (INT64_C(1) << 40) / N) return QG_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return QG_EWORKSPACE;
+  if (!aligned(x, 16) || !aligned(y, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* x16 = static_cast<uint16_t*>(workspace);
+  rc = launch_status(qg_launch_to_f16(x, x_dtype, M, K, x16, s));
+  if (rc) return rc;
+  return launch_status(qg_launch_gemm_deq_f16(static_cast<const uint8_t*>(q_weights), x16, M, N, K, y, s));
+}
+
+const char* qgemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt != QG_Q4_K || M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
+  return qg_gemm_deq_f16_kernel_name(M, N, K);
+}
+
 }  // extern "C"

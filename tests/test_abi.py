@@ -148,3 +148,32 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 8, 8, 300, AUTO) is None
     assert kn(Q4, 9, 8, 256, SKINNY) is None
     assert kn(Q4, 0, 8, 256, AUTO) is None
+
+
+def test_deq_f16_branch_host_side():
+    """The dequantise-to-fp16 branch: workspace sizing, argument checks and kernel
+    choice (no GPU call)."""
+    lib = qg.load()
+    ws = qg.qgemm_deq_f16_workspace_bytes
+    assert ws(0, 256) == 0 and ws(4, 300) == 0 and ws(1, 1 << 40) == 0
+    assert ws(1, 256) == 512 and ws(3, 256) == 1536 and ws(5, 256) == 2560
+    assert ws(512, 4096) == 512 * 4096 * 2
+    wsb = ws(4, 256)
+    call = lambda **k: lib.qgemm_prefill_deq_f16(
+        k.get("w", A), k.get("fmt", 0), k.get("x", A), k.get("xdt", 1), k.get("M", 4),
+        k.get("N", 8), k.get("K", 256), k.get("y", A), k.get("ws", A), k.get("wsb", wsb), None)
+    assert call(w=None) == -1 and call(M=0) == -1 and call(K=300) == -1
+    assert call(fmt=1) == -2 and call(fmt=5) == -2          # Q4_K only
+    assert call(xdt=3) == -3
+    assert call(ws=None) == -4 and call(wsb=wsb - 1) == -4 and call(ws=A + 64) == -4
+    assert call(x=A + 2) == -5 and call(y=A + 4) == -5 and call(w=A + 8) == -5
+    assert lib.qgemm_to_f16(A, 1, 4, 12, A, None) == -1     # K % 8 != 0
+    assert lib.qgemm_to_f16(A, 4, 4, 16, A, None) == -3
+    assert lib.qgemm_to_f16(A, 1, 4, 16, A + 2, None) == -5
+    assert lib.qgemm_dequant_f16(A, 0, 8, 100, A, None) == -1
+    assert lib.qgemm_dequant_f16(A, 2, 8, 256, A, None) == -2
+    assert lib.qgemm_dequant_f16(A, 0, 8, 256, A + 2, None) == -5
+    kn = qg.qgemm_deq_f16_kernel_name
+    assert kn(1, 512, 4096, 1024) is None and kn(0, 512, 4096, 1000) is None
+    assert kn(0, 512, 4096, 1024) == "gemm_deq_f16_kernel<2, 1, 1, 4, 3, 4>"
+    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<2, 1, 2, 4, 3, 4>"
