@@ -21,8 +21,9 @@ roofline of the dominant kernel (the GEMM kernel with the largest share of the
 step; its launches run back to back), the large-M headline
 projections (K=4096 -> N=24576 Q4_K and K=12288 -> N=4096 Q6_K at M=512), the
 decode-sized GEMV (M = 1 and 8) over every projection shape of the workloads,
-the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K) and the CPU oracle timed
-on the host.
+the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K), the other design branch
+(weights dequantised to fp16 in the GEMM, fp16 matrix cores) beside the int8
+method on every Q4_K projection shape, and the CPU oracle timed on the host.
 
 --calib-copy-mib N additionally runs a plain elementwise copy kernel over
 N MiB (read N, write N) three times: the reference dispatch for scaling HBM
@@ -138,6 +139,7 @@ def parse():
     p.add_argument("--big-steps", type=int, default=30)   # 0: skip the large-M GEMMs
     p.add_argument("--gemv-steps", type=int, default=200)  # 0: skip the decode GEMV table
     p.add_argument("--set-steps", type=int, default=10)   # 0: skip the config 3/4 projection sets
+    p.add_argument("--branch-steps", type=int, default=5)  # 0: skip the fp16 design-branch table
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -395,6 +397,46 @@ def main():
         del Ws
     torch.cuda.empty_cache()
 
+    # ---------------- the other design branch (dequantise to fp16, float matrix-core
+    # GEMM) beside the int8 method, per Q4_K projection shape: both timed as whole
+    # calls (int8: quantiser + GEMM; fp16: x -> binary16 + GEMM), back to back
+    branch = {}
+    for cfg in (2, 3, 4) if args.branch_steps > 0 else ():
+        for g in synth.CONFIGS[cfg]:
+            if g.fmt != qg.QG_Q4_K:
+                continue
+            Wb = to_dev(synth.make_weights(g))
+            xb = to_dev(synth.make_acts(g))
+            yb = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
+            ws8 = qg.alloc_workspace(g.M, g.K, dev)
+            ws16 = torch.empty(qg.qgemm_deq_f16_workspace_bytes(g.M, g.K), dtype=torch.uint8,
+                               device=dev)
+            calls = {
+                "int8": lambda: qg.qgemm_prefill(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws8, stream),
+                "f16": lambda: qg.qgemm_prefill_deq_f16(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws16,
+                                                        stream)}
+            us = {}
+            for k, fn in calls.items():
+                for _ in range(2):
+                    fn()
+                a, b = ev(), ev()
+                a.record(stream)
+                for _ in range(args.branch_steps):
+                    fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                us[k] = 1e3 * a.elapsed_time(b) / args.branch_steps
+            branch[f"c{cfg}_{g.name}"] = {
+                "shape": f"M={g.M} K={g.K} N={g.N} Q4_K",
+                "int8_us": round(us["int8"], 2),
+                "int8_tops": round(g.ops / (us["int8"] * 1e-6) / 1e12, 1),
+                "f16_us": round(us["f16"], 2),
+                "f16_tflops": round(g.ops / (us["f16"] * 1e-6) / 1e12, 1),
+                "f16_kernel": qg.qgemm_deq_f16_kernel_name(g.fmt, g.M, g.N, g.K),
+                "f16_over_int8_speed": round(us["int8"] / us["f16"], 3)}
+            del Wb, xb, yb, ws8, ws16
+    torch.cuda.empty_cache()
+
     # ---------------- decode-sized GEMV over every projection shape of the workloads
     # (M = 1 and M = 8 rows; weight bytes / kernel time against 8 TB/s)
     gemv = {}
@@ -546,6 +588,7 @@ def main():
         "projection_sets": sets,
         "decode_gemv": gemv,
         "lm_head": lm_out,
+        "design_branch_f16": branch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

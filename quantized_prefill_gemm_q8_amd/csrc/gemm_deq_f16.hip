@@ -310,20 +310,26 @@ static void launch_deq(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t
 }  // namespace qg
 
 namespace {
-enum class DeqPick { k128x128, k64x128 };
+enum class DeqPick { k256x128, k128x128, k64x128 };
 
-// 128x128 blocks (8 waves, 64x32 each) when they cover the CUs, else 64x128
-// blocks (4 waves).
+// Measured on the workloads' Q4_K shapes: 256x128 blocks of 8 waves (128x32
+// each: four row tiles share one dequantised weight fragment) when they cover
+// the CUs; 128x128 blocks of 4 such waves when those nearly do; else 64x128
+// blocks of 4 waves with two row tiles each (more, smaller workgroups).
 DeqPick pick_deq(int64_t M, int64_t N) {
+  const int64_t b256 = ((M + 255) / 256) * ((N + 127) / 128);
   const int64_t b128 = ((M + 127) / 128) * ((N + 127) / 128);
-  return b128 >= 256 ? DeqPick::k128x128 : DeqPick::k64x128;
+  if (b256 >= 256) return DeqPick::k256x128;
+  if (b128 >= 200) return DeqPick::k128x128;
+  return DeqPick::k64x128;
 }
 }  // namespace
 
 const char* qg_gemm_deq_f16_kernel_name(int64_t M, int64_t N, int64_t K) {
   (void)K;
   switch (pick_deq(M, N)) {
-    case DeqPick::k128x128: return "gemm_deq_f16_kernel<2, 1, 2, 4, 3, 4>";
+    case DeqPick::k256x128: return "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4>";
+    case DeqPick::k128x128: return "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4>";
     case DeqPick::k64x128: return "gemm_deq_f16_kernel<2, 1, 1, 4, 3, 4>";
   }
   return "?";
@@ -357,7 +363,8 @@ hipError_t qg_launch_dequant_f16(const uint8_t* W, int fmt, int64_t N, int64_t K
 hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N,
                                   int64_t K, float* y, hipStream_t stream) {
   switch (pick_deq(M, N)) {
-    case DeqPick::k128x128: qg::launch_deq<2, 1, 2, 4, 3, 4>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k256x128: qg::launch_deq<4, 1, 2, 4, 2, 4>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k128x128: qg::launch_deq<4, 1, 1, 4, 2, 4>(W, x16, M, N, K, y, stream); break;
     case DeqPick::k64x128: qg::launch_deq<2, 1, 1, 4, 3, 4>(W, x16, M, N, K, y, stream); break;
   }
   return hipGetLastError();

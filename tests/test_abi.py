@@ -176,4 +176,6 @@ def test_deq_f16_branch_host_side():
     kn = qg.qgemm_deq_f16_kernel_name
     assert kn(1, 512, 4096, 1024) is None and kn(0, 512, 4096, 1000) is None
     assert kn(0, 512, 4096, 1024) == "gemm_deq_f16_kernel<2, 1, 1, 4, 3, 4>"
-    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<2, 1, 2, 4, 3, 4>"
+    assert kn(0, 512, 7168, 1024) == "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4>"
+    assert kn(0, 512, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4>"
+    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4>"

@@ -90,6 +90,18 @@ def test_gemm_full_parity(M, N, K):
     check_deq(gpu_deq(W, x, N), W, x, N, K, what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(700, 11000, 512), (300, 8500, 512)])
+def test_gemm_large_tiles_sampled(M, N, K):
+    """The 256x128 and 128x128 block kernels on ragged shapes (tails in M and N)."""
+    W = synth.pack(qg.QG_Q4_K, synth.normal(690 + M, (N, K), 0.0, 0.02))
+    x = synth.to_bf16_bits(synth.normal(691 + N, (M, K)))
+    y = gpu_deq(W, x, N)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(M - 40, M), rng.integers(0, M, 24)]))
+    cols = np.unique(np.concatenate([[0, N - 1], np.arange(N - 70, N), rng.integers(0, N, 40)]))
+    check_deq(y, W, x, N, K, rows=rows, cols=cols, what=f"{M}x{N}x{K}")
+
+
 def test_gemm_f32_input_and_wide_scales():
     M, N, K = 96, 160, 1024
     W = synth.random_blocks(qg.QG_Q4_K, N, K, seed=660, emin=5, emax=18)
