@@ -166,8 +166,11 @@ __global__ __launch_bounds__(256) void dequant_f16_q6k_kernel(const uint8_t* __r
 
 // ---------------------------------------------------------------- the GEMM
 
-template <int TM, int TN, int WM, int WN, int NS, int OCC>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_deq_f16_kernel(
+// KS > 1: KS groups of WM x WN waves compute the same block over disjoint
+// ranges of stages, each with its own ring; the partial blocks are summed
+// through LDS in group order at the end (deterministic, no atomics).
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_deq_f16_kernel(
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ x16, int64_t M, int64_t N, int64_t K,
     float* __restrict__ y) {
   constexpr int NW = WM * WN;
@@ -181,18 +184,25 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
   constexpr int STAGE = A_BYTES + W_BYTES;
   static_assert(BM % 16 == 0 && BN % 32 == 0, "tile shape");
   static_assert(NS >= 2 && LPT * (NS - 1) < 64, "vmcnt range");
-  static_assert(NS * STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
+  static_assert(KS * NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(KS == 1 || (KS - 1) * NW * TM * TN * 4096 <= KS * NS * STAGE, "reduction space");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[KS * NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / NW, wave = wave_all - grp * NW;  // K-group, wave within the group
+  uint8_t* const lds = lds_all + grp * NS * STAGE;            // this group's ring
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
   const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * BN;
   const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
-  const int64_t nsb = K / 256, stages = K / 64;
+  const int64_t nsb = K / 256, nst = K / 64;
   const int64_t wrow = nsb * kQ4Bytes;
+  // this group's stages: st0 .. st0 + cnt - 1 (the launcher keeps KS <= K/64);
+  // every group runs the longest group's count so that the barriers match
+  const int64_t st0 = grp * nst / KS, cnt = (grp + 1) * nst / KS - st0;
+  const int64_t stages = (nst + KS - 1) / KS;
 
   // Per-lane byte offsets of this wave's loads (computed once; tail rows and
   // columns clamped to the last valid one).  Load it of this wave is wave-load
@@ -220,7 +230,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
   const uint8_t* const a_base = reinterpret_cast<const uint8_t*>(x16) + m_cta * K * 2;
   const uint8_t* const w_base = W + n_cta * wrow;
 
-  auto issue_stage = [&](int64_t s, int buf) {
+  auto issue_stage = [&](int64_t sl, int buf) {
+    const int64_t s = st0 + (sl < cnt ? sl : cnt - 1);  // past the group's range: reload its last
     const int64_t sb = s >> 2;
     const uint32_t qt = static_cast<uint32_t>(s & 3);
     uint8_t* sbase = lds + buf * STAGE;
@@ -253,10 +264,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
     if (s + NS - 1 <= stages) wait_vm_barrier<LPT * (NS - 2)>();
     else wait_vm_barrier<0>();
     if (s + NS - 1 < stages) issue_stage(s + NS - 1, static_cast<int>((s + NS - 1) % NS));
+    if (KS > 1 && s >= cnt) continue;  // a shorter group idles through the last step
 
     const uint8_t* sA = lds + buf * STAGE;
     const uint8_t* sW = sA + A_BYTES;
-    const int qt = static_cast<int>(s & 3);
+    const int qt = static_cast<int>((st0 + s) & 3);
     uint32_t bq[TN][16];
 #pragma unroll
     for (int j = 0; j < TN; j++) {
@@ -285,6 +297,39 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
     }
   }
 
+  if constexpr (KS > 1) {
+    // groups 1..KS-1 leave their blocks in LDS (the rings are free once every
+    // wave has passed the first barrier); group 0 adds them in group order
+    float4* red = reinterpret_cast<float4*>(lds_all);  // [KS-1][NW][TM*TN*4][64]
+    __syncthreads();
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            red[((((grp - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; g++)
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const float4 v = red[((((g - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane];
+            acc[i][j][4 * q] += v.x;
+            acc[i][j][4 * q + 1] += v.y;
+            acc[i][j][4 * q + 2] += v.z;
+            acc[i][j][4 * q + 3] += v.w;
+          }
+  }
+
 #pragma unroll
   for (int j = 0; j < TN; j++) {
     const int64_t n = n_cta + nl0 + 32 * j + l32;
@@ -299,38 +344,46 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OC
   }
 }
 
-template <int TM, int TN, int WM, int WN, int NS, int OCC>
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS = 1>
 static void launch_deq(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N, int64_t K,
                        float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_deq_f16_kernel<TM, TN, WM, WN, NS, OCC><<<grid, dim3(64 * WM * WN), 0, stream>>>(W, x16, M, N, K, y);
+  gemm_deq_f16_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
+      W, x16, M, N, K, y);
 }
 
 }  // namespace qg
 
 namespace {
-enum class DeqPick { k256x128, k128x128, k64x128 };
+enum class DeqPick { k256x128, k128x128, k64x128K2, k128x64K4, k32x64K4 };
 
-// Measured on the workloads' Q4_K shapes: 256x128 blocks of 8 waves (128x32
-// each: four row tiles share one dequantised weight fragment) when they cover
-// the CUs; 128x128 blocks of 4 such waves when those nearly do; else 64x128
-// blocks of 4 waves with two row tiles each (more, smaller workgroups).
+// Measured on the workloads' Q4_K shapes.  Large grids: 256x128 blocks of 8
+// waves (128x32 each: four row tiles share one dequantised weight fragment)
+// when they cover the CUs, else 128x128 blocks of 4 such waves when there are
+// at least 200.  Smaller grids split K inside the workgroup: 64x128 blocks
+// with two K-groups, 128x64 blocks with four, or 32x64 blocks with four.  Every
+// split keeps at least one 64-value stage per group (K >= 256).
 DeqPick pick_deq(int64_t M, int64_t N) {
   const int64_t b256 = ((M + 255) / 256) * ((N + 127) / 128);
   const int64_t b128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t b64 = ((M + 63) / 64) * ((N + 127) / 128);
   if (b256 >= 256) return DeqPick::k256x128;
   if (b128 >= 200) return DeqPick::k128x128;
-  return DeqPick::k64x128;
+  if (b64 >= 256) return DeqPick::k64x128K2;
+  if (b64 >= 128) return DeqPick::k128x64K4;
+  return DeqPick::k32x64K4;
 }
 }  // namespace
 
 const char* qg_gemm_deq_f16_kernel_name(int64_t M, int64_t N, int64_t K) {
   (void)K;
   switch (pick_deq(M, N)) {
-    case DeqPick::k256x128: return "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4>";
-    case DeqPick::k128x128: return "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4>";
-    case DeqPick::k64x128: return "gemm_deq_f16_kernel<2, 1, 1, 4, 3, 4>";
+    case DeqPick::k256x128: return "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>";
+    case DeqPick::k128x128: return "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4, 1>";
+    case DeqPick::k64x128K2: return "gemm_deq_f16_kernel<2, 1, 1, 4, 2, 4, 2>";
+    case DeqPick::k128x64K4: return "gemm_deq_f16_kernel<4, 1, 1, 2, 2, 2, 4>";
+    case DeqPick::k32x64K4: return "gemm_deq_f16_kernel<1, 1, 1, 2, 2, 4, 4>";
   }
   return "?";
 }
@@ -363,9 +416,11 @@ hipError_t qg_launch_dequant_f16(const uint8_t* W, int fmt, int64_t N, int64_t K
 hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N,
                                   int64_t K, float* y, hipStream_t stream) {
   switch (pick_deq(M, N)) {
-    case DeqPick::k256x128: qg::launch_deq<4, 1, 2, 4, 2, 4>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k128x128: qg::launch_deq<4, 1, 1, 4, 2, 4>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k64x128: qg::launch_deq<2, 1, 1, 4, 3, 4>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k256x128: qg::launch_deq<4, 1, 2, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k128x128: qg::launch_deq<4, 1, 1, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k64x128K2: qg::launch_deq<2, 1, 1, 4, 2, 4, 2>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k128x64K4: qg::launch_deq<4, 1, 1, 2, 2, 2, 4>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k32x64K4: qg::launch_deq<1, 1, 1, 2, 2, 4, 4>(W, x16, M, N, K, y, stream); break;
   }
   return hipGetLastError();
 }
