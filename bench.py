@@ -146,11 +146,14 @@ def parse():
     p.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_JSON"))
     p.add_argument("--single", metavar="WORKLOAD",
                    help="time one workload GEMM only (e.g. c4_gate_up_M512) and print its line")
+    p.add_argument("--single-branch", choices=("int8", "f16"), default="int8",
+                   help="with --single: the int8 method (default) or the fp16 design branch")
     return p.parse_args()
 
 
-def run_single(name: str, steps: int) -> None:
-    """Quantise once, then time `steps` back-to-back launches of one workload GEMM."""
+def run_single(name: str, steps: int, branch: str = "int8") -> None:
+    """Quantise once, then time `steps` back-to-back launches of one workload GEMM
+    (branch "f16": whole calls of the fp16 design branch, conversion included)."""
     import numpy as np
     import torch
 
@@ -168,22 +171,30 @@ def run_single(name: str, steps: int) -> None:
     x = torch.from_numpy(xb.view(np.int16) if xb.dtype == np.uint16 else xb).to(dev)
     if xb.dtype == np.uint16:
         x = x.view(torch.bfloat16)
-    ws = qg.alloc_workspace(g.M, g.K, dev)
     y = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
-    qg.qgemm_quantize_workspace(x, g.M, g.K, ws)
+    if branch == "f16":
+        ws = torch.empty(qg.qgemm_deq_f16_workspace_bytes(g.M, g.K), dtype=torch.uint8, device=dev)
+        call = lambda: qg.qgemm_prefill_deq_f16(W, g.fmt, x, g.M, g.N, g.K, y, ws)
+        kname = qg.qgemm_deq_f16_kernel_name(g.fmt, g.M, g.N, g.K)
+    else:
+        ws = qg.alloc_workspace(g.M, g.K, dev)
+        qg.qgemm_quantize_workspace(x, g.M, g.K, ws)
+        call = lambda: qg.qgemm_gemm_quantized(W, g.fmt, ws, g.M, g.N, g.K, y)
+        kname = qg.qgemm_kernel_name(g.fmt, g.M, g.N, g.K)
     for _ in range(3):
-        qg.qgemm_gemm_quantized(W, g.fmt, ws, g.M, g.N, g.K, y)
+        call()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
-        qg.qgemm_gemm_quantized(W, g.fmt, ws, g.M, g.N, g.K, y)
+        call()
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / steps
-    print(json.dumps({"workload": name, "shape": [g.M, g.K, g.N], "fmt": "Q4_K" if g.fmt == 0 else "Q6_K",
-                      "kernel": qg.qgemm_kernel_name(g.fmt, g.M, g.N, g.K), "avg_launch_us": round(us, 3),
+    print(json.dumps({"workload": name, "branch": branch, "shape": [g.M, g.K, g.N],
+                      "fmt": "Q4_K" if g.fmt == 0 else "Q6_K",
+                      "kernel": kname, "avg_launch_us": round(us, 3),
                       "tops": round(g.ops / (us * 1e-6) / 1e12, 2),
                       "gbps_weights": round(g.w_bytes / (us * 1e-6) / 1e9, 1)}), flush=True)
 
@@ -194,7 +205,7 @@ def main():
         pmc_summary(*args.pmc_summary, calib_mib=args.calib_copy_mib or 1024)
         return
     if args.single:
-        run_single(args.single, max(1, min(args.steps, 50)))
+        run_single(args.single, max(1, min(args.steps, 50)), args.single_branch)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

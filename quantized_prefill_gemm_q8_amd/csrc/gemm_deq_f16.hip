@@ -95,12 +95,13 @@ __device__ __forceinline__ uint32_t deq_pair(uint32_t L, h2 dsc, h2 ndmn) {
 }
 
 // The 32 binary16 weights that one lane takes from 16 code bytes of quarter
-// qt of a Q4_K super-block (raw: bytes 16h..16h+15 of the quarter's 32):
-//   out[0..7]  pairs of the low nibbles  (sub-block 2qt), in byte order
-//   out[8..15] pairs of the high nibbles (sub-block 2qt+1), in byte order
+// qt of a Q4_K super-block (raw: bytes 16h..16h+15 of the quarter's 32), as
+// the B operands of the quarter's four K-steps (pairs of values per dword):
+//   out[0], out[1]  low nibbles of bytes 0-7, 8-15   (sub-block 2qt)
+//   out[2], out[3]  high nibbles of bytes 0-7, 8-15  (sub-block 2qt+1)
 // hdr: the block's first 16 bytes (d, dmin, packed scales).
 __device__ __forceinline__ void q4k_quarter_f16(const uint4& hdr, int qt, const uint4& raw,
-                                                uint32_t (&out)[16]) {
+                                                v4i (&out)[4]) {
   const Q4Scales s = unpack_q4_scales(hdr.y, hdr.z, hdr.w);
   const float d = half_to_float(hdr.x & 0xFFFFu), dmin = half_to_float(hdr.x >> 16);
   const int j0 = 2 * qt, j1 = 2 * qt + 1;
@@ -115,10 +116,11 @@ __device__ __forceinline__ void q4k_quarter_f16(const uint4& hdr, int qt, const 
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-    out[2 * i] = deq_pair<0x04010400u>(lo, a0, c0);
-    out[2 * i + 1] = deq_pair<0x04030402u>(lo, a0, c0);
-    out[8 + 2 * i] = deq_pair<0x04010400u>(hi, a1, c1);
-    out[8 + 2 * i + 1] = deq_pair<0x04030402u>(hi, a1, c1);
+    const int t = i >> 1, e = 2 * (i & 1);
+    out[t][e] = static_cast<int>(deq_pair<0x04010400u>(lo, a0, c0));
+    out[t][e + 1] = static_cast<int>(deq_pair<0x04030402u>(lo, a0, c0));
+    out[2 + t][e] = static_cast<int>(deq_pair<0x04010400u>(hi, a1, c1));
+    out[2 + t][e + 1] = static_cast<int>(deq_pair<0x04030402u>(hi, a1, c1));
   }
 }
 
@@ -134,14 +136,14 @@ __global__ __launch_bounds__(256) void dequant_f16_q4k_kernel(const uint8_t* __r
   const uint8_t* b = W + blk * kQ4Bytes;
   const uint4 hdr = *reinterpret_cast<const uint4*>(b);
   const uint4 raw = *reinterpret_cast<const uint4*>(b + 16 + 32 * qt + 16 * h);
-  uint32_t out[16];
+  v4i out[4];
   q4k_quarter_f16(hdr, qt, raw, out);
-  // value index of out pair p: low nibbles 64qt + 16h + 2p, high 64qt + 32 + 16h + 2(p-8)
-  uint32_t* o = reinterpret_cast<uint32_t*>(w16 + blk * 256 + 64 * qt + 16 * h);
-#pragma unroll
-  for (int p = 0; p < 8; p++) o[p] = out[p];
-#pragma unroll
-  for (int p = 0; p < 8; p++) o[16 + p] = out[8 + p];
+  // out[0..1]: values 64qt + 16h + 0..15; out[2..3]: values 64qt + 32 + 16h + 0..15
+  v4i* o = reinterpret_cast<v4i*>(w16 + blk * 256 + 64 * qt + 16 * h);
+  o[0] = out[0];
+  o[1] = out[1];
+  o[4] = out[2];
+  o[5] = out[3];
 }
 
 // Q6_K weights as binary16 for the same hook: dsc = f16(d*sc) (exact product in
@@ -238,12 +240,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int it = 0; it < LPT; it++) {
       const int g = wave + it * NW;
-      if (g < A_WL) {
-        lds_dma16_sv(a_base + s * 128, voff[it], sbase + 1024 * g);
-      } else {
+      auto load_a = [&] { lds_dma16_sv(a_base + s * 128, voff[it], sbase + 1024 * g); };
+      auto load_w = [&] {
         const int wl = (g - A_WL) % W_WLR;
         lds_dma16_sv(w_base + sb * kQ4Bytes, voff[it] + qmul[it] * qt, sbase + A_BYTES + 1024 * wl);
-      }
+      };
+      // once unrolled, whether load `it` is an A or a W load folds to a
+      // constant unless the boundary falls inside this round of NW wave-loads
+      if ((it + 1) * NW <= A_WL || (it * NW < A_WL && g < A_WL)) load_a();
+      else load_w();
     }
   };
 
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
     const uint8_t* sA = lds + buf * STAGE;
     const uint8_t* sW = sA + A_BYTES;
     const int qt = static_cast<int>((st0 + s) & 3);
-    uint32_t bq[TN][16];
+    v4i bq[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int col = nl0 + 32 * j + l32;
@@ -288,8 +293,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
       }
 #pragma unroll
       for (int j = 0; j < TN; j++) {
-        const h8 b = __builtin_bit_cast(
-            h8, v4i{int(bq[j][4 * t]), int(bq[j][4 * t + 1]), int(bq[j][4 * t + 2]), int(bq[j][4 * t + 3])});
+        const h8 b = __builtin_bit_cast(h8, bq[j][t]);
 #pragma unroll
         for (int i = 0; i < TM; i++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
