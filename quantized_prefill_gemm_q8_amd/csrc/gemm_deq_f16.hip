@@ -360,18 +360,21 @@ static void launch_deq(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t
 }  // namespace qg
 
 namespace {
-enum class DeqPick { k256x128, k128x128, k64x128K2, k128x64K4, k32x64K4 };
+enum class DeqPick { k256x256, k256x128, k128x128, k64x128K2, k128x64K4, k32x64K4 };
 
-// Measured on the workloads' Q4_K shapes.  Large grids: 256x128 blocks of 8
-// waves (128x32 each: four row tiles share one dequantised weight fragment)
-// when they cover the CUs, else 128x128 blocks of 4 such waves when there are
-// at least 200.  Smaller grids split K inside the workgroup: 64x128 blocks
+// Measured on the workloads' Q4_K shapes.  Waves of 128x32 (four row tiles
+// share one dequantised weight fragment) in 256x256 blocks of 16 waves (one
+// per CU) when there are at least 160 of those (up to 399, or any number for
+// K >= 4096), 256x128 blocks of 8 waves (two per CU) when they cover the CUs,
+// else 128x128 blocks of 4 when there are at least 200.  Smaller grids split K inside the workgroup: 64x128 blocks
 // with two K-groups, 128x64 blocks with four, or 32x64 blocks with four.  Every
 // split keeps at least one 64-value stage per group (K >= 256).
-DeqPick pick_deq(int64_t M, int64_t N) {
+DeqPick pick_deq(int64_t M, int64_t N, int64_t K) {
+  const int64_t b256w = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t b256 = ((M + 255) / 256) * ((N + 127) / 128);
   const int64_t b128 = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t b64 = ((M + 63) / 64) * ((N + 127) / 128);
+  if (b256w >= 160 && (b256w < 400 || K >= 4096)) return DeqPick::k256x256;
   if (b256 >= 256) return DeqPick::k256x128;
   if (b128 >= 200) return DeqPick::k128x128;
   if (b64 >= 256) return DeqPick::k64x128K2;
@@ -381,8 +384,8 @@ DeqPick pick_deq(int64_t M, int64_t N) {
 }  // namespace
 
 const char* qg_gemm_deq_f16_kernel_name(int64_t M, int64_t N, int64_t K) {
-  (void)K;
-  switch (pick_deq(M, N)) {
+  switch (pick_deq(M, N, K)) {
+    case DeqPick::k256x256: return "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>";
     case DeqPick::k256x128: return "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>";
     case DeqPick::k128x128: return "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4, 1>";
     case DeqPick::k64x128K2: return "gemm_deq_f16_kernel<2, 1, 1, 4, 2, 4, 2>";
@@ -419,7 +422,8 @@ hipError_t qg_launch_dequant_f16(const uint8_t* W, int fmt, int64_t N, int64_t K
 
 hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N,
                                   int64_t K, float* y, hipStream_t stream) {
-  switch (pick_deq(M, N)) {
+  switch (pick_deq(M, N, K)) {
+    case DeqPick::k256x256: qg::launch_deq<4, 1, 2, 8, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
     case DeqPick::k256x128: qg::launch_deq<4, 1, 2, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
     case DeqPick::k128x128: qg::launch_deq<4, 1, 1, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
     case DeqPick::k64x128K2: qg::launch_deq<2, 1, 1, 4, 2, 4, 2>(W, x16, M, N, K, y, stream); break;

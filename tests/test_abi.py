@@ -175,8 +175,11 @@ def test_deq_f16_branch_host_side():
     assert lib.qgemm_dequant_f16(A, 0, 8, 256, A + 2, None) == -5
     kn = qg.qgemm_deq_f16_kernel_name
     assert kn(1, 512, 4096, 1024) is None and kn(0, 512, 4096, 1000) is None
-    assert kn(0, 512, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>"
-    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 512, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>"
+    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>"
+    assert kn(0, 4096, 2560, 9728) == "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>"
+    assert kn(0, 4096, 9728, 2560) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 700, 11000, 512) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>"
     assert kn(0, 512, 7168, 1024) == "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4, 1>"
     # smaller grids split K inside the workgroup
     assert kn(0, 512, 4096, 1024) == "gemm_deq_f16_kernel<2, 1, 1, 4, 2, 4, 2>"

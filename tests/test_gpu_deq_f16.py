@@ -90,11 +90,11 @@ def test_gemm_full_parity(M, N, K):
     check_deq(gpu_deq(W, x, N), W, x, N, K, what=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(700, 11000, 512), (300, 8500, 512), (520, 4000, 768),
-                                   (520, 2560, 1280)])
+@pytest.mark.parametrize("M,N,K", [(1100, 9000, 512), (700, 11000, 512), (300, 8500, 512),
+                                   (520, 4000, 768), (520, 2560, 1280)])
 def test_gemm_large_tiles_sampled(M, N, K):
-    """The 256x128 and 128x128 block kernels and the two-group 64x128 and
-    four-group 128x64 K splits, on ragged shapes (tails in M and N)."""
+    """The 256x256, 256x128 and 128x128 block kernels and the two-group 64x128
+    and four-group 128x64 K splits, on ragged shapes (tails in M and N)."""
     W = synth.pack(qg.QG_Q4_K, synth.normal(690 + M, (N, K), 0.0, 0.02))
     x = synth.to_bf16_bits(synth.normal(691 + N, (M, K)))
     y = gpu_deq(W, x, N)
