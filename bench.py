@@ -23,7 +23,7 @@ projections (K=4096 -> N=24576 Q4_K and K=12288 -> N=4096 Q6_K at M=512), the
 decode-sized GEMV (M = 1 and 8) over every projection shape of the workloads,
 the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K), the other design branch
 (weights dequantised to fp16 in the GEMM, fp16 matrix cores) beside the int8
-method on every Q4_K projection shape, and the CPU oracle timed on the host.
+method on every projection shape, and the CPU oracle timed on the host.
 
 --calib-copy-mib N additionally runs a plain elementwise copy kernel over
 N MiB (read N, write N) three times: the reference dispatch for scaling HBM
@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, vendor figure
 COLD_BYTES = 600 * 1000 ** 2  # weight footprint that defeats the 256 MB MALL (cold-cache GEMV)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workload.json")
 CALIB_KERNEL = "neg_kernel"  # the copy kernel --calib-copy-mib launches
@@ -409,13 +410,11 @@ def main():
     torch.cuda.empty_cache()
 
     # ---------------- the other design branch (dequantise to fp16, float matrix-core
-    # GEMM) beside the int8 method, per Q4_K projection shape: both timed as whole
+    # GEMM) beside the int8 method, per projection shape: both timed as whole
     # calls (int8: quantiser + GEMM; fp16: x -> binary16 + GEMM), back to back
     branch = {}
     for cfg in (2, 3, 4) if args.branch_steps > 0 else ():
         for g in synth.CONFIGS[cfg]:
-            if g.fmt != qg.QG_Q4_K:
-                continue
             Wb = to_dev(synth.make_weights(g))
             xb = to_dev(synth.make_acts(g))
             yb = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
@@ -438,11 +437,12 @@ def main():
                 torch.cuda.synchronize()
                 us[k] = 1e3 * a.elapsed_time(b) / args.branch_steps
             branch[f"c{cfg}_{g.name}"] = {
-                "shape": f"M={g.M} K={g.K} N={g.N} Q4_K",
+                "shape": f"M={g.M} K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'}",
                 "int8_us": round(us["int8"], 2),
                 "int8_tops": round(g.ops / (us["int8"] * 1e-6) / 1e12, 1),
                 "f16_us": round(us["f16"], 2),
                 "f16_tflops": round(g.ops / (us["f16"] * 1e-6) / 1e12, 1),
+                "f16_frac_fp16_peak": round(g.ops / (us["f16"] * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
                 "f16_kernel": qg.qgemm_deq_f16_kernel_name(g.fmt, g.M, g.N, g.K),
                 "f16_over_int8_speed": round(us["int8"] / us["f16"], 3)}
             del Wb, xb, yb, ws8, ws16

@@ -165,9 +165,10 @@ int qgemm_block_partials(const void *q_weights, int fmt, const int8_t *qx, int64
  *   x16 = f16(x)  (x as its fp32 value; bf16 widens exactly)
  *   per sub-block j: dsc = f16(d*sc[j]), dmn = f16(dmin*m[j]); w16 = f16(dsc*q - dmn)
  *   y[m][n] = sum_k x16[m][k] * w16[n][k], accumulated in fp32 on the matrix cores.
+ * For Q6_K: dsc = f16(d*sc[s]) per 16-value sub-block, w16 = f16(dsc*(q6 - 32)).
  * Activations of magnitude 65520 and above become infinite in binary16, and
  * weights whose d*sc or dmin*m reach 65520 are outside the domain (results
- * unspecified).  Q4_K only (QG_EFMT otherwise). */
+ * unspecified). */
 
 /* Workspace bytes for qgemm_prefill_deq_f16: the binary16 copy of x (M*K*2,
  * rounded up to 256).  0 when M < 1, K < 256, K % 256 != 0 or on overflow. */
@@ -188,8 +189,7 @@ const char *qgemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 /* Test hooks of this branch.  qgemm_to_f16: x [M][K] -> binary16 bits x16 [M][K]
  * (K % 8 == 0; x and x16 16-byte aligned).  qgemm_dequant_f16: every weight of
  * W [N][K] as binary16 bits w16 [N][K] (16-byte aligned), through the GEMM's own
- * decoder for Q4_K; for Q6_K: dsc = f16(d*sc[s]), w16 = f16(dsc*(q6 - 32)).
- * A zero weight may be returned as -0. */
+ * decoders.  A zero weight may be returned as -0. */
 int qgemm_to_f16(const void *x, int x_dtype, int64_t M, int64_t K, uint16_t *x16, void *stream);
 int qgemm_dequant_f16(const void *q_weights, int fmt, int64_t N, int64_t K, uint16_t *w16,
                       void *stream);

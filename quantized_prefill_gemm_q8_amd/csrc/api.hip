@@ -264,7 +264,6 @@ int qgemm_prefill_deq_f16(const void* q_weights, int fmt, const void* x, int x_d
                           void* stream) {
   int rc = check_common(q_weights, fmt, N, K);
   if (rc) return rc;
-  if (fmt != QG_Q4_K) return QG_EFMT;
   if (!x || !y || M < 1) return QG_EINVAL;
   if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
   const size_t need = qgemm_deq_f16_workspace_bytes(M, K);
@@ -277,12 +276,13 @@ int qgemm_prefill_deq_f16(const void* q_weights, int fmt, const void* x, int x_d
   uint16_t* x16 = static_cast<uint16_t*>(workspace);
   rc = launch_status(qg_launch_to_f16(x, x_dtype, M, K, x16, s));
   if (rc) return rc;
-  return launch_status(qg_launch_gemm_deq_f16(static_cast<const uint8_t*>(q_weights), x16, M, N, K, y, s));
+  return launch_status(qg_launch_gemm_deq_f16(static_cast<const uint8_t*>(q_weights), fmt, x16, M, N, K,
+                                              y, s));
 }
 
 const char* qgemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
-  if (fmt != QG_Q4_K || M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
-  return qg_gemm_deq_f16_kernel_name(M, N, K);
+  if ((fmt != QG_Q4_K && fmt != QG_Q6_K) || M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
+  return qg_gemm_deq_f16_kernel_name(fmt, M, N, K);
 }
 
 }  // extern "C"

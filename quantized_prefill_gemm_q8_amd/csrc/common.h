@@ -134,8 +134,8 @@ hipError_t qg_launch_to_f16(const void* x, int x_dtype, int64_t M, int64_t K, ui
                             hipStream_t stream);
 hipError_t qg_launch_dequant_f16(const uint8_t* W, int fmt, int64_t N, int64_t K, uint16_t* w16,
                                  hipStream_t stream);
-hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N,
-                                  int64_t K, float* y, hipStream_t stream);
-const char* qg_gemm_deq_f16_kernel_name(int64_t M, int64_t N, int64_t K);
+hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, int fmt, const uint16_t* x16, int64_t M,
+                                  int64_t N, int64_t K, float* y, hipStream_t stream);
+const char* qg_gemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t qg_launch_block_partials(const uint8_t* W, int fmt, const int8_t* qx, int64_t M,
                                     int64_t N, int64_t K, int32_t* out, hipStream_t stream);

@@ -146,24 +146,68 @@ __global__ __launch_bounds__(256) void dequant_f16_q4k_kernel(const uint8_t* __r
   o[5] = out[3];
 }
 
-// Q6_K weights as binary16 for the same hook: dsc = f16(d*sc) (exact product in
-// fp32: binary16 times an int8), w16 = f16(dsc*(q6 - 32)) (one rounding).
+// Q6_K: the 32 binary16 weights that lane half h takes from quarter qq of a
+// super-block (values 64qq + 16t + 8h + 0..7 for K-steps t = 0..3: each
+// K-step inside one 16-value sub-block, so one scale per step).  Value v of
+// the quarter (l = v % 32) has its low 4 bits in ql[64(qq/2) + 32(v/32) + l]
+// (the low nibble for even qq, the high one for odd) and its top 2 bits in
+// qh[32(qq/2) + l], bits 4(qq%2) + 2(v/32) and up.  The lane passes its eight
+// ql bytes of each K-step (ql[t]: bytes 16(t%2) + 8h + 0..7 of the 32 at
+// offset 32(t/2)) and its qh bytes (qh[t%2]: bytes 16(t%2) + 8h + 0..7),
+// the quarter's four int8 scales and d:  dsc = f16(d*sc), w16 = f16(dsc*(q6-32))
+// (one rounding each: d*sc is exact in fp32, q6-32 in fp16).  0x64qq is the
+// binary16 1024 + q6, so subtracting 1056 leaves q6 - 32 exactly.
+__device__ __forceinline__ void q6k_quarter_f16(const uint2 (&ql)[4], const uint2 (&qh)[2],
+                                                uint32_t sc4, uint32_t d_bits, int qq,
+                                                v4i (&out)[4]) {
+  const float d = half_to_float(d_bits);
+  const uint32_t s_lo = 4u * static_cast<uint32_t>(qq & 1);
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const float scf = static_cast<float>(static_cast<int8_t>((sc4 >> (8 * t)) & 0xFFu));
+    const _Float16 dsc = static_cast<_Float16>(d * scf);
+    const h2 a = {dsc, dsc};
+    const uint32_t s_hi = s_lo + 2u * static_cast<uint32_t>(t >> 1);
+    const uint32_t lw[2] = {ql[t].x, ql[t].y}, hw[2] = {qh[t & 1].x, qh[t & 1].y};
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const uint32_t q6 = (((hw[k] >> s_hi) & 0x03030303u) << 4) | ((lw[k] >> s_lo) & 0x0F0F0F0Fu);
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        const uint32_t pb = __builtin_amdgcn_perm(0x64646464u, q6, e ? 0x04030402u : 0x04010400u);
+        const h2 q = __builtin_bit_cast(h2, pb) +
+                     h2{static_cast<_Float16>(-1056.0f), static_cast<_Float16>(-1056.0f)};
+        out[t][2 * k + e] = static_cast<int>(__builtin_bit_cast(uint32_t, q * a));
+      }
+    }
+  }
+}
+
+// Test hook for Q6_K: every weight as binary16 bits through q6k_quarter_f16.
+// One thread per (block, quarter, half).
 __global__ __launch_bounds__(256) void dequant_f16_q6k_kernel(const uint8_t* __restrict__ W,
-                                                              int64_t total,
+                                                              int64_t nthreads,
                                                               uint16_t* __restrict__ w16) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int64_t blkno = i >> 8;
-  const int v = static_cast<int>(i & 255);
-  const uint8_t* blk = W + blkno * kQ6Bytes;
-  const int half = v >> 7, r = v & 127, c = r >> 5, l = r & 31;
-  const uint8_t lb = blk[64 * half + 32 * (c & 1) + l];
-  const int lo = c < 2 ? (lb & 15) : (lb >> 4);
-  const int hi = (blk[128 + 32 * half + l] >> (2 * c)) & 3;
-  const float d = half_to_float(load_u16(blk + 208));
-  const _Float16 dsc = static_cast<_Float16>(d * static_cast<float>(static_cast<int8_t>(blk[192 + (v >> 4)])));
-  const _Float16 w = dsc * static_cast<_Float16>(static_cast<float>((lo | (hi << 4)) - 32));
-  w16[i] = __builtin_bit_cast(uint16_t, w);
+  if (i >= nthreads) return;
+  const int64_t blk = i >> 3;
+  const int qq = static_cast<int>((i >> 1) & 3), h = static_cast<int>(i & 1);
+  const uint8_t* b = W + blk * kQ6Bytes;
+  const uint8_t* qlp = b + 64 * (qq >> 1);
+  const uint8_t* qhp = b + 128 + 32 * (qq >> 1);
+  uint2 ql[4], qh[2];
+#pragma unroll
+  for (int t = 0; t < 4; t++)
+    ql[t] = make_uint2(load_u32_a2(qlp + 32 * (t >> 1) + 16 * (t & 1) + 8 * h),
+                       load_u32_a2(qlp + 32 * (t >> 1) + 16 * (t & 1) + 8 * h + 4));
+#pragma unroll
+  for (int k = 0; k < 2; k++)
+    qh[k] = make_uint2(load_u32_a2(qhp + 16 * k + 8 * h), load_u32_a2(qhp + 16 * k + 8 * h + 4));
+  v4i out[4];
+  q6k_quarter_f16(ql, qh, load_u32_a2(b + 192 + 4 * qq), load_u16(b + 208), qq, out);
+  v4i* o = reinterpret_cast<v4i*>(w16 + blk * 256 + 64 * qq + 8 * h);
+#pragma unroll
+  for (int t = 0; t < 4; t++) o[2 * t] = out[t];   // values 64qq + 16t + 8h + 0..7
 }
 
 // ---------------------------------------------------------------- the GEMM
@@ -171,14 +215,21 @@ __global__ __launch_bounds__(256) void dequant_f16_q6k_kernel(const uint8_t* __r
 // KS > 1: KS groups of WM x WN waves compute the same block over disjoint
 // ranges of stages, each with its own ring; the partial blocks are summed
 // through LDS in group order at the end (deterministic, no atomics).
-template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+// FMT: QG_Q4_K or QG_Q6_K.  Per column and stage the W region holds, piece-
+// major (16 B per piece): Q4_K -- the block header and the quarter's 32 code
+// bytes (3 pieces); Q6_K -- the 64 ql bytes and 32 qh bytes of the quarter's
+// half super-block, the 16 scales and the block's last 16 bytes (holding d)
+// (8 pieces).
+template <int FMT, int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
 __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_deq_f16_kernel(
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ x16, int64_t M, int64_t N, int64_t K,
     float* __restrict__ y) {
   constexpr int NW = WM * WN;
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   constexpr int A_WL = BM * 8 / 64;                    // wave-loads of A per stage (whole)
-  constexpr int W_CH = 3 * BN, W_WLR = (W_CH + 63) / 64;  // W chunks, real wave-loads
+  constexpr bool Q6 = FMT == QG_Q6_K;
+  constexpr int PIECES = Q6 ? 8 : 3, BLK = Q6 ? kQ6Bytes : kQ4Bytes;
+  constexpr int W_CH = PIECES * BN, W_WLR = (W_CH + 63) / 64;  // W chunks, real wave-loads
   // W padded so that every wave issues the same number of loads per stage
   constexpr int TOT = ((A_WL + W_WLR + NW - 1) / NW) * NW, W_WL = TOT - A_WL;
   constexpr int LPT = TOT / NW;                        // loads per thread per stage
@@ -200,7 +251,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * BN;
   const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
   const int64_t nsb = K / 256, nst = K / 64;
-  const int64_t wrow = nsb * kQ4Bytes;
+  const int64_t wrow = nsb * BLK;
   // this group's stages: st0 .. st0 + cnt - 1 (the launcher keeps KS <= K/64);
   // every group runs the longest group's count so that the barriers match
   const int64_t st0 = grp * nst / KS, cnt = (grp + 1) * nst / KS - st0;
@@ -211,7 +262,10 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   // g = wave + it*NW of the combined list: A wave-loads first, then the W ones
   // (taken modulo the real count, so the padding repeats real wave-loads).
   uint32_t voff[LPT];
-  uint32_t qmul[LPT];  // 32 for the code pieces of W (advance with the quarter), else 0
+  // the W pieces that move within a block with the stage: Q4_K code pieces by
+  // 32 bytes per quarter; Q6_K ql pieces by 64 and qh pieces by 32 bytes per
+  // half super-block; 0 for the rest
+  uint32_t qmul[LPT];
 #pragma unroll
   for (int it = 0; it < LPT; it++) {
     const int g = wave + it * NW;
@@ -225,8 +279,17 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
       const int piece = p / BN, col = p - piece * BN;
       const int64_t n = n_cta + col < N ? n_cta + col : N - 1;
       const bool real = p < W_CH;
-      voff[it] = real ? static_cast<uint32_t>((n - n_cta) * wrow + (piece == 0 ? 0 : 16 * piece)) : 0u;
-      qmul[it] = real && piece > 0 ? 32u : 0u;
+      uint32_t off, mul;
+      if (Q6) {
+        // pieces: ql 0..3 (bytes 16p), qh 4..5 (128 + 16(p-4)), scales (192), tail (194)
+        off = piece < 4 ? 16u * piece : piece < 6 ? 128u + 16u * (piece - 4) : piece == 6 ? 192u : 194u;
+        mul = piece < 4 ? 64u : piece < 6 ? 32u : 0u;
+      } else {
+        off = piece == 0 ? 0u : 16u * piece;
+        mul = piece > 0 ? 32u : 0u;
+      }
+      voff[it] = real ? static_cast<uint32_t>((n - n_cta) * wrow) + off : 0u;
+      qmul[it] = real ? mul : 0u;
     }
   }
   const uint8_t* const a_base = reinterpret_cast<const uint8_t*>(x16) + m_cta * K * 2;
@@ -235,7 +298,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   auto issue_stage = [&](int64_t sl, int buf) {
     const int64_t s = st0 + (sl < cnt ? sl : cnt - 1);  // past the group's range: reload its last
     const int64_t sb = s >> 2;
-    const uint32_t qt = static_cast<uint32_t>(s & 3);
+    // the stage's step inside its block: Q4_K the quarter, Q6_K the half
+    const uint32_t qt = Q6 ? static_cast<uint32_t>((s & 3) >> 1) : static_cast<uint32_t>(s & 3);
     uint8_t* sbase = lds + buf * STAGE;
 #pragma unroll
     for (int it = 0; it < LPT; it++) {
@@ -243,7 +307,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
       auto load_a = [&] { lds_dma16_sv(a_base + s * 128, voff[it], sbase + 1024 * g); };
       auto load_w = [&] {
         const int wl = (g - A_WL) % W_WLR;
-        lds_dma16_sv(w_base + sb * kQ4Bytes, voff[it] + qmul[it] * qt, sbase + A_BYTES + 1024 * wl);
+        lds_dma16_sv(w_base + sb * BLK, voff[it] + qmul[it] * qt, sbase + A_BYTES + 1024 * wl);
       };
       // once unrolled, whether load `it` is an A or a W load folds to a
       // constant unless the boundary falls inside this round of NW wave-loads
@@ -278,13 +342,26 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int col = nl0 + 32 * j + l32;
-      const uint4 hdr = *reinterpret_cast<const uint4*>(sW + 16 * col);
-      const uint4 raw = *reinterpret_cast<const uint4*>(sW + 16 * ((1 + h) * BN + col));
-      q4k_quarter_f16(hdr, qt, raw, bq[j]);
+      if constexpr (Q6) {
+        uint2 ql[4], qh[2];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+          ql[t] = *reinterpret_cast<const uint2*>(sW + 16 * ((2 * (t >> 1) + (t & 1)) * BN + col) + 8 * h);
+#pragma unroll
+        for (int k = 0; k < 2; k++) qh[k] = *reinterpret_cast<const uint2*>(sW + 16 * ((4 + k) * BN + col) + 8 * h);
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(sW + 16 * (6 * BN + col) + 4 * qt);
+        const uint32_t dw = *reinterpret_cast<const uint32_t*>(sW + 16 * (7 * BN + col) + 12);
+        q6k_quarter_f16(ql, qh, sc4, dw >> 16, qt, bq[j]);
+      } else {
+        const uint4 hdr = *reinterpret_cast<const uint4*>(sW + 16 * col);
+        const uint4 raw = *reinterpret_cast<const uint4*>(sW + 16 * ((1 + h) * BN + col));
+        q4k_quarter_f16(hdr, qt, raw, bq[j]);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-      const int c = 2 * h + (t & 1) + 4 * (t >> 1);
+      // the activation chunk holding the K-step's eight values for this lane half
+      const int c = Q6 ? 2 * t + h : 2 * h + (t & 1) + 4 * (t >> 1);
       h8 a[TM];
 #pragma unroll
       for (int i = 0; i < TM; i++) {
@@ -348,28 +425,29 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   }
 }
 
-template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS = 1>
+template <int FMT, int TM, int TN, int WM, int WN, int NS, int OCC, int KS = 1>
 static void launch_deq(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N, int64_t K,
                        float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_deq_f16_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
+  gemm_deq_f16_kernel<FMT, TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
       W, x16, M, N, K, y);
 }
 
 }  // namespace qg
 
 namespace {
-enum class DeqPick { k256x256, k256x128, k128x128, k64x128K2, k128x64K4, k32x64K4 };
+enum class DeqPick { k256x256, k256x128, k128x128, k64x128K2, k128x64K4, k128x64K3, k32x64K4 };
 
-// Measured on the workloads' Q4_K shapes.  Waves of 128x32 (four row tiles
-// share one dequantised weight fragment) in 256x256 blocks of 16 waves (one
-// per CU) when there are at least 160 of those (up to 399, or any number for
+// Measured on the workloads' shapes.  Waves of 128x32 (four row tiles share
+// one dequantised weight fragment) in 256x256 blocks of 16 waves (one per CU)
+// when there are at least 160 of those (up to 399, or any number for
 // K >= 4096), 256x128 blocks of 8 waves (two per CU) when they cover the CUs,
-// else 128x128 blocks of 4 when there are at least 200.  Smaller grids split K inside the workgroup: 64x128 blocks
-// with two K-groups, 128x64 blocks with four, or 32x64 blocks with four.  Every
-// split keeps at least one 64-value stage per group (K >= 256).
-DeqPick pick_deq(int64_t M, int64_t N, int64_t K) {
+// else 128x128 blocks of 4 when there are at least 200.  Smaller grids split K
+// inside the workgroup: Q4_K 64x128 blocks with two K-groups, 128x64 with four
+// or 32x64 with four; Q6_K 128x64 with three or 32x64 with four.  Every split
+// keeps at least one 64-value stage per group (K >= 256).
+DeqPick pick_deq(int fmt, int64_t M, int64_t N, int64_t K) {
   const int64_t b256w = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t b256 = ((M + 255) / 256) * ((N + 127) / 128);
   const int64_t b128 = ((M + 127) / 128) * ((N + 127) / 128);
@@ -377,20 +455,25 @@ DeqPick pick_deq(int64_t M, int64_t N, int64_t K) {
   if (b256w >= 160 && (b256w < 400 || K >= 4096)) return DeqPick::k256x256;
   if (b256 >= 256) return DeqPick::k256x128;
   if (b128 >= 200) return DeqPick::k128x128;
+  // Q6_K (eight weight pieces per column): 128x64 blocks with three K-groups
+  // from 128 such 64x128 blocks on (four two-stage rings would not fit LDS)
+  if (fmt == QG_Q6_K) return b64 >= 128 ? DeqPick::k128x64K3 : DeqPick::k32x64K4;
   if (b64 >= 256) return DeqPick::k64x128K2;
   if (b64 >= 128) return DeqPick::k128x64K4;
   return DeqPick::k32x64K4;
 }
 }  // namespace
 
-const char* qg_gemm_deq_f16_kernel_name(int64_t M, int64_t N, int64_t K) {
-  switch (pick_deq(M, N, K)) {
-    case DeqPick::k256x256: return "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>";
-    case DeqPick::k256x128: return "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>";
-    case DeqPick::k128x128: return "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4, 1>";
-    case DeqPick::k64x128K2: return "gemm_deq_f16_kernel<2, 1, 1, 4, 2, 4, 2>";
-    case DeqPick::k128x64K4: return "gemm_deq_f16_kernel<4, 1, 1, 2, 2, 2, 4>";
-    case DeqPick::k32x64K4: return "gemm_deq_f16_kernel<1, 1, 1, 2, 2, 4, 4>";
+const char* qg_gemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
+  const bool q6 = fmt == QG_Q6_K;
+  switch (pick_deq(fmt, M, N, K)) {
+    case DeqPick::k256x256: return q6 ? "gemm_deq_f16_kernel<1, 4, 1, 2, 8, 2, 4, 1>" : "gemm_deq_f16_kernel<0, 4, 1, 2, 8, 2, 4, 1>";
+    case DeqPick::k256x128: return q6 ? "gemm_deq_f16_kernel<1, 4, 1, 2, 4, 2, 4, 1>" : "gemm_deq_f16_kernel<0, 4, 1, 2, 4, 2, 4, 1>";
+    case DeqPick::k128x128: return q6 ? "gemm_deq_f16_kernel<1, 4, 1, 1, 4, 2, 4, 1>" : "gemm_deq_f16_kernel<0, 4, 1, 1, 4, 2, 4, 1>";
+    case DeqPick::k64x128K2: return q6 ? "gemm_deq_f16_kernel<1, 2, 1, 1, 4, 2, 4, 2>" : "gemm_deq_f16_kernel<0, 2, 1, 1, 4, 2, 4, 2>";
+    case DeqPick::k128x64K4: return "gemm_deq_f16_kernel<0, 4, 1, 1, 2, 2, 2, 4>";
+    case DeqPick::k128x64K3: return "gemm_deq_f16_kernel<1, 4, 1, 1, 2, 2, 2, 3>";
+    case DeqPick::k32x64K4: return q6 ? "gemm_deq_f16_kernel<1, 1, 1, 1, 2, 2, 4, 4>" : "gemm_deq_f16_kernel<0, 1, 1, 1, 2, 2, 4, 4>";
   }
   return "?";
 }
@@ -413,22 +496,35 @@ hipError_t qg_launch_dequant_f16(const uint8_t* W, int fmt, int64_t N, int64_t K
     qg::dequant_f16_q4k_kernel<<<dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0,
                                  stream>>>(W, nthreads, w16);
   } else {
-    const int64_t total = N * K;
-    qg::dequant_f16_q6k_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
-                                 stream>>>(W, total, w16);
+    const int64_t nthreads = N * (K / 256) * 8;
+    qg::dequant_f16_q6k_kernel<<<dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0,
+                                 stream>>>(W, nthreads, w16);
   }
   return hipGetLastError();
 }
 
-hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N,
-                                  int64_t K, float* y, hipStream_t stream) {
-  switch (pick_deq(M, N, K)) {
-    case DeqPick::k256x256: qg::launch_deq<4, 1, 2, 8, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k256x128: qg::launch_deq<4, 1, 2, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k128x128: qg::launch_deq<4, 1, 1, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k64x128K2: qg::launch_deq<2, 1, 1, 4, 2, 4, 2>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k128x64K4: qg::launch_deq<4, 1, 1, 2, 2, 2, 4>(W, x16, M, N, K, y, stream); break;
-    case DeqPick::k32x64K4: qg::launch_deq<1, 1, 1, 2, 2, 4, 4>(W, x16, M, N, K, y, stream); break;
+template <int FMT>
+static void launch_deq_fmt(DeqPick pick, const uint8_t* W, const uint16_t* x16, int64_t M, int64_t N,
+                           int64_t K, float* y, hipStream_t stream) {
+  switch (pick) {
+    case DeqPick::k256x256: qg::launch_deq<FMT, 4, 1, 2, 8, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k256x128: qg::launch_deq<FMT, 4, 1, 2, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k128x128: qg::launch_deq<FMT, 4, 1, 1, 4, 2, 4, 1>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k64x128K2: qg::launch_deq<FMT, 2, 1, 1, 4, 2, 4, 2>(W, x16, M, N, K, y, stream); break;
+    case DeqPick::k128x64K4:
+      if constexpr (FMT == QG_Q4_K) qg::launch_deq<FMT, 4, 1, 1, 2, 2, 2, 4>(W, x16, M, N, K, y, stream);
+      break;
+    case DeqPick::k128x64K3:
+      if constexpr (FMT == QG_Q6_K) qg::launch_deq<FMT, 4, 1, 1, 2, 2, 2, 3>(W, x16, M, N, K, y, stream);
+      break;
+    case DeqPick::k32x64K4: qg::launch_deq<FMT, 1, 1, 1, 2, 2, 4, 4>(W, x16, M, N, K, y, stream); break;
   }
+}
+
+hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, int fmt, const uint16_t* x16, int64_t M, int64_t N,
+                                  int64_t K, float* y, hipStream_t stream) {
+  const DeqPick pick = pick_deq(fmt, M, N, K);
+  if (fmt == QG_Q6_K) launch_deq_fmt<QG_Q6_K>(pick, W, x16, M, N, K, y, stream);
+  else launch_deq_fmt<QG_Q4_K>(pick, W, x16, M, N, K, y, stream);
   return hipGetLastError();
 }

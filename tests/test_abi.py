@@ -163,7 +163,7 @@ def test_deq_f16_branch_host_side():
         k.get("w", A), k.get("fmt", 0), k.get("x", A), k.get("xdt", 1), k.get("M", 4),
         k.get("N", 8), k.get("K", 256), k.get("y", A), k.get("ws", A), k.get("wsb", wsb), None)
     assert call(w=None) == -1 and call(M=0) == -1 and call(K=300) == -1
-    assert call(fmt=1) == -2 and call(fmt=5) == -2          # Q4_K only
+    assert call(fmt=2) == -2 and call(fmt=5) == -2
     assert call(xdt=3) == -3
     assert call(ws=None) == -4 and call(wsb=wsb - 1) == -4 and call(ws=A + 64) == -4
     assert call(x=A + 2) == -5 and call(y=A + 4) == -5 and call(w=A + 8) == -5
@@ -174,15 +174,20 @@ def test_deq_f16_branch_host_side():
     assert lib.qgemm_dequant_f16(A, 2, 8, 256, A, None) == -2
     assert lib.qgemm_dequant_f16(A, 0, 8, 256, A + 2, None) == -5
     kn = qg.qgemm_deq_f16_kernel_name
-    assert kn(1, 512, 4096, 1024) is None and kn(0, 512, 4096, 1000) is None
-    assert kn(0, 512, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>"
-    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>"
-    assert kn(0, 4096, 2560, 9728) == "gemm_deq_f16_kernel<4, 1, 2, 8, 2, 4, 1>"
-    assert kn(0, 4096, 9728, 2560) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>"
-    assert kn(0, 700, 11000, 512) == "gemm_deq_f16_kernel<4, 1, 2, 4, 2, 4, 1>"
-    assert kn(0, 512, 7168, 1024) == "gemm_deq_f16_kernel<4, 1, 1, 4, 2, 4, 1>"
+    assert kn(2, 512, 4096, 1024) is None and kn(0, 512, 4096, 1000) is None
+    assert kn(0, 512, 24576, 4096) == "gemm_deq_f16_kernel<0, 4, 1, 2, 8, 2, 4, 1>"
+    assert kn(0, 2048, 24576, 4096) == "gemm_deq_f16_kernel<0, 4, 1, 2, 8, 2, 4, 1>"
+    assert kn(0, 4096, 2560, 9728) == "gemm_deq_f16_kernel<0, 4, 1, 2, 8, 2, 4, 1>"
+    assert kn(0, 4096, 9728, 2560) == "gemm_deq_f16_kernel<0, 4, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 700, 11000, 512) == "gemm_deq_f16_kernel<0, 4, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 512, 7168, 1024) == "gemm_deq_f16_kernel<0, 4, 1, 1, 4, 2, 4, 1>"
     # smaller grids split K inside the workgroup
-    assert kn(0, 512, 4096, 1024) == "gemm_deq_f16_kernel<2, 1, 1, 4, 2, 4, 2>"
-    assert kn(0, 512, 2560, 9728) == "gemm_deq_f16_kernel<4, 1, 1, 2, 2, 2, 4>"
-    assert kn(0, 512, 1024, 3584) == "gemm_deq_f16_kernel<1, 1, 1, 2, 2, 4, 4>"
-    assert kn(0, 1, 77, 256) == "gemm_deq_f16_kernel<1, 1, 1, 2, 2, 4, 4>"
+    assert kn(0, 512, 4096, 1024) == "gemm_deq_f16_kernel<0, 2, 1, 1, 4, 2, 4, 2>"
+    assert kn(0, 512, 2560, 9728) == "gemm_deq_f16_kernel<0, 4, 1, 1, 2, 2, 2, 4>"
+    assert kn(0, 512, 1024, 3584) == "gemm_deq_f16_kernel<0, 1, 1, 1, 2, 2, 4, 4>"
+    assert kn(0, 1, 77, 256) == "gemm_deq_f16_kernel<0, 1, 1, 1, 2, 2, 4, 4>"
+    # Q6_K: the same large blocks; small grids take 128x64 blocks with three K-groups
+    assert kn(1, 512, 4096, 12288) == "gemm_deq_f16_kernel<1, 4, 1, 1, 2, 2, 2, 3>"
+    assert kn(1, 512, 2560, 4096) == "gemm_deq_f16_kernel<1, 4, 1, 1, 2, 2, 2, 3>"
+    assert kn(1, 64, 1024, 1024) == "gemm_deq_f16_kernel<1, 1, 1, 1, 2, 2, 4, 4>"
+    assert kn(1, 8192, 4096, 12288) == "gemm_deq_f16_kernel<1, 4, 1, 2, 8, 2, 4, 1>"

@@ -36,17 +36,17 @@ def gamma(K: int) -> float:
     return K * u / (1 - K * u)
 
 
-def gpu_deq(W: np.ndarray, x: np.ndarray, N: int) -> np.ndarray:
+def gpu_deq(W: np.ndarray, x: np.ndarray, N: int, fmt: int = qg.QG_Q4_K) -> np.ndarray:
     M, K = x.shape
     ws = torch.empty(qg.qgemm_deq_f16_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)
-    qg.qgemm_prefill_deq_f16(to_dev(W), qg.QG_Q4_K, to_dev(x), M, N, K, y, ws)
+    qg.qgemm_prefill_deq_f16(to_dev(W), fmt, to_dev(x), M, N, K, y, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
-def check_deq(y: np.ndarray, W, x, N, K, rows=None, cols=None, what=""):
-    ref, refabs = oracle.gemm_deq_f16(oracle.Q4_K, W, x, N, rows=rows, cols=cols)
+def check_deq(y: np.ndarray, W, x, N, K, rows=None, cols=None, what="", fmt=qg.QG_Q4_K):
+    ref, refabs = oracle.gemm_deq_f16(fmt, W, x, N, rows=rows, cols=cols)
     sub = y if rows is None else y[np.ix_(rows, cols)]
     err = np.abs(sub.astype(np.float64) - ref)
     tol = gamma(K) * refabs
@@ -82,59 +82,68 @@ def test_dequant_f16_bitexact(fmt):
         assert np.array_equal(_plus_zero(got), _plus_zero(oracle.dequant_f16(fmt, W, N, K)))
 
 
+FMTS = [qg.QG_Q4_K, qg.QG_Q6_K]
+FID = ["q4k", "q6k"]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID)
 @pytest.mark.parametrize("M,N,K", [(64, 1024, 1024), (200, 300, 512), (130, 260, 768), (1, 77, 256),
                                    (129, 129, 256), (600, 500, 2560)])
-def test_gemm_full_parity(M, N, K):
-    W = synth.pack(qg.QG_Q4_K, synth.normal(640 + M, (N, K), 0.0, 0.02))
+def test_gemm_full_parity(M, N, K, fmt):
+    W = synth.pack(fmt, synth.normal(640 + M, (N, K), 0.0, 0.02))
     x = synth.to_bf16_bits(synth.normal(650 + N, (M, K)))
-    check_deq(gpu_deq(W, x, N), W, x, N, K, what=f"{M}x{N}x{K}")
+    check_deq(gpu_deq(W, x, N, fmt), W, x, N, K, what=f"{M}x{N}x{K}", fmt=fmt)
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FID)
 @pytest.mark.parametrize("M,N,K", [(1100, 9000, 512), (700, 11000, 512), (300, 8500, 512),
-                                   (520, 4000, 768), (520, 2560, 1280)])
-def test_gemm_large_tiles_sampled(M, N, K):
+                                   (520, 4000, 768), (520, 2560, 1280), (500, 2000, 768)])
+def test_gemm_large_tiles_sampled(M, N, K, fmt):
     """The 256x256, 256x128 and 128x128 block kernels and the two-group 64x128
-    and four-group 128x64 K splits, on ragged shapes (tails in M and N)."""
-    W = synth.pack(qg.QG_Q4_K, synth.normal(690 + M, (N, K), 0.0, 0.02))
+    and four-group 128x64 (Q4_K) K splits, on ragged shapes (tails in M and N)."""
+    W = synth.pack(fmt, synth.normal(690 + M, (N, K), 0.0, 0.02))
     x = synth.to_bf16_bits(synth.normal(691 + N, (M, K)))
-    y = gpu_deq(W, x, N)
+    y = gpu_deq(W, x, N, fmt)
     rng = np.random.default_rng(M)
     rows = np.unique(np.concatenate([[0, M - 1], np.arange(M - 40, M), rng.integers(0, M, 24)]))
     cols = np.unique(np.concatenate([[0, N - 1], np.arange(N - 70, N), rng.integers(0, N, 40)]))
-    check_deq(y, W, x, N, K, rows=rows, cols=cols, what=f"{M}x{N}x{K}")
+    check_deq(y, W, x, N, K, rows=rows, cols=cols, what=f"{M}x{N}x{K}", fmt=fmt)
 
 
-def test_gemm_f32_input_and_wide_scales():
+@pytest.mark.parametrize("fmt", FMTS, ids=FID)
+def test_gemm_f32_input_and_wide_scales(fmt):
     M, N, K = 96, 160, 1024
-    W = synth.random_blocks(qg.QG_Q4_K, N, K, seed=660, emin=5, emax=18)
+    W = synth.random_blocks(fmt, N, K, seed=660 + fmt, emin=5, emax=18)
     x = synth.normal(661, (M, K)) * np.float32(3.0)
-    check_deq(gpu_deq(W, x, N), W, x, N, K, what="f32 input, random blocks")
+    check_deq(gpu_deq(W, x, N, fmt), W, x, N, K, what="f32 input, random blocks", fmt=fmt)
 
 
-def test_gemm_textbook_exact():
+@pytest.mark.parametrize("fmt", FMTS, ids=FID)
+def test_gemm_textbook_exact(fmt):
     M, N, K = 70, 130, 512
-    W, wv = pins._textbook_blocks(qg.QG_Q4_K, N, K, seed=670)
+    W, wv = pins._textbook_blocks(fmt, N, K, seed=670 + fmt)
     xi = pins._integer_acts(M, K, seed=671)
-    y = gpu_deq(W, xi.astype(np.float32), N)
+    y = gpu_deq(W, xi.astype(np.float32), N, fmt)
     assert np.array_equal(y.astype(np.float64), (xi @ wv.T).astype(np.float64))
 
 
 @pytest.mark.parametrize("cfg,name", [(2, "qkv_gate"), (2, "up_gate"), (2, "down"),
-                                      (3, "gate_up_M512"), (3, "down_M512"), (4, "gate_up_M512")])
+                                      (3, "gate_up_M512"), (3, "down_M512"), (3, "attn_out_M512"),
+                                      (4, "gate_up_M512"), (4, "down_M512")])
 def test_gemm_workload_sampled(cfg, name):
     g = next(g for g in synth.CONFIGS[cfg] if g.name == name)
     W, x = synth.make_weights(g), synth.make_acts(g)
-    y = gpu_deq(W, x, g.N)
+    y = gpu_deq(W, x, g.N, g.fmt)
     rng = np.random.default_rng(680 + cfg)
     rows = np.unique(np.concatenate([[0, g.M - 1], rng.integers(0, g.M, 14)]))
     cols = np.unique(np.concatenate([[0, g.N - 1], rng.integers(0, g.N, 30)]))
-    check_deq(y, W, x, g.N, g.K, rows=rows, cols=cols, what=f"c{cfg} {name}")
+    check_deq(y, W, x, g.N, g.K, rows=rows, cols=cols, what=f"c{cfg} {name}", fmt=g.fmt)
 
 
-def test_rejects_q6k():
+def test_rejects_unknown_format():
     W = torch.zeros(210 * 4, dtype=torch.uint8, device=DEV)
     x = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
     y = torch.empty((2, 4), dtype=torch.float32, device=DEV)
     ws = torch.empty(qg.qgemm_deq_f16_workspace_bytes(2, 256), dtype=torch.uint8, device=DEV)
     with pytest.raises(qg.QgemmError):
-        qg.qgemm_prefill_deq_f16(W, qg.QG_Q6_K, x, 2, 4, 256, y, ws)
+        qg.qgemm_prefill_deq_f16(W, 2, x, 2, 4, 256, y, ws)
