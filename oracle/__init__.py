@@ -64,6 +64,10 @@ def _bind(path: str):
     lib.oracle_dequant_f16.restype = None
     lib.oracle_gemm_deq_f16.argtypes = [ci, vp, vp, ci, i64, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.oracle_gemm_deq_f16.restype = ci
+    lib.oracle_quantize_act256.argtypes = [vp, ci, i64, i64, vp, vp, vp]
+    lib.oracle_quantize_act256.restype = None
+    lib.oracle_gemm_a256.argtypes = [vp, vp, ci, i64, i64, i64, vp, i64, vp, i64, vp]
+    lib.oracle_gemm_a256.restype = ci
     return lib
 
 
@@ -221,6 +225,40 @@ def gemm_deq_f16(fmt: int, W: np.ndarray, x: np.ndarray, N: int, rows=None, cols
     if rc != 0:
         raise MemoryError("oracle_gemm_deq_f16: allocation failed")
     return y, ya
+
+
+def quantize_act256(x: np.ndarray):
+    """Per-256 activation blocks: x [M, K] -> (q int8 [M,K], d float32 [M,K/256],
+    S int32 [M,K/32] per 32-value sub-block)."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    assert K % 256 == 0
+    q = np.empty((M, K), np.int8)
+    d = np.empty((M, K // 256), np.float32)
+    S = np.empty((M, K // 32), np.int32)
+    _load().oracle_quantize_act256(_p(x), _x_dtype(x), M, K, _p(q), _p(d), _p(S))
+    return q, d, S
+
+
+def gemm_a256(W: np.ndarray, x: np.ndarray, N: int, rows=None, cols=None) -> np.ndarray:
+    """Q4_K GEMM with per-256 activation scales: y [len(rows), len(cols)] in fp64."""
+    W = np.ascontiguousarray(W, np.uint8)
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    assert K % 256 == 0 and W.size == N * K // 256 * BLOCK_BYTES[Q4_K]
+    r = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    y = np.empty((nr, nc), np.float64)
+    if nr == 0 or nc == 0:
+        return y
+    rc = _load().oracle_gemm_a256(_p(W), _p(x), _x_dtype(x), M, N, K,
+                                  None if r is None else _p(r), nr,
+                                  None if c is None else _p(c), nc, _p(y))
+    if rc != 0:
+        raise MemoryError("oracle_gemm_a256: allocation failed")
+    return y
 
 
 class Oracle:

@@ -480,3 +480,119 @@ int oracle_gemm_deq_f16(int fmt, const uint8_t *W, const void *x, int x_dtype, i
     free(xd); free(wd);
     return 0;
 }
+
+/* ============================================================================
+ * Per-256 activation scales (the Q8_K-style activation block the CPU issue
+ * names, aprender issue #5475, section "Ask", item 1: "Q4_K x Q8_K"): one fp32
+ * scale per 256-value super-block instead of per 32 values.  The steps are the
+ * per-32 quantiser's over 256 values (amax, d = amax/127, id = 1/d, q =
+ * rint(x*id) clamped to [-127, 127], q = 0 where x = 0), and the int32 code sum
+ * is kept per 32-value sub-block (the weight mins are per sub-block).  The
+ * combine is the per-32 formula with every sub-block of a super-block sharing
+ * its scale:
+ *   Q4_K: y = sum_sb dx[sb] * sum_j ( d*sc[j]*I[j] - dmin*m[j]*S[j] )
+ * ========================================================================== */
+
+/* x [M x K] -> q int8 [M x K], d fp32 [M x K/256], S int32 [M x K/32]. */
+void oracle_quantize_act256(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *q,
+                            float *d256, int32_t *S32) {
+    int64_t nsb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++) {
+        float xf[256];
+        for (int64_t sb = 0; sb < nsb; sb++) {
+            for (int t = 0; t < 256; t++) xf[t] = load_x(x, x_dtype, r * K + 256 * sb + t);
+            float amax = 0.0f;
+            for (int t = 0; t < 256; t++) {
+                float a = fabsf(xf[t]);
+                if (a > amax) amax = a;
+            }
+            int8_t *qo = q + r * K + 256 * sb;
+            int32_t *So = S32 + r * (K / 32) + 8 * sb;
+            if (amax == 0.0f) {
+                memset(qo, 0, 256);
+                d256[r * nsb + sb] = 0.0f;
+                for (int j = 0; j < 8; j++) So[j] = 0;
+                continue;
+            }
+            float d = amax / 127.0f;
+            float id = 1.0f / d;
+            for (int j = 0; j < 8; j++) {
+                int32_t S = 0;
+                for (int t = 32 * j; t < 32 * j + 32; t++) {
+                    int qi = 0;
+                    if (xf[t] != 0.0f) {
+                        float v = xf[t] * id;
+                        float rr = rintf(v);
+                        if (rr > 127.0f) rr = 127.0f;
+                        if (rr < -127.0f) rr = -127.0f;
+                        qi = (int)rr;
+                    }
+                    qo[t] = (int8_t)qi;
+                    S += qi;
+                }
+                So[j] = S;
+            }
+            d256[r * nsb + sb] = d;
+        }
+    }
+}
+
+/* Q4_K GEMM with per-256 activation scales over the selected rows / columns
+ * (all when rows / cols is NULL): exact int32 sub-block dots, fp64 combine in
+ * ascending super-block and sub-block order.  Returns 0, or -1 on allocation
+ * failure. */
+int oracle_gemm_a256(const uint8_t *W, const void *x, int x_dtype, int64_t M, int64_t N, int64_t K,
+                     const int64_t *rows, int64_t nrows, const int64_t *cols, int64_t ncols,
+                     double *y) {
+    if (!rows) nrows = M;
+    if (!cols) ncols = N;
+    int64_t nsb = K / 256, nb32 = K / 32;
+    int8_t *qx = malloc((size_t)(nrows * K));
+    float *dx = malloc(sizeof(float) * (size_t)(nrows * nsb));
+    int32_t *Sx = malloc(sizeof(int32_t) * (size_t)(nrows * nb32));
+    uint8_t *qw = malloc((size_t)(ncols * K));
+    uint8_t *scw = malloc((size_t)(ncols * nb32)), *mw = malloc((size_t)(ncols * nb32));
+    double *dw = malloc(sizeof(double) * (size_t)(ncols * nsb)), *dmw = malloc(sizeof(double) * (size_t)(ncols * nsb));
+    float *xrow = malloc(sizeof(float) * (size_t)K);
+    if (!qx || !dx || !Sx || !qw || !scw || !mw || !dw || !dmw || !xrow) {
+        free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw); free(xrow);
+        return -1;
+    }
+    free(xrow);
+    for (int64_t i = 0; i < nrows; i++) {
+        int64_t r = rows ? rows[i] : i;
+        if (x_dtype == ORACLE_F32)
+            oracle_quantize_act256((const float *)x + r * K, ORACLE_F32, 1, K, qx + i * K,
+                                   dx + i * nsb, Sx + i * nb32);
+        else
+            oracle_quantize_act256((const uint16_t *)x + r * K, ORACLE_BF16, 1, K, qx + i * K,
+                                   dx + i * nsb, Sx + i * nb32);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t sb = 0; sb < nsb; sb++)
+            decode_q4k_block(W + (n * nsb + sb) * 144, qw + j * K + 256 * sb, scw + j * nb32 + 8 * sb,
+                             mw + j * nb32 + 8 * sb, dw + j * nsb + sb, dmw + j * nsb + sb);
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < nrows; i++)
+        for (int64_t j = 0; j < ncols; j++) {
+            double acc = 0.0;
+            for (int64_t sb = 0; sb < nsb; sb++) {
+                double part = 0.0;
+                for (int64_t b = 8 * sb; b < 8 * sb + 8; b++) {
+                    int32_t I = 0;
+                    for (int t = 0; t < 32; t++)
+                        I += (int32_t)qw[j * K + 32 * b + t] * (int32_t)qx[i * K + 32 * b + t];
+                    part += dw[j * nsb + sb] * (double)scw[j * nb32 + b] * (double)I -
+                            dmw[j * nsb + sb] * (double)mw[j * nb32 + b] * (double)Sx[i * nb32 + b];
+                }
+                acc += (double)dx[i * nsb + sb] * part;
+            }
+            y[i * ncols + j] = acc;
+        }
+    free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw);
+    return 0;
+}

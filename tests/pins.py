@@ -20,6 +20,9 @@ mathematics fix:
   * for the dequantise-to-fp16 branch: binary16 rounding against numpy's and
     CPython's own conversions, the worked examples (binary16-exact), the
     rounding chain rebuilt from numpy conversions, brute force and the
+    textbook integer case,
+  * for the per-256 activation variant: quantiser properties, agreement with
+    the per-32 oracle where the two encodings coincide, brute force and the
     textbook integer case.
 
 The mutation tests plant plausible mistakes in a copy of oracle.c and require
@@ -487,10 +490,75 @@ def pin_f16_gemm_textbook(orc):
         assert np.array_equal(ys, y[np.ix_(rows, cols)])
 
 
+# ------------------------------------------------- per-256 activation scales
+
+def pin_a256_quantiser_properties(orc):
+    x = _acts(71, 6, 1024, scale=2.0)
+    x[0, :256] = 0.0                                    # an all-zero super-block
+    x[1, 256:512] *= np.float32(2.0 ** -20)             # tiny values
+    x[2, 300] = np.float32(-9.0)                        # an extreme element
+    q, d, S = orc.quantize_act256(x)
+    assert d[0, 0] == 0 and not q[0, :256].any() and not S[0, :8].any()
+    xq = q.reshape(6, 4, 256).astype(np.float64) * d.astype(np.float64)[:, :, None]
+    err = np.abs(xq.reshape(6, 1024) - x.astype(np.float64))
+    assert np.all(err <= 0.50002 * np.repeat(d.astype(np.float64), 256, axis=1))
+    amax = np.abs(x.reshape(6, 4, 256)).max(2)
+    assert np.array_equal(d, (amax / np.float32(127.0)).astype(np.float32))
+    assert q[2, 300] == -127
+    assert np.array_equal(S, q.reshape(6, 32, 32).astype(np.int64).sum(2))
+    q2, d2, S2 = orc.quantize_act256(-x)
+    assert np.array_equal(q2, -q) and np.array_equal(d2, d) and np.array_equal(S2, -S)
+    q3, d3, _ = orc.quantize_act256((x * np.float32(8.0)).astype(np.float32))
+    assert np.array_equal(q3, q) and np.array_equal(d3, d * np.float32(8.0))
+
+
+def pin_a256_matches_per32_when_scales_agree(orc):
+    """When every 32-value block of a super-block holds the super-block's extreme
+    value, the per-32 and per-256 encodings coincide, and so must the GEMMs."""
+    M, N, K = 4, 7, 768
+    x = _acts(73, M, K)
+    x = np.clip(x, -2.5, 2.5).astype(np.float32)
+    x[:, ::32] = np.float32(3.0) * np.where(np.arange(K // 32) % 2 == 0, 1, -1).astype(np.float32)
+    q, d, S = orc.quantize_act256(x)
+    q32, d32, S32 = orc.quantize_act(x)
+    assert np.array_equal(q, q32) and np.array_equal(S, S32)
+    assert np.array_equal(np.repeat(d, 8, axis=1), d32)
+    W = synth.pack(Q4_K, synth.normal(74, (N, K), 0.0, 0.02))
+    assert np.array_equal(orc.gemm_a256(W, x, N), orc.gemm(Q4_K, W, x, N))
+
+
+def pin_a256_gemm_bruteforce(orc):
+    for (M, N, K, seed) in ((1, 1, 256, 1), (3, 5, 512, 2), (4, 8, 768, 3)):
+        W = synth.random_blocks(Q4_K, N, K, seed=760 + seed, emin=3, emax=18)
+        x = _acts(770 + seed, M, K)
+        for xin in (x, synth.to_bf16_bits(x)):
+            y = orc.gemm_a256(W, xin, N)
+            q, d, _ = orc.quantize_act256(xin)
+            xh = (q.reshape(M, K // 256, 256).astype(np.float64) * d.astype(np.float64)[:, :, None]).reshape(M, K)
+            w = orc.dequant(Q4_K, W, N, K)
+            ref, scale = xh @ w.T, np.abs(xh) @ np.abs(w).T + 1e-300
+            assert np.all(np.abs(y - ref) <= 1e-12 * scale)
+
+
+def pin_a256_gemm_textbook(orc):
+    M, N, K = 5, 6, 512
+    W, wv = _textbook_blocks(Q4_K, N, K, seed=79)
+    rng = np.random.default_rng(80)
+    xi = rng.integers(-127, 128, size=(M, K))
+    xi[:, ::256] = 127                                   # every super-block reaches 127: d = 1
+    y = orc.gemm_a256(W, xi.astype(np.float32), N)
+    assert np.array_equal(y, (xi @ wv.T).astype(np.float64))
+    rows, cols = np.array([3, 0]), np.array([5, 2, 2])
+    assert np.array_equal(orc.gemm_a256(W, xi.astype(np.float32), N, rows=rows, cols=cols),
+                          y[np.ix_(rows, cols)])
+
+
 ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bit_probe,
             pin_q6k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
             pin_quant_symmetry_and_scaling, pin_quant_integer_blocks, pin_quant_bf16_matches_f32,
             pin_gemm_bruteforce, pin_gemm_textbook, pin_gemm_worked_examples,
             pin_gemm_selection_and_scaling, pin_gemm_semantic_bound,
             pin_f16_rounding, pin_f16_activations, pin_f16_dequant_worked_examples,
-            pin_f16_dequant_rounding, pin_f16_gemm_bruteforce, pin_f16_gemm_textbook]
+            pin_f16_dequant_rounding, pin_f16_gemm_bruteforce, pin_f16_gemm_textbook,
+            pin_a256_quantiser_properties, pin_a256_matches_per32_when_scales_agree,
+            pin_a256_gemm_bruteforce, pin_a256_gemm_textbook]

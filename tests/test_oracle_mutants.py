@@ -93,6 +93,18 @@ MUTANTS = [
     ("deq_f16_q6_offset_dropped",
      "o[16 * s + t] = f16_round_scaled(a * ((int64_t)q[16 * s + t] - 32), ea);",
      "o[16 * s + t] = f16_round_scaled(a * ((int64_t)q[16 * s + t]), ea);"),
+    ("a256_divisor_128",
+     "            float d = amax / 127.0f;\n            float id = 1.0f / d;\n            for (int j = 0; j < 8; j++) {",
+     "            float d = amax / 128.0f;\n            float id = 1.0f / d;\n            for (int j = 0; j < 8; j++) {"),
+    ("a256_sum_over_superblock",
+     "                So[j] = S;\n",
+     "                So[j] = S + (j > 0 ? So[j - 1] : 0);\n"),
+    ("a256_min_term_dropped",
+     "                    part += dw[j * nsb + sb] * (double)scw[j * nb32 + b] * (double)I -\n                            dmw[j * nsb + sb] * (double)mw[j * nb32 + b] * (double)Sx[i * nb32 + b];",
+     "                    part += dw[j * nsb + sb] * (double)scw[j * nb32 + b] * (double)I;"),
+    ("a256_scale_of_next_superblock",
+     "                acc += (double)dx[i * nsb + sb] * part;",
+     "                acc += (double)dx[i * nsb + (sb + 1) % nsb] * part;"),
     ("gemm_f16_abs_sum_signed",
      "aabs += fabs(p);",
      "aabs += p;"),
