@@ -22,8 +22,9 @@ step; its launches run back to back), the large-M headline
 projections (K=4096 -> N=24576 Q4_K and K=12288 -> N=4096 Q6_K at M=512), the
 decode-sized GEMV (M = 1 and 8) over every projection shape of the workloads,
 the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K), the other design branch
-(weights dequantised to fp16 in the GEMM, fp16 matrix cores) beside the int8
-method on every projection shape, and the CPU oracle timed on the host.
+(weights dequantised to fp16 in the GEMM, fp16 matrix cores) and the per-256
+activation-scale variant (Q4_K) beside the int8 method on every projection
+shape, and the CPU oracle timed on the host.
 
 --calib-copy-mib N additionally runs a plain elementwise copy kernel over
 N MiB (read N, write N) three times: the reference dispatch for scaling HBM
@@ -140,7 +141,7 @@ def parse():
     p.add_argument("--big-steps", type=int, default=30)   # 0: skip the large-M GEMMs
     p.add_argument("--gemv-steps", type=int, default=200)  # 0: skip the decode GEMV table
     p.add_argument("--set-steps", type=int, default=10)   # 0: skip the config 3/4 projection sets
-    p.add_argument("--branch-steps", type=int, default=5)  # 0: skip the fp16 design-branch table
+    p.add_argument("--branch-steps", type=int, default=5)  # 0: skip the design-variants table
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -409,10 +410,12 @@ def main():
         del Ws
     torch.cuda.empty_cache()
 
-    # ---------------- the other design branch (dequantise to fp16, float matrix-core
-    # GEMM) beside the int8 method, per projection shape: both timed as whole
-    # calls (int8: quantiser + GEMM; fp16: x -> binary16 + GEMM), back to back
-    branch = {}
+    # ---------------- the measured design variants beside the int8 method, per
+    # projection shape, each timed as whole calls back to back (best of three
+    # interleaved rounds): the int8 method
+    # (quantiser + GEMM), per-256 activation scales (Q4_K: quantiser + GEMM) and
+    # the other design branch (x -> binary16 + GEMM on fp16 matrix cores)
+    variants = {}
     for cfg in (2, 3, 4) if args.branch_steps > 0 else ():
         for g in synth.CONFIGS[cfg]:
             Wb = to_dev(synth.make_weights(g))
@@ -425,26 +428,36 @@ def main():
                 "int8": lambda: qg.qgemm_prefill(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws8, stream),
                 "f16": lambda: qg.qgemm_prefill_deq_f16(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws16,
                                                         stream)}
+            if g.fmt == qg.QG_Q4_K:
+                calls["a256"] = lambda: qg.qgemm_prefill_a256(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws8,
+                                                              stream)
+            # interleaved rounds, the best of three per variant (clocks drift
+            # under sustained load; interleaving keeps the comparison fair)
             us = {}
-            for k, fn in calls.items():
+            for fn in calls.values():
                 for _ in range(2):
                     fn()
-                a, b = ev(), ev()
-                a.record(stream)
-                for _ in range(args.branch_steps):
-                    fn()
-                b.record(stream)
-                torch.cuda.synchronize()
-                us[k] = 1e3 * a.elapsed_time(b) / args.branch_steps
-            branch[f"c{cfg}_{g.name}"] = {
-                "shape": f"M={g.M} K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'}",
-                "int8_us": round(us["int8"], 2),
-                "int8_tops": round(g.ops / (us["int8"] * 1e-6) / 1e12, 1),
-                "f16_us": round(us["f16"], 2),
-                "f16_tflops": round(g.ops / (us["f16"] * 1e-6) / 1e12, 1),
-                "f16_frac_fp16_peak": round(g.ops / (us["f16"] * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
-                "f16_kernel": qg.qgemm_deq_f16_kernel_name(g.fmt, g.M, g.N, g.K),
-                "f16_over_int8_speed": round(us["int8"] / us["f16"], 3)}
+            for _ in range(3):
+                for k, fn in calls.items():
+                    a, b = ev(), ev()
+                    a.record(stream)
+                    for _ in range(args.branch_steps):
+                        fn()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    us[k] = min(us.get(k, 1e30), 1e3 * a.elapsed_time(b) / args.branch_steps)
+            rate = lambda k: round(g.ops / (us[k] * 1e-6) / 1e12, 1)
+            row = {"shape": f"M={g.M} K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'}",
+                   "int8_us": round(us["int8"], 2), "int8_tops": rate("int8")}
+            if "a256" in us:
+                row.update({"a256_us": round(us["a256"], 2), "a256_tops": rate("a256"),
+                            "a256_kernel": qg.qgemm_kernel_name_a256(g.fmt, g.M, g.N, g.K),
+                            "a256_over_int8_speed": round(us["int8"] / us["a256"], 3)})
+            row.update({"f16_us": round(us["f16"], 2), "f16_tflops": rate("f16"),
+                        "f16_frac_fp16_peak": round(rate("f16") / PEAK_FP16_TFLOPS, 4),
+                        "f16_kernel": qg.qgemm_deq_f16_kernel_name(g.fmt, g.M, g.N, g.K),
+                        "f16_over_int8_speed": round(us["int8"] / us["f16"], 3)})
+            variants[f"c{cfg}_{g.name}"] = row
             del Wb, xb, yb, ws8, ws16
     torch.cuda.empty_cache()
 
@@ -599,7 +612,7 @@ def main():
         "projection_sets": sets,
         "decode_gemv": gemv,
         "lm_head": lm_out,
-        "design_branch_f16": branch,
+        "design_variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -153,6 +153,42 @@ int qgemm_dequant(const void *q_weights, int fmt, int64_t N, int64_t K, float *w
 int qgemm_block_partials(const void *q_weights, int fmt, const int8_t *qx, int64_t M, int64_t N,
                          int64_t K, int32_t *out, void *stream);
 
+/* ---- per-256 activation scales (Q4_K) ----
+ *
+ * The activation block the same issue pairs with Q4_K ("Q4_K x Q8_K", aprender
+ * issue #5475, section "Ask", item 1): one fp32 scale per 256-value super-block
+ * instead of per 32 values, with the code sums kept per 32-value sub-block.
+ * The quantiser takes the steps of qgemm_quantize_act over each super-block
+ * (d = amax/127, codes rint(x * (1/d)) ties to even clamped to [-127, 127],
+ * code 0 where x == 0); the GEMM computes
+ *   y[m][n] = sum_sb dx[sb] * sum_j ( d*sc[j]*I[j] - dmin*m[j]*S[j] )
+ * with exact int32 sub-block partials I[j] -- a different (coarser) activation
+ * encoding than the per-32 entry points, not their result.  Q4_K only
+ * (QG_EFMT otherwise).  The workspace is sized by qgemm_workspace_bytes; its
+ * layout is the per-32 one with every 32-value block holding its super-block's
+ * scale, which lets the tiled kernels combine a super-block's eight partials
+ * in integers and apply the fp32 scales once per super-block. */
+
+/* Quantise x [M][K] per 256 values into `workspace` (argument rules and codes
+ * as qgemm_quantize_workspace). */
+int qgemm_quantize_workspace_a256(const void *x, int x_dtype, int64_t M, int64_t K,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+/* y = x . W^T from a workspace filled by qgemm_quantize_workspace_a256 with the
+ * same M and K (argument rules and codes as qgemm_gemm_quantized, path AUTO). */
+int qgemm_gemm_quantized_a256(const void *q_weights, int fmt, const void *workspace,
+                              size_t workspace_bytes, int64_t M, int64_t N, int64_t K, float *y,
+                              void *stream);
+/* The two above in one call (argument rules and codes as qgemm_prefill). */
+int qgemm_prefill_a256(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
+                       int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,
+                       void *stream);
+/* Name of the GEMM kernel qgemm_gemm_quantized_a256 launches, or NULL. */
+const char *qgemm_kernel_name_a256(int fmt, int64_t M, int64_t N, int64_t K);
+/* Test hook: the per-256 quantiser alone.  q [M][K] int8, d [M][K/256] fp32,
+ * S [M][K/32] int32 (sub-block code sums); K % 256 == 0. */
+int qgemm_quantize_act_a256(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *q, float *d,
+                            int32_t *S, void *stream);
+
 /* ---- the other design branch: dequantise to binary16, float matrix-core GEMM ----
  *
  * aprender issue #5475 ("apr serve / apr run: Qwen3.5 on CPU prefills one token

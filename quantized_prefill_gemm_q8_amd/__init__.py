@@ -25,7 +25,9 @@ SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_
            "qgemm_quantize_workspace", "qgemm_gemm_quantized",
            "qgemm_strerror", "qgemm_kernel_name", "qgemm_quantize_act", "qgemm_dequant",
            "qgemm_block_partials", "qgemm_deq_f16_workspace_bytes", "qgemm_prefill_deq_f16",
-           "qgemm_deq_f16_kernel_name", "qgemm_to_f16", "qgemm_dequant_f16")
+           "qgemm_deq_f16_kernel_name", "qgemm_to_f16", "qgemm_dequant_f16",
+           "qgemm_quantize_workspace_a256", "qgemm_gemm_quantized_a256", "qgemm_prefill_a256",
+           "qgemm_kernel_name_a256", "qgemm_quantize_act_a256")
 
 
 class QgemmError(RuntimeError):
@@ -82,6 +84,16 @@ def load() -> ctypes.CDLL:
         lib.qgemm_to_f16.restype = ci
         lib.qgemm_dequant_f16.argtypes = [vp, ci, i64, i64, vp, vp]
         lib.qgemm_dequant_f16.restype = ci
+        lib.qgemm_quantize_workspace_a256.argtypes = [vp, ci, i64, i64, vp, sz, vp]
+        lib.qgemm_quantize_workspace_a256.restype = ci
+        lib.qgemm_gemm_quantized_a256.argtypes = [vp, ci, vp, sz, i64, i64, i64, vp, vp]
+        lib.qgemm_gemm_quantized_a256.restype = ci
+        lib.qgemm_prefill_a256.argtypes = [vp, ci, vp, ci, i64, i64, i64, vp, vp, sz, vp]
+        lib.qgemm_prefill_a256.restype = ci
+        lib.qgemm_kernel_name_a256.argtypes = [ci, i64, i64, i64]
+        lib.qgemm_kernel_name_a256.restype = ctypes.c_char_p
+        lib.qgemm_quantize_act_a256.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
+        lib.qgemm_quantize_act_a256.restype = ci
         _lib = lib
     return _lib
 
@@ -173,6 +185,37 @@ def qgemm_dequant(q_weights, fmt, N, K, w, stream=None):
 def qgemm_block_partials(q_weights, fmt, qx, M, N, K, out, stream=None):
     _check(load().qgemm_block_partials(_ptr(q_weights), fmt, _ptr(qx), M, N, K, _ptr(out),
                                        _stream(stream)), "qgemm_block_partials")
+
+
+# ---- per-256 activation scales (Q4_K) ----
+
+def qgemm_quantize_workspace_a256(x, M, K, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_quantize_workspace_a256(_ptr(x), _dtype_code(x), M, K, _ptr(workspace),
+                                                ws_bytes, _stream(stream)),
+           "qgemm_quantize_workspace_a256")
+
+
+def qgemm_gemm_quantized_a256(q_weights, fmt, workspace, M, N, K, y, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_gemm_quantized_a256(_ptr(q_weights), fmt, _ptr(workspace), ws_bytes, M, N, K,
+                                            _ptr(y), _stream(stream)), "qgemm_gemm_quantized_a256")
+
+
+def qgemm_prefill_a256(q_weights, fmt, x, M, N, K, y, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_prefill_a256(_ptr(q_weights), fmt, _ptr(x), _dtype_code(x), M, N, K, _ptr(y),
+                                     _ptr(workspace), ws_bytes, _stream(stream)), "qgemm_prefill_a256")
+
+
+def qgemm_kernel_name_a256(fmt: int, M: int, N: int, K: int) -> str | None:
+    r = load().qgemm_kernel_name_a256(fmt, M, N, K)
+    return None if r is None else r.decode()
+
+
+def qgemm_quantize_act_a256(x, M, K, q, d, S, stream=None):
+    _check(load().qgemm_quantize_act_a256(_ptr(x), _dtype_code(x), M, K, _ptr(q), _ptr(d), _ptr(S),
+                                          _stream(stream)), "qgemm_quantize_act_a256")
 
 
 # ---- the dequantise-to-fp16 branch (measured beside the int8 method) ----

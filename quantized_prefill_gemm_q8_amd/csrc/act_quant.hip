@@ -114,7 +114,118 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
   }
 }
 
+// Per-256 activation scales (the Q8_K-style block of aprender issue #5475,
+// section "Ask"): the same steps over a whole 256-value super-block -- 32
+// lanes of eight values, amax over the 32 lanes -- with the code sums kept per
+// 32-value sub-block.  WS: the GEMM workspace of the per-32 quantiser with the
+// super-block's scale in all eight of its blocks (dx, dxT) and dS = d * S per
+// sub-block (so every GEMM kernel reads it unchanged); otherwise the hook
+// layout (q [M][K], d [M][K/256], S [M][K/32] int32).
+template <int XDT, bool WS>
+__global__ __launch_bounds__(256) void act_quant256_kernel(const void* __restrict__ x, int64_t M,
+                                                           int64_t K, int8_t* __restrict__ q,
+                                                           float* __restrict__ d,
+                                                           int32_t* __restrict__ S_int,
+                                                           float* __restrict__ dS,
+                                                           uint16_t* __restrict__ dsp,
+                                                           float* __restrict__ dxT, int64_t Mp) {
+  const int64_t per_row = K / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= M * per_row) return;  // whole groups of 32 lanes leave together (K % 256 == 0)
+  const int64_t row = idx / per_row;
+  const int64_t c8 = idx - row * per_row;
+  const int64_t b = c8 >> 2, sb = c8 >> 5;
+
+  float v[8];
+  if (XDT == QG_BF16) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * K + 8 * c8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + row * K + 8 * c8);
+    const float4 a = p[0], c = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  }
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+
+  float dv = 0.0f, id = 0.0f;
+  if (amax != 0.0f) {
+    dv = amax / 127.0f;  // correctly rounded IEEE division
+    id = 1.0f / dv;      // correctly rounded IEEE division
+  }
+  uint32_t packed[2] = {0u, 0u};
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    int qi = 0;
+    if (v[i] != 0.0f) {
+      float r = rintf(v[i] * id);
+      r = r > 127.0f ? 127.0f : r;
+      r = r < -127.0f ? -127.0f : r;
+      qi = static_cast<int>(r);
+    }
+    s += qi;
+    packed[i >> 2] |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * (i & 3));
+  }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+
+  *reinterpret_cast<uint2*>(q + row * K + 8 * c8) = make_uint2(packed[0], packed[1]);
+  if ((c8 & 3) == 0) {
+    const int64_t nb = K / 32;
+    if (WS) {
+      const float ds = dv * static_cast<float>(s);
+      d[row * nb + b] = dv;
+      dxT[b * Mp + row] = dv;
+      dS[row * nb + b] = ds;
+      uint16_t p0, p1, p2;
+      split3_bf16(ds, p0, p1, p2);
+      uint16_t* o = dsp + ((row * (K / 256) + (b >> 3)) * 3) * 8 + (b & 7);
+      o[0] = p0;
+      o[8] = p1;
+      o[16] = p2;
+    } else {
+      S_int[row * nb + b] = s;
+      if ((c8 & 31) == 0) d[row * (K / 256) + sb] = dv;
+    }
+  }
+}
+
 }  // namespace qg
+
+hipError_t qg_launch_act_quant256_ws(const void* x, int x_dtype, int64_t M, int64_t K,
+                                     const QgWorkspace& ws, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>((M * (K / 8) + 255) / 256));
+  if (x_dtype == QG_BF16)
+    qg::act_quant256_kernel<QG_BF16, true><<<g, dim3(256), 0, stream>>>(x, M, K, ws.q, ws.dx, nullptr,
+                                                                        ws.dS, ws.dsp, ws.dxT, ws.Mp);
+  else
+    qg::act_quant256_kernel<QG_F32, true><<<g, dim3(256), 0, stream>>>(x, M, K, ws.q, ws.dx, nullptr,
+                                                                       ws.dS, ws.dsp, ws.dxT, ws.Mp);
+  return hipGetLastError();
+}
+
+hipError_t qg_launch_act_quant256_hook(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
+                                       float* d256, int32_t* S32, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>((M * (K / 8) + 255) / 256));
+  if (x_dtype == QG_BF16)
+    qg::act_quant256_kernel<QG_BF16, false><<<g, dim3(256), 0, stream>>>(x, M, K, q, d256, S32, nullptr,
+                                                                         nullptr, nullptr, 0);
+  else
+    qg::act_quant256_kernel<QG_F32, false><<<g, dim3(256), 0, stream>>>(x, M, K, q, d256, S32, nullptr,
+                                                                        nullptr, nullptr, 0);
+  return hipGetLastError();
+}
 
 hipError_t qg_launch_act_quant_ws(const void* x, int x_dtype, int64_t M, int64_t K,
                                   const QgWorkspace& ws, hipStream_t stream) {

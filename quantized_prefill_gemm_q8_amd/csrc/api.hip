@@ -230,6 +230,84 @@ int qgemm_block_partials(const void* q_weights, int fmt, const int8_t* qx, int64
                                                 M, N, K, out, static_cast<hipStream_t>(stream)));
 }
 
+// ---- per-256 activation scales ----
+
+int qgemm_quantize_workspace_a256(const void* x, int x_dtype, int64_t M, int64_t K, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!x || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  int rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  if (!aligned(x, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const QgWorkspace ws = carve(workspace, L);
+  return launch_status(qg_launch_act_quant256_ws(x, x_dtype, M, K, ws, static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_gemm_quantized_a256(const void* q_weights, int fmt, const void* workspace,
+                              size_t workspace_bytes, int64_t M, int64_t N, int64_t K, float* y,
+                              void* stream) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (fmt != QG_Q4_K) return QG_EFMT;
+  if (!y || M < 1) return QG_EINVAL;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / N) return QG_EINVAL;
+  rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  if (!aligned(y, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
+  const uint8_t* W = static_cast<const uint8_t*>(q_weights);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the skinny and small-grid kernels read the per-block scales, which the
+  // per-256 workspace holds too
+  if (auto_skinny(fmt, M)) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
+  return launch_status(qg_launch_gemm_q4k(W, ws, M, N, K, y, s, true));
+}
+
+int qgemm_prefill_a256(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M,
+                       int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = check_common(q_weights, fmt, N, K);
+  if (rc) return rc;
+  if (fmt != QG_Q4_K) return QG_EFMT;
+  if (!x || !y || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / N) return QG_EINVAL;
+  rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  if (!aligned(x, 16) || !aligned(y, 16)) return QG_EALIGN;
+  rc = qgemm_quantize_workspace_a256(x, x_dtype, M, K, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  return qgemm_gemm_quantized_a256(q_weights, fmt, workspace, workspace_bytes, M, N, K, y, stream);
+}
+
+const char* qgemm_kernel_name_a256(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt != QG_Q4_K || M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
+  if (auto_skinny(fmt, M)) return qg_gemm_skinny_kernel_name(fmt, M, N, K);
+  return qg_gemm_q4k_kernel_name(M, N, K, true);
+}
+
+int qgemm_quantize_act_a256(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* d,
+                            int32_t* S, void* stream) {
+  if (!x || !q || !d || !S || M < 1 || K < 256 || K % 256 != 0) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / K) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(d, 4) || !aligned(S, 4)) return QG_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_act_quant256_hook(x, x_dtype, M, K, q, d, S,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 // ---- the dequantise-to-fp16 branch ----
 
 size_t qgemm_deq_f16_workspace_bytes(int64_t M, int64_t K) {

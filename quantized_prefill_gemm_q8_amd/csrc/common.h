@@ -116,15 +116,21 @@ hipError_t qg_launch_act_quant_ws(const void* x, int x_dtype, int64_t M, int64_t
                                   const QgWorkspace& ws, hipStream_t stream);
 hipError_t qg_launch_act_quant_hook(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
                                     float* d, int32_t* S, hipStream_t stream);
+// per-256 activation scales: the same workspace layout with each super-block's
+// scale in all eight of its 32-value blocks; hook layout d [M][K/256], S [M][K/32]
+hipError_t qg_launch_act_quant256_ws(const void* x, int x_dtype, int64_t M, int64_t K,
+                                     const QgWorkspace& ws, hipStream_t stream);
+hipError_t qg_launch_act_quant256_hook(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
+                                       float* d256, int32_t* S32, hipStream_t stream);
 hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
-                              int64_t K, float* y, hipStream_t stream);
+                              int64_t K, float* y, hipStream_t stream, bool a256 = false);
 hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream);
 hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
                                  int64_t N, int64_t K, float* y, hipStream_t stream);
 // Name of the kernel each launcher picks for a problem (diagnostics: matches
 // the kernel names a profiler reports).
-const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K);
+const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256 = false);
 const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t K);
 const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t qg_launch_dequant(const uint8_t* W, int fmt, int64_t N, int64_t K, float* w,

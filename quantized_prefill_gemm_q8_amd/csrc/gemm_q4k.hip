@@ -79,7 +79,12 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 // DPP: activation scales staged row-major and applied with the DPP-broadcast
 // epilogue; otherwise staged block-major ([8][BM], from dxT) and read as 16
 // per-element values per tile (four 16-byte broadcast reads).
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC, int KS>
+// A256: activations quantised with one scale per 256-value super-block (the
+// workspace then holds that scale for each of its eight 32-value blocks).  The
+// eight sub-block partials of a super-block are combined in integers,
+// J = sum_j sc[j] * I[j] (v_mad_i32_i24 per element and block; |J| < 2^25), and
+// the fp32 epilogue runs once per super-block: acc += fl(fl(J) * d) * dx.
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC, int KS, bool A256 = false>
 __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_lds_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
@@ -177,6 +182,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; r++) magic[r] = kMagicBits;
+  static_assert(!(A256 && DPP), "the per-256 epilogue reads row scales from LDS");
   float acc[TM][TN][16];
 #pragma unroll
   for (int i = 0; i < TM; i++)
@@ -184,6 +190,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
     for (int j = 0; j < TN; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+  v16i acc_i[TM][TN];  // A256: the super-block's integer sum J
 
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; s0++)
@@ -255,6 +262,24 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
           dsc[j] = d[j] * static_cast<float>(sub_byte(sc[j].sc_lo, sc[j].sc_hi, jb));
           cc[j] = -kMagic * dsc[j];
         }
+        if constexpr (A256) {
+          // I from a zero-started accumulator; J += sc * I in integers
+#pragma unroll
+          for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+              const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][e], b[j], v16i{}, 0, 0, 0);
+              const int scj = static_cast<int>(sub_byte(sc[j].sc_lo, sc[j].sc_hi, jb));
+              if (jb == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc_i[i][j][r] = __mul24(D[r], scj);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc_i[i][j][r] = __mul24(D[r], scj) + acc_i[i][j][r];
+              }
+            }
+          continue;
+        }
         v16i D[TM][TN];
 #pragma unroll
         for (int i = 0; i < TM; i++)
@@ -286,6 +311,24 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
               }
           }
         }
+      }
+    }
+    if constexpr (A256) {
+      // once per super-block: acc += fl(fl(J) * d) * dx, dx the rows' super-block
+      // scale (the first of the stage's eight equal block scales)
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        float dxv[16];
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const float4 v = *reinterpret_cast<const float4*>(sX + ml0 + 32 * i + 8 * g + 4 * h);
+          dxv[4 * g] = v.x; dxv[4 * g + 1] = v.y; dxv[4 * g + 2] = v.z; dxv[4 * g + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            acc[i][j][r] = __builtin_fmaf(static_cast<float>(acc_i[i][j][r]) * d[j], dxv[r], acc[i][j][r]);
       }
     }
     // min term of the super-block on the matrix core
@@ -499,12 +542,13 @@ static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int
 
 // OCC: waves per SIMD the register allocation must allow (launch bound);
 // KS: K-groups per workgroup (at most the number of super-blocks)
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC = (WM * WN + 3) / 4, int KS = 1>
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC = (WM * WN + 3) / 4, int KS = 1,
+          bool A256 = false>
 static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                        float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
+  gemm_q4k_lds_kernel<TM, TN, WM, WN, DPP, NS, OCC, KS, A256><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
       W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
 }
 
@@ -541,12 +585,21 @@ Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K) {
+// Kernel names as a profiler lists them (A256 is the last template argument).
+const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256) {
   switch (pick_q4k(M, N, K)) {
-    case Q4Pick::kLds128x256: return "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1>";
-    case Q4Pick::kLds64x128: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1>";
-    case Q4Pick::kLds64x128K2: return "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>";
-    case Q4Pick::kLds32x64K4: return "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>";
+    case Q4Pick::kLds128x256:
+      return a256 ? "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, true>"
+                  : "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>";
+    case Q4Pick::kLds64x128:
+      return a256 ? "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, true>"
+                  : "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>";
+    case Q4Pick::kLds64x128K2:
+      return a256 ? "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2, true>"
+                  : "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2, false>";
+    case Q4Pick::kLds32x64K4:
+      return a256 ? "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, true>"
+                  : "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, false>";
     case Q4Pick::kSmall1: return "gemm_q4k_small_kernel<1>";
     case Q4Pick::kSmall2: return "gemm_q4k_small_kernel<2>";
     case Q4Pick::kSmall4: return "gemm_q4k_small_kernel<4>";
@@ -555,13 +608,31 @@ const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K) {
   return "?";
 }
 
+// a256: the per-256 workspace (every 32-value block of a super-block holds the
+// super-block's scale).  The LDS kernels then combine sub-blocks in integers
+// (for long prompts in 64x128 blocks: the 2x2-tile waves would need the
+// integer sums of four tiles on top of their fp32 ones and spill; measured
+// 725 against 514 TOPS at M = 8192); the small-grid kernel computes the same
+// result with its per-block epilogue.
 hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
-                              int64_t K, float* y, hipStream_t stream) {
+                              int64_t K, float* y, hipStream_t stream, bool a256) {
   switch (pick_q4k(M, N, K)) {
-    case Q4Pick::kLds128x256: qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream); break;
-    case Q4Pick::kLds64x128: qg::launch_lds<1, 1, 2, 4, false, 2, 4>(W, ws, M, N, K, y, stream); break;
-    case Q4Pick::kLds64x128K2: qg::launch_lds<1, 1, 2, 4, false, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
-    case Q4Pick::kLds32x64K4: qg::launch_lds<1, 1, 1, 2, false, 2, 2, 4>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds128x256:
+      if (a256) qg::launch_lds<1, 1, 2, 4, false, 2, 4, 1, true>(W, ws, M, N, K, y, stream);
+      else qg::launch_lds<2, 2, 2, 4, false, 2>(W, ws, M, N, K, y, stream);
+      break;
+    case Q4Pick::kLds64x128:
+      if (a256) qg::launch_lds<1, 1, 2, 4, false, 2, 4, 1, true>(W, ws, M, N, K, y, stream);
+      else qg::launch_lds<1, 1, 2, 4, false, 2, 4>(W, ws, M, N, K, y, stream);
+      break;
+    case Q4Pick::kLds64x128K2:
+      if (a256) qg::launch_lds<1, 1, 2, 4, false, 2, 4, 2, true>(W, ws, M, N, K, y, stream);
+      else qg::launch_lds<1, 1, 2, 4, false, 2, 4, 2>(W, ws, M, N, K, y, stream);
+      break;
+    case Q4Pick::kLds32x64K4:
+      if (a256) qg::launch_lds<1, 1, 1, 2, false, 2, 2, 4, true>(W, ws, M, N, K, y, stream);
+      else qg::launch_lds<1, 1, 1, 2, false, 2, 2, 4>(W, ws, M, N, K, y, stream);
+      break;
     case Q4Pick::kSmall1: qg::launch_small<1>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall2: qg::launch_small<2>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall4: qg::launch_small<4>(W, ws, M, N, K, y, stream); break;

@@ -130,14 +130,14 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 1, 80, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
     assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1>"
     # tiled tile choice by grid size
-    assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1>"
-    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1>"
+    assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>"
+    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>"
     assert kn(Q4, 64, 1024, 1024, AUTO).startswith("gemm_q4k_small_kernel<")
     # few output blocks: K split inside the workgroup
-    assert kn(Q4, 512, 2560, 9728, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>"
-    assert kn(Q4, 512, 1024, 3584, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>"
-    assert kn(Q4, 330, 2700, 1280, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2>"
-    assert kn(Q4, 170, 2800, 2816, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4>"
+    assert kn(Q4, 512, 2560, 9728, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2, false>"
+    assert kn(Q4, 512, 1024, 3584, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, false>"
+    assert kn(Q4, 330, 2700, 1280, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2, false>"
+    assert kn(Q4, 170, 2800, 2816, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, false>"
     assert kn(Q4, 512, 1024, 1792, AUTO).startswith("gemm_q4k_small_kernel<")   # too few super-blocks
     assert kn(Q6, 8192, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<2, 1, 2, 4, 2, 2, 1>"
     assert kn(Q6, 1536, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
@@ -148,6 +148,27 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 8, 8, 300, AUTO) is None
     assert kn(Q4, 9, 8, 256, SKINNY) is None
     assert kn(Q4, 0, 8, 256, AUTO) is None
+
+
+def test_a256_host_side():
+    """Per-256 entry points: argument checks and kernel choice (no GPU call)."""
+    lib = qg.load()
+    wsb = qg.qgemm_workspace_bytes(4, 256)
+    call = lambda **k: lib.qgemm_prefill_a256(
+        k.get("w", A), k.get("fmt", 0), k.get("x", A), k.get("xdt", 1), k.get("M", 4),
+        k.get("N", 8), k.get("K", 256), k.get("y", A), k.get("ws", A), k.get("wsb", wsb), None)
+    assert call(w=None) == -1 and call(M=0) == -1 and call(K=300) == -1
+    assert call(fmt=1) == -2 and call(xdt=3) == -3
+    assert call(ws=None) == -4 and call(wsb=wsb - 1) == -4
+    assert call(x=A + 2) == -5 and call(y=A + 4) == -5
+    assert lib.qgemm_quantize_act_a256(A, 1, 4, 288, A, A, A, None) == -1   # K % 256 != 0
+    assert lib.qgemm_quantize_act_a256(A, 1, 4, 512, A, A + 2, A, None) == -5
+    kn = qg.qgemm_kernel_name_a256
+    assert kn(1, 512, 4096, 1024) is None
+    assert kn(0, 512, 24576, 4096) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, true>"
+    assert kn(0, 8192, 24576, 4096) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, true>"
+    assert kn(0, 64, 1024, 1024).startswith("gemm_q4k_small_kernel<")
+    assert kn(0, 3, 300, 1024).startswith("skinny_kernel<0, 3,")
 
 
 def test_deq_f16_branch_host_side():
