@@ -68,6 +68,12 @@ def _bind(path: str):
     lib.oracle_quantize_act256.restype = None
     lib.oracle_gemm_a256.argtypes = [vp, vp, ci, i64, i64, i64, vp, i64, vp, i64, vp]
     lib.oracle_gemm_a256.restype = ci
+    lib.oracle_rms_scale.argtypes = [vp, ci, i64, i64, ctypes.c_float, vp, vp, vp]
+    lib.oracle_rms_scale.restype = None
+    lib.oracle_rmsnorm.argtypes = [vp, ci, vp, vp, i64, i64, vp]
+    lib.oracle_rmsnorm.restype = None
+    lib.oracle_swiglu.argtypes = [vp, vp, i64, vp]
+    lib.oracle_swiglu.restype = None
     return lib
 
 
@@ -259,6 +265,62 @@ def gemm_a256(W: np.ndarray, x: np.ndarray, N: int, rows=None, cols=None) -> np.
     if rc != 0:
         raise MemoryError("oracle_gemm_a256: allocation failed")
     return y
+
+
+def rms_scale(x: np.ndarray, eps: float):
+    """RMSNorm scale per row: (r32, r32_lo, r32_hi), float32 [M] each.  r32 is the
+    oracle's own; [r32_lo, r32_hi] holds the r32 of any summation order of the
+    row's sum of squares (equal ends: every order gives r32)."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    r, lo, hi = (np.empty(M, np.float32) for _ in range(3))
+    _load().oracle_rms_scale(_p(x), _x_dtype(x), M, K, float(np.float32(eps)), _p(r), _p(lo), _p(hi))
+    return r, lo, hi
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, r32: np.ndarray) -> np.ndarray:
+    """Normalised rows xn = f32(f32(x * r32[row]) * g[col]), float32 [M, K]."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    g = np.ascontiguousarray(g, np.float32)
+    r32 = np.ascontiguousarray(r32, np.float32)
+    assert g.shape == (K,) and r32.shape == (M,)
+    xn = np.empty((M, K), np.float32)
+    _load().oracle_rmsnorm(_p(x), _x_dtype(x), _p(g), _p(r32), M, K, _p(xn))
+    return xn
+
+
+def rmsnorm_quantize(x: np.ndarray, g: np.ndarray, eps: float):
+    """RMSNorm then the per-32 quantiser: (q, d, S) as quantize_act returns them,
+    plus the rows whose r32 another summation order could change (a bool mask)
+    and, for those, the codes of the interval's two ends: alt = [(q, d, S) at
+    r32_lo, (q, d, S) at r32_hi]."""
+    r, lo, hi = rms_scale(x, eps)
+    q, d, S = quantize_act(rmsnorm(x, g, r))
+    amb = lo != hi
+    alt = [quantize_act(rmsnorm(x, g, np.where(amb, e, r))) for e in (lo, hi)]
+    return q, d, S, amb, alt
+
+
+def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """h = silu(gate) * up elementwise, in fp64."""
+    gate = np.ascontiguousarray(gate, np.float64)
+    up = np.ascontiguousarray(up, np.float64)
+    assert gate.shape == up.shape
+    h = np.empty(gate.shape, np.float64)
+    _load().oracle_swiglu(_p(gate), _p(up), gate.size, _p(h))
+    return h
+
+
+def gemm_swiglu(fmt: int, W: np.ndarray, x: np.ndarray, F: int, rows=None, cols=None):
+    """SwiGLU of a stacked gate+up projection (W holds 2F rows: gate, then up):
+    h [len(rows), len(cols)] in fp64, cols indexing 0..F-1, and the gate and up
+    GEMM outputs it was formed from."""
+    M = x.shape[0]
+    c = np.arange(F, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, np.int64)
+    y = gemm(fmt, W, x, 2 * F, rows=rows, cols=np.concatenate([c, c + F]))
+    g, u = y[:, :c.size], y[:, c.size:]
+    return swiglu(g, u), g, u
 
 
 class Oracle:

@@ -596,3 +596,76 @@ int oracle_gemm_a256(const uint8_t *W, const void *x, int x_dtype, int64_t M, in
     free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw);
     return 0;
 }
+
+/* ============================================================================
+ * Fusions on either side of the GEMM.  aprender issue #4220 ("CRUX parity
+ * spike: apr serve vs ollama"), table of the techniques llama.cpp uses that
+ * apr lacks: technique 2 counts a layer's per-token launches, among them its
+ * norms and its swiglu as launches of their own; technique 6 is llama.cpp's
+ * norm fused with the multiply by its weight.  sparkinfer PR #464, section
+ * "Summary": the projection path's written-then-re-read scratch is the cost
+ * its fused kernel removes.  The pages print neither formula; the readings
+ * taken are the standard ones of the Qwen-family layers they discuss:
+ *
+ *   RMSNorm of a row x (length K) with the fp32 norm weight g and epsilon eps:
+ *     ss  = sum_k x_k^2           binary64 (each x_k^2 is exact: x has at most
+ *                                 24 significant bits)
+ *     v   = ss / K + eps          binary64, correctly rounded steps
+ *     r   = f32(1 / sqrt(v))      binary64 square root and division, rounded
+ *                                 once to binary32
+ *     xn_k = f32(f32(x_k * r) * g_k)
+ *   and xn goes through the per-32 activation quantiser above.
+ *
+ *   SwiGLU on the gate and up projections of one FFN, stacked as the weight
+ *   rows [gate (F rows); up (F rows)] of one matrix:
+ *     h[m][f] = silu(y[m][f]) * y[m][F + f],   silu(z) = z / (1 + e^-z),
+ *   evaluated here in binary64 from the oracle's fp64 GEMM output.
+ * ========================================================================== */
+
+/* Per row: r32 as above, and the interval [r32_lo, r32_hi] holding the r32 of
+ * ANY summation order of ss.  Every order's binary64 sum of the K nonnegative
+ * squares lies within (K-1)*2^-53/(1-(K-1)*2^-53) of the exact sum, so within
+ * the band ss*(1 -+ delta), delta = 2*(K+1)*2^-53, around this one; r is a
+ * monotone function of ss and so is every correctly rounded step, hence the
+ * band's ends bound every order's r32. */
+static float rms_r32(double ss, int64_t K, float eps) {
+    double v = ss / (double)K + (double)eps;
+    return (float)(1.0 / sqrt(v));
+}
+
+void oracle_rms_scale(const void *x, int x_dtype, int64_t M, int64_t K, float eps, float *r32,
+                      float *r32_lo, float *r32_hi) {
+    double delta = 2.0 * (double)(K + 1) * ldexp(1.0, -53);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double xv = (double)load_x(x, x_dtype, i * K + k);
+            ss += xv * xv;
+        }
+        r32[i] = rms_r32(ss, K, eps);
+        float a = rms_r32(ss * (1.0 - delta), K, eps), b = rms_r32(ss * (1.0 + delta), K, eps);
+        r32_lo[i] = a < b ? a : b;
+        r32_hi[i] = a < b ? b : a;
+    }
+}
+
+/* xn[i][k] = f32(f32(x[i][k] * r32[i]) * g[k]) */
+void oracle_rmsnorm(const void *x, int x_dtype, const float *g, const float *r32, int64_t M,
+                    int64_t K, float *xn) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t k = 0; k < K; k++) {
+            float t = load_x(x, x_dtype, i * K + k) * r32[i];
+            xn[i * K + k] = t * g[k];
+        }
+}
+
+/* h[i] = silu(gate[i]) * up[i] in binary64, silu(z) = z / (1 + exp(-z)). */
+void oracle_swiglu(const double *gate, const double *up, int64_t n, double *h) {
+    for (int64_t i = 0; i < n; i++) {
+        double z = gate[i];
+        double silu = z / (1.0 + exp(-z));
+        h[i] = silu * up[i];
+    }
+}

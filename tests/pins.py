@@ -23,7 +23,12 @@ mathematics fix:
     textbook integer case,
   * for the per-256 activation variant: quantiser properties, agreement with
     the per-32 oracle where the two encodings coincide, brute force and the
-    textbook integer case.
+    textbook integer case,
+  * for RMSNorm -> quantiser: closed forms (one nonzero value, constant rows,
+    a zero row), numpy's fp64 formula within three fp32 roundings, unit mean
+    square, power-of-two and sign covariance, row independence,
+  * for SwiGLU: silu written with tanh, its limits, and brute force over the
+    stacked gate/up product.
 
 The mutation tests plant plausible mistakes in a copy of oracle.c and require
 that at least one of these functions fails for each.
@@ -553,6 +558,155 @@ def pin_a256_gemm_textbook(orc):
                           y[np.ix_(rows, cols)])
 
 
+# ------------------------------------------- RMSNorm -> quantiser, and SwiGLU
+
+def pin_rms_single_nonzero(orc):
+    """One nonzero value a (a power of two) in a row of K = 1024, eps = 0: the
+    mean square is a^2/1024, so r = 32/|a| exactly and xn = -32*g there (a < 0),
+    0 elsewhere; the quantiser maps that value to -127*sign(g)."""
+    K = 1024
+    g = synth.normal(901, (K,), 0.0, 1.0).astype(np.float32)
+    x = np.zeros((2, K), np.float32)
+    x[0, 37] = np.float32(-0.5)
+    x[1, 1000] = np.float32(2.0 ** -40)
+    r, lo, hi = orc.rms_scale(x, 0.0)
+    assert r[0] == 64.0 and r[1] == np.float32(2.0 ** 45)
+    assert np.array_equal(lo, r) and np.array_equal(hi, r)
+    xn = orc.rmsnorm(x, g, r)
+    assert xn[0, 37] == np.float32(-32.0) * g[37] and xn[1, 1000] == np.float32(32.0) * g[1000]
+    assert np.count_nonzero(xn[0]) == 1 and np.count_nonzero(xn[1]) == 1
+    q, d, S, amb, _ = orc.rmsnorm_quantize(x, g, 0.0)
+    assert not amb.any()
+    assert q[0, 37] == -127 * np.sign(g[37]) and q[1, 1000] == 127 * np.sign(g[1000])
+    assert np.count_nonzero(q) == 2 and S[0, 1] == q[0, 37]
+
+
+def pin_rms_constant_rows(orc):
+    """x = c on the whole row, eps = 0: r = 1/|c| and xn = sign(c)*g (exactly for
+    a power of two c, within one fp32 rounding of each of the three steps else)."""
+    K = 512
+    g = synth.normal(902, (K,), 0.0, 2.0).astype(np.float32)
+    cs = np.array([0.25, -8.0, 3.0, -0.7, 1e-20, 1e20], np.float32)
+    x = np.repeat(cs[:, None], K, axis=1)
+    r, _, _ = orc.rms_scale(x, 0.0)
+    xn = orc.rmsnorm(x, g, r).astype(np.float64)
+    ref = np.sign(cs.astype(np.float64))[:, None] * g.astype(np.float64)[None, :]
+    assert np.array_equal(xn[:2], ref[:2])
+    assert np.all(np.abs(xn - ref) <= 4 * 2.0 ** -24 * np.abs(ref))
+
+
+def pin_rms_zero_row_and_eps(orc):
+    """A zero row gives r = f32(1/sqrt(eps)), xn = 0 and all-zero blocks; eps
+    enters as v = mean + eps (a row far below eps is scaled by ~1/sqrt(eps))."""
+    K, eps = 256, 1e-6
+    g = np.full(K, 1.0, np.float32)
+    x = np.zeros((2, K), np.float32)
+    x[1] = np.float32(1e-9)
+    r, _, _ = orc.rms_scale(x, eps)
+    e64 = float(np.float32(eps))
+    assert r[0] == np.float32(1.0 / np.sqrt(e64))
+    assert abs(float(r[1]) - 1.0 / np.sqrt(e64 + float(np.float32(1e-9)) ** 2)) <= 2.0 ** -23 * float(r[1])
+    q, d, S, _, _ = orc.rmsnorm_quantize(x, g, eps)
+    assert not q[0].any() and not d[0].any() and not S[0].any()
+    assert np.all(np.abs(q[1]) == 127)
+
+
+def pin_rms_against_numpy(orc):
+    """Random rows of several lengths (fp32 and bf16 input, with eps): xn within
+    three fp32 roundings of x*g/sqrt(mean(x^2)+eps) evaluated by numpy in fp64;
+    the normalised rows have unit mean square (eps = 0)."""
+    for K, eps, seed in ((256, 1e-6, 903), (1024, 1e-5, 904), (4096, 0.0, 905)):
+        x = _acts(seed, 5, K, scale=3.0)
+        x[2] *= np.float32(1e-3)
+        g = synth.normal(seed + 1, (K,), 1.0, 0.3).astype(np.float32)
+        for xin in (x, synth.to_bf16_bits(x)):
+            xf = xin if xin.dtype == np.float32 else synth.bf16_bits_to_f32(xin)
+            r, lo, hi = orc.rms_scale(xin, eps)
+            assert np.all(lo <= r) and np.all(r <= hi)
+            xn = orc.rmsnorm(xin, g, r).astype(np.float64)
+            x64 = xf.astype(np.float64)
+            ref = x64 * g.astype(np.float64) / np.sqrt((x64 ** 2).mean(1, keepdims=True) + float(np.float32(eps)))
+            assert np.all(np.abs(xn - ref) <= 3 * 2.0 ** -24 * np.abs(ref) + 1e-300)
+            if eps == 0.0:
+                ms = ((xn / g.astype(np.float64)) ** 2).mean(1)
+                assert np.all(np.abs(ms - 1.0) < 1e-6)
+
+
+def pin_rms_scale_invariance_and_rows(orc):
+    """eps = 0: scaling a row by a power of two leaves xn unchanged and negating
+    it negates xn; each row is normalised by its own statistics only."""
+    K = 768
+    x = _acts(906, 4, K)
+    g = synth.normal(907, (K,), 0.0, 1.0).astype(np.float32)
+    q, d, S, _, _ = orc.rmsnorm_quantize(x, g, 0.0)
+    for k in (-30, 7):
+        q2, d2, S2, _, _ = orc.rmsnorm_quantize((x * np.float32(2.0 ** k)).astype(np.float32), g, 0.0)
+        assert np.array_equal(q2, q) and np.array_equal(d2, d) and np.array_equal(S2, S)
+    q3, d3, S3, _, _ = orc.rmsnorm_quantize(-x, g, 0.0)
+    assert np.array_equal(q3, -q) and np.array_equal(d3, d)
+    x4 = x.copy()
+    x4[1:] *= np.float32(5.0)
+    q4, d4, _, _, _ = orc.rmsnorm_quantize(x4, g, 0.0)
+    assert np.array_equal(q4[0], q[0]) and np.array_equal(d4[0], d[0])
+
+
+def pin_rms_order_band(orc):
+    """The sum of squares in another order can give another r32: a row of 1000
+    small values (each square under a quarter of the big value's spacing) and
+    one big value last.  Summed in row order the small squares survive and
+    r32 = 1; summed big value first each is rounded away and r32 = 1 + 2^-23.
+    Both orders' r32 must lie in the oracle's band."""
+    K = 4096
+    x = np.zeros((1, K), np.float32)
+    x[0, :1000] = np.float32(1.5 * 2.0 ** -22)
+    x[0, K - 1] = np.float32(64.0 * (1.0 - 2.0 ** -24))
+    r, lo, hi = orc.rms_scale(x, 0.0)
+    sq = [float(t) * float(t) for t in x[0]]
+    got = []
+    for order in (sq, sq[::-1]):
+        ss = 0.0
+        for t in order:
+            ss += t
+        got.append(np.float32(1.0 / np.sqrt(ss / K)))
+    assert got[0] != got[1]
+    assert r[0] == got[0] and lo[0] <= min(got) and max(got) <= hi[0]
+
+
+def pin_swiglu_closed_forms(orc):
+    """silu(z) = z * (1 + tanh(z/2)) / 2 (the logistic function written with
+    tanh), silu(0) = 0, silu(z) -> z for large z and -> 0 (no NaN) for very
+    negative z."""
+    z = np.linspace(-30.0, 30.0, 601)
+    u = synth.normal(908, (601,), 0.0, 2.0).astype(np.float64)
+    h = orc.swiglu(z, u)
+    ref = z * (1.0 + np.tanh(z / 2.0)) / 2.0 * u
+    assert np.all(np.abs(h - ref) <= 1e-14 * np.abs(z * u) + 1e-300)
+    h = orc.swiglu(np.array([0.0, 800.0, -800.0, 40.0, -1.0]), np.array([5.0, 2.0, 3.0, 1.0, 1.0]))
+    assert h[0] == 0.0 and h[1] == 1600.0 and h[2] == 0.0 and h[3] == 40.0
+    assert abs(h[4] - (-1.0 / (1.0 + np.e))) <= 1e-16
+
+
+def pin_gemm_swiglu_bruteforce(orc):
+    """SwiGLU over the stacked [gate; up] weight rows: brute force from the
+    quantised activations and the dequantised weights in fp64, gate = columns
+    0..F-1 and up = F..2F-1 of the stacked product."""
+    for fmt, (M, F, K, seed) in ((Q4_K, (3, 5, 512, 1)), (Q6_K, (2, 4, 256, 2))):
+        W = synth.random_blocks(fmt, 2 * F, K, seed=910 + seed, emin=3, emax=18)
+        x = _acts(920 + seed, M, K, scale=4.0)
+        h, g, u = orc.gemm_swiglu(fmt, W, x, F)
+        xh = _dequant_acts(orc, x)
+        w = orc.dequant(fmt, W, 2 * F, K)
+        y = xh @ w.T
+        gate, up = y[:, :F], y[:, F:]
+        scale = np.abs(xh) @ np.abs(w).T
+        assert np.all(np.abs(g - gate) <= 1e-12 * scale[:, :F]) and np.all(np.abs(u - up) <= 1e-12 * scale[:, F:])
+        ref = gate * (1.0 + np.tanh(gate / 2.0)) / 2.0 * up
+        assert np.all(np.abs(h - ref) <= 1e-9 * (scale[:, :F] * scale[:, F:] + 1e-300))
+        rows, cols = np.array([M - 1, 0]), np.array([F - 1, 1, 1])
+        hs, _, _ = orc.gemm_swiglu(fmt, W, x, F, rows=rows, cols=cols)
+        assert np.array_equal(hs, h[np.ix_(rows, cols)])
+
+
 ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bit_probe,
             pin_q6k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
             pin_quant_symmetry_and_scaling, pin_quant_integer_blocks, pin_quant_bf16_matches_f32,
@@ -561,4 +715,8 @@ ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bi
             pin_f16_rounding, pin_f16_activations, pin_f16_dequant_worked_examples,
             pin_f16_dequant_rounding, pin_f16_gemm_bruteforce, pin_f16_gemm_textbook,
             pin_a256_quantiser_properties, pin_a256_matches_per32_when_scales_agree,
-            pin_a256_gemm_bruteforce, pin_a256_gemm_textbook]
+            pin_a256_gemm_bruteforce, pin_a256_gemm_textbook,
+            pin_rms_single_nonzero, pin_rms_constant_rows, pin_rms_zero_row_and_eps,
+            pin_rms_against_numpy, pin_rms_scale_invariance_and_rows, pin_rms_order_band,
+            pin_swiglu_closed_forms,
+            pin_gemm_swiglu_bruteforce]

@@ -105,6 +105,33 @@ MUTANTS = [
     ("a256_scale_of_next_superblock",
      "                acc += (double)dx[i * nsb + sb] * part;",
      "                acc += (double)dx[i * nsb + (sb + 1) % nsb] * part;"),
+    ("rms_mean_not_divided",
+     "double v = ss / (double)K + (double)eps;",
+     "double v = ss + (double)eps;"),
+    ("rms_eps_dropped",
+     "double v = ss / (double)K + (double)eps;",
+     "double v = ss / (double)K;"),
+    ("rms_no_square_root",
+     "return (float)(1.0 / sqrt(v));",
+     "return (float)(1.0 / v);"),
+    ("rms_band_too_narrow",
+     "double delta = 2.0 * (double)(K + 1) * ldexp(1.0, -53);",
+     "double delta = 0.0;"),
+    ("rms_weight_dropped",
+     "xn[i * K + k] = t * g[k];",
+     "xn[i * K + k] = t;"),
+    ("rms_weight_reversed",
+     "xn[i * K + k] = t * g[k];",
+     "xn[i * K + k] = t * g[K - 1 - k];"),
+    ("rms_squares_of_row_zero",
+     "double xv = (double)load_x(x, x_dtype, i * K + k);",
+     "double xv = (double)load_x(x, x_dtype, k);"),
+    ("swiglu_logistic_sign",
+     "double silu = z / (1.0 + exp(-z));",
+     "double silu = z / (1.0 + exp(z));"),
+    ("swiglu_gate_up_swapped",
+     "        double z = gate[i];\n        double silu = z / (1.0 + exp(-z));\n        h[i] = silu * up[i];",
+     "        double z = up[i];\n        double silu = z / (1.0 + exp(-z));\n        h[i] = silu * gate[i];"),
     ("gemm_f16_abs_sum_signed",
      "aabs += fabs(p);",
      "aabs += p;"),
