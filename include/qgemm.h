@@ -230,6 +230,69 @@ int qgemm_to_f16(const void *x, int x_dtype, int64_t M, int64_t K, uint16_t *x16
 int qgemm_dequant_f16(const void *q_weights, int fmt, int64_t N, int64_t K, uint16_t *w16,
                       void *stream);
 
+/* ---- fusions either side of the GEMM ----
+ *
+ * aprender issue #4220 ("CRUX parity spike: apr serve vs ollama"), table of the
+ * techniques llama.cpp uses that apr lacks: technique 2 counts a layer's
+ * per-token launches, its norms and its swiglu among them; technique 6 is the
+ * norm fused with the multiply by its weight.  sparkinfer PR #464, section
+ * "Summary": the cost removed is the projection path's scratch written and
+ * read back.  Here the norm is fused into the activation quantiser (the
+ * normalised row never reaches memory) and SwiGLU into the gate+up GEMM's
+ * epilogue (the fp32 gate and up outputs never reach memory; h is written as
+ * bfloat16, 2 bytes per value against 8 for the two fp32 outputs). */
+
+/* RMSNorm of each row of x [M][K] with the fp32 weight g [K] and epsilon eps,
+ * then the per-32 quantiser of qgemm_quantize_workspace, into `workspace`
+ * (sized by qgemm_workspace_bytes(M, K)); qgemm_gemm_quantized and
+ * qgemm_gemm_quantized_swiglu take the workspace as from that function.
+ * Numerics (the standard RMSNorm; the pages print no formula):
+ *   ss = sum_k x_k^2 in binary64 (each square exact), r = f32(1/sqrt(ss/K + eps))
+ *   with binary64 steps, xn_k = f32(f32(x_k * r) * g_k), then the quantiser on xn.
+ * The order of the binary64 sum is the kernel's; another order can change r
+ * only where r lies within a few binary64 units of an fp32 rounding boundary.
+ * Rules: 256 <= K <= 32768, K % 256 == 0; 1 <= M <= 2^31 - 1; eps finite and
+ * >= 0 (QG_EINVAL otherwise); x and g 16-byte aligned (QG_EALIGN); other
+ * arguments and codes as qgemm_quantize_workspace. */
+int qgemm_rmsnorm_quantize_workspace(const void *x, int x_dtype, const float *g, float eps, int64_t M,
+                                     int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+/* Test hook: the same into the layout of qgemm_quantize_act (q [M][K] int8,
+ * d [M][K/32] fp32, S [M][K/32] int32). */
+int qgemm_rmsnorm_quantize_act(const void *x, int x_dtype, const float *g, float eps, int64_t M,
+                               int64_t K, int8_t *q, float *d, int32_t *S, void *stream);
+
+/* SwiGLU over a gate+up projection.  q_weights holds 2F weight rows of length
+ * K: the gate rows (0..F-1), then the up rows (F..2F-1), i.e. the two GGUF
+ * tensors stacked.  With y = x . W^T under the method's quantisation ([M][2F]):
+ *   h[m][f] = bf16( silu(y[m][f]) * y[m][F + f] ),  silu(z) = z / (1 + e^-z),
+ * in fp32 from the fp32 GEMM result, rounded once to bfloat16 (nearest even).
+ * h is bfloat16 bits [M][F], 16-byte aligned.  Q4_K problems on the tiled
+ * kernels run as ONE kernel (the gate and up columns of an output tile are
+ * computed by paired waves and combined in LDS); decode-sized batches (the
+ * skinny path), small grids and Q6_K weights run the plain GEMM into the
+ * workspace, then a SwiGLU kernel. */
+
+/* Workspace bytes for the SwiGLU entry points: the quantised activations and,
+ * where the problem does not run fused, the fp32 [M][2F] GEMM output.  0 for a
+ * bad format, M, F < 1, K < 256, K % 256 != 0 or on overflow. */
+size_t qgemm_swiglu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K);
+/* h from a workspace filled by qgemm_quantize_workspace or
+ * qgemm_rmsnorm_quantize_workspace with the same M and K (argument rules and
+ * codes as qgemm_gemm_quantized with N = 2F, path AUTO; workspace sized by
+ * qgemm_swiglu_workspace_bytes). */
+int qgemm_gemm_quantized_swiglu(const void *q_weights, int fmt, const void *workspace,
+                                size_t workspace_bytes, int64_t M, int64_t F, int64_t K, uint16_t *h,
+                                void *stream);
+/* Quantise x, then qgemm_gemm_quantized_swiglu (rules as qgemm_prefill). */
+int qgemm_prefill_swiglu(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M, int64_t F,
+                         int64_t K, uint16_t *h, void *workspace, size_t workspace_bytes, void *stream);
+/* Name of the kernel the SwiGLU entry points launch for the GEMM (the fused
+ * kernel, or the plain GEMM kernel that precedes the SwiGLU kernel), or NULL. */
+const char *qgemm_kernel_name_swiglu(int fmt, int64_t M, int64_t F, int64_t K);
+/* The SwiGLU step alone: h [M][F] from the fp32 gate+up output y [M][2F] (y
+ * and h 16-byte aligned; M * F <= 2^38). */
+int qgemm_swiglu(const float *y, int64_t M, int64_t F, uint16_t *h, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

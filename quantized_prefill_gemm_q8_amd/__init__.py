@@ -27,7 +27,10 @@ SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_
            "qgemm_block_partials", "qgemm_deq_f16_workspace_bytes", "qgemm_prefill_deq_f16",
            "qgemm_deq_f16_kernel_name", "qgemm_to_f16", "qgemm_dequant_f16",
            "qgemm_quantize_workspace_a256", "qgemm_gemm_quantized_a256", "qgemm_prefill_a256",
-           "qgemm_kernel_name_a256", "qgemm_quantize_act_a256")
+           "qgemm_kernel_name_a256", "qgemm_quantize_act_a256",
+           "qgemm_rmsnorm_quantize_workspace", "qgemm_rmsnorm_quantize_act",
+           "qgemm_swiglu_workspace_bytes", "qgemm_gemm_quantized_swiglu", "qgemm_prefill_swiglu",
+           "qgemm_kernel_name_swiglu", "qgemm_swiglu")
 
 
 class QgemmError(RuntimeError):
@@ -94,6 +97,21 @@ def load() -> ctypes.CDLL:
         lib.qgemm_kernel_name_a256.restype = ctypes.c_char_p
         lib.qgemm_quantize_act_a256.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
         lib.qgemm_quantize_act_a256.restype = ci
+        f32 = ctypes.c_float
+        lib.qgemm_rmsnorm_quantize_workspace.argtypes = [vp, ci, vp, f32, i64, i64, vp, sz, vp]
+        lib.qgemm_rmsnorm_quantize_workspace.restype = ci
+        lib.qgemm_rmsnorm_quantize_act.argtypes = [vp, ci, vp, f32, i64, i64, vp, vp, vp, vp]
+        lib.qgemm_rmsnorm_quantize_act.restype = ci
+        lib.qgemm_swiglu_workspace_bytes.argtypes = [ci, i64, i64, i64]
+        lib.qgemm_swiglu_workspace_bytes.restype = sz
+        lib.qgemm_gemm_quantized_swiglu.argtypes = [vp, ci, vp, sz, i64, i64, i64, vp, vp]
+        lib.qgemm_gemm_quantized_swiglu.restype = ci
+        lib.qgemm_prefill_swiglu.argtypes = [vp, ci, vp, ci, i64, i64, i64, vp, vp, sz, vp]
+        lib.qgemm_prefill_swiglu.restype = ci
+        lib.qgemm_kernel_name_swiglu.argtypes = [ci, i64, i64, i64]
+        lib.qgemm_kernel_name_swiglu.restype = ctypes.c_char_p
+        lib.qgemm_swiglu.argtypes = [vp, i64, i64, vp, vp]
+        lib.qgemm_swiglu.restype = ci
         _lib = lib
     return _lib
 
@@ -244,6 +262,45 @@ def qgemm_to_f16(x, M, K, x16, stream=None):
 def qgemm_dequant_f16(q_weights, fmt, N, K, w16, stream=None):
     _check(load().qgemm_dequant_f16(_ptr(q_weights), fmt, N, K, _ptr(w16), _stream(stream)),
            "qgemm_dequant_f16")
+
+
+# ---- fusions either side of the GEMM: RMSNorm -> quantiser, SwiGLU epilogue ----
+
+def qgemm_rmsnorm_quantize_workspace(x, g, eps, M, K, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_rmsnorm_quantize_workspace(_ptr(x), _dtype_code(x), _ptr(g), float(eps), M, K,
+                                                   _ptr(workspace), ws_bytes, _stream(stream)),
+           "qgemm_rmsnorm_quantize_workspace")
+
+
+def qgemm_rmsnorm_quantize_act(x, g, eps, M, K, q, d, S, stream=None):
+    _check(load().qgemm_rmsnorm_quantize_act(_ptr(x), _dtype_code(x), _ptr(g), float(eps), M, K, _ptr(q),
+                                             _ptr(d), _ptr(S), _stream(stream)), "qgemm_rmsnorm_quantize_act")
+
+
+def qgemm_swiglu_workspace_bytes(fmt: int, M: int, F: int, K: int) -> int:
+    return int(load().qgemm_swiglu_workspace_bytes(fmt, M, F, K))
+
+
+def qgemm_gemm_quantized_swiglu(q_weights, fmt, workspace, M, F, K, h, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_gemm_quantized_swiglu(_ptr(q_weights), fmt, _ptr(workspace), ws_bytes, M, F, K,
+                                              _ptr(h), _stream(stream)), "qgemm_gemm_quantized_swiglu")
+
+
+def qgemm_prefill_swiglu(q_weights, fmt, x, M, F, K, h, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qgemm_prefill_swiglu(_ptr(q_weights), fmt, _ptr(x), _dtype_code(x), M, F, K, _ptr(h),
+                                       _ptr(workspace), ws_bytes, _stream(stream)), "qgemm_prefill_swiglu")
+
+
+def qgemm_kernel_name_swiglu(fmt: int, M: int, F: int, K: int) -> str | None:
+    r = load().qgemm_kernel_name_swiglu(fmt, M, F, K)
+    return None if r is None else r.decode()
+
+
+def qgemm_swiglu(y, M, F, h, stream=None):
+    _check(load().qgemm_swiglu(_ptr(y), M, F, _ptr(h), _stream(stream)), "qgemm_swiglu")
 
 
 # ---- plumbing helpers: device buffers for callers that do not manage their own ----

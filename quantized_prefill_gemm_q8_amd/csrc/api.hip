@@ -363,4 +363,125 @@ const char* qgemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) 
   return qg_gemm_deq_f16_kernel_name(fmt, M, N, K);
 }
 
+// ---- fusions either side of the GEMM: RMSNorm -> quantiser, SwiGLU epilogue ----
+
+static int check_rms(const void* x, int x_dtype, const float* g, float eps, int64_t M, int64_t K) {
+  if (!x || !g || M < 1 || M > INT64_C(0x7FFFFFFF)) return QG_EINVAL;  // one workgroup per row
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  if (K < 256 || K % 256 != 0 || K > kRmsMaxK) return QG_EINVAL;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return QG_EINVAL;  // NaN, negative or infinite eps
+  if (!aligned(x, 16) || !aligned(g, 16)) return QG_EALIGN;
+  return QG_OK;
+}
+
+int qgemm_rmsnorm_quantize_workspace(const void* x, int x_dtype, const float* g, float eps, int64_t M,
+                                     int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_rms(x, x_dtype, g, eps, M, K);
+  if (rc) return rc;
+  Layout L;
+  if (!layout_for(M, K, &L)) return QG_EINVAL;
+  rc = check_workspace(workspace, workspace_bytes, L);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  const QgWorkspace ws = carve(workspace, L);
+  return launch_status(qg_launch_rmsnorm_quant_ws(x, x_dtype, g, eps, M, K, ws, static_cast<hipStream_t>(stream)));
+}
+
+int qgemm_rmsnorm_quantize_act(const void* x, int x_dtype, const float* g, float eps, int64_t M, int64_t K,
+                               int8_t* q, float* d, int32_t* S, void* stream) {
+  int rc = check_rms(x, x_dtype, g, eps, M, K);
+  if (rc) return rc;
+  if (!q || !d || !S) return QG_EINVAL;
+  if (M > (INT64_C(1) << 40) / K) return QG_EINVAL;
+  if (!aligned(q, 8) || !aligned(d, 4) || !aligned(S, 4)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_rmsnorm_quant_hook(x, x_dtype, g, eps, M, K, q, d, S,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+// The gate+up GEMM with the SwiGLU epilogue runs fused for Q4_K weights on the
+// LDS-tiled kernels; otherwise the plain GEMM writes the fp32 gate+up output
+// into the workspace after the quantised activations and the SwiGLU kernel
+// reads it from there.
+static bool swiglu_fused(int fmt, int64_t M, int64_t F, int64_t K) {
+  return fmt == QG_Q4_K && !auto_skinny(fmt, M) && qg_q4k_swiglu_fusable(M, F, K);
+}
+
+static bool swiglu_layout(int fmt, int64_t M, int64_t F, int64_t K, Layout* L, int64_t* total) {
+  if (F < 1 || F > (INT64_C(1) << 39) / K) return false;  // 2F * K <= 2^40
+  if (!layout_for(M, K, L)) return false;
+  if (M > (INT64_C(1) << 38) / F) return false;             // M * 2F * 4 bytes <= 2^41
+  *total = L->total + (swiglu_fused(fmt, M, F, K) ? 0 : (M * 2 * F * 4 + 255) / 256 * 256);
+  return true;
+}
+
+size_t qgemm_swiglu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K) {
+  if (fmt != QG_Q4_K && fmt != QG_Q6_K) return 0;
+  Layout L;
+  int64_t total;
+  if (!swiglu_layout(fmt, M, F, K, &L, &total)) return 0;
+  return static_cast<size_t>(total);
+}
+
+int qgemm_gemm_quantized_swiglu(const void* q_weights, int fmt, const void* workspace,
+                                size_t workspace_bytes, int64_t M, int64_t F, int64_t K, uint16_t* h,
+                                void* stream) {
+  if (F < 1 || F > (INT64_C(1) << 39) / 256) return QG_EINVAL;
+  int rc = check_common(q_weights, fmt, 2 * F, K);
+  if (rc) return rc;
+  if (!h || M < 1) return QG_EINVAL;
+  Layout L;
+  int64_t total;
+  if (!swiglu_layout(fmt, M, F, K, &L, &total)) return QG_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < static_cast<size_t>(total)) return QG_EWORKSPACE;
+  if (!aligned(h, 16)) return QG_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
+  const uint8_t* W = static_cast<const uint8_t*>(q_weights);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (swiglu_fused(fmt, M, F, K)) return launch_status(qg_launch_gemm_q4k_swiglu(W, ws, M, F, K, h, s));
+  float* y = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) + L.total);
+  if (auto_skinny(fmt, M)) rc = launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, 2 * F, K, y, s));
+  else rc = launch_status(fmt == QG_Q4_K ? qg_launch_gemm_q4k(W, ws, M, 2 * F, K, y, s)
+                                         : qg_launch_gemm_q6k(W, ws, M, 2 * F, K, y, s));
+  if (rc) return rc;
+  return launch_status(qg_launch_swiglu(y, M, F, h, s));
+}
+
+int qgemm_prefill_swiglu(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M, int64_t F,
+                         int64_t K, uint16_t* h, void* workspace, size_t workspace_bytes, void* stream) {
+  // validate everything the GEMM half checks before launching the quantiser
+  if (F < 1 || F > (INT64_C(1) << 39) / 256) return QG_EINVAL;
+  int rc = check_common(q_weights, fmt, 2 * F, K);
+  if (rc) return rc;
+  if (!x || !h || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F32 && x_dtype != QG_BF16) return QG_EDTYPE;
+  Layout L;
+  int64_t total;
+  if (!swiglu_layout(fmt, M, F, K, &L, &total)) return QG_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < static_cast<size_t>(total)) return QG_EWORKSPACE;
+  if (!aligned(x, 16) || !aligned(h, 16)) return QG_EALIGN;
+  rc = qgemm_quantize_workspace(x, x_dtype, M, K, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  return qgemm_gemm_quantized_swiglu(q_weights, fmt, workspace, workspace_bytes, M, F, K, h, stream);
+}
+
+const char* qgemm_kernel_name_swiglu(int fmt, int64_t M, int64_t F, int64_t K) {
+  if ((fmt != QG_Q4_K && fmt != QG_Q6_K) || M < 1 || F < 1 || K < 256 || K % 256 != 0) return NULL;
+  if (F > (INT64_C(1) << 39) / K) return NULL;
+  if (swiglu_fused(fmt, M, F, K)) return qg_gemm_q4k_swiglu_kernel_name(M, F, K);
+  return qgemm_kernel_name(fmt, M, 2 * F, K, QG_PATH_AUTO);
+}
+
+int qgemm_swiglu(const float* y, int64_t M, int64_t F, uint16_t* h, void* stream) {
+  if (!y || !h || M < 1 || F < 1 || M > (INT64_C(1) << 38) / F) return QG_EINVAL;
+  if (!aligned(y, 16) || !aligned(h, 16)) return QG_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_swiglu(y, M, F, h, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

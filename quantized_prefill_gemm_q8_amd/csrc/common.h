@@ -92,6 +92,21 @@ __device__ __forceinline__ uint16_t load_u16(const uint8_t* p) {
 // still read (measured 1-5% faster on the workloads' shapes).
 __device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
+// fp32 -> bfloat16 bits, rounded to nearest with ties to even (a NaN stays a
+// quiet NaN; values past the largest bfloat16 round to infinity).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((b >> 16) | 0x0040u);
+  return static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// SwiGLU of one gate/up pair: silu(g) * u with silu(g) = g / (1 + e^-g), in
+// fp32, rounded once to bfloat16.  e^-g overflowing to infinity (g < -88)
+// gives silu = -0, as the limit.
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
+  return f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
+}
+
 }  // namespace qg
 
 // ---- workspace: the quantised activations, as the GEMM kernels read them ----
@@ -131,6 +146,21 @@ hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& w
 // Name of the kernel each launcher picks for a problem (diagnostics: matches
 // the kernel names a profiler reports).
 const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256 = false);
+// Q4_K gate+up GEMM with the SwiGLU epilogue (W: 2F rows, gate then up; h:
+// bfloat16 [M][F]).  Fusable when the problem takes one of the LDS-tiled
+// kernels and the weight offsets fit the kernels' 32-bit load offsets.
+bool qg_q4k_swiglu_fusable(int64_t M, int64_t F, int64_t K);
+hipError_t qg_launch_gemm_q4k_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F,
+                                     int64_t K, uint16_t* h, hipStream_t stream);
+const char* qg_gemm_q4k_swiglu_kernel_name(int64_t M, int64_t F, int64_t K);
+// h [M][F] = bfloat16(silu(y[m][f]) * y[m][F + f]) from y [M][2F] fp32
+hipError_t qg_launch_swiglu(const float* y, int64_t M, int64_t F, uint16_t* h, hipStream_t stream);
+// RMSNorm fused into the per-32 quantiser (K <= kRmsMaxK)
+constexpr int64_t kRmsMaxK = 32768;
+hipError_t qg_launch_rmsnorm_quant_ws(const void* x, int x_dtype, const float* g, float eps, int64_t M,
+                                      int64_t K, const QgWorkspace& ws, hipStream_t stream);
+hipError_t qg_launch_rmsnorm_quant_hook(const void* x, int x_dtype, const float* g, float eps, int64_t M,
+                                        int64_t K, int8_t* q, float* d, int32_t* S, hipStream_t stream);
 const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t K);
 const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t qg_launch_dequant(const uint8_t* W, int fmt, int64_t N, int64_t K, float* w,

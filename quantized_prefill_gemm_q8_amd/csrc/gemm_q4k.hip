@@ -84,11 +84,18 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 // eight sub-block partials of a super-block are combined in integers,
 // J = sum_j sc[j] * I[j] (v_mad_i32_i24 per element and block; |J| < 2^25), and
 // the fp32 epilogue runs once per super-block: acc += fl(fl(J) * d) * dx.
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC, int KS, bool A256 = false>
-__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_lds_kernel(
+// SW: SwiGLU epilogue over a gate+up weight stacked as [gate (F rows); up (F
+// rows)] (N = 2F).  A block computes BN/2 output columns f: its tile columns
+// 0..BN/2-1 are the gate rows f and BN/2..BN-1 the up rows F + f, so the
+// waves wn < WN/2 hold gate values and the waves wn + WN/2 the up values of
+// the same (row, column) in the same lane and register; the latter pass them
+// through LDS and the former write h = silu(gate) * up as bfloat16 [M][F].
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int KS, bool A256, bool SW>
+__device__ __forceinline__ void q4k_lds_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ y) {
+    int64_t N, int64_t K, float* __restrict__ y, uint16_t* __restrict__ hout, int64_t F) {
+  static_assert(!SW || (WN % 2 == 0 && !A256 && !DPP), "SwiGLU pairs waves wn and wn + WN/2");
   constexpr int NW = WM * WN;  // waves per group
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * BN;
+  const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * (SW ? BN / 2 : BN);  // first weight row / column
   const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
   const int64_t nsb = K / 256, nb = K / 32;
   const int64_t wrow_bytes = nsb * kQ4Bytes;
@@ -137,7 +144,14 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 #pragma unroll
   for (int it = 0; it < LW; it++) {
     const int qq = ((wave + it * NW) % W_WL) * 64 + lane, row = qq / 9, part = qq - 9 * row;
-    const int64_t n = n_cta + row < N ? n_cta + row : N - 1;
+    int64_t n;
+    if constexpr (SW) {  // tile column row -> gate row f or up row F + f
+      const int o = row % (BN / 2);
+      const int64_t f = n_cta + o < F ? n_cta + o : F - 1;
+      n = (row >= BN / 2 ? F : 0) + f;
+    } else {
+      n = n_cta + row < N ? n_cta + row : N - 1;
+    }
     voff[LA + it] = qq < W_CH ? static_cast<uint32_t>((n - n_cta) * wrow_bytes + 16 * part) : 0u;
   }
 #pragma unroll
@@ -370,21 +384,67 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     }
     __syncthreads();
-    if (grp > 0) return;
+    if constexpr (!SW) {
+      if (grp > 0) return;
+    }
+    if (grp == 0) {
 #pragma unroll
-    for (int g = 1; g < KS; g++)
+      for (int g = 1; g < KS; g++)
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+          for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const float4 v = red[((((g - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane];
+              acc[i][j][4 * q] += v.x;
+              acc[i][j][4 * q + 1] += v.y;
+              acc[i][j][4 * q + 2] += v.z;
+              acc[i][j][4 * q + 3] += v.w;
+            }
+    }
+  }
+
+  if constexpr (SW) {
+    // the up waves (wn >= WN/2) of group 0 leave their sums in LDS past the
+    // K-group reduction space; after the barrier each gate wave reads its
+    // partner's (same wm, wn + WN/2: the same rows and output columns)
+    constexpr int HW = WN / 2;
+    constexpr int XOFF = (KS - 1) * NW * TM * TN * 4096;
+    static_assert(XOFF + HW * WM * TM * TN * 4096 <= KS * NS * STAGE, "exchange space");
+    float4* xch = reinterpret_cast<float4*>(lds + XOFF);  // [WM][HW][TM][TN][4][64]
+    if constexpr (KS == 1) __syncthreads();  // no wave reads the stage ring any more
+    if (grp == 0 && wn >= HW) {
 #pragma unroll
       for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
+          for (int q = 0; q < 4; q++)
+            xch[((((wm * HW + wn - HW) * TM + i) * TN + j) * 4 + q) * 64 + lane] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+    __syncthreads();
+    if (grp == 0 && wn < HW) {
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        const int64_t f = n_cta + nl0 + 32 * j + l32;
+        if (f >= F) continue;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
           for (int q = 0; q < 4; q++) {
-            const float4 v = red[((((g - 1) * NW + wave) * TM + i) * TN + j) * 4 * 64 + q * 64 + lane];
-            acc[i][j][4 * q] += v.x;
-            acc[i][j][4 * q + 1] += v.y;
-            acc[i][j][4 * q + 2] += v.z;
-            acc[i][j][4 * q + 3] += v.w;
+            const float4 u4 = xch[((((wm * HW + wn) * TM + i) * TN + j) * 4 + q) * 64 + lane];
+            const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const int64_t m = m_cta + ml0 + 32 * i + acc_row(4 * q + e, h);
+              if (m < M) __builtin_nontemporal_store(swiglu_bf16(acc[i][j][4 * q + e], u[e]), hout + m * F + f);
+            }
           }
+      }
+    }
+    return;
   }
 
 #pragma unroll
@@ -399,6 +459,25 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
         if (m < M) store_out(y + m * N + n, acc[i][j][r]);
       }
   }
+}
+
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int OCC, int KS, bool A256 = false>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_lds_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
+    const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ y) {
+  q4k_lds_body<TM, TN, WM, WN, DPP, NS, KS, A256, false>(W, qx, dx, dxT, Mp, dsp, M, N, K, y, nullptr, 0);
+}
+
+// The same kernel with the SwiGLU epilogue: W holds 2F rows (gate, then up),
+// the output is h [M][F] in bfloat16.
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q4k_swiglu_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t F, int64_t K,
+    uint16_t* __restrict__ h) {
+  q4k_lds_body<TM, TN, WM, WN, false, NS, KS, false, true>(W, qx, nullptr, dxT, Mp, dsp, M, 2 * F, K, nullptr,
+                                                           h, F);
 }
 
 // ---------------------------------------------------------------- small-grid kernel
@@ -532,6 +611,15 @@ __global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
   }
 }
 
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+static void launch_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F, int64_t K,
+                          uint16_t* h, hipStream_t stream) {
+  constexpr int BM = 32 * TM * WM, BO = 16 * TN * WN;  // output columns per block: half the weight rows
+  const dim3 grid(static_cast<unsigned>((F + BO - 1) / BO), static_cast<unsigned>((M + BM - 1) / BM));
+  gemm_q4k_swiglu_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
+      W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, F, K, h);
+}
+
 template <int SK>
 static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                          float* y, hipStream_t stream) {
@@ -637,6 +725,42 @@ hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M
     case Q4Pick::kSmall2: qg::launch_small<2>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall4: qg::launch_small<4>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall8: qg::launch_small<8>(W, ws, M, N, K, y, stream); break;
+  }
+  return hipGetLastError();
+}
+
+// SwiGLU-fused gate+up projection: the block shapes the plain GEMM takes for
+// the 2F-column problem (a block covers half as many output columns, over the
+// gate and the up rows of each); problems on the small-grid kernel are not
+// fused.  Weight rows are addressed with 32-bit offsets from a block's first
+// gate row, so (F + 128) rows must span less than 4 GiB.
+bool qg_q4k_swiglu_fusable(int64_t M, int64_t F, int64_t K) {
+  if (F < 1 || (F + 128) * (K / 256) * qg::kQ4Bytes >= (INT64_C(1) << 32)) return false;
+  const Q4Pick p = pick_q4k(M, 2 * F, K);
+  return p == Q4Pick::kLds128x256 || p == Q4Pick::kLds64x128 || p == Q4Pick::kLds64x128K2 ||
+         p == Q4Pick::kLds32x64K4;
+}
+
+const char* qg_gemm_q4k_swiglu_kernel_name(int64_t M, int64_t F, int64_t K) {
+  if (!qg_q4k_swiglu_fusable(M, F, K)) return nullptr;
+  switch (pick_q4k(M, 2 * F, K)) {
+    case Q4Pick::kLds128x256: return "gemm_q4k_swiglu_kernel<2, 2, 2, 4, 2, 2, 1>";
+    case Q4Pick::kLds64x128: return "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>";
+    case Q4Pick::kLds64x128K2: return "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 2>";
+    case Q4Pick::kLds32x64K4: return "gemm_q4k_swiglu_kernel<1, 1, 1, 2, 2, 2, 4>";
+    default: return nullptr;
+  }
+}
+
+hipError_t qg_launch_gemm_q4k_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F,
+                                     int64_t K, uint16_t* h, hipStream_t stream) {
+  if (!qg_q4k_swiglu_fusable(M, F, K)) return hipErrorInvalidValue;
+  switch (pick_q4k(M, 2 * F, K)) {
+    case Q4Pick::kLds128x256: qg::launch_swiglu<2, 2, 2, 4, 2, 2, 1>(W, ws, M, F, K, h, stream); break;
+    case Q4Pick::kLds64x128: qg::launch_swiglu<1, 1, 2, 4, 2, 4, 1>(W, ws, M, F, K, h, stream); break;
+    case Q4Pick::kLds64x128K2: qg::launch_swiglu<1, 1, 2, 4, 2, 4, 2>(W, ws, M, F, K, h, stream); break;
+    case Q4Pick::kLds32x64K4: qg::launch_swiglu<1, 1, 1, 2, 2, 2, 4>(W, ws, M, F, K, h, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

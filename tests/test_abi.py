@@ -212,3 +212,45 @@ def test_deq_f16_branch_host_side():
     assert kn(1, 512, 2560, 4096) == "gemm_deq_f16_kernel<1, 4, 1, 1, 2, 2, 2, 3>"
     assert kn(1, 64, 1024, 1024) == "gemm_deq_f16_kernel<1, 1, 1, 1, 2, 2, 4, 4>"
     assert kn(1, 8192, 4096, 12288) == "gemm_deq_f16_kernel<1, 4, 1, 2, 8, 2, 4, 1>"
+
+
+def test_fusion_host_side():
+    """RMSNorm -> quantiser and the SwiGLU entry points: workspace sizing,
+    argument checks and kernel choice (no GPU call)."""
+    lib = qg.load()
+    wsz = qg.qgemm_swiglu_workspace_bytes
+    base = qg.qgemm_workspace_bytes
+    assert wsz(0, 512, 12288, 4096) == base(512, 4096)            # fused: no fp32 scratch
+    assert wsz(0, 512, 3584, 1024) == base(512, 1024)
+    assert wsz(1, 512, 1536, 4096) == base(512, 4096) + 512 * 3072 * 4   # Q6_K: GEMM + SwiGLU kernel
+    assert wsz(0, 3, 1000, 256) == base(3, 256) + (3 * 2000 * 4 + 255) // 256 * 256  # skinny
+    assert wsz(2, 4, 8, 256) == 0 and wsz(0, 0, 8, 256) == 0 and wsz(0, 4, 0, 256) == 0
+    assert wsz(0, 4, 8, 300) == 0
+    kn = qg.qgemm_kernel_name_swiglu
+    assert kn(0, 512, 3584, 1024) == "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 512, 12288, 4096) == "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 8192, 12288, 4096) == "gemm_q4k_swiglu_kernel<2, 2, 2, 4, 2, 2, 1>"
+    assert kn(0, 64, 512, 1024).startswith("gemm_q4k_small_kernel<")
+    assert kn(0, 3, 1000, 256).startswith("skinny_kernel<0, 3,")
+    assert kn(1, 512, 1536, 4096).startswith("gemm_q6k_lds_kernel<")
+    assert kn(2, 512, 8, 256) is None and kn(0, 512, 8, 300) is None
+    wsb = wsz(0, 4, 8, 256)
+    call = lambda **k: lib.qgemm_prefill_swiglu(
+        k.get("w", A), k.get("fmt", 0), k.get("x", A), k.get("xdt", 1), k.get("M", 4),
+        k.get("F", 8), k.get("K", 256), k.get("h", A), k.get("ws", A), k.get("wsb", wsb), None)
+    assert call(w=None) == -1 and call(M=0) == -1 and call(F=0) == -1 and call(K=300) == -1
+    assert call(h=None) == -1 and call(fmt=2) == -2 and call(xdt=3) == -3
+    assert call(ws=None) == -4 and call(wsb=wsb - 1) == -4
+    assert call(x=A + 2) == -5 and call(h=A + 2) == -5
+    assert lib.qgemm_gemm_quantized_swiglu(A, 0, A, wsb, 4, 8, 256, A + 8, None) == -5
+    assert lib.qgemm_swiglu(A, 4, 0, A, None) == -1 and lib.qgemm_swiglu(A + 4, 4, 8, A, None) == -5
+    rbytes = base(4, 512)
+    rms = lambda **k: lib.qgemm_rmsnorm_quantize_workspace(
+        k.get("x", A), k.get("xdt", 1), k.get("g", A), k.get("eps", 1e-6), k.get("M", 4), k.get("K", 512),
+        k.get("ws", A), k.get("wsb", rbytes), None)
+    assert rms(x=None) == -1 and rms(g=None) == -1 and rms(M=0) == -1 and rms(K=300) == -1
+    assert rms(K=65536) == -1 and rms(eps=-1e-6) == -1 and rms(eps=float("nan")) == -1
+    assert rms(eps=float("inf")) == -1 and rms(M=1 << 31) == -1
+    assert rms(xdt=3) == -3 and rms(g=A + 4) == -5 and rms(x=A + 2) == -5
+    assert rms(ws=None) == -4 and rms(wsb=rbytes - 1) == -4
+    assert lib.qgemm_rmsnorm_quantize_act(A, 1, A, 1e-6, 4, 512, A, A + 2, A, None) == -5
