@@ -24,7 +24,9 @@ decode-sized GEMV (M = 1 and 8) over every projection shape of the workloads,
 the M=1 LM-head bandwidth (K=4096 -> N=152064, Q6_K), the other design branch
 (weights dequantised to fp16 in the GEMM, fp16 matrix cores) and the per-256
 activation-scale variant (Q4_K) beside the int8 method on every projection
-shape, and the CPU oracle timed on the host.
+shape, the fusions either side of the GEMM (RMSNorm -> quantiser, the gate+up
+GEMM with the SwiGLU epilogue, and whole FFN blocks) against the unfused
+chains, and the CPU oracle timed on the host.
 
 --calib-copy-mib N additionally runs a plain elementwise copy kernel over
 N MiB (read N, write N) three times: the reference dispatch for scaling HBM
@@ -142,6 +144,7 @@ def parse():
     p.add_argument("--gemv-steps", type=int, default=200)  # 0: skip the decode GEMV table
     p.add_argument("--set-steps", type=int, default=10)   # 0: skip the config 3/4 projection sets
     p.add_argument("--branch-steps", type=int, default=5)  # 0: skip the design-variants table
+    p.add_argument("--fusion-steps", type=int, default=5)  # 0: skip the fusions table
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0)
@@ -461,6 +464,95 @@ def main():
             del Wb, xb, yb, ws8, ws16
     torch.cuda.empty_cache()
 
+    # ---------------- fusions either side of the GEMM, per gate+up projection of the
+    # workloads (its 2F weight rows read as the stacked gate and up tensors) and
+    # per FFN block (gate+up, SwiGLU, down): unfused = quantiser, GEMM to fp32
+    # [M][2F], SwiGLU kernel (and the down projection's quantiser + GEMM); fused
+    # = RMSNorm -> quantiser, gate+up GEMM with the SwiGLU epilogue writing bf16
+    # (and the same down projection).  The fused chain also does the norm, which
+    # the unfused one leaves out, so its advantage is understated.  Each call
+    # sequence is timed back to back, best of three interleaved rounds.
+    fusions = {}
+    for cfg in (2, 3, 4) if args.fusion_steps > 0 else ():
+        ups = [g for g in synth.CONFIGS[cfg] if (g.name == "up_gate" or g.name.startswith("gate_up"))
+               and g.fmt == qg.QG_Q4_K]
+        for g in ups:
+            down = next(d for d in synth.CONFIGS[cfg] if d.name.startswith("down") and d.M == g.M)
+            if down.K == g.N:
+                # one of the two K->F tensors (the down projection reads F = N): stack it
+                # with a second one of the same recipe as the up tensor
+                F = g.N
+                Wnp = np.concatenate([synth.make_weights(g),
+                                      synth.pack(g.fmt, synth.normal(g.w_seed + 5, (g.N, g.K), 0.0, 0.02))])
+            else:
+                F = g.N // 2                       # already the stacked [gate; up] tensor
+                assert down.K == F
+                Wnp = synth.make_weights(g)
+            gu_ops = 2 * g.M * 2 * F * g.K
+            Wb = to_dev(Wnp)
+            del Wnp
+            xb = to_dev(synth.make_acts(g))
+            gn = to_dev(synth.normal(7000 + g.K, (g.K,), 1.0, 0.25))
+            ws = torch.empty(qg.qgemm_swiglu_workspace_bytes(g.fmt, g.M, F, g.K), dtype=torch.uint8,
+                             device=dev)
+            y2 = torch.empty((g.M, 2 * F), dtype=torch.float32, device=dev)
+            hb = torch.empty((g.M, F), dtype=torch.bfloat16, device=dev)
+            Wd = to_dev(synth.make_weights(down))
+            wsd = qg.alloc_workspace(down.M, down.K, dev)
+            yd = torch.empty((down.M, down.N), dtype=torch.float32, device=dev)
+            calls = {
+                "quant": lambda: qg.qgemm_quantize_workspace(xb, g.M, g.K, ws, stream),
+                "rmsnorm_quant": lambda: qg.qgemm_rmsnorm_quantize_workspace(xb, gn, 1e-6, g.M, g.K, ws,
+                                                                             stream),
+                "gemm_fp32": lambda: qg.qgemm_gemm_quantized(Wb, g.fmt, ws, g.M, 2 * F, g.K, y2, stream),
+                "gemm_swiglu": lambda: qg.qgemm_gemm_quantized_swiglu(Wb, g.fmt, ws, g.M, F, g.K, hb, stream),
+                "swiglu": lambda: qg.qgemm_swiglu(y2, g.M, F, hb, stream)}
+
+            def unfused():
+                calls["quant"]()
+                calls["gemm_fp32"]()
+                calls["swiglu"]()
+
+            def fused():
+                calls["rmsnorm_quant"]()
+                calls["gemm_swiglu"]()
+            calls["unfused_chain"], calls["fused_chain"] = unfused, fused
+
+            def down_proj():
+                qg.qgemm_prefill(Wd, down.fmt, hb, down.M, down.N, down.K, yd, wsd, stream)
+            calls["ffn_unfused"] = lambda: (unfused(), down_proj())
+            calls["ffn_fused"] = lambda: (fused(), down_proj())
+            us = {}
+            for fn in calls.values():
+                for _ in range(2):
+                    fn()
+            for _ in range(3):
+                for k, fn in calls.items():
+                    a, b = ev(), ev()
+                    a.record(stream)
+                    for _ in range(args.fusion_steps):
+                        fn()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    us[k] = min(us.get(k, 1e30), 1e3 * a.elapsed_time(b) / args.fusion_steps)
+            rms_bytes = g.M * g.K * 2 + g.K * 4 + g.M * g.K + g.M * (g.K // 32) * (4 + 4 + 4 + 6)
+            ops = gu_ops + down.ops
+            row = {"shape": f"M={g.M} K={g.K} gate+up 2x{F} Q4_K, down {down.K}->{down.N} "
+                            f"{'Q4_K' if down.fmt == qg.QG_Q4_K else 'Q6_K'}",
+                   "fused_kernel": qg.qgemm_kernel_name_swiglu(g.fmt, g.M, F, g.K),
+                   **{f"{k}_us": round(v, 2) for k, v in us.items()},
+                   "gemm_swiglu_tops": round(gu_ops / (us["gemm_swiglu"] * 1e-6) / 1e12, 1),
+                   "gemm_swiglu_over_gemm_fp32_speed": round(us["gemm_fp32"] / us["gemm_swiglu"], 3),
+                   "fused_over_unfused_chain_speed": round(us["unfused_chain"] / us["fused_chain"], 3),
+                   "output_bytes_fp32_vs_bf16": [g.M * 2 * F * 4, g.M * F * 2],
+                   "rmsnorm_quant_gbps": round(rms_bytes / (us["rmsnorm_quant"] * 1e-6) / 1e9, 1),
+                   "ffn_fused_tok_s": round(g.M / (us["ffn_fused"] * 1e-6), 1),
+                   "ffn_fused_tops": round(ops / (us["ffn_fused"] * 1e-6) / 1e12, 1),
+                   "ffn_fused_over_unfused_speed": round(us["ffn_unfused"] / us["ffn_fused"], 3)}
+            fusions[f"c{cfg}_{g.name}"] = row
+            del Wb, xb, gn, ws, y2, hb, Wd, wsd, yd
+    torch.cuda.empty_cache()
+
     # ---------------- decode-sized GEMV over every projection shape of the workloads
     # (M = 1 and M = 8 rows; weight bytes / kernel time against 8 TB/s)
     gemv = {}
@@ -613,6 +705,7 @@ def main():
         "decode_gemv": gemv,
         "lm_head": lm_out,
         "design_variants": variants,
+        "fusions": fusions,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -100,11 +100,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-// SwiGLU of one gate/up pair: silu(g) * u with silu(g) = g / (1 + e^-g), in
-// fp32, rounded once to bfloat16.  e^-g overflowing to infinity (g < -88)
-// gives silu = -0, as the limit.
+// SwiGLU of one gate/up pair: silu(g) * u with silu(g) = g / (1 + e^-g),
+// rounded once to bfloat16.  In fp32 on the hardware's exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32; 1 ulp each): e^-g = 2^(-g*log2 e), whose argument
+// rounding moves e^-g by at most |g| * 2^-24 relative; with the add and the
+// two products the fp32 value is within |g| * 2^-24 + 2^-20 of silu(g) * u
+// relative, under 2^-17 for |g| < 88.7 and far below the 2^-8 of the bfloat16
+// rounding.  For g < -87.3 the reciprocal falls below the normal range and
+// returns 0 (below -88.7 e^-g overflows to infinity first), so silu evaluates
+// to -0 where the exact value is below 1.1e-36 in magnitude; for large g it
+// is g.
 __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
-  return f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float e = __builtin_amdgcn_exp2f(-g * kLog2e);
+  return f32_to_bf16_rne(g * __builtin_amdgcn_rcpf(1.0f + e) * u);
 }
 
 }  // namespace qg

@@ -29,6 +29,8 @@
 // bfloat16) and dS = dx*S is split exactly into three bfloat16 pieces by the
 // activation quantiser, so two K=16 bf16 MFMAs per tile and super-block give
 // sum_j m_j * dS_j to fp32 accuracy; one FMA per element then applies -dmin.
+#include <type_traits>
+
 #include "common.h"
 #include "lds_stage.h"
 #include "mfma_epilogue.h"
@@ -406,42 +408,83 @@ __device__ __forceinline__ void q4k_lds_body(
   }
 
   if constexpr (SW) {
-    // the up waves (wn >= WN/2) of group 0 leave their sums in LDS past the
-    // K-group reduction space; after the barrier each gate wave reads its
-    // partner's (same wm, wn + WN/2: the same rows and output columns)
-    constexpr int HW = WN / 2;
-    constexpr int XOFF = (KS - 1) * NW * TM * TN * 4096;
-    static_assert(XOFF + HW * WM * TM * TN * 4096 <= KS * NS * STAGE, "exchange space");
-    float4* xch = reinterpret_cast<float4*>(lds + XOFF);  // [WM][HW][TM][TN][4][64]
-    if constexpr (KS == 1) __syncthreads();  // no wave reads the stage ring any more
-    if (grp == 0 && wn >= HW) {
+    // Wave pair (wm, wn) / (wm, wn + WN/2) holds the gate and the up values of
+    // the same rows and output columns in the same lanes and registers.  Each
+    // wave of the pair takes half of the SwiGLU work: the gate wave registers
+    // 0..7, the up wave 8..15, after swapping the other halves through LDS.
+    // The bf16 results go to an h tile [BM][BN/2] in LDS and leave it as
+    // 16-byte row segments.
+    constexpr int HW = WN / 2, BO = BN / 2;
+    constexpr int XOFF = (KS - 1) * NW * TM * TN * 4096;  // past the K-group reduction space
+    constexpr int HOFF = XOFF + HW * WM * TM * TN * 4096;
+    static_assert(HOFF + BM * BO * 2 <= KS * NS * STAGE, "exchange space");
+    float4* xch = reinterpret_cast<float4*>(lds + XOFF);  // [pair][TM][TN][side][2][64]
+    uint16_t* ht = reinterpret_cast<uint16_t*>(lds + HOFF);
+    const bool up_wave = wn >= HW;
+    const int pair = wm * HW + (up_wave ? wn - HW : wn);
+    // side 0: the gate wave's registers 8..15; side 1: the up wave's registers 0..7
+    auto slot = [&](int i, int j, int side, int q) {
+      return ((((pair * TM + i) * TN + j) * 2 + side) * 2 + q) * 64 + lane;
+    };
+    // The register halves are compile-time constants in each branch (a
+    // run-time register index would put the accumulators in private memory).
+    auto give = [&](auto up) {  // this wave's half that the partner finishes
+      constexpr int r0 = decltype(up)::value ? 0 : 8;
 #pragma unroll
       for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
-          for (int q = 0; q < 4; q++)
-            xch[((((wm * HW + wn - HW) * TM + i) * TN + j) * 4 + q) * 64 + lane] =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    }
-    __syncthreads();
-    if (grp == 0 && wn < HW) {
+          for (int q = 0; q < 2; q++)
+            xch[slot(i, j, decltype(up)::value ? 1 : 0, q)] =
+                make_float4(acc[i][j][r0 + 4 * q], acc[i][j][r0 + 4 * q + 1], acc[i][j][r0 + 4 * q + 2],
+                            acc[i][j][r0 + 4 * q + 3]);
+    };
+    auto finish = [&](auto up) {  // the half this wave finishes, with the partner's values
+      constexpr bool UP = decltype(up)::value;
+      constexpr int r0 = UP ? 8 : 0;
+      const int col0 = (UP ? nl0 - BO : nl0) + l32;
 #pragma unroll
-      for (int j = 0; j < TN; j++) {
-        const int64_t f = n_cta + nl0 + 32 * j + l32;
-        if (f >= F) continue;
+      for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+        for (int j = 0; j < TN; j++)
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const float4 u4 = xch[((((wm * HW + wn) * TM + i) * TN + j) * 4 + q) * 64 + lane];
-            const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+          for (int q = 0; q < 2; q++) {
+            const float4 o4 = xch[slot(i, j, UP ? 0 : 1, q)];
+            const float o[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-              const int64_t m = m_cta + ml0 + 32 * i + acc_row(4 * q + e, h);
-              if (m < M) __builtin_nontemporal_store(swiglu_bf16(acc[i][j][4 * q + e], u[e]), hout + m * F + f);
+              const float a = acc[i][j][r0 + 4 * q + e];
+              ht[(ml0 + 32 * i + acc_row(r0 + 4 * q + e, h)) * BO + col0 + 32 * j] =
+                  UP ? swiglu_bf16(o[e], a) : swiglu_bf16(a, o[e]);
             }
           }
+    };
+    using kGate = std::integral_constant<bool, false>;
+    using kUp = std::integral_constant<bool, true>;
+    if constexpr (KS == 1) __syncthreads();  // no wave reads the stage ring any more
+    if (grp == 0) {
+      if (up_wave) give(kUp{});
+      else give(kGate{});
+    }
+    __syncthreads();
+    if (grp == 0) {
+      if (up_wave) finish(kUp{});
+      else finish(kGate{});
+    }
+    __syncthreads();
+    constexpr int CPR = BO / 8;  // 16-byte chunks per h row of the block
+    for (int c = tid; c < BM * CPR; c += 64 * NW * KS) {
+      const int row = c / CPR, c8 = c - row * CPR;
+      const int64_t m = m_cta + row, f = n_cta + 8 * c8;
+      if (m >= M || f >= F) continue;
+      const v4i v = *reinterpret_cast<const v4i*>(ht + row * BO + 8 * c8);
+      uint16_t* dst = hout + m * F + f;
+      if (F % 8 == 0) {  // then f + 8 <= F and dst is 16-byte aligned
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
+      } else {
+        const uint16_t* src = ht + row * BO + 8 * c8;
+        for (int e = 0; e < 8 && f + e < F; e++) dst[e] = src[e];
       }
     }
     return;
