@@ -24,9 +24,10 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 Q4_K = 0
 Q6_K = 1
+Q5_K = 2
 F32 = 0
 BF16 = 1
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176}
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
@@ -46,6 +47,8 @@ def _bind(path: str):
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_decode_q4k.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_decode_q4k.restype = None
+    lib.oracle_decode_q5k.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.oracle_decode_q5k.restype = None
     lib.oracle_decode_q6k.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.oracle_decode_q6k.restype = None
     lib.oracle_dequant.argtypes = [ci, vp, i64, i64, vp]
@@ -119,6 +122,19 @@ def decode_q4k(W: np.ndarray, N: int, K: int):
     return q, sc, m, d, dmin
 
 
+def decode_q5k(W: np.ndarray, N: int, K: int):
+    """Returns (q [N,K] uint8 in 0..31, sc [N,K/32], m [N,K/32] uint8, d, dmin [N,K/256] f64)."""
+    W = np.ascontiguousarray(W, np.uint8)
+    assert W.size == N * K // 256 * 176
+    q = np.empty((N, K), np.uint8)
+    sc = np.empty((N, K // 32), np.uint8)
+    m = np.empty((N, K // 32), np.uint8)
+    d = np.empty((N, K // 256), np.float64)
+    dmin = np.empty((N, K // 256), np.float64)
+    _load().oracle_decode_q5k(_p(W), N, K, _p(q), _p(sc), _p(m), _p(d), _p(dmin))
+    return q, sc, m, d, dmin
+
+
 def decode_q6k(W: np.ndarray, N: int, K: int):
     """Returns (q6 [N,K] uint8 in 0..63, sc [N,K/16] int8, d [N,K/256] f64)."""
     W = np.ascontiguousarray(W, np.uint8)
@@ -152,11 +168,12 @@ def quantize_act(x: np.ndarray):
 
 
 def block_partials(fmt: int, W: np.ndarray, qx: np.ndarray, N: int) -> np.ndarray:
-    """Integer partials: Q4_K [M, N, K/32], Q6_K [M, N, K/16] (int32)."""
+    """Integer partials: Q4_K and Q5_K [M, N, K/32], Q6_K [M, N, K/16] (int32)."""
     W = np.ascontiguousarray(W, np.uint8)
     qx = np.ascontiguousarray(qx, np.int8)
     M, K = qx.shape
-    L = 32 if fmt == Q4_K else 16
+    assert W.size == N * K // 256 * BLOCK_BYTES[fmt]
+    L = 16 if fmt == Q6_K else 32
     out = np.empty((M, N, K // L), np.int32)
     _load().oracle_block_partials(fmt, _p(W), _p(qx), M, N, K, _p(out))
     return out

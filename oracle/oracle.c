@@ -34,6 +34,12 @@
  *      Q6_K, 210 B / 256 values: ql[128] low nibbles, qh[64] high bit pairs,
  *        16 int8 sub-block scales (16 values each), fp16 d;
  *        w = d*sc[v/16]*(q6 - 32), q6 in [0, 63].
+ *      Q5_K, 176 B / 256 values (named beside Q4_K / Q6_K in aprender issue
+ *        #5305's decode-GEMV ticket #5221, where it is the slowest format): the
+ *        Q4_K header (fp16 d, dmin, the same 12 bytes of 6-bit sc[8] / m[8]),
+ *        qh[32] holding the fifth bit of every code, 128 bytes of low nibbles
+ *        placed as Q4_K's codes; q5 = low | 16*((qh[v % 32] >> (v / 32)) & 1)
+ *        in [0, 31]; w = d*sc[j]*q5 - dmin*m[j] for sub-block j = v/32.
  *
  * The combine is done in fp64 in ascending block order.  Integer partials are
  * exact int32.  All floating point here is IEEE binary32/binary64 with no
@@ -45,7 +51,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_Q4_K = 0, ORACLE_Q6_K = 1 };
+enum { ORACLE_Q4_K = 0, ORACLE_Q6_K = 1, ORACLE_Q5_K = 2 };
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
 
 /* IEEE binary16 bit pattern -> exact double (normals, subnormals, inf, nan). */
@@ -62,10 +68,9 @@ static inline uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] <
 
 /* ---------------------------------------------------------------- Q4_K decode */
 
-/* Decode one Q4_K block into codes q[256] (0..15), scales sc[8], mins m[8],
- * and the two binary16 super-scales as doubles. */
-static void decode_q4k_block(const uint8_t *blk, uint8_t *q, uint8_t *sc, uint8_t *m,
-                             double *d, double *dmin) {
+/* The 16-byte header Q4_K and Q5_K share: the two binary16 super-scales as
+ * doubles and the six-bit scales sc[8] and mins m[8]. */
+static void decode_k_header(const uint8_t *blk, uint8_t *sc, uint8_t *m, double *d, double *dmin) {
     *d = oracle_half_to_double(rd16(blk));
     *dmin = oracle_half_to_double(rd16(blk + 2));
     const uint8_t *s = blk + 4;
@@ -80,11 +85,33 @@ static void decode_q4k_block(const uint8_t *blk, uint8_t *q, uint8_t *sc, uint8_
             m[j] = (uint8_t)((s[j + 4] >> 4) | ((s[j] >> 6) << 4));
         }
     }
-    const uint8_t *qs = blk + 16;
+}
+
+/* Low four bits of the 256 codes from the 128 nibble bytes qs: value v sits in
+ * byte 32*(v/64) + v%32, the low nibble for the first 32 values of each 64. */
+static void decode_nibbles(const uint8_t *qs, uint8_t *q) {
     for (int v = 0; v < 256; v++) {
         uint8_t byte = qs[32 * (v / 64) + (v % 32)];
         q[v] = (v % 64) < 32 ? (byte & 0x0F) : (byte >> 4);
     }
+}
+
+/* Decode one Q4_K block into codes q[256] (0..15), scales sc[8], mins m[8],
+ * and the two binary16 super-scales as doubles. */
+static void decode_q4k_block(const uint8_t *blk, uint8_t *q, uint8_t *sc, uint8_t *m,
+                             double *d, double *dmin) {
+    decode_k_header(blk, sc, m, d, dmin);
+    decode_nibbles(blk + 16, q);
+}
+
+/* Decode one Q5_K block into codes q[256] (0..31), scales, mins and super-scales
+ * (the Q4_K header; qh at bytes 16-47, nibbles at 48-175). */
+static void decode_q5k_block(const uint8_t *blk, uint8_t *q, uint8_t *sc, uint8_t *m,
+                             double *d, double *dmin) {
+    decode_k_header(blk, sc, m, d, dmin);
+    const uint8_t *qh = blk + 16;
+    decode_nibbles(blk + 48, q);
+    for (int v = 0; v < 256; v++) q[v] = (uint8_t)(q[v] | (((qh[v % 32] >> (v / 32)) & 1) << 4));
 }
 
 /* Decode W [N x K] Q4_K: q [N*K], sc, m [N*K/32], d, dmin [N*K/256]. */
@@ -94,6 +121,15 @@ void oracle_decode_q4k(const uint8_t *W, int64_t N, int64_t K, uint8_t *q, uint8
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N * nb; i++)
         decode_q4k_block(W + i * 144, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);
+}
+
+/* Decode W [N x K] Q5_K: q [N*K] (0..31), sc, m [N*K/32], d, dmin [N*K/256]. */
+void oracle_decode_q5k(const uint8_t *W, int64_t N, int64_t K, uint8_t *q, uint8_t *sc,
+                       uint8_t *m, double *d, double *dmin) {
+    int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N * nb; i++)
+        decode_q5k_block(W + i * 176, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);
 }
 
 /* ---------------------------------------------------------------- Q6_K decode */
@@ -128,10 +164,11 @@ void oracle_dequant(int fmt, const uint8_t *W, int64_t N, int64_t K, double *w) 
     for (int64_t i = 0; i < N * nb; i++) {
         uint8_t q[256];
         double *o = w + i * 256;
-        if (fmt == ORACLE_Q4_K) {
+        if (fmt == ORACLE_Q4_K || fmt == ORACLE_Q5_K) {
             uint8_t sc[8], m[8];
             double d, dmin;
-            decode_q4k_block(W + i * 144, q, sc, m, &d, &dmin);
+            if (fmt == ORACLE_Q4_K) decode_q4k_block(W + i * 144, q, sc, m, &d, &dmin);
+            else decode_q5k_block(W + i * 176, q, sc, m, &d, &dmin);
             for (int v = 0; v < 256; v++) o[v] = d * sc[v / 32] * q[v] - dmin * m[v / 32];
         } else {
             int8_t sc[16];
@@ -202,16 +239,17 @@ void oracle_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_
 
 /* ----------------------------------------------------- integer block partials */
 
-/* Q4_K: out[m][n][b] = sum_{t<32} q_w[n][32b+t] * q_x[m][32b+t]      (K/32 per pair)
+/* Q4_K, Q5_K: out[m][n][b] = sum_{t<32} q_w[n][32b+t] * q_x[m][32b+t] (K/32 per pair)
  * Q6_K: out[m][n][s] = sum_{t<16} (q6[n][16s+t] - 32) * q_x[m][16s+t] (K/16 per pair) */
 void oracle_block_partials(int fmt, const uint8_t *W, const int8_t *qx, int64_t M, int64_t N,
                            int64_t K, int32_t *out) {
     uint8_t *qw = (uint8_t *)malloc((size_t)(N * K));
     int64_t nb = K / 256;
-    if (fmt == ORACLE_Q4_K) {
+    if (fmt == ORACLE_Q4_K || fmt == ORACLE_Q5_K) {
         uint8_t *sc = malloc((size_t)(N * K / 32)), *m = malloc((size_t)(N * K / 32));
         double *d = malloc(sizeof(double) * (size_t)(N * nb)), *dm = malloc(sizeof(double) * (size_t)(N * nb));
-        oracle_decode_q4k(W, N, K, qw, sc, m, d, dm);
+        if (fmt == ORACLE_Q4_K) oracle_decode_q4k(W, N, K, qw, sc, m, d, dm);
+        else oracle_decode_q5k(W, N, K, qw, sc, m, d, dm);
         free(sc); free(m); free(d); free(dm);
     } else {
         int8_t *sc = malloc((size_t)(N * K / 16));
@@ -219,7 +257,7 @@ void oracle_block_partials(int fmt, const uint8_t *W, const int8_t *qx, int64_t 
         oracle_decode_q6k(W, N, K, qw, sc, d);
         free(sc); free(d);
     }
-    int L = fmt == ORACLE_Q4_K ? 32 : 16, off = fmt == ORACLE_Q4_K ? 0 : 32;
+    int L = fmt == ORACLE_Q6_K ? 16 : 32, off = fmt == ORACLE_Q6_K ? 32 : 0;
     int64_t nblk = K / L;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t mi = 0; mi < M; mi++)
@@ -240,7 +278,7 @@ void oracle_block_partials(int fmt, const uint8_t *W, const int8_t *qx, int64_t 
  * [nrows x ncols].  Steps: quantise the activation rows, decode the weight
  * rows, form every per-block int32 dot product, then combine in fp64 in
  * ascending block order:
- *   Q4_K: y = sum_b dx[b] * ( d*sc[b]*I[b] - dmin*m[b]*S[b] )
+ *   Q4_K, Q5_K: y = sum_b dx[b] * ( d*sc[b]*I[b] - dmin*m[b]*S[b] )
  *   Q6_K: y = sum_b dx[b] * d * ( sc[2b]*I16[2b] + sc[2b+1]*I16[2b+1] )
  * where b runs over 32-value activation blocks and d, dmin belong to the
  * super-block holding b.  Returns 0, or -1 on allocation failure. */
@@ -250,7 +288,7 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
     if (!rows) nrows = M;
     if (!cols) ncols = N;
     int64_t nb32 = K / 32, nsb = K / 256;
-    int64_t bbytes = fmt == ORACLE_Q4_K ? 144 : 210;
+    int64_t bbytes = fmt == ORACLE_Q4_K ? 144 : fmt == ORACLE_Q5_K ? 176 : 210;
 
     int8_t *qx = malloc((size_t)(nrows * K));
     float *dx = malloc(sizeof(float) * (size_t)(nrows * nb32));
@@ -284,6 +322,9 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
             if (fmt == ORACLE_Q4_K)
                 decode_q4k_block(blk, qw + j * K + 256 * sb, scw + j * nb32 + 8 * sb,
                                  mw + j * nb32 + 8 * sb, dw + j * nsb + sb, dmw + j * nsb + sb);
+            else if (fmt == ORACLE_Q5_K)
+                decode_q5k_block(blk, qw + j * K + 256 * sb, scw + j * nb32 + 8 * sb,
+                                 mw + j * nb32 + 8 * sb, dw + j * nsb + sb, dmw + j * nsb + sb);
             else
                 decode_q6k_block(blk, qw + j * K + 256 * sb, (int8_t *)scw + j * (K / 16) + 16 * sb,
                                  dw + j * nsb + sb);
@@ -299,7 +340,7 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
             for (int64_t b = 0; b < nb32; b++) {
                 double d = dw[j * nsb + b / 8];
                 double dxb = (double)dx[i * nb32 + b];
-                if (fmt == ORACLE_Q4_K) {
+                if (fmt != ORACLE_Q6_K) {  /* Q4_K, Q5_K */
                     int32_t I = 0;
                     for (int t = 0; t < 32; t++) I += (int32_t)wq[32 * b + t] * (int32_t)xq[32 * b + t];
                     double sc = scw[j * nb32 + b], m = mw[j * nb32 + b];

@@ -21,9 +21,10 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 Q4_K = 0
 Q6_K = 1
+Q5_K = 2
 F32 = 0
 BF16 = 1
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176}
 
 
 def build() -> str:
@@ -55,6 +56,7 @@ def _load():
         lib.synth_rmsnorm_rows_f32.argtypes = [vp, i64, i64, dbl]
         lib.synth_f32_to_bf16.argtypes = [vp, i64, vp]
         lib.synth_pack_q4k.argtypes = [vp, i64, i64, vp]
+        lib.synth_pack_q5k.argtypes = [vp, i64, i64, vp]
         lib.synth_pack_q6k.argtypes = [vp, i64, i64, vp]
         lib.synth_random_blocks.argtypes = [u64, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, vp]
@@ -122,7 +124,7 @@ def pack(fmt: int, w: np.ndarray) -> np.ndarray:
     N, K = w.shape
     assert K % 256 == 0
     out = np.empty((N, K // 256 * BLOCK_BYTES[fmt]), np.uint8)
-    fn = _load().synth_pack_q4k if fmt == Q4_K else _load().synth_pack_q6k
+    fn = {Q4_K: _load().synth_pack_q4k, Q5_K: _load().synth_pack_q5k, Q6_K: _load().synth_pack_q6k}[fmt]
     fn(_ptr(w), N, K, _ptr(out))
     return out
 

@@ -1,5 +1,5 @@
 /*
- * synth.c -- seeded synthetic inputs for the Q4_K / Q6_K x int8 prefill GEMM.
+ * synth.c -- seeded synthetic inputs for the Q4_K / Q5_K / Q6_K x int8 prefill GEMM.
  *
  * This module only MAKES inputs.  It holds none of the GEMM's arithmetic
  * (no block decoding, no activation quantisation, no contraction).  Both the
@@ -25,6 +25,8 @@
  *     nibble when v%64 < 32, else high nibble.
  *   Q6_K, 210 B / 256 values: ql[128] low 4 bits | qh[64] high 2 bits |
  *     16 int8 scales (one per 16 values) | d (fp16).
+ *   Q5_K, 176 B / 256 values: the Q4_K header | qh[32], bit v/32 of byte v%32
+ *     the fifth bit of value v | 128 B of low 4 bits placed as Q4_K's.
  */
 #include <math.h>
 #include <stdint.h>
@@ -143,13 +145,16 @@ static inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ?
 
 /* ---------- packers ---------- */
 
-/* Pack w [N x K] (K % 256 == 0) into Q4_K super-blocks, row n = K/256 blocks. */
-void synth_pack_q4k(const float *w, int64_t N, int64_t K, uint8_t *out) {
+/* Pack w [N x K] (K % 256 == 0) into Q4_K (q5 = 0) or Q5_K (q5 = 1)
+ * super-blocks, row n = K/256 blocks.  Both share the header; Q5_K codes take
+ * 32 levels, their fifth bit going to qh (bit v/32 of byte v%32). */
+static void pack_k(const float *w, int64_t N, int64_t K, uint8_t *out, int q5) {
+    const int bytes = q5 ? 176 : 144, qmax = q5 ? 31 : 15;
     int64_t nb = K / 256;
 #pragma omp parallel for schedule(static)
     for (int64_t blk = 0; blk < N * nb; blk++) {
         const float *x = w + blk * 256; /* rows are contiguous, so block blk is w[256*blk..] */
-        uint8_t *o = out + blk * 144;
+        uint8_t *o = out + blk * bytes;
         double scale[8], mn[8];
         double smax = 0.0, mmax = 0.0;
         for (int j = 0; j < 8; j++) {
@@ -159,7 +164,7 @@ void synth_pack_q4k(const float *w, int64_t N, int64_t K, uint8_t *out) {
                 if (v < lo) lo = v;
                 if (v > hi) hi = v;
             }
-            scale[j] = (hi - lo) / 15.0;
+            scale[j] = (hi - lo) / qmax;
             mn[j] = -lo;
             if (scale[j] > smax) smax = scale[j];
             if (mn[j] > mmax) mmax = mn[j];
@@ -171,7 +176,7 @@ void synth_pack_q4k(const float *w, int64_t N, int64_t K, uint8_t *out) {
             sc[j] = d > 0.0 ? clampi((int)nearbyint(scale[j] / d), 0, 63) : 0;
             m[j] = dmin > 0.0 ? clampi((int)nearbyint(mn[j] / dmin), 0, 63) : 0;
         }
-        memset(o, 0, 144);
+        memset(o, 0, (size_t)bytes);
         o[0] = (uint8_t)(hd & 0xFF); o[1] = (uint8_t)(hd >> 8);
         o[2] = (uint8_t)(hm & 0xFF); o[3] = (uint8_t)(hm >> 8);
         uint8_t *s = o + 4;
@@ -180,17 +185,21 @@ void synth_pack_q4k(const float *w, int64_t N, int64_t K, uint8_t *out) {
             s[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
             s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
         }
-        uint8_t *qs = o + 16;
+        uint8_t *qh = o + 16, *qs = o + (q5 ? 48 : 16);
         for (int v = 0; v < 256; v++) {
             int j = v / 32;
             double step = d * sc[j];
-            int q = step > 0.0 ? clampi((int)nearbyint(((double)x[v] + dmin * m[j]) / step), 0, 15) : 0;
+            int q = step > 0.0 ? clampi((int)nearbyint(((double)x[v] + dmin * m[j]) / step), 0, qmax) : 0;
             int byte = 32 * (v / 64) + (v % 32);
-            if ((v % 64) < 32) qs[byte] |= (uint8_t)q;
-            else qs[byte] |= (uint8_t)(q << 4);
+            if ((v % 64) < 32) qs[byte] |= (uint8_t)(q & 15);
+            else qs[byte] |= (uint8_t)((q & 15) << 4);
+            if (q5) qh[v % 32] |= (uint8_t)(((q >> 4) & 1) << (v / 32));
         }
     }
 }
+
+void synth_pack_q4k(const float *w, int64_t N, int64_t K, uint8_t *out) { pack_k(w, N, K, out, 0); }
+void synth_pack_q5k(const float *w, int64_t N, int64_t K, uint8_t *out) { pack_k(w, N, K, out, 1); }
 
 /* Pack w [N x K] into Q6_K super-blocks. */
 void synth_pack_q6k(const float *w, int64_t N, int64_t K, uint8_t *out) {
@@ -233,21 +242,21 @@ void synth_pack_q6k(const float *w, int64_t N, int64_t K, uint8_t *out) {
 /* Random legal blocks: every byte random except the binary16 scale fields,
  * which get a random sign, a random mantissa and an exponent field drawn from
  * [emin, emax] (0 = subnormal) so that d and dmin are always finite.  fmt 0 =
- * Q4_K, 1 = Q6_K.  Block b uses counters 256*b .. 256*b+255. */
+ * Q4_K, 1 = Q6_K, 2 = Q5_K.  Block b uses counters 256*b .. 256*b+255. */
 void synth_random_blocks(uint64_t seed, int fmt, int64_t nblocks, int emin, int emax,
                          int allow_negative, uint8_t *out) {
-    int bytes = fmt == 0 ? 144 : 210;
+    int bytes = fmt == 0 ? 144 : fmt == 2 ? 176 : 210;
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nblocks; b++) {
         uint8_t *o = out + b * bytes;
         for (int i = 0; i < bytes; i++) o[i] = (uint8_t)(synth_u64(seed, (uint64_t)(256 * b + i)) >> 56);
-        int nscale = fmt == 0 ? 2 : 1;
+        int nscale = fmt == 1 ? 1 : 2;
         for (int k = 0; k < nscale; k++) {
             uint64_t r = synth_u64(seed, (uint64_t)(256 * b + 240 + k));
             int E = emin + (int)((r >> 32) % (uint64_t)(emax - emin + 1));
             uint16_t h = (uint16_t)((E << 10) | (int)(r & 1023));
             if (allow_negative && ((r >> 20) & 1)) h |= 0x8000;
-            int off = fmt == 0 ? 2 * k : 208;
+            int off = fmt == 1 ? 208 : 2 * k;
             o[off] = (uint8_t)(h & 0xFF);
             o[off + 1] = (uint8_t)(h >> 8);
         }

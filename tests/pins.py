@@ -6,7 +6,7 @@ AssertionError when the oracle disagrees with what the block format and the
 mathematics fix:
 
   * hand-packed super-blocks whose decoded values are known in closed form
-    (tests/golden/*.txt),
+    (tests/golden/*.txt; Q4_K, Q5_K, Q6_K),
   * bit probes: every stored bit changes exactly one decoded field by a power
     of two, and every field receives exactly its width in bits,
   * binary16 values fixed by IEEE 754,
@@ -42,7 +42,7 @@ import numpy as np
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-Q4_K, Q6_K = 0, 1
+Q4_K, Q6_K, Q5_K = 0, 1, 2
 
 
 def read_fixture(name: str) -> dict:
@@ -65,6 +65,13 @@ def q4k_example_block() -> tuple[np.ndarray, dict]:
     fx = read_fixture("q4k_worked_example.txt")
     b = _hex(fx["bytes_0_15"]) + _hex(fx["qs_chunk_32B_repeated_4x"]) * 4
     assert len(b) == 144
+    return np.array(b, np.uint8), fx
+
+
+def q5k_example_block() -> tuple[np.ndarray, dict]:
+    fx = read_fixture("q5k_worked_example.txt")
+    b = _hex(fx["bytes_0_15"]) + _hex(fx["qh_32B"]) + _hex(fx["qs_chunk_32B_repeated_4x"]) * 4
+    assert len(b) == 176
     return np.array(b, np.uint8), fx
 
 
@@ -103,6 +110,21 @@ def pin_q4k_worked_example(orc):
     assert w.sum() == float(fx["sum_w"]) and w.min() == float(fx["min_w"]) and w.max() == float(fx["max_w"])
 
 
+def pin_q5k_worked_example(orc):
+    blk, fx = q5k_example_block()
+    q, sc, m, d, dmin = orc.decode_q5k(blk, 1, 256)
+    assert d[0, 0] == 1.0 and dmin[0, 0] == 0.5, (d, dmin)
+    assert list(sc[0]) == [int(t) for t in fx["sc"].split()], sc
+    assert list(m[0]) == [int(t) for t in fx["m"].split()], m
+    v = np.arange(256)
+    j, l = v // 32, v % 32
+    low = np.where(j % 2 == 0, v % 16, 15 - v % 16)
+    expect_q = low + 16 * ((l >> j) & 1)
+    assert np.array_equal(q[0].astype(int), expect_q)
+    w = orc.dequant(Q5_K, blk, 1, 256)[0]
+    assert w.sum() == float(fx["sum_w"]) and w.min() == float(fx["min_w"]) and w.max() == float(fx["max_w"])
+
+
 def pin_q6k_worked_example(orc):
     blk, fx = q6k_example_block()
     q6, sc, d = orc.decode_q6k(blk, 1, 256)
@@ -118,6 +140,12 @@ def pin_q6k_worked_example(orc):
 
 def _fields_q4k(orc, blk):
     q, sc, m, d, dmin = orc.decode_q4k(blk, 1, 256)
+    return {"q": q[0].astype(np.int64), "sc": sc[0].astype(np.int64), "m": m[0].astype(np.int64),
+            "d": d[0], "dmin": dmin[0]}
+
+
+def _fields_q5k(orc, blk):
+    q, sc, m, d, dmin = orc.decode_q5k(blk, 1, 256)
     return {"q": q[0].astype(np.int64), "sc": sc[0].astype(np.int64), "m": m[0].astype(np.int64),
             "d": d[0], "dmin": dmin[0]}
 
@@ -168,6 +196,11 @@ def _bit_probe(orc, blk, nbytes, fields_fn, widths, half_fields):
 def pin_q4k_bit_probe(orc):
     blk = synth.random_blocks(Q4_K, 1, 256, seed=77, emin=1, emax=14, allow_negative=False)[0]
     _bit_probe(orc, blk, 144, _fields_q4k, {"q": 4, "sc": 6, "m": 6}, {"d": 0, "dmin": 2})
+
+
+def pin_q5k_bit_probe(orc):
+    blk = synth.random_blocks(Q5_K, 1, 256, seed=79, emin=1, emax=14, allow_negative=False)[0]
+    _bit_probe(orc, blk, 176, _fields_q5k, {"q": 5, "sc": 6, "m": 6}, {"d": 0, "dmin": 2})
 
 
 def pin_q6k_bit_probe(orc):
@@ -281,7 +314,7 @@ def _bruteforce_case(orc, fmt, W, x, N):
 
 
 def pin_gemm_bruteforce(orc):
-    for fmt in (Q4_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K):
         for (M, N, K, seed) in ((1, 1, 256, 1), (3, 5, 256, 2), (4, 8, 512, 3), (2, 7, 768, 4)):
             Wr = synth.random_blocks(fmt, N, K, seed=100 + seed, emin=3, emax=18)
             Wp = synth.pack(fmt, synth.normal(200 + seed, (N, K), 0.0, 0.02))
@@ -307,6 +340,18 @@ def _textbook_blocks(fmt, N, K, seed):
             shift = 0 if v % 64 < 32 else 4
             W[:, :, byte] |= (codes[:, :, v] << shift).astype(np.uint8)
         vals = codes
+    elif fmt == Q5_K:
+        W = np.zeros((N, nb, 176), np.uint8)
+        W[:, :, 0:2] = (0x00, 0x3C)              # d = 1
+        W[:, :, 4:8] = 1                         # sc[0..3] = 1; dmin = 0, m = 0
+        W[:, :, 12:16] = 0x01                    # sc[4..7] = 1
+        codes = rng.integers(0, 32, size=(N, nb, 256))
+        for v in range(256):
+            byte = 48 + 32 * (v // 64) + v % 32
+            shift = 0 if v % 64 < 32 else 4
+            W[:, :, byte] |= ((codes[:, :, v] & 15) << shift).astype(np.uint8)
+            W[:, :, 16 + v % 32] |= (((codes[:, :, v] >> 4) & 1) << (v // 32)).astype(np.uint8)
+        vals = codes
     else:
         W = np.zeros((N, nb, 210), np.uint8)
         W[:, :, 192:208] = 1                     # sc = 1
@@ -330,7 +375,7 @@ def _integer_acts(M, K, seed):
 
 
 def pin_gemm_textbook(orc):
-    for fmt in (Q4_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K):
         M, N, K = 5, 6, 512
         W, wv = _textbook_blocks(fmt, N, K, seed=9 + fmt)
         xi = _integer_acts(M, K, seed=19 + fmt)
@@ -338,7 +383,7 @@ def pin_gemm_textbook(orc):
         exact = xi @ wv.T                          # int64 textbook matmul
         assert np.array_equal(y, exact.astype(np.float64)), np.abs(y - exact).max()
         # per-block integer partials are block-wise textbook matmuls
-        L = 32 if fmt == Q4_K else 16
+        L = 16 if fmt == Q6_K else 32
         P = orc.block_partials(fmt, W, xi.astype(np.int8), N)
         ref = np.einsum("mbt,nbt->mnb", xi.reshape(M, K // L, L), wv.reshape(N, K // L, L))
         assert np.array_equal(P.astype(np.int64), ref)
@@ -350,13 +395,16 @@ def pin_gemm_worked_examples(orc):
     blk4, fx4 = q4k_example_block()
     y4 = orc.gemm(Q4_K, blk4, x, 1)[0, 0]
     assert abs(y4 - float(fx4["sum_w"]) * 127 * dx) <= 1e-9, y4
+    blk5, fx5 = q5k_example_block()
+    y5 = orc.gemm(Q5_K, blk5, x, 1)[0, 0]
+    assert abs(y5 - float(fx5["sum_w"]) * 127 * dx) <= 1e-9, y5
     blk6, fx6 = q6k_example_block()
     y6 = orc.gemm(Q6_K, blk6, x, 1)[0, 0]
     assert abs(y6 - float(fx6["sum_w"]) * 127 * dx) <= 1e-12, y6
 
 
 def pin_gemm_selection_and_scaling(orc):
-    for fmt in (Q4_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K):
         M, N, K = 6, 9, 512
         W = synth.pack(fmt, synth.normal(41 + fmt, (N, K), 0.0, 0.02))
         x = _acts(43 + fmt, M, K)
@@ -373,7 +421,7 @@ def pin_gemm_selection_and_scaling(orc):
 def pin_gemm_semantic_bound(orc):
     """The quantised result stays within the activation-rounding bound of the
     unquantised product (catches a quantiser that only agrees with itself)."""
-    for fmt in (Q4_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K):
         M, N, K = 4, 6, 768
         W = synth.pack(fmt, synth.normal(51 + fmt, (N, K), 0.0, 0.02))
         x = _acts(53 + fmt, M, K)
@@ -708,7 +756,7 @@ def pin_gemm_swiglu_bruteforce(orc):
 
 
 ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bit_probe,
-            pin_q6k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
+            pin_q6k_bit_probe, pin_q5k_worked_example, pin_q5k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
             pin_quant_symmetry_and_scaling, pin_quant_integer_blocks, pin_quant_bf16_matches_f32,
             pin_gemm_bruteforce, pin_gemm_textbook, pin_gemm_worked_examples,
             pin_gemm_selection_and_scaling, pin_gemm_semantic_bound,

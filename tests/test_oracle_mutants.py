@@ -105,6 +105,18 @@ MUTANTS = [
     ("a256_scale_of_next_superblock",
      "                acc += (double)dx[i * nsb + sb] * part;",
      "                acc += (double)dx[i * nsb + (sb + 1) % nsb] * part;"),
+    ("q5k_high_bit_from_wrong_pair",
+     "q[v] = (uint8_t)(q[v] | (((qh[v % 32] >> (v / 32)) & 1) << 4));",
+     "q[v] = (uint8_t)(q[v] | (((qh[v % 32] >> (v / 64)) & 1) << 4));"),
+    ("q5k_high_bit_weight",
+     "q[v] = (uint8_t)(q[v] | (((qh[v % 32] >> (v / 32)) & 1) << 4));",
+     "q[v] = (uint8_t)(q[v] | (((qh[v % 32] >> (v / 32)) & 1) << 5));"),
+    ("q5k_nibbles_read_from_qh",
+     "decode_nibbles(blk + 48, q);",
+     "decode_nibbles(blk + 16, q);"),
+    ("q5k_block_stride",
+     "decode_q5k_block(W + i * 176, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);",
+     "decode_q5k_block(W + i * 144, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);"),
     ("rms_mean_not_divided",
      "double v = ss / (double)K + (double)eps;",
      "double v = ss + (double)eps;"),
