@@ -18,6 +18,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kQ4Bytes = 144;  // bytes per Q4_K super-block (256 values)
 constexpr int kQ6Bytes = 210;  // bytes per Q6_K super-block (256 values)
+constexpr int kQ5Bytes = 176;  // bytes per Q5_K super-block (256 values)
 constexpr int kRowPad = 256;   // activation rows are padded to this multiple in the workspace
 
 // 1.5 * 2^23 as an fp32 bit pattern.  An int32 accumulator started at this
@@ -155,6 +156,10 @@ hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& w
 // Name of the kernel each launcher picks for a problem (diagnostics: matches
 // the kernel names a profiler reports).
 const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256 = false);
+// Q5_K: the Q4_K kernels with the fifth code bit or-ed into the nibble codes
+hipError_t qg_launch_gemm_q5k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream);
+const char* qg_gemm_q5k_kernel_name(int64_t M, int64_t N, int64_t K);
 // Q4_K gate+up GEMM with the SwiGLU epilogue (W: 2F rows, gate then up; h:
 // bfloat16 [M][F]).  Fusable when the problem takes one of the LDS-tiled
 // kernels and the weight offsets fit the kernels' 32-bit load offsets.

@@ -10,6 +10,8 @@ namespace qg {
 
 constexpr int kProbeWM = 2, kProbeWN = 2;
 
+// Q5: Q5_K blocks (nibbles at byte 48, the fifth bit from qh)
+template <bool Q5>
 __global__ __launch_bounds__(256) void partials_q4k_kernel(const uint8_t* __restrict__ W,
                                                            const int8_t* __restrict__ qx, int64_t M,
                                                            int64_t N, int64_t K,
@@ -23,13 +25,16 @@ __global__ __launch_bounds__(256) void partials_q4k_kernel(const uint8_t* __rest
   const int64_t nsb = K / 256, nb = K / 32;
   const int8_t* arow = qx + m_a * K + 16 * h;
   for (int64_t sb = 0; sb < nsb; sb++) {
-    const uint8_t* blk = W + (n_ld * nsb + sb) * kQ4Bytes;
+    const uint8_t* blk = W + (n_ld * nsb + sb) * (Q5 ? kQ5Bytes : kQ4Bytes);
+    const uint4 qh = Q5 ? *reinterpret_cast<const uint4*>(blk + 16 + 16 * h) : uint4{};
     for (int c = 0; c < 4; c++) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c + 16 * h);
+      const uint4 raw = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 32 * c + 16 * h);
       for (int e = 0; e < 2; e++) {
         const int64_t b = 8 * sb + 2 * c + e;
         const v4i a = *reinterpret_cast<const v4i*>(arow + 32 * b);
-        const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, q4_codes(raw, e), v16i{}, 0, 0, 0);
+        v4i bq = q4_codes(raw, e);
+        if (Q5) bq |= q5_high(qh, 2 * c + e);
+        const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, v16i{}, 0, 0, 0);
         if (n < N) {
 #pragma unroll
           for (int r = 0; r < 16; r++) {
@@ -78,7 +83,9 @@ hipError_t qg_launch_block_partials(const uint8_t* W, int fmt, const int8_t* qx,
   const dim3 grid(static_cast<unsigned>((N + 32 * qg::kProbeWN - 1) / (32 * qg::kProbeWN)),
                   static_cast<unsigned>((M + 32 * qg::kProbeWM - 1) / (32 * qg::kProbeWM)));
   if (fmt == QG_Q4_K)
-    qg::partials_q4k_kernel<<<grid, dim3(256), 0, stream>>>(W, qx, M, N, K, out);
+    qg::partials_q4k_kernel<false><<<grid, dim3(256), 0, stream>>>(W, qx, M, N, K, out);
+  else if (fmt == QG_Q5_K)
+    qg::partials_q4k_kernel<true><<<grid, dim3(256), 0, stream>>>(W, qx, M, N, K, out);
   else
     qg::partials_q6k_kernel<<<grid, dim3(256), 0, stream>>>(W, qx, M, N, K, out);
   return hipGetLastError();

@@ -92,16 +92,20 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 // waves wn < WN/2 hold gate values and the waves wn + WN/2 the up values of
 // the same (row, column) in the same lane and register; the latter pass them
 // through LDS and the former write h = silu(gate) * up as bfloat16 [M][F].
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int KS, bool A256, bool SW>
+// Q5: Q5_K blocks (176 bytes: the Q4_K header, qh[32], the nibbles); each
+// lane also stages its 16 qh bytes and ors bit jb of each into its codes.
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int KS, bool A256, bool SW, bool Q5 = false>
 __device__ __forceinline__ void q4k_lds_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
     int64_t N, int64_t K, float* __restrict__ y, uint16_t* __restrict__ hout, int64_t F) {
   static_assert(!SW || (WN % 2 == 0 && !A256 && !DPP), "SwiGLU pairs waves wn and wn + WN/2");
+  static_assert(!Q5 || (!A256 && !DPP && !SW), "Q5_K runs the per-32 method");
   constexpr int NW = WM * WN;  // waves per group
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  constexpr int BB = Q5 ? kQ5Bytes : kQ4Bytes, BB16 = BB / 16, QS = Q5 ? 48 : 16;  // block bytes, nibble offset
   static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
-  constexpr int A_CH = BM * 256 / 16, W_CH = BN * kQ4Bytes / 16, X_CH = BM * 32 / 16, P_CH = BM * 48 / 16;
+  constexpr int A_CH = BM * 256 / 16, W_CH = BN * BB16, X_CH = BM * 32 / 16, P_CH = BM * 48 / 16;
   // wave-loads per region and region sizes in LDS (whole wave-loads)
   constexpr int A_WL = (A_CH + 63) / 64, W_WL = (W_CH + 63) / 64, X_WL = (X_CH + 63) / 64, P_WL = (P_CH + 63) / 64;
   constexpr int A_BYTES = A_WL * 1024, W_BYTES = W_WL * 1024, X_BYTES = X_WL * 1024, P_BYTES = P_WL * 1024;
@@ -119,7 +123,7 @@ __device__ __forceinline__ void q4k_lds_body(
   const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * (SW ? BN / 2 : BN);  // first weight row / column
   const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
   const int64_t nsb = K / 256, nb = K / 32;
-  const int64_t wrow_bytes = nsb * kQ4Bytes;
+  const int64_t wrow_bytes = nsb * BB;
   const int drow = dpp_scale_row(lane);
   uint8_t* const glds = lds + grp * NS * STAGE;  // this group's ring
   // this group's super-blocks: sb0 .. sb0 + cnt - 1 (the launcher keeps KS <= nsb)
@@ -145,7 +149,7 @@ __device__ __forceinline__ void q4k_lds_body(
   }
 #pragma unroll
   for (int it = 0; it < LW; it++) {
-    const int qq = ((wave + it * NW) % W_WL) * 64 + lane, row = qq / 9, part = qq - 9 * row;
+    const int qq = ((wave + it * NW) % W_WL) * 64 + lane, row = qq / BB16, part = qq - BB16 * row;
     int64_t n;
     if constexpr (SW) {  // tile column row -> gate row f or up row F + f
       const int o = row % (BN / 2);
@@ -188,7 +192,7 @@ __device__ __forceinline__ void q4k_lds_body(
     const int64_t sb = sb0 + (s < cnt ? s : cnt - 1);  // past the group's range: reload its last
     uint8_t* sbase = glds + buf * STAGE;
     issue_region(qx + m_cta * K + sb * 256, 0, LA, A_WL, 0, sbase);
-    issue_region(W + n_cta * wrow_bytes + sb * kQ4Bytes, LA, LW, W_WL, A_BYTES, sbase);
+    issue_region(W + n_cta * wrow_bytes + sb * BB, LA, LW, W_WL, A_BYTES, sbase);
     issue_region(DPP ? static_cast<const void*>(dx + m_cta * nb + 8 * sb)
                      : static_cast<const void*>(dxT + 8 * sb * Mp + m_cta),
                  LA + LW, LX, X_WL, A_BYTES + W_BYTES, sbase);
@@ -230,9 +234,11 @@ __device__ __forceinline__ void q4k_lds_body(
     float d[TN], dmin[TN];
     Q4Scales sc[TN];
     const uint8_t* wr[TN];
+    uint4 qh5[TN];  // Q5: the lane's 16 qh bytes of each weight column
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-      wr[j] = sW + (nl0 + 32 * j + l32) * kQ4Bytes;
+      wr[j] = sW + (nl0 + 32 * j + l32) * BB;
+      if constexpr (Q5) qh5[j] = *reinterpret_cast<const uint4*>(wr[j] + 16 + 16 * h);
       const uint4 hdr = *reinterpret_cast<const uint4*>(wr[j]);
       d[j] = half_to_float(hdr.x & 0xFFFFu);
       dmin[j] = half_to_float(hdr.x >> 16);
@@ -256,7 +262,7 @@ __device__ __forceinline__ void q4k_lds_body(
     for (int c = 0; c < 4; c++) {
       uint4 wraw[TN];
 #pragma unroll
-      for (int j = 0; j < TN; j++) wraw[j] = *reinterpret_cast<const uint4*>(wr[j] + 16 + 32 * c + 16 * h);
+      for (int j = 0; j < TN; j++) wraw[j] = *reinterpret_cast<const uint4*>(wr[j] + QS + 32 * c + 16 * h);
       v4i a[TM][2];
 #pragma unroll
       for (int i = 0; i < TM; i++) {
@@ -275,6 +281,7 @@ __device__ __forceinline__ void q4k_lds_body(
 #pragma unroll
         for (int j = 0; j < TN; j++) {
           b[j] = q4_codes(wraw[j], e);
+          if constexpr (Q5) b[j] |= q5_high(qh5[j], jb);
           dsc[j] = d[j] * static_cast<float>(sub_byte(sc[j].sc_lo, sc[j].sc_hi, jb));
           cc[j] = -kMagic * dsc[j];
         }
@@ -512,6 +519,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
   q4k_lds_body<TM, TN, WM, WN, DPP, NS, KS, A256, false>(W, qx, dx, dxT, Mp, dsp, M, N, K, y, nullptr, 0);
 }
 
+// The same kernel over Q5_K weights.
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q5k_lds_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K, float* __restrict__ y) {
+  q4k_lds_body<TM, TN, WM, WN, false, NS, KS, false, false, true>(W, qx, nullptr, dxT, Mp, dsp, M, N, K, y,
+                                                                  nullptr, 0);
+}
+
 // The same kernel with the SwiGLU epilogue: W holds 2F rows (gate, then up),
 // the output is h [M][F] in bfloat16.
 template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
@@ -537,16 +553,17 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 // order, so the result does not depend on timing.
 struct SmallStage {
   v4i a[8];
-  uint4 w[4], hdr;
+  uint4 w[4], hdr, qh;  // qh: Q5_K only
   v4i p01, p2;
   float4 xs;
 };
 
-template <int SK>
-__global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
+template <int SK, bool Q5>
+__device__ __forceinline__ void q4k_small_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
     int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
     float* __restrict__ y) {
+  constexpr int BB = Q5 ? kQ5Bytes : kQ4Bytes, QS = Q5 ? 48 : 16;
   __shared__ __attribute__((aligned(16))) float s_x[SK][2][8 * 32];
   __shared__ __attribute__((aligned(16))) float4 s_red[SK > 1 ? SK : 1][4][64];
 
@@ -560,16 +577,17 @@ __global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
   m = m < M ? m : M - 1;
   n = n < N ? n : N - 1;
   const int8_t* arow = qx + m * K + 16 * h;
-  const uint8_t* wrow = W + n * nsb * kQ4Bytes;
+  const uint8_t* wrow = W + n * nsb * BB;
   const uint16_t* prow = dsp + (m0 + l32) * nsb * 24;  // rows up to the padding (m0 + 31 < Mp)
 
   auto load = [&](int64_t sb, SmallStage& st) {
 #pragma unroll
     for (int b = 0; b < 8; b++) st.a[b] = *reinterpret_cast<const v4i*>(arow + 256 * sb + 32 * b);
-    const uint8_t* blk = wrow + sb * kQ4Bytes;
+    const uint8_t* blk = wrow + sb * BB;
     st.hdr = *reinterpret_cast<const uint4*>(blk);
 #pragma unroll
-    for (int c = 0; c < 4; c++) st.w[c] = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c + 16 * h);
+    for (int c = 0; c < 4; c++) st.w[c] = *reinterpret_cast<const uint4*>(blk + QS + 32 * c + 16 * h);
+    if constexpr (Q5) st.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * h);
     st.p01 = *reinterpret_cast<const v4i*>(prow + sb * 24 + 8 * h);
     st.p2 = *reinterpret_cast<const v4i*>(prow + sb * 24 + 16);
     // activation scales of the 32 rows, 8 blocks: lane -> (block lane/8, rows 4*(lane%8)..+3)
@@ -593,8 +611,9 @@ __global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
     const Q4Scales sc = unpack_q4_scales(cur.hdr.y, cur.hdr.z, cur.hdr.w);
 #pragma unroll
     for (int jb = 0; jb < 8; jb++) {
-      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[jb], q4_codes(cur.w[jb >> 1], jb & 1),
-                                                           magic, 0, 0, 0);
+      v4i bq = q4_codes(cur.w[jb >> 1], jb & 1);
+      if constexpr (Q5) bq |= q5_high(cur.qh, jb);
+      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[jb], bq, magic, 0, 0, 0);
       const float dsc = d * static_cast<float>(sub_byte(sc.sc_lo, sc.sc_hi, jb));
       const float cc = -kMagic * dsc;
       float dxv[16];
@@ -664,11 +683,38 @@ static void launch_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, in
 }
 
 template <int SK>
+__global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ y) {
+  q4k_small_body<SK, false>(W, qx, dxT, Mp, dsp, M, N, K, y);
+}
+
+template <int SK>
+__global__ __launch_bounds__(64 * SK) void gemm_q5k_small_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ y) {
+  q4k_small_body<SK, true>(W, qx, dxT, Mp, dsp, M, N, K, y);
+}
+
+template <int SK, bool Q5 = false>
 static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                          float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((N + 31) / 32), static_cast<unsigned>((M + 31) / 32));
-  gemm_q4k_small_kernel<SK><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp,
-                                                                  M, N, K, y);
+  if constexpr (Q5)
+    gemm_q5k_small_kernel<SK><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+  else
+    gemm_q4k_small_kernel<SK><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+}
+
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+static void launch_q5k_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
+                           float* y, hipStream_t stream) {
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
+  gemm_q5k_lds_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
+      W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
 }
 
 // OCC: waves per SIMD the register allocation must allow (launch bound);
@@ -804,6 +850,39 @@ hipError_t qg_launch_gemm_q4k_swiglu(const uint8_t* W, const QgWorkspace& ws, in
     case Q4Pick::kLds64x128K2: qg::launch_swiglu<1, 1, 2, 4, 2, 4, 2>(W, ws, M, F, K, h, stream); break;
     case Q4Pick::kLds32x64K4: qg::launch_swiglu<1, 1, 1, 2, 2, 2, 4>(W, ws, M, F, K, h, stream); break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Q5_K: the Q4_K dispatch rule with the block shapes that fit its 176-byte
+// blocks in LDS (two stages of 128x256 or of 64x128 with two K-groups would
+// take 172 KB): 64x128 blocks for the two largest shapes, 32x64 with three
+// K-groups for the split-K ones.
+const char* qg_gemm_q5k_kernel_name(int64_t M, int64_t N, int64_t K) {
+  switch (pick_q4k(M, N, K)) {
+    case Q4Pick::kLds128x256:
+    case Q4Pick::kLds64x128: return "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 4, 1>";
+    case Q4Pick::kLds64x128K2:
+    case Q4Pick::kLds32x64K4: return "gemm_q5k_lds_kernel<1, 1, 1, 2, 2, 2, 3>";
+    case Q4Pick::kSmall1: return "gemm_q5k_small_kernel<1>";
+    case Q4Pick::kSmall2: return "gemm_q5k_small_kernel<2>";
+    case Q4Pick::kSmall4: return "gemm_q5k_small_kernel<4>";
+    case Q4Pick::kSmall8: return "gemm_q5k_small_kernel<8>";
+  }
+  return "?";
+}
+
+hipError_t qg_launch_gemm_q5k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream) {
+  switch (pick_q4k(M, N, K)) {
+    case Q4Pick::kLds128x256:
+    case Q4Pick::kLds64x128: qg::launch_q5k_lds<1, 1, 2, 4, 2, 4, 1>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds64x128K2:
+    case Q4Pick::kLds32x64K4: qg::launch_q5k_lds<1, 1, 1, 2, 2, 2, 3>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall1: qg::launch_small<1, true>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall2: qg::launch_small<2, true>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall4: qg::launch_small<4, true>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kSmall8: qg::launch_small<8, true>(W, ws, M, N, K, y, stream); break;
   }
   return hipGetLastError();
 }

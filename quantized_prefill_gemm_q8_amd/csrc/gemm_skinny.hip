@@ -13,6 +13,8 @@
 //   Q4_K  lane s (0..3): the 16-byte header (d, dmin, packed scales) and the
 //         32 code bytes qs[32s .. 32s+31], i.e. sub-blocks 2s (low nibbles)
 //         and 2s+1 (high nibbles).
+//   Q5_K  the same (qs at byte 48) plus the 32 qh bytes, whose bits 2s and
+//         2s+1 are the fifth bits of the lane's two sub-blocks: five loads.
 //   Q6_K  lane s = 2*half + lh: ql[64half + 16lh ..+16], ql[64half + 32 +
 //         16lh ..+16] and qh[32half + 16lh ..+16], i.e. the values
 //         128half + 32c + 16lh + i (c = 0..3, i < 16), which are the 16-value
@@ -65,6 +67,8 @@ struct SkRaw {
   uint4 a, b, c;    // Q4_K: header, qs lo 16, qs hi 16.  Q6_K: ql0, ql1, qh
   uint32_t s0, s1;  // Q6_K: 8 bytes of the scales / d region (see the load)
   uint4 e;          // Q6_K, coalesced loads: a, b, c, e are the step's chunks l, l+64, l+128, l+192
+                    // Q5_K: qh[0..15]
+  uint4 f;          // Q5_K: qh[16..31]
 };
 
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
@@ -102,7 +106,7 @@ __device__ __forceinline__ float group_sum_last(float v) {
   return v;
 }
 
-// FMT: QG_Q4_K / QG_Q6_K.  MR: activation rows.  R: rows per wavefront step
+// FMT: QG_Q4_K / QG_Q5_K / QG_Q6_K.  MR: activation rows.  R: rows per wavefront step
 // (16/nsb when that divides, else 1).  XM: where the activations are read.
 // CO (Q6_K only): coalesced loads.  A step's sixteen super-blocks are 3360
 // contiguous bytes; when every step starts 16-byte aligned and the matrix ends
@@ -119,9 +123,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     const float* __restrict__ gdS, int64_t N, int64_t K, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   static_assert(CO == kCoNone || FMT == QG_Q6_K, "coalesced loads are for Q6_K");
+  constexpr bool KQ = FMT != QG_Q6_K;  // Q4_K or Q5_K: the Q4_K header and nibble layout
+  constexpr bool Q5 = FMT == QG_Q5_K;
   constexpr int NBUF = CO == kCoDma ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t rowbuf[CO ? kSkThreads / 64 : 1][NBUF][CO ? 4096 : 16];
-  constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : kQ6Bytes;
+  constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : Q5 ? kQ5Bytes : kQ6Bytes;
   constexpr int G = 64 / R;  // lanes per row within a step
   const int64_t nsb = K / 256, nb = K / 32;
   const int lane = threadIdx.x & 63;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       reinterpret_cast<uint4*>(lq)[i] = reinterpret_cast<const uint4*>(qx)[i];
     for (int64_t i = threadIdx.x; i < nd; i += kSkThreads) {
       reinterpret_cast<float4*>(ld)[i] = reinterpret_cast<const float4*>(gdx)[i];
-      if (FMT == QG_Q4_K) reinterpret_cast<float4*>(lS)[i] = reinterpret_cast<const float4*>(gdS)[i];
+      if (KQ) reinterpret_cast<float4*>(lS)[i] = reinterpret_cast<const float4*>(gdS)[i];
     }
     __syncthreads();
     xs = lq;
@@ -165,9 +171,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   uint8_t* const lrow0 = rowbuf[CO ? threadIdx.x >> 6 : 0][0];
   uint8_t* const lrow1 = rowbuf[CO ? threadIdx.x >> 6 : 0][NBUF - 1];
   // lane offset inside a super-block of each of its loads
-  const uint32_t off_a = FMT == QG_Q4_K ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
-  const uint32_t off_b = FMT == QG_Q4_K ? 16u + 32u * s : static_cast<uint32_t>(64 * half + 32 + 16 * lh);
-  const uint32_t off_c = FMT == QG_Q4_K ? 32u + 32u * s : static_cast<uint32_t>(128 + 32 * half + 16 * lh);
+  constexpr uint32_t QS = Q5 ? 48u : 16u;  // first nibble byte (Q4_K, Q5_K)
+  const uint32_t off_a = KQ ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
+  const uint32_t off_b = KQ ? QS + 32u * s : static_cast<uint32_t>(64 * half + 32 + 16 * lh);
+  const uint32_t off_c = KQ ? QS + 16u + 32u * s : static_cast<uint32_t>(128 + 32 * half + 16 * lh);
 
   // per-lane activation data for XREG (a lane's super-block never changes)
   constexpr int XR = XM == kXReg ? MR : 1;
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     const int64_t jb = jb0 < nsb ? jb0 : nsb - 1;  // idle lanes (jb0 >= nsb) read valid data
 #pragma unroll
     for (int m = 0; m < MR; m++) {
-      if (FMT == QG_Q4_K) {
+      if (KQ) {
         const uint4* xv = reinterpret_cast<const uint4*>(qx + m * K + 256 * jb + 64 * s);
 #pragma unroll
         for (int c = 0; c < 4; c++) xr[m][c] = xv[c];
@@ -231,10 +238,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       n = n < N ? n : N - 1;
       jb = jb < nsb ? jb : nsb - 1;
       const uint8_t* blk = W + n * row_bytes + jb * BB;
-      if (FMT == QG_Q4_K) {
+      if (KQ) {
         r.a = *reinterpret_cast<const uint4*>(blk + off_a);
         r.b = *reinterpret_cast<const uint4*>(blk + off_b);
         r.c = *reinterpret_cast<const uint4*>(blk + off_c);
+        if (Q5) {
+          r.e = *reinterpret_cast<const uint4*>(blk + 16);
+          r.f = *reinterpret_cast<const uint4*>(blk + 32);
+        }
       } else {
         r.a = ld16_a2(blk + off_a);
         r.b = ld16_a2(blk + off_b);
@@ -258,6 +269,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     const bool valid = n < N && jbr < nsb;
     const int64_t jb = jbr < nsb ? jbr : nsb - 1;
     uint4 fa, fb, fc;  // this lane's fields (see SkRaw)
+    uint4 fe = {}, ff = {};  // Q5_K: the qh bytes
     uint32_t fs0, fs1;
     if constexpr (CO) {
       // through this wavefront's LDS row buffer: the step's chunks in, this
@@ -286,11 +298,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       fa = raw.a;
       fb = raw.b;
       fc = raw.c;
+      fe = raw.e;
+      ff = raw.f;
       fs0 = raw.s0;
       fs1 = raw.s1;
     }
     {
-      if (FMT == QG_Q4_K) {
+      if (KQ) {
         const float d = half_to_float(fa.x & 0xFFFFu), dmin = half_to_float(fa.x >> 16);
         const Q4Scales sc = unpack_q4_scales(fa.y, fa.z, fa.w);
         const uint32_t scw = s < 2 ? sc.sc_lo : sc.sc_hi, mw = s < 2 ? sc.m_lo : sc.m_hi;
@@ -305,6 +319,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
         for (int i = 0; i < 8; i++) {
           lo[i] = w[i] & 0x0F0F0F0Fu;
           hi[i] = (w[i] >> 4) & 0x0F0F0F0Fu;
+        }
+        if (Q5) {  // bits 2s and 2s+1 of qh[l] are the fifth bits of values 64s + l and 64s + 32 + l
+          const uint32_t qh[8] = {fe.x, fe.y, fe.z, fe.w, ff.x, ff.y, ff.z, ff.w};
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            lo[i] |= ((qh[i] >> (2 * s)) & 0x01010101u) << 4;
+            hi[i] |= ((qh[i] >> (2 * s + 1)) & 0x01010101u) << 4;
+          }
         }
         const int64_t b0 = 8 * jb + 2 * s;
 #pragma unroll
@@ -445,7 +467,7 @@ inline int skinny_rows_per_step(int64_t K) {
 }
 
 inline int64_t skinny_lds_bytes(int fmt, int64_t M, int64_t K) {
-  return fmt == QG_Q4_K ? M * K + 2 * M * (K / 32) * 4 : M * K + M * (K / 32) * 4;
+  return fmt != QG_Q6_K ? M * K + 2 * M * (K / 32) * 4 : M * K + M * (K / 32) * 4;
 }
 
 inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
@@ -549,6 +571,7 @@ const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K)
 
 hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M,
                                  int64_t N, int64_t K, float* y, hipStream_t stream) {
-  return fmt == QG_Q4_K ? qg::launch_skinny_fmt<QG_Q4_K>(W, ws, M, N, K, y, stream)
-                        : qg::launch_skinny_fmt<QG_Q6_K>(W, ws, M, N, K, y, stream);
+  if (fmt == QG_Q4_K) return qg::launch_skinny_fmt<QG_Q4_K>(W, ws, M, N, K, y, stream);
+  if (fmt == QG_Q5_K) return qg::launch_skinny_fmt<QG_Q5_K>(W, ws, M, N, K, y, stream);
+  return qg::launch_skinny_fmt<QG_Q6_K>(W, ws, M, N, K, y, stream);
 }

@@ -53,6 +53,14 @@ __device__ __forceinline__ v4i q4_codes(const uint4& raw, int high) {
              int((raw.z >> sh) & 0x0F0F0F0Fu), int((raw.w >> sh) & 0x0F0F0F0Fu)};
 }
 
+// Q5_K: the fifth code bit of a lane's 16 values of sub-block jb -- bit jb of
+// each of its 16 qh bytes (qh[16h .. 16h + 15] for lane half h) -- moved to
+// bit 4 of each byte, to be or-ed into the nibble codes of q4_codes.
+__device__ __forceinline__ v4i q5_high(const uint4& qh, int jb) {
+  return v4i{int(((qh.x >> jb) & 0x01010101u) << 4), int(((qh.y >> jb) & 0x01010101u) << 4),
+             int(((qh.z >> jb) & 0x01010101u) << 4), int(((qh.w >> jb) & 0x01010101u) << 4)};
+}
+
 // Q6_K: 8 codes, as signed bytes q6 - 32, of 16-value sub-block s for lane half
 // h: values v = 16s + 8h + i, i < 8.  With half = s/8, quarter c = (s%8)/2 and
 // l0 = 16*(s%2) + 8h, the low nibbles are ql[64*half + 32*(c%2) + l0 + i] (low

@@ -189,7 +189,9 @@ SW_SHAPES = [(qg.QG_Q4_K, 512, 3584, 1024),     # fused, 64x128 blocks
              (qg.QG_Q4_K, 100, 2100, 2048),     # fused, 32x64 blocks with four K-groups
              (qg.QG_Q4_K, 64, 512, 1024),       # small-grid GEMM + SwiGLU kernel
              (qg.QG_Q4_K, 3, 1000, 1024),       # skinny GEMM + SwiGLU kernel
-             (qg.QG_Q6_K, 300, 700, 768)]       # Q6_K GEMM + SwiGLU kernel
+             (qg.QG_Q6_K, 300, 700, 768),       # Q6_K GEMM + SwiGLU kernel
+             (qg.QG_Q5_K, 300, 700, 768),       # Q5_K GEMM + SwiGLU kernel
+             (qg.QG_Q5_K, 2, 500, 1024)]        # Q5_K skinny GEMM + SwiGLU kernel
 
 
 @pytest.mark.parametrize("fmt,M,F,K", SW_SHAPES)

@@ -22,8 +22,8 @@ import pins  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [qg.QG_Q4_K, qg.QG_Q6_K]
-FMT_ID = {qg.QG_Q4_K: "q4k", qg.QG_Q6_K: "q6k"}
+FMTS = [qg.QG_Q4_K, qg.QG_Q6_K, qg.QG_Q5_K]
+FMT_ID = {qg.QG_Q4_K: "q4k", qg.QG_Q6_K: "q6k", qg.QG_Q5_K: "q5k"}
 
 
 def gpu_prefill(W: np.ndarray, fmt: int, x: np.ndarray, N: int, path=qg.QG_PATH_AUTO) -> np.ndarray:
@@ -114,7 +114,7 @@ def test_block_partials_bitexact(fmt, shape):
     qx = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
     qx[:, ::32] = 127
     qx[0, :] = -128
-    L = 32 if fmt == qg.QG_Q4_K else 16
+    L = 16 if fmt == qg.QG_Q6_K else 32
     out = torch.empty((M, N, K // L), dtype=torch.int32, device=DEV)
     qg.qgemm_block_partials(to_dev(W), fmt, to_dev(qx), M, N, K, out)
     torch.cuda.synchronize()
@@ -183,7 +183,8 @@ def test_textbook_integer_matmul_exact(fmt, path):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
 def test_worked_examples_all_ones(fmt):
-    blk, fx = pins.q4k_example_block() if fmt == qg.QG_Q4_K else pins.q6k_example_block()
+    blk, fx = {qg.QG_Q4_K: pins.q4k_example_block, qg.QG_Q5_K: pins.q5k_example_block,
+               qg.QG_Q6_K: pins.q6k_example_block}[fmt]()
     x = np.ones((3, 256), np.float32)
     ref = oracle.gemm(fmt, blk, x, 1)
     for p in (qg.QG_PATH_TILED, qg.QG_PATH_SKINNY):
@@ -287,6 +288,12 @@ def test_skinny_all_row_splits(fmt, K, N):
     (qg.QG_Q6_K, 70, 300, 256),        # 64x64 tiles, one super-block
     (qg.QG_Q4_K, 65, 230, 2048),       # one 32x32 tile per wave, K split over 8 waves
     (qg.QG_Q4_K, 100, 200, 512),       # K split over 2 waves
+    (qg.QG_Q5_K, 2049, 16480, 1024),   # Q5_K: 64x128 tiles (the 128x256 pick), ragged
+    (qg.QG_Q5_K, 577, 8240, 768),      # 64x128 tiles, ragged
+    (qg.QG_Q5_K, 330, 2700, 1280),     # 32x64 blocks, K split over 3 groups (1 + 2 + 2)
+    (qg.QG_Q5_K, 170, 2800, 2816),     # 32x64 blocks, K split over 3 groups (3 + 4 + 4)
+    (qg.QG_Q5_K, 65, 230, 2048),       # one 32x32 tile per wave, K split over 8 waves
+    (qg.QG_Q5_K, 100, 200, 512),       # K split over 2 waves
 ])
 def test_tiled_configs_ragged(fmt, M, N, K):
     """Every tiled kernel configuration the dispatcher can pick, on shapes whose
