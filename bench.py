@@ -217,6 +217,8 @@ def main():
               "(the kernel is shown at one GPU's share of the work).", file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
     import numpy as np
     import torch
 
@@ -434,6 +436,9 @@ def main():
             if g.fmt == qg.QG_Q4_K:
                 calls["a256"] = lambda: qg.qgemm_prefill_a256(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws8,
                                                               stream)
+                # the same shape with Q5_K weights (int8 method)
+                W5 = to_dev(synth.make_weights(dataclasses.replace(g, fmt=qg.QG_Q5_K)))
+                calls["q5k"] = lambda: qg.qgemm_prefill(W5, qg.QG_Q5_K, xb, g.M, g.N, g.K, yb, ws8, stream)
             # interleaved rounds, the best of three per variant (clocks drift
             # under sustained load; interleaving keeps the comparison fair)
             us = {}
@@ -452,6 +457,10 @@ def main():
             rate = lambda k: round(g.ops / (us[k] * 1e-6) / 1e12, 1)
             row = {"shape": f"M={g.M} K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'}",
                    "int8_us": round(us["int8"], 2), "int8_tops": rate("int8")}
+            if "q5k" in us:
+                row.update({"q5k_us": round(us["q5k"], 2), "q5k_tops": rate("q5k"),
+                            "q5k_kernel": qg.qgemm_kernel_name(qg.QG_Q5_K, g.M, g.N, g.K)})
+                del W5
             if "a256" in us:
                 row.update({"a256_us": round(us["a256"], 2), "a256_tops": rate("a256"),
                             "a256_kernel": qg.qgemm_kernel_name_a256(g.fmt, g.M, g.N, g.K),
@@ -557,50 +566,54 @@ def main():
     # (M = 1 and M = 8 rows; weight bytes / kernel time against 8 TB/s)
     gemv = {}
     seen = set()
-    for cfg in (2, 3, 4) if args.gemv_steps > 0 else ():
-        for g in synth.CONFIGS[cfg]:
-            key = (g.K, g.N, g.fmt)
-            if key in seen:
-                continue
-            seen.add(key)
-            Wg = to_dev(synth.make_weights(g))
-            xg = to_dev(synth.make_acts(g, rows=8))
-            for Mg in (1, 8):
-                wsg = qg.alloc_workspace(Mg, g.K, dev)
-                yg = torch.empty((Mg, g.N), dtype=torch.float32, device=dev)
-                qg.qgemm_quantize_workspace(xg[:Mg].contiguous(), Mg, g.K, wsg, stream)
+    fmt_name = {qg.QG_Q4_K: "Q4_K", qg.QG_Q5_K: "Q5_K", qg.QG_Q6_K: "Q6_K"}
+    # every Q4_K projection also as Q5_K (the format the pages' decode-GEMV ticket
+    # finds slowest): the same shape and weight recipe, 176-byte blocks
+    gemv_shapes = [g2 for cfg in ((2, 3, 4) if args.gemv_steps > 0 else ()) for g in synth.CONFIGS[cfg]
+                   for g2 in ([g, dataclasses.replace(g, fmt=qg.QG_Q5_K)] if g.fmt == qg.QG_Q4_K else [g])]
+    for g in gemv_shapes:
+        key = (g.K, g.N, g.fmt)
+        if key in seen:
+            continue
+        seen.add(key)
+        Wg = to_dev(synth.make_weights(g))
+        xg = to_dev(synth.make_acts(g, rows=8))
+        for Mg in (1, 8):
+            wsg = qg.alloc_workspace(Mg, g.K, dev)
+            yg = torch.empty((Mg, g.N), dtype=torch.float32, device=dev)
+            qg.qgemm_quantize_workspace(xg[:Mg].contiguous(), Mg, g.K, wsg, stream)
 
-                def gemv_call(g=g, Wg=Wg, wsg=wsg, yg=yg, Mg=Mg):
-                    qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
-                for _ in range(3):
-                    gemv_call()
-                n, r = per_graph(args.gemv_steps)
-                gg = capture(gemv_call, n)
-                time_replays(gg, 1)
-                us = 1e3 * time_replays(gg, r) / (n * r)
-                del gg
-                # cold: launches rotate through copies of W whose footprint exceeds
-                # twice the 256 MB MALL, so every launch streams its weights from HBM
-                copies = [Wg] + [Wg.clone() for _ in range(max(1, -(-COLD_BYTES // g.w_bytes)) - 1)]
-                ring = iter(range(1 << 30))
+            def gemv_call(g=g, Wg=Wg, wsg=wsg, yg=yg, Mg=Mg):
+                qg.qgemm_gemm_quantized(Wg, g.fmt, wsg, Mg, g.N, g.K, yg, stream)
+            for _ in range(3):
+                gemv_call()
+            n, r = per_graph(args.gemv_steps)
+            gg = capture(gemv_call, n)
+            time_replays(gg, 1)
+            us = 1e3 * time_replays(gg, r) / (n * r)
+            del gg
+            # cold: launches rotate through copies of W whose footprint exceeds
+            # twice the 256 MB MALL, so every launch streams its weights from HBM
+            copies = [Wg] + [Wg.clone() for _ in range(max(1, -(-COLD_BYTES // g.w_bytes)) - 1)]
+            ring = iter(range(1 << 30))
 
-                def gemv_cold(g=g, wsg=wsg, yg=yg, Mg=Mg, copies=copies, ring=ring):
-                    qg.qgemm_gemm_quantized(copies[next(ring) % len(copies)], g.fmt, wsg, Mg, g.N, g.K,
-                                            yg, stream)
-                nc = max(n, len(copies))
-                gc = capture(gemv_cold, nc)
-                time_replays(gc, 1)
-                us_cold = 1e3 * time_replays(gc, r) / (nc * r)
-                del gc, copies
-                gbs = g.w_bytes / (us * 1e-6) / 1e9
-                gbs_cold = g.w_bytes / (us_cold * 1e-6) / 1e9
-                gemv[f"K={g.K} N={g.N} {'Q4_K' if g.fmt == qg.QG_Q4_K else 'Q6_K'} M={Mg}"] = {
-                    "kernel": qg.qgemm_kernel_name(g.fmt, Mg, g.N, g.K),
-                    "weight_bytes": g.w_bytes, "avg_launch_us": round(us, 2),
-                    "gbps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                    "cold_avg_launch_us": round(us_cold, 2), "cold_gbps": round(gbs_cold, 1),
-                    "cold_frac_hbm": round(gbs_cold / PEAK_HBM_GBS, 4)}
-            del Wg, xg
+            def gemv_cold(g=g, wsg=wsg, yg=yg, Mg=Mg, copies=copies, ring=ring):
+                qg.qgemm_gemm_quantized(copies[next(ring) % len(copies)], g.fmt, wsg, Mg, g.N, g.K,
+                                        yg, stream)
+            nc = max(n, len(copies))
+            gc = capture(gemv_cold, nc)
+            time_replays(gc, 1)
+            us_cold = 1e3 * time_replays(gc, r) / (nc * r)
+            del gc, copies
+            gbs = g.w_bytes / (us * 1e-6) / 1e9
+            gbs_cold = g.w_bytes / (us_cold * 1e-6) / 1e9
+            gemv[f"K={g.K} N={g.N} {fmt_name[g.fmt]} M={Mg}"] = {
+                "kernel": qg.qgemm_kernel_name(g.fmt, Mg, g.N, g.K),
+                "weight_bytes": g.w_bytes, "avg_launch_us": round(us, 2),
+                "gbps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                "cold_avg_launch_us": round(us_cold, 2), "cold_gbps": round(gbs_cold, 1),
+                "cold_frac_hbm": round(gbs_cold / PEAK_HBM_GBS, 4)}
+        del Wg, xg
 
     # ---------------- LM head on the last token: M = 1, K = 4096 -> N = 152064, Q6_K
     lm_out = None
