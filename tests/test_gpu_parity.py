@@ -277,7 +277,8 @@ def test_skinny_all_row_splits(fmt, K, N):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [
-    (qg.QG_Q4_K, 2049, 16480, 1024),   # 128x256 tiles, ragged M and N
+    (qg.QG_Q4_K, 2049, 15300, 1024),   # 128x256 tiles, ragged M and N
+    (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
     (qg.QG_Q4_K, 577, 8240, 768),      # 64x128 tiles at 4 waves/SIMD, ragged
     (qg.QG_Q4_K, 330, 2700, 1280),     # 64x128 blocks, K split over 2 groups (2 + 3 super-blocks)
     (qg.QG_Q4_K, 170, 2800, 2816),     # 32x64 blocks, K split over 4 groups (2 + 3 + 3 + 3)
