@@ -25,9 +25,10 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 Q4_K = 0
 Q6_K = 1
 Q5_K = 2
+Q8_0 = 3
 F32 = 0
 BF16 = 1
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176, Q8_0: 272}   # bytes per 256 values (Q8_0: 8 x 34)
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
@@ -49,6 +50,8 @@ def _bind(path: str):
     lib.oracle_decode_q4k.restype = None
     lib.oracle_decode_q5k.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_decode_q5k.restype = None
+    lib.oracle_decode_q80.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_decode_q80.restype = None
     lib.oracle_decode_q6k.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.oracle_decode_q6k.restype = None
     lib.oracle_dequant.argtypes = [ci, vp, i64, i64, vp]
@@ -135,6 +138,16 @@ def decode_q5k(W: np.ndarray, N: int, K: int):
     return q, sc, m, d, dmin
 
 
+def decode_q80(W: np.ndarray, N: int, K: int):
+    """Q8_0 (K % 32 == 0): returns (q [N,K] int8, d [N,K/32] f64)."""
+    W = np.ascontiguousarray(W, np.uint8)
+    assert K % 32 == 0 and W.size == N * K // 32 * 34
+    q = np.empty((N, K), np.int8)
+    d = np.empty((N, K // 32), np.float64)
+    _load().oracle_decode_q80(_p(W), N, K, _p(q), _p(d))
+    return q, d
+
+
 def decode_q6k(W: np.ndarray, N: int, K: int):
     """Returns (q6 [N,K] uint8 in 0..63, sc [N,K/16] int8, d [N,K/256] f64)."""
     W = np.ascontiguousarray(W, np.uint8)
@@ -168,7 +181,7 @@ def quantize_act(x: np.ndarray):
 
 
 def block_partials(fmt: int, W: np.ndarray, qx: np.ndarray, N: int) -> np.ndarray:
-    """Integer partials: Q4_K and Q5_K [M, N, K/32], Q6_K [M, N, K/16] (int32)."""
+    """Integer partials: Q4_K, Q5_K, Q8_0 [M, N, K/32], Q6_K [M, N, K/16] (int32)."""
     W = np.ascontiguousarray(W, np.uint8)
     qx = np.ascontiguousarray(qx, np.int8)
     M, K = qx.shape

@@ -40,6 +40,9 @@
  *        qh[32] holding the fifth bit of every code, 128 bytes of low nibbles
  *        placed as Q4_K's codes; q5 = low | 16*((qh[v % 32] >> (v / 32)) & 1)
  *        in [0, 31]; w = d*sc[j]*q5 - dmin*m[j] for sub-block j = v/32.
+ *      Q8_0, 34 B / 32 values (named on aprender issue #5475's page among the
+ *        formats its CPU path runs row by row): fp16 d, then 32 int8 codes q;
+ *        w = d*q.  No mins.
  *
  * The combine is done in fp64 in ascending block order.  Integer partials are
  * exact int32.  All floating point here is IEEE binary32/binary64 with no
@@ -51,7 +54,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_Q4_K = 0, ORACLE_Q6_K = 1, ORACLE_Q5_K = 2 };
+enum { ORACLE_Q4_K = 0, ORACLE_Q6_K = 1, ORACLE_Q5_K = 2, ORACLE_Q8_0 = 3 };
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
 
 /* IEEE binary16 bit pattern -> exact double (normals, subnormals, inf, nan). */
@@ -132,6 +135,19 @@ void oracle_decode_q5k(const uint8_t *W, int64_t N, int64_t K, uint8_t *q, uint8
         decode_q5k_block(W + i * 176, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);
 }
 
+/* ---------------------------------------------------------------- Q8_0 decode */
+
+/* Decode W [N x K] Q8_0 (K % 32 == 0): q [N*K] int8, d [N*K/32]. */
+void oracle_decode_q80(const uint8_t *W, int64_t N, int64_t K, int8_t *q, double *d) {
+    int64_t nb = N * (K / 32);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nb; i++) {
+        const uint8_t *blk = W + i * 34;
+        d[i] = oracle_half_to_double(rd16(blk));
+        for (int t = 0; t < 32; t++) q[i * 32 + t] = (int8_t)blk[2 + t];
+    }
+}
+
 /* ---------------------------------------------------------------- Q6_K decode */
 
 /* Decode one Q6_K block into 6-bit codes q6[256] (0..63), scales sc[16], d. */
@@ -159,6 +175,14 @@ void oracle_decode_q6k(const uint8_t *W, int64_t N, int64_t K, uint8_t *q6, int8
 
 /* Dequantised weights w [N x K] in fp64 (brute-force reference values). */
 void oracle_dequant(int fmt, const uint8_t *W, int64_t N, int64_t K, double *w) {
+    if (fmt == ORACLE_Q8_0) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < N * (K / 32); i++) {
+            double d = oracle_half_to_double(rd16(W + i * 34));
+            for (int t = 0; t < 32; t++) w[i * 32 + t] = d * (double)(int8_t)W[i * 34 + 2 + t];
+        }
+        return;
+    }
     int64_t nb = K / 256;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N * nb; i++) {
@@ -239,12 +263,29 @@ void oracle_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_
 
 /* ----------------------------------------------------- integer block partials */
 
-/* Q4_K, Q5_K: out[m][n][b] = sum_{t<32} q_w[n][32b+t] * q_x[m][32b+t] (K/32 per pair)
+/* Q4_K, Q5_K, Q8_0: out[m][n][b] = sum_{t<32} q_w[n][32b+t] * q_x[m][32b+t] (K/32 per pair)
  * Q6_K: out[m][n][s] = sum_{t<16} (q6[n][16s+t] - 32) * q_x[m][16s+t] (K/16 per pair) */
 void oracle_block_partials(int fmt, const uint8_t *W, const int8_t *qx, int64_t M, int64_t N,
                            int64_t K, int32_t *out) {
     uint8_t *qw = (uint8_t *)malloc((size_t)(N * K));
     int64_t nb = K / 256;
+    if (fmt == ORACLE_Q8_0) {
+        int8_t *q8 = malloc((size_t)(N * K));
+        double *d = malloc(sizeof(double) * (size_t)(N * K / 32));
+        oracle_decode_q80(W, N, K, q8, d);
+        int64_t nblk = K / 32;
+#pragma omp parallel for collapse(2) schedule(static)
+        for (int64_t mi = 0; mi < M; mi++)
+            for (int64_t n = 0; n < N; n++)
+                for (int64_t b = 0; b < nblk; b++) {
+                    int32_t acc = 0;
+                    for (int t = 0; t < 32; t++)
+                        acc += (int32_t)q8[n * K + b * 32 + t] * (int32_t)qx[mi * K + b * 32 + t];
+                    out[(mi * N + n) * nblk + b] = acc;
+                }
+        free(q8); free(d); free(qw);
+        return;
+    }
     if (fmt == ORACLE_Q4_K || fmt == ORACLE_Q5_K) {
         uint8_t *sc = malloc((size_t)(N * K / 32)), *m = malloc((size_t)(N * K / 32));
         double *d = malloc(sizeof(double) * (size_t)(N * nb)), *dm = malloc(sizeof(double) * (size_t)(N * nb));
@@ -279,6 +320,7 @@ void oracle_block_partials(int fmt, const uint8_t *W, const int8_t *qx, int64_t 
  * rows, form every per-block int32 dot product, then combine in fp64 in
  * ascending block order:
  *   Q4_K, Q5_K: y = sum_b dx[b] * ( d*sc[b]*I[b] - dmin*m[b]*S[b] )
+ *   Q8_0: y = sum_b dx[b] * d[b] * I[b]  (d the weight block's own scale)
  *   Q6_K: y = sum_b dx[b] * d * ( sc[2b]*I16[2b] + sc[2b+1]*I16[2b+1] )
  * where b runs over 32-value activation blocks and d, dmin belong to the
  * super-block holding b.  Returns 0, or -1 on allocation failure. */
@@ -288,7 +330,7 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
     if (!rows) nrows = M;
     if (!cols) ncols = N;
     int64_t nb32 = K / 32, nsb = K / 256;
-    int64_t bbytes = fmt == ORACLE_Q4_K ? 144 : fmt == ORACLE_Q5_K ? 176 : 210;
+    int64_t bbytes = fmt == ORACLE_Q4_K ? 144 : fmt == ORACLE_Q5_K ? 176 : fmt == ORACLE_Q8_0 ? 272 : 210;
 
     int8_t *qx = malloc((size_t)(nrows * K));
     float *dx = malloc(sizeof(float) * (size_t)(nrows * nb32));
@@ -296,7 +338,7 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
     uint8_t *qw = malloc((size_t)(ncols * K));
     uint8_t *scw = malloc((size_t)(ncols * K / 16));   /* Q4_K uses K/32 of it */
     uint8_t *mw = malloc((size_t)(ncols * nb32));
-    double *dw = malloc(sizeof(double) * (size_t)(ncols * nsb));
+    double *dw = malloc(sizeof(double) * (size_t)(ncols * nb32));   /* Q8_0: one per 32 values */
     double *dmw = malloc(sizeof(double) * (size_t)(ncols * nsb));
     if (!qx || !dx || !Sx || !qw || !scw || !mw || !dw || !dmw) {
         free(qx); free(dx); free(Sx); free(qw); free(scw); free(mw); free(dw); free(dmw);
@@ -317,6 +359,10 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < ncols; j++) {
         int64_t n = cols ? cols[j] : j;
+        if (fmt == ORACLE_Q8_0) {
+            oracle_decode_q80(W + n * nsb * bbytes, 1, K, (int8_t *)qw + j * K, dw + j * nb32);
+            continue;
+        }
         for (int64_t sb = 0; sb < nsb; sb++) {
             const uint8_t *blk = W + (n * nsb + sb) * bbytes;
             if (fmt == ORACLE_Q4_K)
@@ -340,7 +386,12 @@ int oracle_gemm(int fmt, const uint8_t *W, const void *x, int x_dtype, int64_t M
             for (int64_t b = 0; b < nb32; b++) {
                 double d = dw[j * nsb + b / 8];
                 double dxb = (double)dx[i * nb32 + b];
-                if (fmt != ORACLE_Q6_K) {  /* Q4_K, Q5_K */
+                if (fmt == ORACLE_Q8_0) {
+                    const int8_t *w8 = (const int8_t *)wq;
+                    int32_t I = 0;
+                    for (int t = 0; t < 32; t++) I += (int32_t)w8[32 * b + t] * (int32_t)xq[32 * b + t];
+                    acc += dxb * dw[j * nb32 + b] * (double)I;
+                } else if (fmt != ORACLE_Q6_K) {  /* Q4_K, Q5_K */
                     int32_t I = 0;
                     for (int t = 0; t < 32; t++) I += (int32_t)wq[32 * b + t] * (int32_t)xq[32 * b + t];
                     double sc = scw[j * nb32 + b], m = mw[j * nb32 + b];

@@ -22,9 +22,10 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 Q4_K = 0
 Q6_K = 1
 Q5_K = 2
+Q8_0 = 3
 F32 = 0
 BF16 = 1
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176, Q8_0: 272}   # bytes per 256 values
 
 
 def build() -> str:
@@ -58,6 +59,7 @@ def _load():
         lib.synth_pack_q4k.argtypes = [vp, i64, i64, vp]
         lib.synth_pack_q5k.argtypes = [vp, i64, i64, vp]
         lib.synth_pack_q6k.argtypes = [vp, i64, i64, vp]
+        lib.synth_pack_q80.argtypes = [vp, i64, i64, vp]
         lib.synth_random_blocks.argtypes = [u64, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, vp]
         for f in ("synth_uniform_f64", "synth_normal_f32", "synth_outliers_f32",
@@ -124,7 +126,8 @@ def pack(fmt: int, w: np.ndarray) -> np.ndarray:
     N, K = w.shape
     assert K % 256 == 0
     out = np.empty((N, K // 256 * BLOCK_BYTES[fmt]), np.uint8)
-    fn = {Q4_K: _load().synth_pack_q4k, Q5_K: _load().synth_pack_q5k, Q6_K: _load().synth_pack_q6k}[fmt]
+    fn = {Q4_K: _load().synth_pack_q4k, Q5_K: _load().synth_pack_q5k, Q6_K: _load().synth_pack_q6k,
+          Q8_0: _load().synth_pack_q80}[fmt]
     fn(_ptr(w), N, K, _ptr(out))
     return out
 

@@ -27,6 +27,7 @@
  *     16 int8 scales (one per 16 values) | d (fp16).
  *   Q5_K, 176 B / 256 values: the Q4_K header | qh[32], bit v/32 of byte v%32
  *     the fifth bit of value v | 128 B of low 4 bits placed as Q4_K's.
+ *   Q8_0, 34 B / 32 values: d (fp16) | 32 int8 codes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -239,24 +240,42 @@ void synth_pack_q6k(const float *w, int64_t N, int64_t K, uint8_t *out) {
     }
 }
 
+/* Pack w [N x K] (K % 32 == 0) into Q8_0 blocks: per 32 values d = f16(amax/127),
+ * q = clamp(rint(w / d), -127, 127). */
+void synth_pack_q80(const float *w, int64_t N, int64_t K, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < N * (K / 32); blk++) {
+        const float *x = w + blk * 32;
+        uint8_t *o = out + blk * 34;
+        double amax = 0.0;
+        for (int t = 0; t < 32; t++) if (fabs((double)x[t]) > amax) amax = fabs((double)x[t]);
+        uint16_t hd = to_half(amax / 127.0);
+        double d = from_half(hd);
+        o[0] = (uint8_t)(hd & 0xFF); o[1] = (uint8_t)(hd >> 8);
+        for (int t = 0; t < 32; t++)
+            o[2 + t] = (uint8_t)(int8_t)(d > 0.0 ? clampi((int)nearbyint((double)x[t] / d), -127, 127) : 0);
+    }
+}
+
 /* Random legal blocks: every byte random except the binary16 scale fields,
  * which get a random sign, a random mantissa and an exponent field drawn from
  * [emin, emax] (0 = subnormal) so that d and dmin are always finite.  fmt 0 =
- * Q4_K, 1 = Q6_K, 2 = Q5_K.  Block b uses counters 256*b .. 256*b+255. */
+ * Q4_K, 1 = Q6_K, 2 = Q5_K, 3 = Q8_0 (a block = 256 values: eight 34-byte Q8_0
+ * blocks).  Block b uses counters 256*b .. 256*b+255. */
 void synth_random_blocks(uint64_t seed, int fmt, int64_t nblocks, int emin, int emax,
                          int allow_negative, uint8_t *out) {
-    int bytes = fmt == 0 ? 144 : fmt == 2 ? 176 : 210;
+    int bytes = fmt == 0 ? 144 : fmt == 2 ? 176 : fmt == 3 ? 272 : 210;
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nblocks; b++) {
         uint8_t *o = out + b * bytes;
         for (int i = 0; i < bytes; i++) o[i] = (uint8_t)(synth_u64(seed, (uint64_t)(256 * b + i)) >> 56);
-        int nscale = fmt == 1 ? 1 : 2;
+        int nscale = fmt == 1 ? 1 : fmt == 3 ? 8 : 2;
         for (int k = 0; k < nscale; k++) {
             uint64_t r = synth_u64(seed, (uint64_t)(256 * b + 240 + k));
             int E = emin + (int)((r >> 32) % (uint64_t)(emax - emin + 1));
             uint16_t h = (uint16_t)((E << 10) | (int)(r & 1023));
             if (allow_negative && ((r >> 20) & 1)) h |= 0x8000;
-            int off = fmt == 1 ? 208 : 2 * k;
+            int off = fmt == 1 ? 208 : fmt == 3 ? 34 * k : 2 * k;
             o[off] = (uint8_t)(h & 0xFF);
             o[off + 1] = (uint8_t)(h >> 8);
         }

@@ -6,7 +6,7 @@ AssertionError when the oracle disagrees with what the block format and the
 mathematics fix:
 
   * hand-packed super-blocks whose decoded values are known in closed form
-    (tests/golden/*.txt; Q4_K, Q5_K, Q6_K),
+    (tests/golden/*.txt; Q4_K, Q5_K, Q6_K, Q8_0),
   * bit probes: every stored bit changes exactly one decoded field by a power
     of two, and every field receives exactly its width in bits,
   * binary16 values fixed by IEEE 754,
@@ -42,7 +42,7 @@ import numpy as np
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-Q4_K, Q6_K, Q5_K = 0, 1, 2
+Q4_K, Q6_K, Q5_K, Q8_0 = 0, 1, 2, 3
 
 
 def read_fixture(name: str) -> dict:
@@ -72,6 +72,14 @@ def q5k_example_block() -> tuple[np.ndarray, dict]:
     fx = read_fixture("q5k_worked_example.txt")
     b = _hex(fx["bytes_0_15"]) + _hex(fx["qh_32B"]) + _hex(fx["qs_chunk_32B_repeated_4x"]) * 4
     assert len(b) == 176
+    return np.array(b, np.uint8), fx
+
+
+def q80_example_block() -> tuple[np.ndarray, dict]:
+    """One 34-byte Q8_0 block (32 values)."""
+    fx = read_fixture("q80_worked_example.txt")
+    b = _hex(fx["bytes"])
+    assert len(b) == 34
     return np.array(b, np.uint8), fx
 
 
@@ -125,6 +133,16 @@ def pin_q5k_worked_example(orc):
     assert w.sum() == float(fx["sum_w"]) and w.min() == float(fx["min_w"]) and w.max() == float(fx["max_w"])
 
 
+def pin_q80_worked_example(orc):
+    blk, fx = q80_example_block()
+    q, d = orc.decode_q80(blk, 1, 32)
+    assert d[0, 0] == 0.5 and np.array_equal(q[0].astype(int), np.arange(32) - 16)
+    blk8 = np.tile(blk, 8)                              # eight blocks: one 256-value row
+    w = orc.dequant(Q8_0, blk8, 1, 256)[0]
+    assert w[:32].sum() == float(fx["sum_w"]) and w.min() == float(fx["min_w"]) and w.max() == float(fx["max_w"])
+    assert np.array_equal(w, np.tile(w[:32], 8))
+
+
 def pin_q6k_worked_example(orc):
     blk, fx = q6k_example_block()
     q6, sc, d = orc.decode_q6k(blk, 1, 256)
@@ -148,6 +166,11 @@ def _fields_q5k(orc, blk):
     q, sc, m, d, dmin = orc.decode_q5k(blk, 1, 256)
     return {"q": q[0].astype(np.int64), "sc": sc[0].astype(np.int64), "m": m[0].astype(np.int64),
             "d": d[0], "dmin": dmin[0]}
+
+
+def _fields_q80(orc, blk):
+    q, d = orc.decode_q80(blk, 1, 32)
+    return {"q": q[0].astype(np.int64), "d": d[0]}
 
 
 def _fields_q6k(orc, blk):
@@ -201,6 +224,11 @@ def pin_q4k_bit_probe(orc):
 def pin_q5k_bit_probe(orc):
     blk = synth.random_blocks(Q5_K, 1, 256, seed=79, emin=1, emax=14, allow_negative=False)[0]
     _bit_probe(orc, blk, 176, _fields_q5k, {"q": 5, "sc": 6, "m": 6}, {"d": 0, "dmin": 2})
+
+
+def pin_q80_bit_probe(orc):
+    blk = synth.random_blocks(Q8_0, 1, 256, seed=80, emin=1, emax=14, allow_negative=False)[0][:34]
+    _bit_probe(orc, blk.copy(), 34, _fields_q80, {"q": 8}, {"d": 0})
 
 
 def pin_q6k_bit_probe(orc):
@@ -314,7 +342,7 @@ def _bruteforce_case(orc, fmt, W, x, N):
 
 
 def pin_gemm_bruteforce(orc):
-    for fmt in (Q4_K, Q5_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K, Q8_0):
         for (M, N, K, seed) in ((1, 1, 256, 1), (3, 5, 256, 2), (4, 8, 512, 3), (2, 7, 768, 4)):
             Wr = synth.random_blocks(fmt, N, K, seed=100 + seed, emin=3, emax=18)
             Wp = synth.pack(fmt, synth.normal(200 + seed, (N, K), 0.0, 0.02))
@@ -339,6 +367,12 @@ def _textbook_blocks(fmt, N, K, seed):
             byte = 16 + 32 * (v // 64) + v % 32
             shift = 0 if v % 64 < 32 else 4
             W[:, :, byte] |= (codes[:, :, v] << shift).astype(np.uint8)
+        vals = codes
+    elif fmt == Q8_0:
+        W = np.zeros((N, nb, 8, 34), np.uint8)
+        W[:, :, :, 0:2] = (0x00, 0x3C)           # d = 1 in every 32-value block
+        codes = rng.integers(-127, 128, size=(N, nb, 8, 32))
+        W[:, :, :, 2:] = codes.astype(np.int8).view(np.uint8)
         vals = codes
     elif fmt == Q5_K:
         W = np.zeros((N, nb, 176), np.uint8)
@@ -375,7 +409,7 @@ def _integer_acts(M, K, seed):
 
 
 def pin_gemm_textbook(orc):
-    for fmt in (Q4_K, Q5_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K, Q8_0):
         M, N, K = 5, 6, 512
         W, wv = _textbook_blocks(fmt, N, K, seed=9 + fmt)
         xi = _integer_acts(M, K, seed=19 + fmt)
@@ -398,13 +432,16 @@ def pin_gemm_worked_examples(orc):
     blk5, fx5 = q5k_example_block()
     y5 = orc.gemm(Q5_K, blk5, x, 1)[0, 0]
     assert abs(y5 - float(fx5["sum_w"]) * 127 * dx) <= 1e-9, y5
+    blk8, fx8 = q80_example_block()
+    y8 = orc.gemm(Q8_0, np.tile(blk8, 8), x, 1)[0, 0]
+    assert abs(y8 - 8 * float(fx8["sum_w"]) * 127 * dx) <= 1e-12, y8
     blk6, fx6 = q6k_example_block()
     y6 = orc.gemm(Q6_K, blk6, x, 1)[0, 0]
     assert abs(y6 - float(fx6["sum_w"]) * 127 * dx) <= 1e-12, y6
 
 
 def pin_gemm_selection_and_scaling(orc):
-    for fmt in (Q4_K, Q5_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K, Q8_0):
         M, N, K = 6, 9, 512
         W = synth.pack(fmt, synth.normal(41 + fmt, (N, K), 0.0, 0.02))
         x = _acts(43 + fmt, M, K)
@@ -421,7 +458,7 @@ def pin_gemm_selection_and_scaling(orc):
 def pin_gemm_semantic_bound(orc):
     """The quantised result stays within the activation-rounding bound of the
     unquantised product (catches a quantiser that only agrees with itself)."""
-    for fmt in (Q4_K, Q5_K, Q6_K):
+    for fmt in (Q4_K, Q5_K, Q6_K, Q8_0):
         M, N, K = 4, 6, 768
         W = synth.pack(fmt, synth.normal(51 + fmt, (N, K), 0.0, 0.02))
         x = _acts(53 + fmt, M, K)
@@ -756,7 +793,8 @@ def pin_gemm_swiglu_bruteforce(orc):
 
 
 ALL_PINS = [pin_half, pin_q4k_worked_example, pin_q6k_worked_example, pin_q4k_bit_probe,
-            pin_q6k_bit_probe, pin_q5k_worked_example, pin_q5k_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
+            pin_q6k_bit_probe, pin_q5k_worked_example, pin_q5k_bit_probe, pin_q80_worked_example,
+            pin_q80_bit_probe, pin_quant_all_ones, pin_quant_zero_block, pin_quant_properties,
             pin_quant_symmetry_and_scaling, pin_quant_integer_blocks, pin_quant_bf16_matches_f32,
             pin_gemm_bruteforce, pin_gemm_textbook, pin_gemm_worked_examples,
             pin_gemm_selection_and_scaling, pin_gemm_semantic_bound,

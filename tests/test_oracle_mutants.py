@@ -117,6 +117,15 @@ MUTANTS = [
     ("q5k_block_stride",
      "decode_q5k_block(W + i * 176, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);",
      "decode_q5k_block(W + i * 144, q + i * 256, sc + i * 8, m + i * 8, d + i, dmin + i);"),
+    ("q80_codes_unsigned",
+     "for (int t = 0; t < 32; t++) q[i * 32 + t] = (int8_t)blk[2 + t];",
+     "for (int t = 0; t < 32; t++) q[i * 32 + t] = (int8_t)(blk[2 + t] & 0x7F);"),
+    ("q80_scale_from_codes",
+     "d[i] = oracle_half_to_double(rd16(blk));",
+     "d[i] = oracle_half_to_double(rd16(blk + 32));"),
+    ("q80_gemm_first_block_scale",
+     "acc += dxb * dw[j * nb32 + b] * (double)I;",
+     "acc += dxb * dw[j * nb32 + b / 8 * 8] * (double)I;"),
     ("rms_mean_not_divided",
      "double v = ss / (double)K + (double)eps;",
      "double v = ss + (double)eps;"),
