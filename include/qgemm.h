@@ -29,8 +29,14 @@
  *         placed as Q4_K's codes; w = d*sc*q5 - dmin*m, q5 in [0, 31].  The
  *         format aprender issue #5305's decode-GEMV ticket #5221 finds slowest;
  *         it runs through the Q4_K kernels (tiled, small-grid, skinny) with the
- *         fifth bit or-ed into the codes.  The per-256 entry points take
- *         Q4_K only and the fp16-branch ones Q4_K / Q6_K (QG_EFMT for Q5_K).
+ *         fifth bit or-ed into the codes.
+ *   Q8_0: 34 bytes per 32 values -- d, then 32 int8 codes; w = d*q (named on
+ *         aprender issue #5475's page among the formats its CPU path runs row
+ *         by row).  K is still a multiple of 256 (a row is K/32 blocks).  The
+ *         codes go to the matrix core as they are, with d as the block scale
+ *         and no min term; the skinny kernel takes it for M <= 4.
+ * The per-256 entry points take Q4_K only and the fp16-branch ones Q4_K /
+ * Q6_K (QG_EFMT for Q5_K and Q8_0).
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
@@ -57,7 +63,7 @@ extern "C" {
 #endif
 
 /* weight formats */
-enum { QG_Q4_K = 0, QG_Q6_K = 1, QG_Q5_K = 2 };
+enum { QG_Q4_K = 0, QG_Q6_K = 1, QG_Q5_K = 2, QG_Q8_0 = 3 };
 /* activation element types: IEEE binary32, or bfloat16 (raw 16-bit patterns) */
 enum { QG_F32 = 0, QG_BF16 = 1 };
 /* kernel path selection for qgemm_prefill_ex */
@@ -66,7 +72,7 @@ enum { QG_PATH_AUTO = 0, QG_PATH_TILED = 1, QG_PATH_SKINNY = 2 };
 enum {
     QG_OK = 0,
     QG_EINVAL = -1,     /* null pointer, M/N/K < 1, K % 256 != 0, size overflow, bad path */
-    QG_EFMT = -2,       /* fmt not QG_Q4_K / QG_Q5_K / QG_Q6_K, or not one the entry point takes */
+    QG_EFMT = -2,       /* fmt not QG_Q4_K / QG_Q5_K / QG_Q6_K / QG_Q8_0, or not one the entry point takes */
     QG_EDTYPE = -3,     /* x_dtype not QG_F32 / QG_BF16 */
     QG_EWORKSPACE = -4, /* workspace NULL, smaller than qgemm_workspace_bytes, or not 256-B aligned */
     QG_EALIGN = -5,     /* q_weights not 16-B aligned, x not aligned to 16 B, y not 16-B aligned */

@@ -1,5 +1,5 @@
 """Python binding of libqgemm.so (include/qgemm.h): the MI355X batched prefill
-matmul over GGUF Q4_K / Q5_K / Q6_K weights with int8-quantised activations.
+matmul over GGUF Q4_K / Q5_K / Q6_K / Q8_0 weights with int8-quantised activations.
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of libqgemm.so; this module turns torch tensors into device pointers
@@ -16,11 +16,11 @@ import torch
 
 from ._build import LIB as _LIB_PATH
 
-QG_Q4_K, QG_Q6_K, QG_Q5_K = 0, 1, 2
+QG_Q4_K, QG_Q6_K, QG_Q5_K, QG_Q8_0 = 0, 1, 2, 3
 QG_F32, QG_BF16 = 0, 1
 QG_PATH_AUTO, QG_PATH_TILED, QG_PATH_SKINNY = 0, 1, 2
 QG_SKINNY_MAX_M = 8
-BLOCK_BYTES = {QG_Q4_K: 144, QG_Q6_K: 210, QG_Q5_K: 176}
+BLOCK_BYTES = {QG_Q4_K: 144, QG_Q6_K: 210, QG_Q5_K: 176, QG_Q8_0: 272}  # per 256 values
 SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_lm_head",
            "qgemm_quantize_workspace", "qgemm_gemm_quantized",
            "qgemm_strerror", "qgemm_kernel_name", "qgemm_quantize_act", "qgemm_dequant",

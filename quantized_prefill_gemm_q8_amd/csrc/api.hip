@@ -55,7 +55,7 @@ int check_device() {
 
 int check_common(const void* W, int fmt, int64_t N, int64_t K) {
   if (!W) return QG_EINVAL;
-  if (fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K) return QG_EFMT;
+  if (fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K && fmt != QG_Q8_0) return QG_EFMT;
   if (N < 1 || K < 256 || K % 256 != 0) return QG_EINVAL;
   if (N > (INT64_C(1) << 40) / K) return QG_EINVAL;
   if (!aligned(W, 16)) return QG_EALIGN;
@@ -69,11 +69,12 @@ hipError_t launch_tiled(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_
                         float* y, hipStream_t s) {
   if (fmt == QG_Q4_K) return qg_launch_gemm_q4k(W, ws, M, N, K, y, s);
   if (fmt == QG_Q5_K) return qg_launch_gemm_q5k(W, ws, M, N, K, y, s);
+  if (fmt == QG_Q8_0) return qg_launch_gemm_q80(W, ws, M, N, K, y, s);
   return qg_launch_gemm_q6k(W, ws, M, N, K, y, s);
 }
 
-// QG_PATH_AUTO: the skinny kernel for M <= 8 Q6_K rows and M <= 4 Q4_K / Q5_K
-// rows (measured: from 5 rows on, the Q4_K tiled kernels are faster, while the
+// QG_PATH_AUTO: the skinny kernel for M <= 8 Q6_K rows and M <= 4 Q4_K / Q5_K /
+// Q8_0 rows (measured: from 5 rows on, the Q4_K tiled kernels are faster, while the
 // Q6_K skinny kernel stays ahead up to 8 rows).
 bool auto_skinny(int fmt, int64_t M) { return M <= (fmt == QG_Q6_K ? QG_SKINNY_MAX_M : 4); }
 
@@ -179,13 +180,14 @@ int qgemm_lm_head(const void* q_weights, int fmt, const void* x_row, int x_dtype
 }
 
 const char* qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path) {
-  if (fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K) return NULL;
+  if (fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K && fmt != QG_Q8_0) return NULL;
   if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
   if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return NULL;
   if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return NULL;
   const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
   if (skinny) return qg_gemm_skinny_kernel_name(fmt, M, N, K);
   if (fmt == QG_Q5_K) return qg_gemm_q5k_kernel_name(M, N, K);
+  if (fmt == QG_Q8_0) return qg_gemm_q80_kernel_name(M, N, K);
   return fmt == QG_Q4_K ? qg_gemm_q4k_kernel_name(M, N, K) : qg_gemm_q6k_kernel_name(M, N, K);
 }
 
@@ -193,7 +195,7 @@ const char* qgemm_strerror(int code) {
   switch (code) {
     case QG_OK: return "success";
     case QG_EINVAL: return "invalid argument (null pointer, size < 1, K not a multiple of 256, size overflow or bad path)";
-    case QG_EFMT: return "unsupported weight format (QG_Q4_K, QG_Q5_K, QG_Q6_K; the per-256 entry points take Q4_K only, the fp16 branch Q4_K and Q6_K)";
+    case QG_EFMT: return "unsupported weight format (QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_Q8_0; the per-256 entry points take Q4_K only, the fp16 branch Q4_K and Q6_K)";
     case QG_EDTYPE: return "unsupported activation type (expected QG_F32 or QG_BF16)";
     case QG_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case QG_EALIGN: return "pointer not 16-byte aligned";
@@ -335,7 +337,7 @@ int qgemm_to_f16(const void* x, int x_dtype, int64_t M, int64_t K, uint16_t* x16
 
 int qgemm_dequant_f16(const void* q_weights, int fmt, int64_t N, int64_t K, uint16_t* w16,
                       void* stream) {
-  if (fmt == QG_Q5_K) return QG_EFMT;
+  if (fmt == QG_Q5_K || fmt == QG_Q8_0) return QG_EFMT;
   int rc = check_common(q_weights, fmt, N, K);
   if (rc) return rc;
   if (!w16) return QG_EINVAL;
@@ -349,7 +351,7 @@ int qgemm_dequant_f16(const void* q_weights, int fmt, int64_t N, int64_t K, uint
 int qgemm_prefill_deq_f16(const void* q_weights, int fmt, const void* x, int x_dtype, int64_t M,
                           int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  if (fmt == QG_Q5_K) return QG_EFMT;
+  if (fmt == QG_Q5_K || fmt == QG_Q8_0) return QG_EFMT;
   int rc = check_common(q_weights, fmt, N, K);
   if (rc) return rc;
   if (!x || !y || M < 1) return QG_EINVAL;
@@ -428,7 +430,7 @@ static bool swiglu_layout(int fmt, int64_t M, int64_t F, int64_t K, Layout* L, i
 }
 
 size_t qgemm_swiglu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K) {
-  if (fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K) return 0;
+  if (fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K && fmt != QG_Q8_0) return 0;
   Layout L;
   int64_t total;
   if (!swiglu_layout(fmt, M, F, K, &L, &total)) return 0;
@@ -479,7 +481,7 @@ int qgemm_prefill_swiglu(const void* q_weights, int fmt, const void* x, int x_dt
 }
 
 const char* qgemm_kernel_name_swiglu(int fmt, int64_t M, int64_t F, int64_t K) {
-  if ((fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K) || M < 1 || F < 1 || K < 256 || K % 256 != 0)
+  if ((fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K && fmt != QG_Q8_0) || M < 1 || F < 1 || K < 256 || K % 256 != 0)
     return NULL;
   if (F > (INT64_C(1) << 39) / K) return NULL;
   if (swiglu_fused(fmt, M, F, K)) return qg_gemm_q4k_swiglu_kernel_name(M, F, K);

@@ -19,6 +19,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kQ4Bytes = 144;  // bytes per Q4_K super-block (256 values)
 constexpr int kQ6Bytes = 210;  // bytes per Q6_K super-block (256 values)
 constexpr int kQ5Bytes = 176;  // bytes per Q5_K super-block (256 values)
+constexpr int kQ8Bytes = 34;   // bytes per Q8_0 block (32 values)
 constexpr int kRowPad = 256;   // activation rows are padded to this multiple in the workspace
 
 // 1.5 * 2^23 as an fp32 bit pattern.  An int32 accumulator started at this
@@ -160,6 +161,10 @@ const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256 =
 hipError_t qg_launch_gemm_q5k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream);
 const char* qg_gemm_q5k_kernel_name(int64_t M, int64_t N, int64_t K);
+// Q8_0: the tiled Q4_K kernel body with the int8 codes taken as they are
+hipError_t qg_launch_gemm_q80(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream);
+const char* qg_gemm_q80_kernel_name(int64_t M, int64_t N, int64_t K);
 // Q4_K gate+up GEMM with the SwiGLU epilogue (W: 2F rows, gate then up; h:
 // bfloat16 [M][F]).  Fusable when the problem takes one of the LDS-tiled
 // kernels and the weight offsets fit the kernels' 32-bit load offsets.

@@ -1,4 +1,4 @@
-// Debug decoder: GGUF Q4_K / Q5_K / Q6_K super-blocks to fp32 weights, one thread per
+// Debug decoder: GGUF Q4_K / Q5_K / Q6_K / Q8_0 blocks to fp32 weights, one thread per
 // value.  Exposed as a test hook so the GPU's reading of the block layout can be
 // compared value by value with an independent decoder.  Each output is the
 // correctly rounded fp32 value of the exact decoded weight:
@@ -30,6 +30,15 @@ __global__ __launch_bounds__(256) void dequant_q4k_kernel(const uint8_t* __restr
   w[i] = __builtin_fmaf(d * sc, static_cast<float>(q), -(dmin * m));
 }
 
+// Q8_0: d * q, exact in fp32 (an 11-bit binary16 times an 8-bit integer).
+__global__ __launch_bounds__(256) void dequant_q80_kernel(const uint8_t* __restrict__ W,
+                                                          int64_t total, float* __restrict__ w) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const uint8_t* blk = W + (i >> 5) * kQ8Bytes;
+  w[i] = half_to_float(load_u16(blk)) * static_cast<float>(static_cast<int8_t>(blk[2 + (i & 31)]));
+}
+
 __global__ __launch_bounds__(256) void dequant_q6k_kernel(const uint8_t* __restrict__ W,
                                                           int64_t total, float* __restrict__ w) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -56,6 +65,8 @@ hipError_t qg_launch_dequant(const uint8_t* W, int fmt, int64_t N, int64_t K, fl
     qg::dequant_q4k_kernel<false><<<grid, dim3(256), 0, stream>>>(W, total, w);
   else if (fmt == QG_Q5_K)
     qg::dequant_q4k_kernel<true><<<grid, dim3(256), 0, stream>>>(W, total, w);
+  else if (fmt == QG_Q8_0)
+    qg::dequant_q80_kernel<<<grid, dim3(256), 0, stream>>>(W, total, w);
   else
     qg::dequant_q6k_kernel<<<grid, dim3(256), 0, stream>>>(W, total, w);
   return hipGetLastError();

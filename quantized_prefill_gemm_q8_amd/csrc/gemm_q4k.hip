@@ -94,18 +94,23 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 // through LDS and the former write h = silu(gate) * up as bfloat16 [M][F].
 // Q5: Q5_K blocks (176 bytes: the Q4_K header, qh[32], the nibbles); each
 // lane also stages its 16 qh bytes and ors bit jb of each into its codes.
-template <int TM, int TN, int WM, int WN, bool DPP, int NS, int KS, bool A256, bool SW, bool Q5 = false>
+// Q8: Q8_0 blocks (eight 34-byte blocks of an fp16 d and 32 int8 codes per
+// 256 values): the codes go to the matrix core as they are, dsc = d per
+// 32-value block, no min term (no dS pieces staged).
+template <int TM, int TN, int WM, int WN, bool DPP, int NS, int KS, bool A256, bool SW, bool Q5 = false,
+          bool Q8 = false>
 __device__ __forceinline__ void q4k_lds_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
     int64_t N, int64_t K, float* __restrict__ y, uint16_t* __restrict__ hout, int64_t F) {
   static_assert(!SW || (WN % 2 == 0 && !A256 && !DPP), "SwiGLU pairs waves wn and wn + WN/2");
-  static_assert(!Q5 || (!A256 && !DPP && !SW), "Q5_K runs the per-32 method");
+  static_assert(!(Q5 || Q8) || (!A256 && !DPP && !SW), "Q5_K and Q8_0 run the per-32 method");
   constexpr int NW = WM * WN;  // waves per group
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-  constexpr int BB = Q5 ? kQ5Bytes : kQ4Bytes, BB16 = BB / 16, QS = Q5 ? 48 : 16;  // block bytes, nibble offset
+  // bytes per 256 values of a weight row, and where the Q4_K / Q5_K nibbles start
+  constexpr int BB = Q8 ? 8 * kQ8Bytes : Q5 ? kQ5Bytes : kQ4Bytes, BB16 = BB / 16, QS = Q5 ? 48 : 16;
   static_assert(kRowPad % BM == 0, "BM must divide the workspace row padding");
-  constexpr int A_CH = BM * 256 / 16, W_CH = BN * BB16, X_CH = BM * 32 / 16, P_CH = BM * 48 / 16;
+  constexpr int A_CH = BM * 256 / 16, W_CH = BN * BB16, X_CH = BM * 32 / 16, P_CH = Q8 ? 0 : BM * 48 / 16;
   // wave-loads per region and region sizes in LDS (whole wave-loads)
   constexpr int A_WL = (A_CH + 63) / 64, W_WL = (W_CH + 63) / 64, X_WL = (X_CH + 63) / 64, P_WL = (P_CH + 63) / 64;
   constexpr int A_BYTES = A_WL * 1024, W_BYTES = W_WL * 1024, X_BYTES = X_WL * 1024, P_BYTES = P_WL * 1024;
@@ -139,6 +144,7 @@ __device__ __forceinline__ void q4k_lds_body(
   // one, lanes past the region's end to offset 0).
   constexpr int LA = (A_WL + NW - 1) / NW, LW = (W_WL + NW - 1) / NW;
   constexpr int LX = (X_WL + NW - 1) / NW, LP = (P_WL + NW - 1) / NW;
+  constexpr int P_WLM = P_WL > 0 ? P_WL : 1;  // modulus for the (empty, for Q8_0) dS-piece loops
   uint32_t voff[LA + LW + LX + LP];
 #pragma unroll
   for (int it = 0; it < LA; it++) {
@@ -175,7 +181,7 @@ __device__ __forceinline__ void q4k_lds_body(
   }
 #pragma unroll
   for (int it = 0; it < LP; it++) {
-    const int qq = ((wave + it * NW) % P_WL) * 64 + lane, row = qq / 3, piece = qq - 3 * row;
+    const int qq = ((wave + it * NW) % P_WLM) * 64 + lane, row = qq / 3, piece = qq - 3 * row;
     voff[LA + LW + LX + it] = qq < P_CH ? static_cast<uint32_t>(row * nsb * 48 + 16 * piece) : 0u;
   }
   constexpr int LPT = LA + LW + LX + LP;  // loads per thread per stage
@@ -238,6 +244,7 @@ __device__ __forceinline__ void q4k_lds_body(
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       wr[j] = sW + (nl0 + 32 * j + l32) * BB;
+      if constexpr (Q8) continue;  // no super-block header
       if constexpr (Q5) qh5[j] = *reinterpret_cast<const uint4*>(wr[j] + 16 + 16 * h);
       const uint4 hdr = *reinterpret_cast<const uint4*>(wr[j]);
       d[j] = half_to_float(hdr.x & 0xFFFFu);
@@ -262,7 +269,8 @@ __device__ __forceinline__ void q4k_lds_body(
     for (int c = 0; c < 4; c++) {
       uint4 wraw[TN];
 #pragma unroll
-      for (int j = 0; j < TN; j++) wraw[j] = *reinterpret_cast<const uint4*>(wr[j] + QS + 32 * c + 16 * h);
+      for (int j = 0; j < TN; j++)
+        if constexpr (!Q8) wraw[j] = *reinterpret_cast<const uint4*>(wr[j] + QS + 32 * c + 16 * h);
       v4i a[TM][2];
 #pragma unroll
       for (int i = 0; i < TM; i++) {
@@ -280,9 +288,14 @@ __device__ __forceinline__ void q4k_lds_body(
         float dsc[TN], cc[TN];
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-          b[j] = q4_codes(wraw[j], e);
-          if constexpr (Q5) b[j] |= q5_high(qh5[j], jb);
-          dsc[j] = d[j] * static_cast<float>(sub_byte(sc[j].sc_lo, sc[j].sc_hi, jb));
+          if constexpr (Q8) {
+            b[j] = q8_codes(wr[j], jb, h);
+            dsc[j] = q8_scale(wr[j], jb);
+          } else {
+            b[j] = q4_codes(wraw[j], e);
+            if constexpr (Q5) b[j] |= q5_high(qh5[j], jb);
+            dsc[j] = d[j] * static_cast<float>(sub_byte(sc[j].sc_lo, sc[j].sc_hi, jb));
+          }
           cc[j] = -kMagic * dsc[j];
         }
         if constexpr (A256) {
@@ -354,7 +367,8 @@ __device__ __forceinline__ void q4k_lds_body(
             acc[i][j][r] = __builtin_fmaf(static_cast<float>(acc_i[i][j][r]) * d[j], dxv[r], acc[i][j][r]);
       }
     }
-    // min term of the super-block on the matrix core
+    // min term of the super-block on the matrix core (Q8_0 has none)
+    if constexpr (Q8) continue;
     v8bf mb[TN];
 #pragma unroll
     for (int j = 0; j < TN; j++) mb[j] = mins_bf16(sc[j].m_lo, sc[j].m_hi);
@@ -526,6 +540,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
     int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K, float* __restrict__ y) {
   q4k_lds_body<TM, TN, WM, WN, false, NS, KS, false, false, true>(W, qx, nullptr, dxT, Mp, dsp, M, N, K, y,
                                                                   nullptr, 0);
+}
+
+// The same kernel over Q8_0 weights.
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q80_lds_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, int64_t M, int64_t N, int64_t K, float* __restrict__ y) {
+  q4k_lds_body<TM, TN, WM, WN, false, NS, KS, false, false, false, true>(W, qx, nullptr, dxT, Mp, nullptr, M, N,
+                                                                         K, y, nullptr, 0);
 }
 
 // The same kernel with the SwiGLU epilogue: W holds 2F rows (gate, then up),
@@ -709,6 +732,15 @@ static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int
 }
 
 template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+static void launch_q80_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
+                           float* y, hipStream_t stream) {
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
+  gemm_q80_lds_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
+      W, ws.q, ws.dxT, ws.Mp, M, N, K, y);
+}
+
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
 static void launch_q5k_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                            float* y, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
@@ -870,12 +902,12 @@ hipError_t qg_launch_gemm_q4k_swiglu(const uint8_t* W, const QgWorkspace& ws, in
 
 // Q5_K: the Q4_K dispatch rule with the block shapes that fit its 176-byte
 // blocks in LDS (two stages of 128x256 or of 64x128 with two K-groups would
-// take 172 KB): 64x128 blocks for the two largest shapes, 32x64 with three
-// K-groups for the split-K ones.
+// take 172 KB): 64x128 blocks for the two largest shapes (one per CU: 88 KB),
+// 32x64 with three K-groups for the split-K ones.
 const char* qg_gemm_q5k_kernel_name(int64_t M, int64_t N, int64_t K) {
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256:
-    case Q4Pick::kLds64x128: return "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 4, 1>";
+    case Q4Pick::kLds64x128: return "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 2, 1>";
     case Q4Pick::kLds64x128K2:
     case Q4Pick::kLds32x64K4: return "gemm_q5k_lds_kernel<1, 1, 1, 2, 2, 2, 3>";
     case Q4Pick::kSmall1: return "gemm_q5k_small_kernel<1>";
@@ -890,13 +922,47 @@ hipError_t qg_launch_gemm_q5k(const uint8_t* W, const QgWorkspace& ws, int64_t M
                               int64_t K, float* y, hipStream_t stream) {
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256:
-    case Q4Pick::kLds64x128: qg::launch_q5k_lds<1, 1, 2, 4, 2, 4, 1>(W, ws, M, N, K, y, stream); break;
+    case Q4Pick::kLds64x128: qg::launch_q5k_lds<1, 1, 2, 4, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kLds64x128K2:
     case Q4Pick::kLds32x64K4: qg::launch_q5k_lds<1, 1, 1, 2, 2, 2, 3>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall1: qg::launch_small<1, true>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall2: qg::launch_small<2, true>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall4: qg::launch_small<4, true>(W, ws, M, N, K, y, stream); break;
     case Q4Pick::kSmall8: qg::launch_small<8, true>(W, ws, M, N, K, y, stream); break;
+  }
+  return hipGetLastError();
+}
+
+// Q8_0 (272 bytes per 256 values of a row): 64x128 blocks for the large
+// grids (one per CU: two stages take 104 KB), otherwise 32x64 blocks with
+// three K-groups (156 KB), or one where the row has fewer than three
+// super-block lengths.
+namespace {
+enum class Q8Pick { kLds64x128, kLds32x64K3, kLds32x64 };
+Q8Pick pick_q80(int64_t M, int64_t N, int64_t K) {
+  switch (pick_q4k(M, N, K)) {
+    case Q4Pick::kLds128x256:
+    case Q4Pick::kLds64x128: return Q8Pick::kLds64x128;
+    default: return K / 256 >= 3 ? Q8Pick::kLds32x64K3 : Q8Pick::kLds32x64;
+  }
+}
+}  // namespace
+
+const char* qg_gemm_q80_kernel_name(int64_t M, int64_t N, int64_t K) {
+  switch (pick_q80(M, N, K)) {
+    case Q8Pick::kLds64x128: return "gemm_q80_lds_kernel<1, 1, 2, 4, 2, 2, 1>";
+    case Q8Pick::kLds32x64K3: return "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 3>";
+    case Q8Pick::kLds32x64: return "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 1>";
+  }
+  return "?";
+}
+
+hipError_t qg_launch_gemm_q80(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
+                              int64_t K, float* y, hipStream_t stream) {
+  switch (pick_q80(M, N, K)) {
+    case Q8Pick::kLds64x128: qg::launch_q80_lds<1, 1, 2, 4, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
+    case Q8Pick::kLds32x64K3: qg::launch_q80_lds<1, 1, 1, 2, 2, 2, 3>(W, ws, M, N, K, y, stream); break;
+    case Q8Pick::kLds32x64: qg::launch_q80_lds<1, 1, 1, 2, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
   }
   return hipGetLastError();
 }

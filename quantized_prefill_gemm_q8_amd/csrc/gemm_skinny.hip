@@ -15,6 +15,9 @@
 //         and 2s+1 (high nibbles).
 //   Q5_K  the same (qs at byte 48) plus the 32 qh bytes, whose bits 2s and
 //         2s+1 are the fifth bits of the lane's two sub-blocks: five loads.
+//   Q8_0  a super-block's share of a row is eight 34-byte blocks (272 bytes);
+//         lane s reads bytes 68s .. 68s+67 (blocks 2s and 2s+1, d and codes)
+//         with four 16-byte loads and one dword.
 //   Q6_K  lane s = 2*half + lh: ql[64half + 16lh ..+16], ql[64half + 32 +
 //         16lh ..+16] and qh[32half + 16lh ..+16], i.e. the values
 //         128half + 32c + 16lh + i (c = 0..3, i < 16), which are the 16-value
@@ -106,7 +109,7 @@ __device__ __forceinline__ float group_sum_last(float v) {
   return v;
 }
 
-// FMT: QG_Q4_K / QG_Q5_K / QG_Q6_K.  MR: activation rows.  R: rows per wavefront step
+// FMT: QG_Q4_K / QG_Q5_K / QG_Q6_K / QG_Q8_0.  MR: activation rows.  R: rows per wavefront step
 // (16/nsb when that divides, else 1).  XM: where the activations are read.
 // CO (Q6_K only): coalesced loads.  A step's sixteen super-blocks are 3360
 // contiguous bytes; when every step starts 16-byte aligned and the matrix ends
@@ -123,11 +126,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     const float* __restrict__ gdS, int64_t N, int64_t K, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   static_assert(CO == kCoNone || FMT == QG_Q6_K, "coalesced loads are for Q6_K");
-  constexpr bool KQ = FMT != QG_Q6_K;  // Q4_K or Q5_K: the Q4_K header and nibble layout
-  constexpr bool Q5 = FMT == QG_Q5_K;
+  constexpr bool KQ = FMT != QG_Q6_K;  // Q4_K, Q5_K, Q8_0: 64 values per lane, two per-32 blocks
+  constexpr bool Q5 = FMT == QG_Q5_K, Q8 = FMT == QG_Q8_0;
   constexpr int NBUF = CO == kCoDma ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t rowbuf[CO ? kSkThreads / 64 : 1][NBUF][CO ? 4096 : 16];
-  constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : Q5 ? kQ5Bytes : kQ6Bytes;
+  constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : Q5 ? kQ5Bytes : Q8 ? 8 * kQ8Bytes : kQ6Bytes;
   constexpr int G = 64 / R;  // lanes per row within a step
   const int64_t nsb = K / 256, nb = K / 32;
   const int lane = threadIdx.x & 63;
@@ -172,9 +175,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   uint8_t* const lrow1 = rowbuf[CO ? threadIdx.x >> 6 : 0][NBUF - 1];
   // lane offset inside a super-block of each of its loads
   constexpr uint32_t QS = Q5 ? 48u : 16u;  // first nibble byte (Q4_K, Q5_K)
-  const uint32_t off_a = KQ ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
-  const uint32_t off_b = KQ ? QS + 32u * s : static_cast<uint32_t>(64 * half + 32 + 16 * lh);
-  const uint32_t off_c = KQ ? QS + 16u + 32u * s : static_cast<uint32_t>(128 + 32 * half + 16 * lh);
+  const uint32_t off_a = Q8 ? 68u * s : KQ ? 0u : static_cast<uint32_t>(64 * half + 16 * lh);
+  const uint32_t off_b = Q8 ? 68u * s + 16u : KQ ? QS + 32u * s : static_cast<uint32_t>(64 * half + 32 + 16 * lh);
+  const uint32_t off_c = Q8 ? 68u * s + 32u : KQ ? QS + 16u + 32u * s : static_cast<uint32_t>(128 + 32 * half + 16 * lh);
 
   // per-lane activation data for XREG (a lane's super-block never changes)
   constexpr int XR = XM == kXReg ? MR : 1;
@@ -238,7 +241,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       n = n < N ? n : N - 1;
       jb = jb < nsb ? jb : nsb - 1;
       const uint8_t* blk = W + n * row_bytes + jb * BB;
-      if (KQ) {
+      if (Q8) {  // dword-aligned: 68 bytes from 68s
+        r.a = ld16_a2(blk + off_a);
+        r.b = ld16_a2(blk + off_b);
+        r.c = ld16_a2(blk + off_c);
+        r.e = ld16_a2(blk + off_c + 16);
+        r.s0 = *reinterpret_cast<const uint32_t*>(blk + off_c + 32);
+      } else if (KQ) {
         r.a = *reinterpret_cast<const uint4*>(blk + off_a);
         r.b = *reinterpret_cast<const uint4*>(blk + off_b);
         r.c = *reinterpret_cast<const uint4*>(blk + off_c);
@@ -305,20 +314,35 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     }
     {
       if (KQ) {
+        float dsc0, dsc1, dm0 = 0.0f, dm1 = 0.0f;
+        uint32_t lo[8], hi[8];
+        if constexpr (Q8) {
+          // bytes 68s .. 68s+67: d of block 2s, its 32 codes (two bytes past a
+          // dword: realigned), d of block 2s+1, its 32 codes (dword aligned)
+          const uint32_t w[17] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w, fc.x,
+                                  fc.y, fc.z, fc.w, fe.x, fe.y, fe.z, fe.w, fs0};
+          dsc0 = half_to_float(w[0] & 0xFFFFu);
+          dsc1 = half_to_float(w[8] >> 16);
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            lo[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], 2);
+            hi[i] = w[9 + i];
+          }
+        } else {
         const float d = half_to_float(fa.x & 0xFFFFu), dmin = half_to_float(fa.x >> 16);
         const Q4Scales sc = unpack_q4_scales(fa.y, fa.z, fa.w);
         const uint32_t scw = s < 2 ? sc.sc_lo : sc.sc_hi, mw = s < 2 ? sc.m_lo : sc.m_hi;
         const int bi = 2 * (s & 1);
-        const float dsc0 = d * static_cast<float>(byte_of(scw, bi));
-        const float dsc1 = d * static_cast<float>(byte_of(scw, bi + 1));
-        const float dm0 = dmin * static_cast<float>(byte_of(mw, bi));
-        const float dm1 = dmin * static_cast<float>(byte_of(mw, bi + 1));
+        dsc0 = d * static_cast<float>(byte_of(scw, bi));
+        dsc1 = d * static_cast<float>(byte_of(scw, bi + 1));
+        dm0 = dmin * static_cast<float>(byte_of(mw, bi));
+        dm1 = dmin * static_cast<float>(byte_of(mw, bi + 1));
         const uint32_t w[8] = {fb.x, fb.y, fb.z, fb.w, fc.x, fc.y, fc.z, fc.w};
-        uint32_t lo[8], hi[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
           lo[i] = w[i] & 0x0F0F0F0Fu;
           hi[i] = (w[i] >> 4) & 0x0F0F0F0Fu;
+        }
         }
         if (Q5) {  // bits 2s and 2s+1 of qh[l] are the fifth bits of values 64s + l and 64s + 32 + l
           const uint32_t qh[8] = {fe.x, fe.y, fe.z, fe.w, ff.x, ff.y, ff.z, ff.w};
@@ -354,8 +378,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
           float a = acc[m];
           a = __builtin_fmaf(static_cast<float>(I0), dsc0 * dx0, a);
           a = __builtin_fmaf(static_cast<float>(I1), dsc1 * dx1, a);
-          a = __builtin_fmaf(-dm0, dS0, a);
-          a = __builtin_fmaf(-dm1, dS1, a);
+          if constexpr (!Q8) {
+            a = __builtin_fmaf(-dm0, dS0, a);
+            a = __builtin_fmaf(-dm1, dS1, a);
+          }
           acc[m] = valid ? a : acc[m];
         }
       } else {
@@ -573,5 +599,6 @@ hipError_t qg_launch_gemm_skinny(const uint8_t* W, int fmt, const QgWorkspace& w
                                  int64_t N, int64_t K, float* y, hipStream_t stream) {
   if (fmt == QG_Q4_K) return qg::launch_skinny_fmt<QG_Q4_K>(W, ws, M, N, K, y, stream);
   if (fmt == QG_Q5_K) return qg::launch_skinny_fmt<QG_Q5_K>(W, ws, M, N, K, y, stream);
+  if (fmt == QG_Q8_0) return qg::launch_skinny_fmt<QG_Q8_0>(W, ws, M, N, K, y, stream);
   return qg::launch_skinny_fmt<QG_Q6_K>(W, ws, M, N, K, y, stream);
 }

@@ -61,6 +61,25 @@ __device__ __forceinline__ v4i q5_high(const uint4& qh, int jb) {
              int(((qh.z >> jb) & 0x01010101u) << 4), int(((qh.w >> jb) & 0x01010101u) << 4)};
 }
 
+// Q8_0 (a 256-value slice of a weight row = eight 34-byte blocks: fp16 d, then
+// 32 int8 codes; the slice starts 16-byte aligned): the 16 codes of block jb
+// for lane half h, bytes 34*jb + 2 + 16h onwards -- dword aligned for odd jb,
+// two bytes past a dword for even jb (then read from the dwords around them
+// and realigned).  Reads dwords only.
+__device__ __forceinline__ v4i q8_codes(const uint8_t* row, int jb, int h) {
+  const int off = 34 * jb + 2 + 16 * h;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + (off & ~3));
+  if ((off & 3) == 0) return v4i{int(p[0]), int(p[1]), int(p[2]), int(p[3])};
+  const uint32_t w0 = p[0], w1 = p[1], w2 = p[2], w3 = p[3], w4 = p[4];
+  return v4i{int(__builtin_amdgcn_alignbyte(w1, w0, 2)), int(__builtin_amdgcn_alignbyte(w2, w1, 2)),
+             int(__builtin_amdgcn_alignbyte(w3, w2, 2)), int(__builtin_amdgcn_alignbyte(w4, w3, 2))};
+}
+// Q8_0: the scale d of block jb of such a slice.
+__device__ __forceinline__ float q8_scale(const uint8_t* row, int jb) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(row + ((34 * jb) & ~3));
+  return half_to_float((jb & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
 // Q6_K: 8 codes, as signed bytes q6 - 32, of 16-value sub-block s for lane half
 // h: values v = 16s + 8h + i, i < 8.  With half = s/8, quarter c = (s%8)/2 and
 // l0 = 16*(s%2) + 8h, the low nibbles are ql[64*half + 32*(c%2) + l0 + i] (low

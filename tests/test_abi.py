@@ -69,7 +69,7 @@ def _prefill(**kw):
     (dict(w=None), -1), (dict(x=None), -1), (dict(y=None), -1),
     (dict(M=0), -1), (dict(N=0), -1), (dict(K=0), -1), (dict(K=300), -1), (dict(K=128), -1),
     (dict(M=-5), -1), (dict(N=1 << 40), -1),
-    (dict(fmt=3), -2), (dict(fmt=-1), -2),
+    (dict(fmt=4), -2), (dict(fmt=-1), -2),
     (dict(xdt=2), -3),
     (dict(path=3), -1), (dict(path=2, M=9), -1),
     (dict(ws=None), -4), (dict(ws=A + 128), -4), (dict(wsb=100), -4),
@@ -87,7 +87,7 @@ def test_other_entry_points_reject():
     assert lib.qgemm_quantize_act(A, 5, 4, 64, A, A, A, None) == -3
     assert lib.qgemm_quantize_act(A + 2, 1, 4, 64, A, A, A, None) == -5
     assert lib.qgemm_dequant(A, 1, 8, 100, A, None) == -1
-    assert lib.qgemm_dequant(A, 3, 8, 256, A, None) == -2
+    assert lib.qgemm_dequant(A, 9, 8, 256, A, None) == -2
     assert lib.qgemm_block_partials(A, 0, None, 4, 8, 256, A, None) == -1
     assert lib.qgemm_block_partials(A, 0, A + 1, 4, 8, 256, A, None) == -5
 
@@ -144,7 +144,7 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 512, 4096, 12288, AUTO) == "gemm_q6k_lds_kernel<1, 1, 2, 2, 1, 4, 2>"
     assert kn(Q6, 70, 300, 256, AUTO) == "gemm_q6k_lds_kernel<1, 1, 2, 2, 2, 1, 1>"
     # arguments the entry points would reject
-    assert kn(3, 8, 8, 256, AUTO) is None
+    assert kn(4, 8, 8, 256, AUTO) is None
     assert kn(Q4, 8, 8, 300, AUTO) is None
     assert kn(Q4, 9, 8, 256, SKINNY) is None
     assert kn(Q4, 0, 8, 256, AUTO) is None
@@ -224,7 +224,7 @@ def test_fusion_host_side():
     assert wsz(0, 512, 3584, 1024) == base(512, 1024)
     assert wsz(1, 512, 1536, 4096) == base(512, 4096) + 512 * 3072 * 4   # Q6_K: GEMM + SwiGLU kernel
     assert wsz(0, 3, 1000, 256) == base(3, 256) + (3 * 2000 * 4 + 255) // 256 * 256  # skinny
-    assert wsz(3, 4, 8, 256) == 0 and wsz(0, 0, 8, 256) == 0 and wsz(0, 4, 0, 256) == 0
+    assert wsz(4, 4, 8, 256) == 0 and wsz(0, 0, 8, 256) == 0 and wsz(0, 4, 0, 256) == 0
     assert wsz(0, 4, 8, 300) == 0
     kn = qg.qgemm_kernel_name_swiglu
     assert kn(0, 512, 3584, 1024) == "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>"
@@ -233,13 +233,13 @@ def test_fusion_host_side():
     assert kn(0, 64, 512, 1024).startswith("gemm_q4k_small_kernel<")
     assert kn(0, 3, 1000, 256).startswith("skinny_kernel<0, 3,")
     assert kn(1, 512, 1536, 4096).startswith("gemm_q6k_lds_kernel<")
-    assert kn(3, 512, 8, 256) is None and kn(0, 512, 8, 300) is None
+    assert kn(4, 512, 8, 256) is None and kn(0, 512, 8, 300) is None
     wsb = wsz(0, 4, 8, 256)
     call = lambda **k: lib.qgemm_prefill_swiglu(
         k.get("w", A), k.get("fmt", 0), k.get("x", A), k.get("xdt", 1), k.get("M", 4),
         k.get("F", 8), k.get("K", 256), k.get("h", A), k.get("ws", A), k.get("wsb", wsb), None)
     assert call(w=None) == -1 and call(M=0) == -1 and call(F=0) == -1 and call(K=300) == -1
-    assert call(h=None) == -1 and call(fmt=3) == -2 and call(xdt=3) == -3
+    assert call(h=None) == -1 and call(fmt=4) == -2 and call(xdt=3) == -3
     assert call(ws=None) == -4 and call(wsb=wsb - 1) == -4
     assert call(x=A + 2) == -5 and call(h=A + 2) == -5
     assert lib.qgemm_gemm_quantized_swiglu(A, 0, A, wsb, 4, 8, 256, A + 8, None) == -5
@@ -260,8 +260,8 @@ def test_q5k_host_side():
     """Q5_K: kernel choice, its workspace-free SwiGLU fallback, and the entry
     points that do not take it (no GPU call)."""
     kn = qg.qgemm_kernel_name
-    assert kn(2, 512, 4096, 1024) == "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 4, 1>"
-    assert kn(2, 8192, 24576, 4096) == "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 4, 1>"
+    assert kn(2, 512, 4096, 1024) == "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
+    assert kn(2, 8192, 24576, 4096) == "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
     assert kn(2, 512, 1024, 3584) == "gemm_q5k_lds_kernel<1, 1, 1, 2, 2, 2, 3>"
     assert kn(2, 64, 1024, 1024).startswith("gemm_q5k_small_kernel<")
     assert kn(2, 1, 24576, 4096) == "skinny_kernel<2, 1, 1, 0, 0>"
@@ -277,3 +277,18 @@ def test_q5k_host_side():
     assert lib.qgemm_prefill_deq_f16(A, 2, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2
     assert lib.qgemm_dequant_f16(A, 2, 8, 256, A, None) == -2
     assert qg.qgemm_kernel_name_a256(2, 512, 4096, 1024) is None
+
+
+def test_q80_host_side():
+    """Q8_0: kernel choice and the entry points that do not take it (no GPU call)."""
+    kn = qg.qgemm_kernel_name
+    assert kn(3, 512, 4096, 1024) == "gemm_q80_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
+    assert kn(3, 8192, 24576, 4096) == "gemm_q80_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
+    assert kn(3, 512, 1024, 3584) == "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 3>"
+    assert kn(3, 64, 1024, 512) == "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 1>"
+    assert kn(3, 1, 24576, 4096) == "skinny_kernel<3, 1, 1, 0, 0>"
+    assert kn(3, 8, 4096, 1024, qg.QG_PATH_SKINNY).startswith("skinny_kernel<3, 8,")
+    lib = qg.load()
+    assert lib.qgemm_prefill_a256(A, 3, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2
+    assert lib.qgemm_prefill_deq_f16(A, 3, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2
+    assert lib.qgemm_dequant_f16(A, 3, 8, 256, A, None) == -2

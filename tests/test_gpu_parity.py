@@ -22,8 +22,8 @@ import pins  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [qg.QG_Q4_K, qg.QG_Q6_K, qg.QG_Q5_K]
-FMT_ID = {qg.QG_Q4_K: "q4k", qg.QG_Q6_K: "q6k", qg.QG_Q5_K: "q5k"}
+FMTS = [qg.QG_Q4_K, qg.QG_Q6_K, qg.QG_Q5_K, qg.QG_Q8_0]
+FMT_ID = {qg.QG_Q4_K: "q4k", qg.QG_Q6_K: "q6k", qg.QG_Q5_K: "q5k", qg.QG_Q8_0: "q80"}
 
 
 def gpu_prefill(W: np.ndarray, fmt: int, x: np.ndarray, N: int, path=qg.QG_PATH_AUTO) -> np.ndarray:
@@ -184,7 +184,9 @@ def test_textbook_integer_matmul_exact(fmt, path):
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID.get)
 def test_worked_examples_all_ones(fmt):
     blk, fx = {qg.QG_Q4_K: pins.q4k_example_block, qg.QG_Q5_K: pins.q5k_example_block,
-               qg.QG_Q6_K: pins.q6k_example_block}[fmt]()
+               qg.QG_Q6_K: pins.q6k_example_block, qg.QG_Q8_0: pins.q80_example_block}[fmt]()
+    if fmt == qg.QG_Q8_0:                   # one 256-value row: eight copies of the 32-value block
+        blk, fx = np.tile(blk, 8), dict(fx, sum_w=8 * float(fx["sum_w"]))
     x = np.ones((3, 256), np.float32)
     ref = oracle.gemm(fmt, blk, x, 1)
     for p in (qg.QG_PATH_TILED, qg.QG_PATH_SKINNY):
@@ -295,6 +297,9 @@ def test_skinny_all_row_splits(fmt, K, N):
     (qg.QG_Q5_K, 170, 2800, 2816),     # 32x64 blocks, K split over 3 groups (3 + 4 + 4)
     (qg.QG_Q5_K, 65, 230, 2048),       # one 32x32 tile per wave, K split over 8 waves
     (qg.QG_Q5_K, 100, 200, 512),       # K split over 2 waves
+    (qg.QG_Q8_0, 2049, 15300, 1024),   # Q8_0: 64x128 tiles, ragged
+    (qg.QG_Q8_0, 330, 2700, 1280),     # 32x64 blocks, K split over 3 groups
+    (qg.QG_Q8_0, 65, 230, 512),        # 32x64 blocks, one K-group (two super-block lengths)
 ])
 def test_tiled_configs_ragged(fmt, M, N, K):
     """Every tiled kernel configuration the dispatcher can pick, on shapes whose
