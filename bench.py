@@ -436,9 +436,11 @@ def main():
             if g.fmt == qg.QG_Q4_K:
                 calls["a256"] = lambda: qg.qgemm_prefill_a256(Wb, g.fmt, xb, g.M, g.N, g.K, yb, ws8,
                                                               stream)
-                # the same shape with Q5_K weights (int8 method)
+                # the same shape with Q5_K and Q8_0 weights (int8 method)
                 W5 = to_dev(synth.make_weights(dataclasses.replace(g, fmt=qg.QG_Q5_K)))
                 calls["q5k"] = lambda: qg.qgemm_prefill(W5, qg.QG_Q5_K, xb, g.M, g.N, g.K, yb, ws8, stream)
+                W8 = to_dev(synth.make_weights(dataclasses.replace(g, fmt=qg.QG_Q8_0)))
+                calls["q80"] = lambda: qg.qgemm_prefill(W8, qg.QG_Q8_0, xb, g.M, g.N, g.K, yb, ws8, stream)
             # interleaved rounds, the best of three per variant (clocks drift
             # under sustained load; interleaving keeps the comparison fair)
             us = {}
@@ -459,8 +461,10 @@ def main():
                    "int8_us": round(us["int8"], 2), "int8_tops": rate("int8")}
             if "q5k" in us:
                 row.update({"q5k_us": round(us["q5k"], 2), "q5k_tops": rate("q5k"),
-                            "q5k_kernel": qg.qgemm_kernel_name(qg.QG_Q5_K, g.M, g.N, g.K)})
-                del W5
+                            "q5k_kernel": qg.qgemm_kernel_name(qg.QG_Q5_K, g.M, g.N, g.K),
+                            "q80_us": round(us["q80"], 2), "q80_tops": rate("q80"),
+                            "q80_kernel": qg.qgemm_kernel_name(qg.QG_Q8_0, g.M, g.N, g.K)})
+                del W5, W8
             if "a256" in us:
                 row.update({"a256_us": round(us["a256"], 2), "a256_tops": rate("a256"),
                             "a256_kernel": qg.qgemm_kernel_name_a256(g.fmt, g.M, g.N, g.K),
@@ -566,11 +570,12 @@ def main():
     # (M = 1 and M = 8 rows; weight bytes / kernel time against 8 TB/s)
     gemv = {}
     seen = set()
-    fmt_name = {qg.QG_Q4_K: "Q4_K", qg.QG_Q5_K: "Q5_K", qg.QG_Q6_K: "Q6_K"}
+    fmt_name = {qg.QG_Q4_K: "Q4_K", qg.QG_Q5_K: "Q5_K", qg.QG_Q6_K: "Q6_K", qg.QG_Q8_0: "Q8_0"}
     # every Q4_K projection also as Q5_K (the format the pages' decode-GEMV ticket
-    # finds slowest): the same shape and weight recipe, 176-byte blocks
+    # finds slowest) and Q8_0: the same shape and weight recipe
     gemv_shapes = [g2 for cfg in ((2, 3, 4) if args.gemv_steps > 0 else ()) for g in synth.CONFIGS[cfg]
-                   for g2 in ([g, dataclasses.replace(g, fmt=qg.QG_Q5_K)] if g.fmt == qg.QG_Q4_K else [g])]
+                   for g2 in ([g] + [dataclasses.replace(g, fmt=f) for f in (qg.QG_Q5_K, qg.QG_Q8_0)]
+                              if g.fmt == qg.QG_Q4_K else [g])]
     for g in gemv_shapes:
         key = (g.K, g.N, g.fmt)
         if key in seen:
