@@ -279,6 +279,28 @@ def main():
     kname = {g.name: qg.qgemm_kernel_name(g.fmt, M, g.N, g.K, qg.QG_PATH_TILED)
              for g in (qkv, up, down)}
 
+    # ---------------- CPU oracle on the host (same step, whole workload, repeated),
+    # timed before any GPU work of this process
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        host = {g.name: (synth.make_weights(g), synth.make_acts(g)) for g in (qkv, up, down)}
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 1000:
+            s0 = time.perf_counter()
+            for g in (qkv, up, down):
+                Wn, xn = host[g.name]
+                oracle.gemm(g.fmt, Wn, xn, g.N)
+            t_cpu += time.perf_counter() - s0
+            reps += 1
+        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        cpu = {"value": round(step_ops * reps / t_cpu / 1e12, 6), "unit": "TOPS",
+               "cores": cores, "kind": "oracle",
+               "sample": f"the whole step (qkv_gate, up_gate, down at M=512; activation "
+                         f"quantisation included) repeated {reps}x in {t_cpu:.1f} s",
+               "tok_s": round(M * reps / t_cpu, 2)}
+
+
     def gemm(g, ws):
         qg.qgemm_gemm_quantized(Wd[g.name], g.fmt, ws, M, g.N, g.K, y[g.name], stream,
                                 qg.QG_PATH_TILED)
@@ -665,26 +687,6 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-
-    # ---------------- CPU oracle on the host (same step, whole workload, repeated)
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        host = {g.name: (synth.make_weights(g), synth.make_acts(g)) for g in (qkv, up, down)}
-        reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and reps < 1000:
-            s0 = time.perf_counter()
-            for g in (qkv, up, down):
-                Wn, xn = host[g.name]
-                oracle.gemm(g.fmt, Wn, xn, g.N)
-            t_cpu += time.perf_counter() - s0
-            reps += 1
-        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-        cpu = {"value": round(step_ops * reps / t_cpu / 1e12, 6), "unit": "TOPS",
-               "cores": cores, "kind": "oracle",
-               "sample": f"the whole step (qkv_gate, up_gate, down at M=512; activation "
-                         f"quantisation included) repeated {reps}x in {t_cpu:.1f} s",
-               "tok_s": round(M * reps / t_cpu, 2)}
 
     out = {
         "metric": "effective int8 TOPS & prefill tok/s, Q4_K GEMM M=512 (+ GB/s at M=1 LM head)",
