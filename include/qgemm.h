@@ -34,7 +34,7 @@
  *         aprender issue #5475's page among the formats its CPU path runs row
  *         by row).  K is still a multiple of 256 (a row is K/32 blocks).  The
  *         codes go to the matrix core as they are, with d as the block scale
- *         and no min term; the skinny kernel takes it for M <= 4.
+ *         and no min term; the skinny kernel takes it for M <= 8.
  * The per-256 entry points take Q4_K only and the fp16-branch ones Q4_K /
  * Q6_K (QG_EFMT for Q5_K and Q8_0).
  *
@@ -80,9 +80,9 @@ enum {
     QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
 };
 
-/* Largest skinny-path batch.  Under QG_PATH_AUTO, Q6_K problems with
- * M <= QG_SKINNY_MAX_M rows and Q4_K problems with M <= 4 rows go to the
- * bandwidth-bound skinny kernel, larger M to the tiled matrix-core kernels. */
+/* Largest skinny-path batch.  Under QG_PATH_AUTO, Q6_K and Q8_0 problems with
+ * M <= QG_SKINNY_MAX_M rows and Q4_K and Q5_K problems with M <= 5 rows go to
+ * the bandwidth-bound skinny kernel, larger M to the tiled matrix-core kernels. */
 #define QG_SKINNY_MAX_M 8
 
 /* Workspace bytes needed by qgemm_prefill / qgemm_lm_head for M activation rows
@@ -102,7 +102,7 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t K);
  *   workspace : device scratch of at least qgemm_workspace_bytes(M, K) bytes,
  *               256-byte aligned; its contents are scratch on entry and exit.
  *   stream    : hipStream_t (NULL = default stream).
- * Dispatch: the skinny kernel for M <= QG_SKINNY_MAX_M (Q6_K) or M <= 4 (Q4_K),
+ * Dispatch: the skinny kernel for M <= QG_SKINNY_MAX_M (Q6_K, Q8_0) or M <= 5 (Q4_K, Q5_K),
  * otherwise the tiled kernels. */
 int qgemm_prefill(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
                   int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,

@@ -73,10 +73,13 @@ hipError_t launch_tiled(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_
   return qg_launch_gemm_q6k(W, ws, M, N, K, y, s);
 }
 
-// QG_PATH_AUTO: the skinny kernel for M <= 8 Q6_K rows and M <= 4 Q4_K / Q5_K /
-// Q8_0 rows (measured: from 5 rows on, the Q4_K tiled kernels are faster, while the
-// Q6_K skinny kernel stays ahead up to 8 rows).
-bool auto_skinny(int fmt, int64_t M) { return M <= (fmt == QG_Q6_K ? QG_SKINNY_MAX_M : 4); }
+// QG_PATH_AUTO: the skinny kernel for M <= 8 Q6_K and Q8_0 rows and M <= 5
+// Q4_K and Q5_K rows (measured over the workloads' projection shapes: from 6
+// Q4_K / Q5_K rows on the tiled kernels are as fast or faster, while the
+// Q6_K and Q8_0 skinny kernels stay ahead up to 8 rows).
+bool auto_skinny(int fmt, int64_t M) {
+  return M <= (fmt == QG_Q6_K || fmt == QG_Q8_0 ? QG_SKINNY_MAX_M : 5);
+}
 
 }  // namespace
 
