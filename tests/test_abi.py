@@ -133,6 +133,12 @@ def test_kernel_name_dispatch_rule():
     # tiled tile choice by grid size
     assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>"
     assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>"
+    # long prompts: 128x256 blocks unless their last round is much emptier than 64x128's
+    big, mid = ("gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>",
+                "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>")
+    assert kn(Q4, 2048, 24576, 4096, AUTO) == big and kn(Q4, 8192, 24576, 4096, AUTO) == big
+    assert kn(Q4, 4096, 9728, 2560, AUTO) == big
+    assert kn(Q4, 4096, 2560, 9728, AUTO) == mid      # 320 large blocks on 256 CUs
     assert kn(Q4, 64, 1024, 1024, AUTO).startswith("gemm_q4k_small_kernel<")
     # few output blocks: K split inside the workgroup
     assert kn(Q4, 512, 2560, 9728, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2, false>"
