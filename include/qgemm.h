@@ -279,10 +279,10 @@ int qgemm_rmsnorm_quantize_act(const void *x, int x_dtype, const float *g, float
  * tensors stacked.  With y = x . W^T under the method's quantisation ([M][2F]):
  *   h[m][f] = bf16( silu(y[m][f]) * y[m][F + f] ),  silu(z) = z / (1 + e^-z),
  * in fp32 from the fp32 GEMM result, rounded once to bfloat16 (nearest even).
- * h is bfloat16 bits [M][F], 16-byte aligned.  Q4_K problems on the tiled
- * kernels run as ONE kernel (the gate and up columns of an output tile are
- * computed by paired waves and combined in LDS); decode-sized batches (the
- * skinny path), small grids and Q6_K weights run the plain GEMM into the
+ * h is bfloat16 bits [M][F], 16-byte aligned.  Q4_K, Q5_K and Q8_0 problems
+ * on the tiled kernels run as ONE kernel (the gate and up columns of an output
+ * tile are computed by paired waves and combined in LDS); decode-sized batches
+ * (the skinny path), small grids and Q6_K weights run the plain GEMM into the
  * workspace, then a SwiGLU kernel. */
 
 /* Workspace bytes for the SwiGLU entry points: the quantised activations and,

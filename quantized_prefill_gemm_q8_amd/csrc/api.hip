@@ -416,12 +416,12 @@ int qgemm_rmsnorm_quantize_act(const void* x, int x_dtype, const float* g, float
                                                     static_cast<hipStream_t>(stream)));
 }
 
-// The gate+up GEMM with the SwiGLU epilogue runs fused for Q4_K weights on the
-// LDS-tiled kernels; otherwise the plain GEMM writes the fp32 gate+up output
+// The gate+up GEMM with the SwiGLU epilogue runs fused for Q4_K, Q5_K and Q8_0
+// weights on the LDS-tiled kernels; otherwise the plain GEMM writes the fp32 gate+up output
 // into the workspace after the quantised activations and the SwiGLU kernel
 // reads it from there.
 static bool swiglu_fused(int fmt, int64_t M, int64_t F, int64_t K) {
-  return fmt == QG_Q4_K && !auto_skinny(fmt, M) && qg_q4k_swiglu_fusable(M, F, K);
+  return fmt != QG_Q6_K && !auto_skinny(fmt, M) && qg_swiglu_fusable(fmt, M, F, K);
 }
 
 static bool swiglu_layout(int fmt, int64_t M, int64_t F, int64_t K, Layout* L, int64_t* total) {
@@ -457,7 +457,7 @@ int qgemm_gemm_quantized_swiglu(const void* q_weights, int fmt, const void* work
   const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swiglu_fused(fmt, M, F, K)) return launch_status(qg_launch_gemm_q4k_swiglu(W, ws, M, F, K, h, s));
+  if (swiglu_fused(fmt, M, F, K)) return launch_status(qg_launch_gemm_swiglu(W, fmt, ws, M, F, K, h, s));
   float* y = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) + L.total);
   if (auto_skinny(fmt, M)) rc = launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, 2 * F, K, y, s));
   else rc = launch_status(launch_tiled(W, fmt, ws, M, 2 * F, K, y, s));
@@ -487,7 +487,7 @@ const char* qgemm_kernel_name_swiglu(int fmt, int64_t M, int64_t F, int64_t K) {
   if ((fmt != QG_Q4_K && fmt != QG_Q5_K && fmt != QG_Q6_K && fmt != QG_Q8_0) || M < 1 || F < 1 || K < 256 || K % 256 != 0)
     return NULL;
   if (F > (INT64_C(1) << 39) / K) return NULL;
-  if (swiglu_fused(fmt, M, F, K)) return qg_gemm_q4k_swiglu_kernel_name(M, F, K);
+  if (swiglu_fused(fmt, M, F, K)) return qg_gemm_swiglu_kernel_name(fmt, M, F, K);
   return qgemm_kernel_name(fmt, M, 2 * F, K, QG_PATH_AUTO);
 }
 

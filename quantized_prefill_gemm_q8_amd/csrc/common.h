@@ -172,6 +172,11 @@ bool qg_q4k_swiglu_fusable(int64_t M, int64_t F, int64_t K);
 hipError_t qg_launch_gemm_q4k_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F,
                                      int64_t K, uint16_t* h, hipStream_t stream);
 const char* qg_gemm_q4k_swiglu_kernel_name(int64_t M, int64_t F, int64_t K);
+// The same over Q4_K, Q5_K or Q8_0 weights (the format's own block shapes).
+bool qg_swiglu_fusable(int fmt, int64_t M, int64_t F, int64_t K);
+hipError_t qg_launch_gemm_swiglu(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M, int64_t F,
+                                 int64_t K, uint16_t* h, hipStream_t stream);
+const char* qg_gemm_swiglu_kernel_name(int fmt, int64_t M, int64_t F, int64_t K);
 // h [M][F] = bfloat16(silu(y[m][f]) * y[m][F + f]) from y [M][2F] fp32
 hipError_t qg_launch_swiglu(const float* y, int64_t M, int64_t F, uint16_t* h, hipStream_t stream);
 // RMSNorm fused into the per-32 quantiser (K <= kRmsMaxK)

@@ -104,7 +104,7 @@ __device__ __forceinline__ void q4k_lds_body(
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
     int64_t N, int64_t K, float* __restrict__ y, uint16_t* __restrict__ hout, int64_t F) {
   static_assert(!SW || (WN % 2 == 0 && !A256 && !DPP), "SwiGLU pairs waves wn and wn + WN/2");
-  static_assert(!(Q5 || Q8) || (!A256 && !DPP && !SW), "Q5_K and Q8_0 run the per-32 method");
+  static_assert(!(Q5 || Q8) || (!A256 && !DPP), "Q5_K and Q8_0 run the per-32 method");
   constexpr int NW = WM * WN;  // waves per group
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   // bytes per 256 values of a weight row, and where the Q4_K / Q5_K nibbles start
@@ -562,6 +562,25 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
                                                            h, F);
 }
 
+// ... over Q5_K weights
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q5k_swiglu_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t F, int64_t K,
+    uint16_t* __restrict__ h) {
+  q4k_lds_body<TM, TN, WM, WN, false, NS, KS, false, true, true>(W, qx, nullptr, dxT, Mp, dsp, M, 2 * F, K,
+                                                                 nullptr, h, F);
+}
+
+// ... over Q8_0 weights
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_q80_swiglu_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
+    int64_t Mp, int64_t M, int64_t F, int64_t K, uint16_t* __restrict__ h) {
+  q4k_lds_body<TM, TN, WM, WN, false, NS, KS, false, true, false, true>(W, qx, nullptr, dxT, Mp, nullptr, M, 2 * F,
+                                                                        K, nullptr, h, F);
+}
+
 // ---------------------------------------------------------------- small-grid kernel
 //
 // For problems whose output has too few 128x256 tiles to fill the chip (one
@@ -696,13 +715,21 @@ __device__ __forceinline__ void q4k_small_body(
   }
 }
 
-template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
+template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS, int FMT = QG_Q4_K>
 static void launch_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F, int64_t K,
                           uint16_t* h, hipStream_t stream) {
   constexpr int BM = 32 * TM * WM, BO = 16 * TN * WN;  // output columns per block: half the weight rows
   const dim3 grid(static_cast<unsigned>((F + BO - 1) / BO), static_cast<unsigned>((M + BM - 1) / BM));
-  gemm_q4k_swiglu_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, dim3(64 * WM * WN * KS), 0, stream>>>(
-      W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, F, K, h);
+  const dim3 block(64 * WM * WN * KS);
+  if constexpr (FMT == QG_Q5_K)
+    gemm_q5k_swiglu_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, block, 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp,
+                                                                                 M, F, K, h);
+  else if constexpr (FMT == QG_Q8_0)
+    gemm_q80_swiglu_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, block, 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, M, F,
+                                                                                 K, h);
+  else
+    gemm_q4k_swiglu_kernel<TM, TN, WM, WN, NS, OCC, KS><<<grid, block, 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp,
+                                                                                 M, F, K, h);
 }
 
 template <int SK>
@@ -963,6 +990,58 @@ hipError_t qg_launch_gemm_q80(const uint8_t* W, const QgWorkspace& ws, int64_t M
     case Q8Pick::kLds64x128: qg::launch_q80_lds<1, 1, 2, 4, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
     case Q8Pick::kLds32x64K3: qg::launch_q80_lds<1, 1, 1, 2, 2, 2, 3>(W, ws, M, N, K, y, stream); break;
     case Q8Pick::kLds32x64: qg::launch_q80_lds<1, 1, 1, 2, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
+  }
+  return hipGetLastError();
+}
+
+// SwiGLU-fused gate+up projection over Q5_K and Q8_0 weights: the block shapes
+// of each format's plain GEMM for the 2F-column problem (Q5_K's small-grid
+// problems are not fused); 32-bit weight offsets as for Q4_K.
+bool qg_swiglu_fusable(int fmt, int64_t M, int64_t F, int64_t K) {
+  if (fmt == QG_Q4_K) return qg_q4k_swiglu_fusable(M, F, K);
+  const int64_t bb = fmt == QG_Q5_K ? qg::kQ5Bytes : 8 * qg::kQ8Bytes;
+  if ((fmt != QG_Q5_K && fmt != QG_Q8_0) || F < 1 || (F + 128) * (K / 256) * bb >= (INT64_C(1) << 32))
+    return false;
+  if (fmt == QG_Q8_0) return true;
+  const Q4Pick p = pick_q4k(M, 2 * F, K);
+  return p == Q4Pick::kLds128x256 || p == Q4Pick::kLds64x128 || p == Q4Pick::kLds64x128K2 ||
+         p == Q4Pick::kLds32x64K4;
+}
+
+const char* qg_gemm_swiglu_kernel_name(int fmt, int64_t M, int64_t F, int64_t K) {
+  if (!qg_swiglu_fusable(fmt, M, F, K)) return nullptr;
+  if (fmt == QG_Q4_K) return qg_gemm_q4k_swiglu_kernel_name(M, F, K);
+  if (fmt == QG_Q5_K) {
+    switch (pick_q4k(M, 2 * F, K)) {
+      case Q4Pick::kLds128x256:
+      case Q4Pick::kLds64x128: return "gemm_q5k_swiglu_kernel<1, 1, 2, 4, 2, 2, 1>";
+      default: return "gemm_q5k_swiglu_kernel<1, 1, 1, 2, 2, 2, 3>";
+    }
+  }
+  switch (pick_q80(M, 2 * F, K)) {
+    case Q8Pick::kLds64x128: return "gemm_q80_swiglu_kernel<1, 1, 2, 4, 2, 2, 1>";
+    case Q8Pick::kLds32x64K3: return "gemm_q80_swiglu_kernel<1, 1, 1, 2, 2, 2, 3>";
+    default: return "gemm_q80_swiglu_kernel<1, 1, 1, 2, 2, 2, 1>";
+  }
+}
+
+hipError_t qg_launch_gemm_swiglu(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M, int64_t F,
+                                 int64_t K, uint16_t* h, hipStream_t stream) {
+  if (!qg_swiglu_fusable(fmt, M, F, K)) return hipErrorInvalidValue;
+  if (fmt == QG_Q4_K) return qg_launch_gemm_q4k_swiglu(W, ws, M, F, K, h, stream);
+  if (fmt == QG_Q5_K) {
+    switch (pick_q4k(M, 2 * F, K)) {
+      case Q4Pick::kLds128x256:
+      case Q4Pick::kLds64x128:
+        qg::launch_swiglu<1, 1, 2, 4, 2, 2, 1, QG_Q5_K>(W, ws, M, F, K, h, stream); break;
+      default: qg::launch_swiglu<1, 1, 1, 2, 2, 2, 3, QG_Q5_K>(W, ws, M, F, K, h, stream); break;
+    }
+    return hipGetLastError();
+  }
+  switch (pick_q80(M, 2 * F, K)) {
+    case Q8Pick::kLds64x128: qg::launch_swiglu<1, 1, 2, 4, 2, 2, 1, QG_Q8_0>(W, ws, M, F, K, h, stream); break;
+    case Q8Pick::kLds32x64K3: qg::launch_swiglu<1, 1, 1, 2, 2, 2, 3, QG_Q8_0>(W, ws, M, F, K, h, stream); break;
+    default: qg::launch_swiglu<1, 1, 1, 2, 2, 2, 1, QG_Q8_0>(W, ws, M, F, K, h, stream); break;
   }
   return hipGetLastError();
 }

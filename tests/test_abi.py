@@ -276,9 +276,11 @@ def test_q5k_host_side():
     assert kn(2, 5, 4096, 1024).startswith("skinny_kernel<2, 5,")
     assert kn(2, 6, 4096, 1024).startswith("gemm_q5k_small_kernel<")
     assert kn(2, 8, 4096, 1024, qg.QG_PATH_SKINNY).startswith("skinny_kernel<2, 8,")
-    assert qg.qgemm_kernel_name_swiglu(2, 512, 3584, 1024).startswith("gemm_q5k_lds_kernel<")
-    assert qg.qgemm_swiglu_workspace_bytes(2, 512, 3584, 1024) == \
-        qg.qgemm_workspace_bytes(512, 1024) + 512 * 7168 * 4
+    assert qg.qgemm_kernel_name_swiglu(2, 512, 3584, 1024) == "gemm_q5k_swiglu_kernel<1, 1, 2, 4, 2, 2, 1>"
+    assert qg.qgemm_swiglu_workspace_bytes(2, 512, 3584, 1024) == qg.qgemm_workspace_bytes(512, 1024)
+    assert qg.qgemm_kernel_name_swiglu(2, 64, 512, 1024).startswith("gemm_q5k_small_kernel<")  # not fused
+    assert qg.qgemm_swiglu_workspace_bytes(2, 64, 512, 1024) == \
+        qg.qgemm_workspace_bytes(64, 1024) + 64 * 1024 * 4
     lib = qg.load()
     ws = qg.qgemm_workspace_bytes(4, 256)
     assert lib.qgemm_prefill_a256(A, 2, A, 1, 4, 8, 256, A, A, ws, None) == -2
@@ -296,6 +298,9 @@ def test_q80_host_side():
     assert kn(3, 64, 1024, 512) == "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 1>"
     assert kn(3, 1, 24576, 4096) == "skinny_kernel<3, 1, 1, 0, 0>"
     assert kn(3, 8, 4096, 1024, qg.QG_PATH_SKINNY).startswith("skinny_kernel<3, 8,")
+    assert qg.qgemm_kernel_name_swiglu(3, 512, 3584, 1024) == "gemm_q80_swiglu_kernel<1, 1, 2, 4, 2, 2, 1>"
+    assert qg.qgemm_kernel_name_swiglu(3, 300, 700, 768) == "gemm_q80_swiglu_kernel<1, 1, 1, 2, 2, 2, 3>"
+    assert qg.qgemm_kernel_name_swiglu(3, 8, 700, 768).startswith("skinny_kernel<3, 8,")
     lib = qg.load()
     assert lib.qgemm_prefill_a256(A, 3, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2
     assert lib.qgemm_prefill_deq_f16(A, 3, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2

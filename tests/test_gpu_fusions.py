@@ -190,8 +190,14 @@ SW_SHAPES = [(qg.QG_Q4_K, 512, 3584, 1024),     # fused, 64x128 blocks
              (qg.QG_Q4_K, 64, 512, 1024),       # small-grid GEMM + SwiGLU kernel
              (qg.QG_Q4_K, 3, 1000, 1024),       # skinny GEMM + SwiGLU kernel
              (qg.QG_Q6_K, 300, 700, 768),       # Q6_K GEMM + SwiGLU kernel
-             (qg.QG_Q5_K, 300, 700, 768),       # Q5_K GEMM + SwiGLU kernel
-             (qg.QG_Q5_K, 2, 500, 1024)]        # Q5_K skinny GEMM + SwiGLU kernel
+             (qg.QG_Q5_K, 300, 700, 768),       # Q5_K small-grid GEMM + SwiGLU kernel
+             (qg.QG_Q5_K, 2, 500, 1024),        # Q5_K skinny GEMM + SwiGLU kernel
+             (qg.QG_Q5_K, 512, 3584, 1024),     # Q5_K fused, 64x128 blocks
+             (qg.QG_Q5_K, 200, 3000, 1024),     # Q5_K fused, 32x64 blocks with three K-groups
+             (qg.QG_Q8_0, 512, 3584, 1024),     # Q8_0 fused, 64x128 blocks
+             (qg.QG_Q8_0, 300, 700, 768),       # Q8_0 fused, 32x64 blocks with three K-groups
+             (qg.QG_Q8_0, 70, 900, 512),        # Q8_0 fused, 32x64 blocks, one K-group (ragged F)
+             (qg.QG_Q8_0, 6, 500, 1024)]        # Q8_0 skinny GEMM + SwiGLU kernel
 
 
 @pytest.mark.parametrize("fmt,M,F,K", SW_SHAPES)
@@ -209,19 +215,22 @@ def test_gemm_swiglu_parity(fmt, M, F, K):
     check_swiglu(h, W, fmt, x, F, rows, cols, f"{M}x{F}x{K} fmt {fmt} ({name})")
 
 
-@pytest.mark.parametrize("M,F,K", [(512, 3584, 1024), (2100, 5000, 512), (200, 3000, 1024),
-                                   (100, 2100, 2048)])
-def test_fused_equals_gemm_then_swiglu(M, F, K):
+@pytest.mark.parametrize("fmt,M,F,K", [(qg.QG_Q4_K, 512, 3584, 1024), (qg.QG_Q4_K, 2100, 5000, 512),
+                                       (qg.QG_Q4_K, 200, 3000, 1024), (qg.QG_Q4_K, 100, 2100, 2048),
+                                       (qg.QG_Q5_K, 512, 3584, 1024), (qg.QG_Q5_K, 200, 3000, 1024),
+                                       (qg.QG_Q8_0, 512, 3584, 1024), (qg.QG_Q8_0, 300, 700, 768),
+                                       (qg.QG_Q8_0, 70, 900, 512)])
+def test_fused_equals_gemm_then_swiglu(fmt, M, F, K):
     """The fused kernel's h is bit-identical to the plain GEMM's fp32 output fed
     to the SwiGLU kernel."""
-    assert qg.qgemm_kernel_name_swiglu(qg.QG_Q4_K, M, F, K).startswith("gemm_q4k_swiglu_kernel<")
-    W = synth.pack(qg.QG_Q4_K, synth.normal(1150 + F, (2 * F, K), 0.0, 0.02))
+    assert "_swiglu_kernel<" in qg.qgemm_kernel_name_swiglu(fmt, M, F, K)
+    W = synth.pack(fmt, synth.normal(1150 + F, (2 * F, K), 0.0, 0.02))
     x = synth.to_bf16_bits(synth.normal(1151 + M, (M, K)))
-    h = gpu_swiglu(W, qg.QG_Q4_K, x, F)
+    h = gpu_swiglu(W, fmt, x, F)
     ws = torch.empty(qg.qgemm_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
     y = torch.empty((M, 2 * F), dtype=torch.float32, device=DEV)
     h2 = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
-    qg.qgemm_prefill(to_dev(W), qg.QG_Q4_K, to_dev(x), M, 2 * F, K, y, ws)
+    qg.qgemm_prefill(to_dev(W), fmt, to_dev(x), M, 2 * F, K, y, ws)
     qg.qgemm_swiglu(y, M, F, h2)
     torch.cuda.synchronize()
     assert np.array_equal(h, h2.cpu().view(torch.int16).numpy().view(np.uint16))

@@ -87,8 +87,8 @@ def test_graph_replays_match_eager():
 def test_graph_ffn_block_replays_match_eager():
     """One FFN block under capture: RMSNorm -> quantiser, the gate+up GEMM with
     the SwiGLU epilogue (bf16 h), the quantiser of h and the down GEMM; plus
-    the unfused SwiGLU path (Q5_K gate+up: GEMM into the workspace, then the
-    SwiGLU kernel) and a Q8_0 GEMM.  Every replay equals the eager result bit
+    the fused Q5_K gate+up, the unfused SwiGLU path (Q6_K gate+up: GEMM into the
+    workspace, then the SwiGLU kernel) and a Q8_0 GEMM.  Every replay equals the eager result bit
     for bit; the eager h is checked against the oracle's SwiGLU of the oracle's
     normalised rows."""
     stream = torch.cuda.Stream()
@@ -98,28 +98,33 @@ def test_graph_ffn_block_replays_match_eager():
     Wgu_ = synth.pack(qg.QG_Q4_K, synth.normal(742, (2 * F, K), 0.0, 0.02))
     Wd_ = synth.pack(qg.QG_Q6_K, synth.normal(743, (K, F), 0.0, 0.02))
     W5_ = synth.pack(qg.QG_Q5_K, synth.normal(744, (2 * F, K), 0.0, 0.02))
+    W6_ = synth.pack(qg.QG_Q6_K, synth.normal(746, (2 * F, K), 0.0, 0.02))
     W8_ = synth.pack(qg.QG_Q8_0, synth.normal(745, (700, K), 0.0, 0.02))
-    x, gn, Wgu, Wd, W5, W8 = (to_dev(a) for a in (xn_, gn_, Wgu_, Wd_, W5_, W8_))
-    ws = torch.empty(max(qg.qgemm_swiglu_workspace_bytes(qg.QG_Q5_K, M, F, K),
+    x, gn, Wgu, Wd, W5, W6, W8 = (to_dev(a) for a in (xn_, gn_, Wgu_, Wd_, W5_, W6_, W8_))
+    ws = torch.empty(max(qg.qgemm_swiglu_workspace_bytes(qg.QG_Q6_K, M, F, K),
                          qg.qgemm_swiglu_workspace_bytes(qg.QG_Q4_K, M, F, K)), dtype=torch.uint8, device=DEV)
     wsd = qg.alloc_workspace(M, F, DEV)
     h = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
     h5 = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
+    h6 = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
     yd = torch.empty((M, K), dtype=torch.float32, device=DEV)
     y8 = torch.empty((M, 700), dtype=torch.float32, device=DEV)
     assert qg.qgemm_kernel_name_swiglu(qg.QG_Q4_K, M, F, K).startswith("gemm_q4k_swiglu_kernel<")
+    assert qg.qgemm_kernel_name_swiglu(qg.QG_Q5_K, M, F, K).startswith("gemm_q5k_swiglu_kernel<")
+    assert "swiglu" not in qg.qgemm_kernel_name_swiglu(qg.QG_Q6_K, M, F, K)
 
     def run(s):
         qg.qgemm_rmsnorm_quantize_workspace(x, gn, 1e-6, M, K, ws, s)
         qg.qgemm_gemm_quantized_swiglu(Wgu, qg.QG_Q4_K, ws, M, F, K, h, s)
         qg.qgemm_gemm_quantized_swiglu(W5, qg.QG_Q5_K, ws, M, F, K, h5, s)
+        qg.qgemm_gemm_quantized_swiglu(W6, qg.QG_Q6_K, ws, M, F, K, h6, s)
         qg.qgemm_gemm_quantized(W8, qg.QG_Q8_0, ws, M, 700, K, y8, s)
         qg.qgemm_prefill(Wd, qg.QG_Q6_K, h, M, K, F, yd, wsd, s)
 
     with torch.cuda.stream(stream):
         run(stream)
     stream.synchronize()
-    eager = [t.clone() for t in (h, h5, y8, yd)]
+    eager = [t.clone() for t in (h, h5, h6, y8, yd)]
     # the eager h against the oracle on rows whose norm scale every summation order fixes
     r, lo, hi = oracle.rms_scale(xn_, 1e-6)
     xq = oracle.rmsnorm(xn_, gn_, r)
@@ -136,7 +141,7 @@ def test_graph_ffn_block_replays_match_eager():
     with torch.cuda.graph(g, stream=stream):
         run(stream)
     for rep in range(4):
-        for t in (h, h5):
+        for t in (h, h5, h6):
             t.zero_()
         y8.fill_(float("nan"))
         yd.fill_(float("nan"))
@@ -145,5 +150,5 @@ def test_graph_ffn_block_replays_match_eager():
         # unrelated eager library work between replays
         qg.qgemm_swiglu(torch.ones((4, 16), device=DEV), 4, 8, torch.empty((4, 8), dtype=torch.bfloat16, device=DEV))
         torch.cuda.synchronize()
-        for name, t, e in zip(("h", "h5", "y8", "yd"), (h, h5, y8, yd), eager):
+        for name, t, e in zip(("h", "h5", "h6", "y8", "yd"), (h, h5, h6, y8, yd), eager):
             assert torch.equal(t, e), f"replay {rep}: {name} differs from eager"
