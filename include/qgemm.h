@@ -87,6 +87,11 @@ enum {
 
 /* Workspace bytes needed by qgemm_prefill / qgemm_lm_head for M activation rows
  * of length K (int8 codes, per-block fp32 scales and scaled block sums).
+ * Rows are padded to a multiple of 256: the tiled kernels read whole row tiles
+ * (up to 128 rows) of the scale arrays, and a problem of any M, M <= 8
+ * included, may be sent down the tiled path (QG_PATH_TILED), while the
+ * workspace is sized before the path is known.  For one row at K = 4096 the
+ * padding costs 1.6 MB of workspace, against the LM head's 511 MB of weights.
  * Returns 0 when M < 1, K < 1, K % 256 != 0 or the size overflows. */
 size_t qgemm_workspace_bytes(int64_t M, int64_t K);
 
@@ -94,7 +99,7 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t K);
  *   q_weights : GGUF tensor data of a 2-D weight with K contiguous: row n holds
  *               K/256 consecutive blocks starting at byte n*(K/256)*bytes_per_block.
  *               Must be 16-byte aligned.
- *   fmt       : QG_Q4_K or QG_Q6_K.
+ *   fmt       : QG_Q4_K, QG_Q6_K, QG_Q5_K or QG_Q8_0 (block layouts above).
  *   x         : activations [M][K] row-major, element type x_dtype, 16-byte aligned.
  *   M, N, K   : M, N >= 1; K >= 256 and K % 256 == 0.
  *   y         : output [M][N] fp32 row-major (leading dimension N), overwritten.
@@ -155,14 +160,15 @@ int qgemm_quantize_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_t 
                        int32_t *S, void *stream);
 
 /* Decoded weights w [N][K] fp32, each the correctly rounded fp32 value of
- * d*sc*q - dmin*m (Q4_K) or d*sc*(q6 - 32) (Q6_K). */
+ * d*sc*q - dmin*m (Q4_K; Q5_K with q5), d*sc*(q6 - 32) (Q6_K) or d*q (Q8_0). */
 int qgemm_dequant(const void *q_weights, int fmt, int64_t N, int64_t K, float *w, void *stream);
 
 /* Per-block int32 partials computed by the tiled kernel's own decode and matrix
  * instructions: Q4_K out[m][n][b] = sum_{t<32} q[n][32b+t] * qx[m][32b+t]
- * (K/32 per pair, q in 0..15); Q6_K out[m][n][s] = sum_{t<16} (q6[n][16s+t] - 32)
- * * qx[m][16s+t] (K/16 per pair).  qx is int8 [M][K]; out has M*N*K/32 (Q4_K)
- * or M*N*K/16 (Q6_K) elements.  Meant for small shapes. */
+ * (K/32 per pair, q in 0..15; Q5_K the same with q5 in 0..31; Q8_0 with the
+ * int8 codes); Q6_K out[m][n][s] = sum_{t<16} (q6[n][16s+t] - 32)
+ * * qx[m][16s+t] (K/16 per pair).  qx is int8 [M][K]; out has M*N*K/32 (Q4_K,
+ * Q5_K, Q8_0) or M*N*K/16 (Q6_K) elements.  Meant for small shapes. */
 int qgemm_block_partials(const void *q_weights, int fmt, const int8_t *qx, int64_t M, int64_t N,
                          int64_t K, int32_t *out, void *stream);
 
@@ -305,6 +311,23 @@ const char *qgemm_kernel_name_swiglu(int fmt, int64_t M, int64_t F, int64_t K);
 /* The SwiGLU step alone: h [M][F] from the fp32 gate+up output y [M][2F] (y
  * and h 16-byte aligned; M * F <= 2^38). */
 int qgemm_swiglu(const float *y, int64_t M, int64_t F, uint16_t *h, void *stream);
+
+/* ---- diagnostics ---- */
+
+/* Shader clock under int8 matrix-core load, for benchmark receipts (the int8
+ * peak is quoted at the top clock; sustained matrix-core load runs lower).
+ * Launches one kernel on `stream` that keeps every SIMD of the current device
+ * busy with independent int8 32x32x32 MFMA chains (four waves per SIMD, four
+ * MFMAs per iteration, `iters` iterations) and writes to ticks[0..2] (device
+ * memory, 8-byte aligned, 3 x uint64): the shader-clock ticks and the 100 MHz
+ * reference-clock ticks that one wave counted over its loop, and a checksum of
+ * the MFMA results.  Shader clock in MHz = 100 * ticks[0] / ticks[1].
+ * iters in 1 .. 2^24 (QG_EINVAL otherwise).
+ *
+ * Path tracing: with QGEMM_TRACE=1 in the environment, every accepted GEMM call
+ * (plain, per-256, SwiGLU, fp16 branch) writes one line to stderr naming the
+ * entry point, format, M, N, K, the path taken and the kernel launched. */
+int qgemm_sclk_probe(uint64_t *ticks, int iters, void *stream);
 
 #ifdef __cplusplus
 }

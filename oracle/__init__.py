@@ -32,9 +32,10 @@ BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q5_K: 176, Q8_0: 272}   # bytes per 256 val
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile oracle.c with gcc: -O2, OpenMP, IEEE semantics (no fast-math, no contraction)."""
+    """Compile oracle.c with gcc: -O3, OpenMP, IEEE semantics (no fast-math, no contraction:
+    the optimiser may not reassociate or fuse floating-point operations)."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
            "-fno-fast-math", src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
@@ -44,6 +45,8 @@ def build(src: str = _SRC, out: str = _LIB) -> str:
 def _bind(path: str):
     lib = ctypes.CDLL(path)
     i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ci
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_decode_q4k.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
@@ -106,6 +109,11 @@ def _x_dtype(x: np.ndarray) -> int:
     if x.dtype == np.uint16:
         return BF16
     raise TypeError("activations must be float32 or bf16 bit patterns (uint16)")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use (the CPU baseline's core count)."""
+    return int(_load().oracle_num_threads())
 
 
 def half_to_double(h: int) -> float:

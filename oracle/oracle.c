@@ -50,12 +50,17 @@
  * of the activation quantiser are the correctly rounded ones.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { ORACLE_Q4_K = 0, ORACLE_Q6_K = 1, ORACLE_Q5_K = 2, ORACLE_Q8_0 = 3 };
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Threads an OpenMP region of this library runs on (for reporting the CPU
+ * baseline's core count; no arithmetic). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* IEEE binary16 bit pattern -> exact double (normals, subnormals, inf, nan). */
 double oracle_half_to_double(uint16_t h) {

@@ -15,6 +15,7 @@ import os
 import torch
 
 from ._build import LIB as _LIB_PATH
+from . import _build
 
 QG_Q4_K, QG_Q6_K, QG_Q5_K, QG_Q8_0 = 0, 1, 2, 3
 QG_F32, QG_BF16 = 0, 1
@@ -30,7 +31,7 @@ SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_
            "qgemm_kernel_name_a256", "qgemm_quantize_act_a256",
            "qgemm_rmsnorm_quantize_workspace", "qgemm_rmsnorm_quantize_act",
            "qgemm_swiglu_workspace_bytes", "qgemm_gemm_quantized_swiglu", "qgemm_prefill_swiglu",
-           "qgemm_kernel_name_swiglu", "qgemm_swiglu")
+           "qgemm_kernel_name_swiglu", "qgemm_swiglu", "qgemm_sclk_probe")
 
 
 class QgemmError(RuntimeError):
@@ -47,12 +48,16 @@ def library_path() -> str:
 
 
 def load() -> ctypes.CDLL:
-    """Load libqgemm.so (raises if it has not been built)."""
+    """Load libqgemm.so (raises if it has not been built, or was built from other
+    sources than the ones in the tree)."""
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise ImportError(f"{_LIB_PATH} is missing: build it first "
                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        if _build.is_stale():
+            raise ImportError(f"{_LIB_PATH} was built from other sources than csrc/ and include/ "
+                              "hold now: rebuild it (python -c 'import __graft_entry__ as g; g.build()')")
         lib = ctypes.CDLL(_LIB_PATH)
         i64, vp, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         lib.qgemm_workspace_bytes.argtypes = [i64, i64]
@@ -112,6 +117,8 @@ def load() -> ctypes.CDLL:
         lib.qgemm_kernel_name_swiglu.restype = ctypes.c_char_p
         lib.qgemm_swiglu.argtypes = [vp, i64, i64, vp, vp]
         lib.qgemm_swiglu.restype = ci
+        lib.qgemm_sclk_probe.argtypes = [vp, ci, vp]
+        lib.qgemm_sclk_probe.restype = ci
         _lib = lib
     return _lib
 
@@ -301,6 +308,22 @@ def qgemm_kernel_name_swiglu(fmt: int, M: int, F: int, K: int) -> str | None:
 
 def qgemm_swiglu(y, M, F, h, stream=None):
     _check(load().qgemm_swiglu(_ptr(y), M, F, _ptr(h), _stream(stream)), "qgemm_swiglu")
+
+
+# ---- diagnostics ----
+
+def qgemm_sclk_probe(ticks, iters, stream=None):
+    _check(load().qgemm_sclk_probe(_ptr(ticks), iters, _stream(stream)), "qgemm_sclk_probe")
+
+
+def measure_sclk_mhz(iters: int = 8000, stream=None, device="cuda") -> float:
+    """Shader clock (MHz) under int8 matrix-core load, from qgemm_sclk_probe."""
+    ticks = torch.zeros(3, dtype=torch.int64, device=device)
+    qgemm_sclk_probe(ticks, iters, stream)
+    t = ticks.cpu().tolist()
+    if t[1] <= 0:
+        raise RuntimeError("clock probe: no reference ticks")
+    return round(100.0 * t[0] / t[1], 1)
 
 
 # ---- plumbing helpers: device buffers for callers that do not manage their own ----

@@ -1,7 +1,10 @@
 // Host side of the C ABI declared in include/qgemm.h: argument checks,
 // workspace carving and kernel dispatch.  No allocation, no global mutable
-// state apart from a once-per-device architecture check.
+// state apart from a once-per-device architecture check and the trace switch
+// read once from the environment.
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -63,6 +66,36 @@ int check_common(const void* W, int fmt, int64_t N, int64_t K) {
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ELAUNCH; }
+
+// QGEMM_TRACE=1 in the environment: one line on stderr per accepted GEMM call
+// naming the entry point, the problem and the kernel it launches (which path
+// a call took is otherwise invisible to the caller).
+bool trace_on() {
+  static const bool on = [] {
+    const char* v = getenv("QGEMM_TRACE");
+    return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+const char* fmt_name(int fmt) {
+  switch (fmt) {
+    case QG_Q4_K: return "Q4_K";
+    case QG_Q6_K: return "Q6_K";
+    case QG_Q5_K: return "Q5_K";
+    case QG_Q8_0: return "Q8_0";
+    default: return "?";
+  }
+}
+
+// (callers test trace_on() first, so the kernel-name lookup costs nothing
+// when tracing is off)
+void trace(const char* entry, int fmt, int64_t M, int64_t N, int64_t K, const char* path,
+           const char* kernel) {
+  fprintf(stderr, "qgemm: %s fmt=%s M=%lld N=%lld K=%lld path=%s kernel=%s\n", entry, fmt_name(fmt),
+          static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K), path,
+          kernel ? kernel : "?");
+}
 
 // The tiled kernels of each format.
 hipError_t launch_tiled(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
@@ -144,6 +177,9 @@ int qgemm_gemm_quantized(const void* q_weights, int fmt, const void* workspace,
   const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (trace_on())
+    trace("gemm", fmt, M, N, K, skinny ? "skinny" : "tiled",
+        qgemm_kernel_name(fmt, M, N, K, skinny ? QG_PATH_SKINNY : QG_PATH_TILED));
   if (skinny) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
   return launch_status(launch_tiled(W, fmt, ws, M, N, K, y, s));
 }
@@ -278,6 +314,9 @@ int qgemm_gemm_quantized_a256(const void* q_weights, int fmt, const void* worksp
   const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (trace_on())
+    trace("gemm_a256", fmt, M, N, K, auto_skinny(fmt, M) ? "skinny" : "tiled",
+        qgemm_kernel_name_a256(fmt, M, N, K));
   // the skinny and small-grid kernels read the per-block scales, which the
   // per-256 workspace holds too
   if (auto_skinny(fmt, M)) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
@@ -366,6 +405,8 @@ int qgemm_prefill_deq_f16(const void* q_weights, int fmt, const void* x, int x_d
   rc = check_device();
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (trace_on())
+    trace("prefill_deq_f16", fmt, M, N, K, "f16", qgemm_deq_f16_kernel_name(fmt, M, N, K));
   uint16_t* x16 = static_cast<uint16_t*>(workspace);
   rc = launch_status(qg_launch_to_f16(x, x_dtype, M, K, x16, s));
   if (rc) return rc;
@@ -457,6 +498,9 @@ int qgemm_gemm_quantized_swiglu(const void* q_weights, int fmt, const void* work
   const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (trace_on())
+    trace("gemm_swiglu", fmt, M, 2 * F, K, swiglu_fused(fmt, M, F, K) ? "fused" : "gemm+swiglu",
+        qgemm_kernel_name_swiglu(fmt, M, F, K));
   if (swiglu_fused(fmt, M, F, K)) return launch_status(qg_launch_gemm_swiglu(W, fmt, ws, M, F, K, h, s));
   float* y = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) + L.total);
   if (auto_skinny(fmt, M)) rc = launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, 2 * F, K, y, s));
@@ -497,6 +541,16 @@ int qgemm_swiglu(const float* y, int64_t M, int64_t F, uint16_t* h, void* stream
   int rc = check_device();
   if (rc) return rc;
   return launch_status(qg_launch_swiglu(y, M, F, h, static_cast<hipStream_t>(stream)));
+}
+
+// ---- diagnostics ----
+
+int qgemm_sclk_probe(uint64_t* ticks, int iters, void* stream) {
+  if (!ticks || iters < 1 || iters > (1 << 24)) return QG_EINVAL;
+  if (!aligned(ticks, 8)) return QG_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_sclk_probe(ticks, iters, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -2,10 +2,12 @@
 // h[m][f] = bfloat16(silu(y[m][f]) * y[m][F + f]) from y [M][2F] fp32 -- the
 // separate swiglu launch of a layer's per-token launch list in aprender issue
 // #4220 ("CRUX parity spike: apr serve vs ollama", table of techniques
-// llama.cpp uses, technique 2).  The library fuses this step into the Q4_K
-// gate+up GEMM's epilogue; this kernel serves the problems that are not fused
-// (decode-sized batches on the skinny kernel, small grids, Q6_K weights) and
-// the unfused comparison.  HBM-bound: 8 bytes in, 2 bytes out per element.
+// llama.cpp uses, technique 2).  The library fuses this step into the gate+up
+// GEMM's epilogue for Q4_K, Q5_K and Q8_0 problems on the LDS-tiled kernels;
+// this kernel serves the problems that are not fused (decode-sized batches on
+// the skinny kernel, Q4_K and Q5_K problems on the small-grid kernel, Q6_K
+// weights) and the unfused comparison.  HBM-bound: 8 bytes in, 2 bytes out per
+// element.
 #include "common.h"
 
 namespace qg {

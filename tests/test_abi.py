@@ -305,3 +305,20 @@ def test_q80_host_side():
     assert lib.qgemm_prefill_a256(A, 3, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2
     assert lib.qgemm_prefill_deq_f16(A, 3, A, 1, 4, 8, 256, A, A, 1 << 20, None) == -2
     assert lib.qgemm_dequant_f16(A, 3, 8, 256, A, None) == -2
+
+
+def test_sclk_probe_rejects_bad_arguments():
+    lib = qg.load()
+    assert lib.qgemm_sclk_probe(None, 10, None) == -1
+    assert lib.qgemm_sclk_probe(A, 0, None) == -1
+    assert lib.qgemm_sclk_probe(A, (1 << 24) + 1, None) == -1
+    assert lib.qgemm_sclk_probe(A + 4, 10, None) == -5
+
+
+def test_library_matches_its_sources():
+    """The in-tree library was built from the sources the tree holds (the binding
+    refuses a stale one)."""
+    from quantized_prefill_gemm_q8_amd import _build
+    info = _build.build_info()
+    assert info.get("source_sha256") == _build.source_sha256()
+    assert not _build.is_stale()

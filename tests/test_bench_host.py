@@ -83,3 +83,67 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _receipt(**over):
+    out = {"metric": bench.METRIC, "value": 612.3, "unit": "TOPS", "n_gpus": 1, "steps": 100,
+           "warmup": 10, "ms_per_step": 0.168, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int8", "data": "synthetic (seeded)",
+           "config": {"workload": "long-prompt gate+up projection at one 512-row chunk: quantise bf16 "
+                                  "x [512x4096] + Q4_K GEMM 4096->24576",
+                      "M": 512, "K": 4096, "N": 24576, "fmt": "Q4_K", "projections": [[4096, 24576]]},
+           "prefill_tok_s": 3.0e6, "quant_us": 5.1, "gemm_us": 160.2,
+           "step_ms_p10_p50_p90": [0.16, 0.17, 0.18], "wall_s_timed": 0.02,
+           "roofline": {"bound": "mfma", "kernel": "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>",
+                        "achieved": 643.1, "peak": 5000.0, "unit": "TOPS", "frac": 0.1286,
+                        "traffic": 123456789, "avg_launch_us": 160.2, "ops_per_launch": 103079215104},
+           "cpu_baseline": {"value": 0.0958, "unit": "TOPS", "cores": 16, "nproc": 16,
+                            "cpu_model": "AMD EPYC 9575F 64-Core Processor", "kind": "oracle",
+                            "sample": "the whole step (512x4096->24576 Q4_K, activation quantisation "
+                                      "included) x10 in 12.3 s", "tok_s": 470.0},
+           "lm_head": {"kernel_us": 89.1, "gbps": 5734.2, "frac_hbm": 0.7168},
+           "large_m": {f"c4_{s}_M{m}": 0.1234 for m in (512, 2048, 8192) for s in ("gate_up", "down")} |
+                      {f"c3_{s}_M{m}": 0.1234 for m in (512, 4096) for s in ("gate_up", "down", "attn_out")},
+           "layer_tok_s": {f"config{c}_M{m}": 1234567.8 for c, ms in ((2, (512,)), (3, (512, 4096)),
+                                                                    (4, (512, 2048, 8192))) for m in ms},
+           "provenance": {"git_sha": "0123456789ab", "source_sha256": "0123456789abcdef",
+                          "rocm": "7.2.0", "hip": "7.0.51831", "torch": "2.10.0+rocm7.0",
+                          "gpu": "AMD Instinct MI355X gfx950:sramecc+:xnack-", "sclk_mhz_measured": 2100.0,
+                          "cu": 256}}
+    out.update(over)
+    return out
+
+
+def test_compact_line_is_the_receipt_and_fits():
+    line = bench.compact_line(_receipt())
+    assert len(line.encode()) <= bench.LINE_LIMIT
+    d = json.loads(line)
+    for k in bench.REQUIRED:
+        assert k in d, k
+    assert d["config"]["projections"] == [[4096, 24576]]
+    assert d["roofline"]["unit"] == "TOPS" and d["roofline"]["frac"] == pytest.approx(643.1 / 5000, abs=1e-4)
+    assert d["cpu_baseline"]["cpu_model"] and d["cpu_baseline"]["cores"] == 16
+    assert "tables" not in d and "step_ms_p10_p50_p90" not in d
+
+
+def test_compact_line_fails_closed():
+    r = _receipt()
+    del r["roofline"]
+    with pytest.raises(KeyError):
+        bench.compact_line(r)
+    r = _receipt()
+    del r["roofline"]["traffic"]
+    with pytest.raises(KeyError):
+        bench.compact_line(r)
+    r = _receipt()
+    del r["cpu_baseline"]["cpu_model"]
+    with pytest.raises(KeyError):
+        bench.compact_line(r)
+    with pytest.raises(ValueError):
+        bench.compact_line(_receipt(data="x" * 3000))
+
+
+def test_provenance_helpers():
+    assert bench.cpu_model()
+    assert bench.usable_cpus() >= 1
+    assert len(bench.source_hash()) == 64
