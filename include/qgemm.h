@@ -77,7 +77,8 @@ enum {
     QG_EWORKSPACE = -4, /* workspace NULL, smaller than qgemm_workspace_bytes, or not 256-B aligned */
     QG_EALIGN = -5,     /* q_weights not 16-B aligned, x not aligned to 16 B, y not 16-B aligned */
     QG_ELAUNCH = -6,    /* the HIP runtime reported a launch error */
-    QG_EDEVICE = -7     /* the current device is not a gfx950 GPU */
+    QG_EDEVICE = -7,    /* the current device is not a gfx950 GPU */
+    QG_ENOSCRATCH = -8  /* qgemm_prefill_noalloc: the problem's workspace exceeds the static scratch */
 };
 
 /* Largest skinny-path batch.  Under QG_PATH_AUTO, Q6_K and Q8_0 problems with
@@ -311,6 +312,31 @@ const char *qgemm_kernel_name_swiglu(int fmt, int64_t M, int64_t F, int64_t K);
 /* The SwiGLU step alone: h [M][F] from the fp32 gate+up output y [M][2F] (y
  * and h 16-byte aligned; M * F <= 2^38). */
 int qgemm_swiglu(const float *y, int64_t M, int64_t F, uint16_t *h, void *stream);
+
+/* ---- no allocation ----
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * qgemm_prefill_noalloc computes exactly what qgemm_prefill computes (same
+ * kernels, same result bit for bit) with the workspace taken from a static
+ * device array of QG_NOALLOC_SCRATCH_BYTES inside the library instead of a
+ * caller buffer, so it takes no workspace argument and allocates nothing.
+ *   - Limit: problems with qgemm_workspace_bytes(M, K) > QG_NOALLOC_SCRATCH_BYTES
+ *     are refused with QG_ENOSCRATCH before any launch (16 MiB holds e.g.
+ *     M = 2048 rows at K = 4096, or M = 512 at K = 16384).
+ *   - Every GPU the library runs on holds its own copy of the array (device
+ *     memory reserved with the library's code on that device) until the
+ *     process ends.  Its device address is looked up on the first call on
+ *     each device (make that first call outside graph capture).
+ *   - All calls on one GPU share that GPU's array: calls that may overlap on
+ *     one GPU (different streams, different host threads) race and must be
+ *     serialised by the caller.  Nothing in the array needs clearing; it is
+ *     rewritten by each call before it is read.
+ *   - Arguments, alignment, ownership and the other error codes as
+ *     qgemm_prefill (QG_PATH_AUTO). */
+#define QG_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int qgemm_prefill_noalloc(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
+                          int64_t N, int64_t K, float *y, void *stream);
 
 /* ---- diagnostics ---- */
 

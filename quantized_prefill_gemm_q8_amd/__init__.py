@@ -21,6 +21,8 @@ QG_Q4_K, QG_Q6_K, QG_Q5_K, QG_Q8_0 = 0, 1, 2, 3
 QG_F32, QG_BF16 = 0, 1
 QG_PATH_AUTO, QG_PATH_TILED, QG_PATH_SKINNY = 0, 1, 2
 QG_SKINNY_MAX_M = 8
+QG_NOALLOC_SCRATCH_BYTES = 16 << 20
+QG_ENOSCRATCH = -8
 BLOCK_BYTES = {QG_Q4_K: 144, QG_Q6_K: 210, QG_Q5_K: 176, QG_Q8_0: 272}  # per 256 values
 SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_lm_head",
            "qgemm_quantize_workspace", "qgemm_gemm_quantized",
@@ -31,7 +33,8 @@ SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_
            "qgemm_kernel_name_a256", "qgemm_quantize_act_a256",
            "qgemm_rmsnorm_quantize_workspace", "qgemm_rmsnorm_quantize_act",
            "qgemm_swiglu_workspace_bytes", "qgemm_gemm_quantized_swiglu", "qgemm_prefill_swiglu",
-           "qgemm_kernel_name_swiglu", "qgemm_swiglu", "qgemm_sclk_probe")
+           "qgemm_kernel_name_swiglu", "qgemm_swiglu", "qgemm_sclk_probe",
+           "qgemm_prefill_noalloc")
 
 
 class QgemmError(RuntimeError):
@@ -119,6 +122,8 @@ def load() -> ctypes.CDLL:
         lib.qgemm_swiglu.restype = ci
         lib.qgemm_sclk_probe.argtypes = [vp, ci, vp]
         lib.qgemm_sclk_probe.restype = ci
+        lib.qgemm_prefill_noalloc.argtypes = [vp, ci, vp, ci, i64, i64, i64, vp, vp]
+        lib.qgemm_prefill_noalloc.restype = ci
         _lib = lib
     return _lib
 
@@ -308,6 +313,13 @@ def qgemm_kernel_name_swiglu(fmt: int, M: int, F: int, K: int) -> str | None:
 
 def qgemm_swiglu(y, M, F, h, stream=None):
     _check(load().qgemm_swiglu(_ptr(y), M, F, _ptr(h), _stream(stream)), "qgemm_swiglu")
+
+
+# ---- no allocation (static scratch inside the library) ----
+
+def qgemm_prefill_noalloc(q_weights, fmt, x, M, N, K, y, stream=None):
+    _check(load().qgemm_prefill_noalloc(_ptr(q_weights), fmt, _ptr(x), _dtype_code(x), M, N, K, _ptr(y),
+                                        _stream(stream)), "qgemm_prefill_noalloc")
 
 
 # ---- diagnostics ----

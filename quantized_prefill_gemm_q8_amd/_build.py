@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libqgemm.so")
 INFO = LIB + ".json"
 HEADER = os.path.join(os.path.dirname(PKG), "include", "qgemm.h")
 SOURCES = ["act_quant.hip", "gemm_q4k.hip", "gemm_q6k.hip", "gemm_probe.hip", "gemm_skinny.hip",
-           "gemm_deq_f16.hip", "swiglu.hip", "dequant.hip", "clock.hip", "api.hip"]
+           "gemm_deq_f16.hip", "swiglu.hip", "dequant.hip", "clock.hip", "noalloc.hip", "api.hip"]
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -240,6 +240,7 @@ const char* qgemm_strerror(int code) {
     case QG_EALIGN: return "pointer not 16-byte aligned";
     case QG_ELAUNCH: return "kernel launch failed";
     case QG_EDEVICE: return "current device is not a gfx950 (MI355X) GPU";
+    case QG_ENOSCRATCH: return "problem too large for qgemm_prefill_noalloc's static scratch (QG_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

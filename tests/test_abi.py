@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_error_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = qg.qgemm_strerror(code)
         assert s and s != "unknown error code", code
     assert qg.qgemm_strerror(-99) == "unknown error code"
@@ -322,3 +322,14 @@ def test_library_matches_its_sources():
     info = _build.build_info()
     assert info.get("source_sha256") == _build.source_sha256()
     assert not _build.is_stale()
+
+
+def test_noalloc_rejects_before_any_launch():
+    lib = qg.load()
+    f = lib.qgemm_prefill_noalloc
+    assert f(None, 0, A, 1, 1, 1, 256, A, None) == -1
+    assert f(A, 0, A, 1, 1, 1, 300, A, None) == -1
+    assert f(A, 0, A, 1, 0, 1, 256, A, None) == -1
+    # 4096 x 4096 needs 26 MB of workspace: more than the static 16 MiB
+    assert qg.qgemm_workspace_bytes(4096, 4096) > qg.QG_NOALLOC_SCRATCH_BYTES
+    assert f(A, 0, A, 1, 4096, 256, 4096, A, None) == qg.QG_ENOSCRATCH
