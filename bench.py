@@ -9,7 +9,9 @@ HBM.  value = effective int8 TOPS of the step (2*M*N*K / step time); the
 roofline object is the step's GEMM kernel, its launches run back to back
 between two HIP events on the stream it is launched on.
 
-Timing: library calls are issued back to back on one stream between two HIP
+Timing: untimed steps run first for --settle-ms (default 500 ms, so the shader
+clock has ramped up), then the --warmup steps, then exactly --steps timed
+steps.  Library calls are issued back to back on one stream between two HIP
 events on that stream.  The step and the long GEMMs are issued eagerly, one
 call at a time (the host stays ahead of the GPU there); the decode-sized GEMVs
 and the LM head, whose kernels are short enough for the host's per-call cost
@@ -204,8 +206,8 @@ def compact_line(out: dict) -> str:
         for k in REQUIRED_CPU:
             if k not in cpu:
                 raise KeyError(f"cpu_baseline field missing: {k}")
-    keep = REQUIRED + ("prefill_tok_s", "quant_us", "gemm_us", "lm_head", "large_m", "layer_tok_s",
-                       "provenance")
+    keep = REQUIRED + ("prefill_tok_s", "settle_ms", "quant_us", "gemm_us", "lm_head", "large_m",
+                       "layer_tok_s", "provenance")
     line = json.dumps({k: out[k] for k in keep if k in out}, separators=(",", ":"))
     if len(line.encode()) > LINE_LIMIT:
         raise ValueError(f"compact line is {len(line)} bytes (limit {LINE_LIMIT})")
@@ -222,6 +224,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle-ms", type=float, default=500.0,
+                   help="untimed steps first, for this long, so the shader clock has ramped up "
+                        "before the warm-up steps and the timed region")
     p.add_argument("--lm-steps", type=int, default=50)    # 0: skip the LM head
     p.add_argument("--big-steps", type=int, default=10)   # 0: skip the large-M GEMM table
     p.add_argument("--gemv-steps", type=int, default=200)  # 0: skip the decode GEMV table
@@ -403,6 +408,15 @@ def main():
         quant()
         gemm()
 
+    # clock settle: the shader clock ramps up under sustained load over a few
+    # hundred milliseconds; a kernel timed in the first milliseconds of a
+    # process runs up to ~15% slower than the same kernel a moment later
+    settle0 = time.perf_counter()
+    while time.perf_counter() - settle0 < args.settle_ms * 1e-3:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - settle0) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -741,6 +755,7 @@ def main():
                                f"x [{M}x{K}] + Q4_K GEMM {K}->{N}",
                    "M": M, "K": K, "N": N, "fmt": "Q4_K", "projections": [[K, N]]},
         "prefill_tok_s": round(M / (ms_per_step * 1e-3), 1),
+        "settle_ms": round(settle_ms, 1),
         "quant_us": round(quant_us, 2),
         "gemm_us": round(gemm_us, 2),
         "step_ms_p10_p50_p90": [round(pct(step_ms, q), 5) for q in (0.1, 0.5, 0.9)],

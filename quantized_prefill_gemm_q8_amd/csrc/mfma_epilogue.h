@@ -22,27 +22,45 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 // each 16-lane DPP row holds the scale of element k's output row.
 __device__ __forceinline__ int dpp_scale_row(int lane) { return acc_row(lane & 15, lane >> 5); }
 
-// acc[r] += dxr(broadcast from lane r of this DPP row) * u[r], r = 0..15.
-// The statements are not volatile, so the scheduler may interleave them with
-// other work (the next tile's MFMAs, LDS reads).  DPP reads of a VGPR written
-// by a VALU instruction need two wait states; dxr is written at most once
-// before the sixteen reads, and the s_nop in front of the first read covers it.
-#define QG_FMAC_DPP(R, PRE)                                                            \
-  asm(PRE "v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #R                                 \
-      " row_mask:0xf bank_mask:0xf bound_ctrl:1"                                        \
-      : "+v"(acc[R]) : "v"(dxr), "v"(u[R]))
-
+// acc[r] += dxr(broadcast from lane r of this DPP row) * u[r], r = 0..15, with
+// u[r] = fl(I[r] * dsc) from the magic-biased accumulator D.  v_fmac_f32 with a
+// DPP row_newbcast:r source hands lane r's dxr of each 16-lane row to all lanes
+// of that row, so one VGPR per lane carries the sixteen row scales of a tile.
+// Each group of eight opens with the two wait states a DPP read needs after a
+// VALU write of its source, inside the same statement, so nothing the
+// compiler schedules falls between the wait and the reads.
 __device__ __forceinline__ void epilogue_scale(float (&acc)[16], const v16i& D, float dsc, float cc,
                                                float dxr) {
   float u[16];
 #pragma unroll
   for (int r = 0; r < 16; r++) u[r] = __builtin_fmaf(bits_to_float(D[r]), dsc, cc);  // fl(I*dsc)
-  QG_FMAC_DPP(0, "s_nop 1\n\t"); QG_FMAC_DPP(1, ""); QG_FMAC_DPP(2, ""); QG_FMAC_DPP(3, "");
-  QG_FMAC_DPP(4, ""); QG_FMAC_DPP(5, ""); QG_FMAC_DPP(6, ""); QG_FMAC_DPP(7, "");
-  QG_FMAC_DPP(8, ""); QG_FMAC_DPP(9, ""); QG_FMAC_DPP(10, ""); QG_FMAC_DPP(11, "");
-  QG_FMAC_DPP(12, ""); QG_FMAC_DPP(13, ""); QG_FMAC_DPP(14, ""); QG_FMAC_DPP(15, "");
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %8, %9 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %1, %8, %10 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %2, %8, %11 row_newbcast:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %3, %8, %12 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %4, %8, %13 row_newbcast:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %5, %8, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %6, %8, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %7, %8, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
+        "+v"(acc[7])
+      : "v"(dxr), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(u[4]), "v"(u[5]), "v"(u[6]),
+        "v"(u[7]));
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %8, %9 row_newbcast:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %1, %8, %10 row_newbcast:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %2, %8, %11 row_newbcast:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %3, %8, %12 row_newbcast:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %4, %8, %13 row_newbcast:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %5, %8, %14 row_newbcast:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %6, %8, %15 row_newbcast:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %7, %8, %16 row_newbcast:15 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]), "+v"(acc[12]), "+v"(acc[13]), "+v"(acc[14]),
+        "+v"(acc[15])
+      : "v"(dxr), "v"(u[8]), "v"(u[9]), "v"(u[10]), "v"(u[11]), "v"(u[12]), "v"(u[13]), "v"(u[14]),
+        "v"(u[15]));
 }
-#undef QG_FMAC_DPP
 
 // Q4_K: the 16 codes of sub-block j (j = 2c or 2c+1) for lane half h.  Bytes
 // qs[32c + 16h .. +15] hold sub-block 2c in their low nibbles and 2c+1 in their
