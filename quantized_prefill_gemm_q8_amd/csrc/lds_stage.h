@@ -50,10 +50,5 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Wait until this wave's LDS reads are done, then meet the workgroup barrier
-// (after it, no wave still reads a buffer that the next loads refill).
-__device__ __forceinline__ void wait_lgkm_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 }  // namespace qg
