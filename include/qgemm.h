@@ -355,6 +355,22 @@ int qgemm_prefill_noalloc(const void *q_weights, int fmt, const void *x, int x_d
  * entry point, format, M, N, K, the path taken and the kernel launched. */
 int qgemm_sclk_probe(uint64_t *ticks, int iters, void *stream);
 
+/* Planted delay, the falsifier of a benchmark's per-kernel timing rows (the
+ * bench check of aprender issue #3598, "EPIC E2 0.73: Verbs Are Fast", prior
+ * body, row 1: a delay planted in one kernel must move that kernel's row and
+ * the step total, and nothing else).  kernel = QG_PLANT_QUANTIZE: from the
+ * next call on, every launch of the per-32 activation quantiser that writes
+ * a GEMM workspace (qgemm_quantize_workspace, and the quantiser half of
+ * qgemm_prefill / qgemm_prefill_ex) has one wave of its first workgroup sleep
+ * `sleeps` times 64 shader clocks (s_sleep 1 in a loop of `sleeps`
+ * iterations) before it starts; the output is unchanged.  sleeps = 0 removes
+ * the delay.  sleeps in 0 .. QG_PLANT_MAX_SLEEPS, an unknown kernel:
+ * QG_EINVAL.  The setting is process-wide, host-side state (no launch, no
+ * device needed); set it only while no other thread is timing or launching. */
+#define QG_PLANT_QUANTIZE 1
+#define QG_PLANT_MAX_SLEEPS 1000000
+int qgemm_test_plant_delay(int kernel, int sleeps);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,8 @@ QG_PATH_AUTO, QG_PATH_TILED, QG_PATH_SKINNY = 0, 1, 2
 QG_SKINNY_MAX_M = 8
 QG_NOALLOC_SCRATCH_BYTES = 16 << 20
 QG_ENOSCRATCH = -8
+QG_PLANT_QUANTIZE = 1
+QG_PLANT_MAX_SLEEPS = 1000000
 BLOCK_BYTES = {QG_Q4_K: 144, QG_Q6_K: 210, QG_Q5_K: 176, QG_Q8_0: 272}  # per 256 values
 SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_lm_head",
            "qgemm_quantize_workspace", "qgemm_gemm_quantized",
@@ -34,7 +36,7 @@ SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_
            "qgemm_rmsnorm_quantize_workspace", "qgemm_rmsnorm_quantize_act",
            "qgemm_swiglu_workspace_bytes", "qgemm_gemm_quantized_swiglu", "qgemm_prefill_swiglu",
            "qgemm_kernel_name_swiglu", "qgemm_swiglu", "qgemm_sclk_probe",
-           "qgemm_prefill_noalloc")
+           "qgemm_prefill_noalloc", "qgemm_test_plant_delay")
 
 
 class QgemmError(RuntimeError):
@@ -124,6 +126,8 @@ def load() -> ctypes.CDLL:
         lib.qgemm_sclk_probe.restype = ci
         lib.qgemm_prefill_noalloc.argtypes = [vp, ci, vp, ci, i64, i64, i64, vp, vp]
         lib.qgemm_prefill_noalloc.restype = ci
+        lib.qgemm_test_plant_delay.argtypes = [ci, ci]
+        lib.qgemm_test_plant_delay.restype = ci
         _lib = lib
     return _lib
 
@@ -326,6 +330,11 @@ def qgemm_prefill_noalloc(q_weights, fmt, x, M, N, K, y, stream=None):
 
 def qgemm_sclk_probe(ticks, iters, stream=None):
     _check(load().qgemm_sclk_probe(_ptr(ticks), iters, _stream(stream)), "qgemm_sclk_probe")
+
+
+def qgemm_test_plant_delay(kernel, sleeps):
+    """Planted delay of one kernel, for the timing falsifier (0 removes it)."""
+    _check(load().qgemm_test_plant_delay(kernel, sleeps), "qgemm_test_plant_delay")
 
 
 def measure_sclk_mhz(iters: int = 8000, stream=None, device="cuda") -> float:

@@ -15,6 +15,8 @@
 // two 16-byte fp32 loads); amax and S are combined across the four lanes with
 // cross-lane shuffles.  HBM-bound: 2 (bf16) or 4 (fp32) bytes in per value,
 // 1 byte + 8 bytes per 32 values out.
+#include <atomic>
+
 #include "common.h"
 
 namespace qg {
@@ -123,7 +125,12 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
                                                         int32_t* __restrict__ S_int,
                                                         float* __restrict__ dS,
                                                         uint16_t* __restrict__ dsp,
-                                                        float* __restrict__ dxT, int64_t Mp) {
+                                                        float* __restrict__ dxT, int64_t Mp,
+                                                        int sleeps) {
+  // planted delay (timing falsifier): the first wave of the first workgroup
+  // sleeps before it starts; `sleeps` is bounded by the host
+  if (sleeps > 0 && blockIdx.x == 0 && threadIdx.x < 64)
+    for (int i = 0; i < sleeps; i++) __builtin_amdgcn_s_sleep(1);
   const int64_t per_row = K / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= M * per_row) return;  // whole groups of four lanes leave together
@@ -297,16 +304,23 @@ hipError_t qg_launch_act_quant256_hook(const void* x, int x_dtype, int64_t M, in
   return hipGetLastError();
 }
 
+namespace {
+std::atomic<int> g_planted_quant_sleeps{0};
+}  // namespace
+
+void qg_set_planted_quant_sleeps(int sleeps) { g_planted_quant_sleeps.store(sleeps); }
+
 hipError_t qg_launch_act_quant_ws(const void* x, int x_dtype, int64_t M, int64_t K,
                                   const QgWorkspace& ws, hipStream_t stream) {
+  const int sleeps = g_planted_quant_sleeps.load(std::memory_order_relaxed);
   const int64_t blocks = (M * (K / 8) + 255) / 256;
   const dim3 g(static_cast<unsigned>(blocks));
   if (x_dtype == QG_BF16)
     qg::act_quant_kernel<QG_BF16, true><<<g, dim3(256), 0, stream>>>(x, M, K, ws.q, ws.dx, nullptr,
-                                                                     ws.dS, ws.dsp, ws.dxT, ws.Mp);
+                                                                     ws.dS, ws.dsp, ws.dxT, ws.Mp, sleeps);
   else
     qg::act_quant_kernel<QG_F32, true><<<g, dim3(256), 0, stream>>>(x, M, K, ws.q, ws.dx, nullptr,
-                                                                    ws.dS, ws.dsp, ws.dxT, ws.Mp);
+                                                                    ws.dS, ws.dsp, ws.dxT, ws.Mp, sleeps);
   return hipGetLastError();
 }
 
@@ -316,10 +330,10 @@ hipError_t qg_launch_act_quant_hook(const void* x, int x_dtype, int64_t M, int64
   const dim3 g(static_cast<unsigned>(blocks));
   if (x_dtype == QG_BF16)
     qg::act_quant_kernel<QG_BF16, false><<<g, dim3(256), 0, stream>>>(x, M, K, q, d, S, nullptr,
-                                                                      nullptr, nullptr, 0);
+                                                                      nullptr, nullptr, 0, 0);
   else
     qg::act_quant_kernel<QG_F32, false><<<g, dim3(256), 0, stream>>>(x, M, K, q, d, S, nullptr,
-                                                                     nullptr, nullptr, 0);
+                                                                     nullptr, nullptr, 0, 0);
   return hipGetLastError();
 }
 

@@ -546,6 +546,12 @@ int qgemm_swiglu(const float* y, int64_t M, int64_t F, uint16_t* h, void* stream
 
 // ---- diagnostics ----
 
+int qgemm_test_plant_delay(int kernel, int sleeps) {
+  if (kernel != QG_PLANT_QUANTIZE || sleeps < 0 || sleeps > QG_PLANT_MAX_SLEEPS) return QG_EINVAL;
+  qg_set_planted_quant_sleeps(sleeps);
+  return QG_OK;
+}
+
 int qgemm_sclk_probe(uint64_t* ticks, int iters, void* stream) {
   if (!ticks || iters < 1 || iters > (1 << 24)) return QG_EINVAL;
   if (!aligned(ticks, 8)) return QG_EALIGN;

@@ -140,6 +140,9 @@ struct QgWorkspace {
 
 hipError_t qg_launch_act_quant_ws(const void* x, int x_dtype, int64_t M, int64_t K,
                                   const QgWorkspace& ws, hipStream_t stream);
+// Planted delay of the workspace quantiser (timing falsifier), in units of 64
+// shader clocks; 0 = none.
+void qg_set_planted_quant_sleeps(int sleeps);
 hipError_t qg_launch_act_quant_hook(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q,
                                     float* d, int32_t* S, hipStream_t stream);
 // per-256 activation scales: the same workspace layout with each super-block's

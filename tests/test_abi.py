@@ -322,6 +322,22 @@ def test_sclk_probe_rejects_bad_arguments():
     assert lib.qgemm_sclk_probe(A + 4, 10, None) == -5
 
 
+def test_plant_delay_host_side():
+    """The timing falsifier's planted delay: host-side state only, bounded."""
+    lib = qg.load()
+    hdr = open(HEADER).read()
+    assert f"#define QG_PLANT_QUANTIZE {qg.QG_PLANT_QUANTIZE}" in hdr
+    assert f"#define QG_PLANT_MAX_SLEEPS {qg.QG_PLANT_MAX_SLEEPS}" in hdr
+    assert lib.qgemm_test_plant_delay(0, 10) == -1
+    assert lib.qgemm_test_plant_delay(2, 10) == -1
+    assert lib.qgemm_test_plant_delay(qg.QG_PLANT_QUANTIZE, -1) == -1
+    assert lib.qgemm_test_plant_delay(qg.QG_PLANT_QUANTIZE, qg.QG_PLANT_MAX_SLEEPS + 1) == -1
+    try:
+        assert lib.qgemm_test_plant_delay(qg.QG_PLANT_QUANTIZE, qg.QG_PLANT_MAX_SLEEPS) == 0
+    finally:
+        assert lib.qgemm_test_plant_delay(qg.QG_PLANT_QUANTIZE, 0) == 0
+
+
 def test_library_matches_its_sources():
     """The in-tree library was built from the sources the tree holds (the binding
     refuses a stale one)."""
