@@ -124,8 +124,25 @@ __device__ __forceinline__ void q4k_lds_body(
   const int grp = wave_all / NW, wave = wave_all - grp * NW;  // K-group, wave within the group
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
-  const int64_t m_cta = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n_cta = static_cast<int64_t>(blockIdx.x) * (SW ? BN / 2 : BN);  // first weight row / column
+  // Tile order.  Workgroups go to the eight XCDs in turn (consecutive ids,
+  // x fastest), each XCD with its own L2.  For one-tile waves without a K
+  // split (64x128 blocks, two per CU) XCD k takes the k-th eighth of the
+  // tiles, row tiles fastest, so the row tiles that share a weight tile run
+  // on one XCD at the same time (measured at 512x4096->24576: L2 fills 336 ->
+  // 104 MB per launch, the same time; the 2x2-tile blocks measured slower
+  // this way and keep the grid order).
+  uint32_t mt = blockIdx.y, nt = blockIdx.x;
+  if constexpr (TM == 1 && TN == 1 && KS == 1 && !SW && !Q5 && !Q8 && !A256) {
+    const uint32_t G = gridDim.x * gridDim.y;
+    if (G % 8 == 0) {
+      const uint32_t L = blockIdx.y * gridDim.x + blockIdx.x;
+      const uint32_t Lp = (L % 8) * (G / 8) + L / 8;
+      mt = Lp % gridDim.y;
+      nt = Lp / gridDim.y;
+    }
+  }
+  const int64_t m_cta = static_cast<int64_t>(mt) * BM;
+  const int64_t n_cta = static_cast<int64_t>(nt) * (SW ? BN / 2 : BN);  // first weight row / column
   const int ml0 = 32 * TM * wm, nl0 = 32 * TN * wn;
   const int64_t nsb = K / 256, nb = K / 32;
   const int64_t wrow_bytes = nsb * BB;
