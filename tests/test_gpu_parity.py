@@ -281,14 +281,16 @@ def test_skinny_all_row_splits(fmt, K, N):
 @pytest.mark.parametrize("fmt,M,N,K", [
     (qg.QG_Q4_K, 2049, 15300, 1024),   # 128x256 tiles, ragged M and N
     (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
-    (qg.QG_Q4_K, 577, 8240, 768),      # 64x128 tiles at 4 waves/SIMD, ragged
+    (qg.QG_Q4_K, 577, 8240, 768),      # 64x128 tiles at 4 waves/SIMD, ragged (650 blocks: grid order)
+    (qg.QG_Q4_K, 577, 8100, 768),      # the same with 640 blocks: the XCD-aware tile order
     (qg.QG_Q4_K, 330, 2700, 1280),     # 64x128 blocks, K split over 2 groups (2 + 3 super-blocks)
     (qg.QG_Q4_K, 170, 2800, 2816),     # 32x64 blocks, K split over 4 groups (2 + 3 + 3 + 3)
-    (qg.QG_Q6_K, 1100, 8300, 1280),    # 128x128 tiles, ragged
-    (qg.QG_Q6_K, 600, 8300, 512),      # 64x128 tiles, ragged
-    (qg.QG_Q6_K, 300, 8300, 512),      # 64x64 blocks, K split over 2 groups of one stage buffer
-    (qg.QG_Q6_K, 70, 300, 768),        # the same, 1 + 2 super-blocks
-    (qg.QG_Q6_K, 70, 300, 256),        # 64x64 tiles, one super-block
+    (qg.QG_Q6_K, 2000, 4000, 512),     # one-stage 128x128 tiles (512 blocks: whole rounds), ragged
+    (qg.QG_Q6_K, 1100, 8300, 1280),    # half-stage 64x128 tiles (585 128x128 blocks: a ragged round)
+    (qg.QG_Q6_K, 600, 8300, 512),      # half-stage 64x128 tiles, ragged
+    (qg.QG_Q6_K, 300, 8300, 512),      # half-stage 64x64 blocks
+    (qg.QG_Q6_K, 70, 300, 768),        # half-stage 64x64 blocks, K split over 2 groups (1 + 2 super-blocks)
+    (qg.QG_Q6_K, 70, 300, 256),        # half-stage 64x64 blocks, one super-block
     (qg.QG_Q4_K, 65, 230, 2048),       # one 32x32 tile per wave, K split over 8 waves
     (qg.QG_Q4_K, 100, 200, 512),       # K split over 2 waves
     (qg.QG_Q5_K, 2049, 16480, 1024),   # Q5_K: 64x128 tiles (the 128x256 pick), ragged
