@@ -206,12 +206,18 @@ def compact_line(out: dict) -> str:
         for k in REQUIRED_CPU:
             if k not in cpu:
                 raise KeyError(f"cpu_baseline field missing: {k}")
-    keep = REQUIRED + ("prefill_tok_s", "settle_ms", "quant_us", "gemm_us", "lm_head", "large_m",
-                       "layer_tok_s", "provenance")
-    line = json.dumps({k: out[k] for k in keep if k in out}, separators=(",", ":"))
-    if len(line.encode()) > LINE_LIMIT:
-        raise ValueError(f"compact line is {len(line)} bytes (limit {LINE_LIMIT})")
-    return line
+    # optional summaries, the last dropped first while the line is over the limit
+    optional = ("provenance", "prefill_tok_s", "settle_ms", "quant_us", "gemm_us", "lm_head", "large_m",
+                "layer_tok_s")
+    keep = [k for k in REQUIRED + optional if k in out]
+    while True:
+        line = json.dumps({k: out[k] for k in keep}, separators=(",", ":"))
+        if len(line.encode()) <= LINE_LIMIT:
+            return line
+        if keep[-1] in REQUIRED:
+            raise ValueError(f"compact line is {len(line)} bytes with the required fields only "
+                             f"(limit {LINE_LIMIT})")
+        keep.pop()
 
 
 def emit_table(name: str, rows, tables: dict) -> None:

@@ -143,6 +143,18 @@ def test_compact_line_fails_closed():
         bench.compact_line(_receipt(data="x" * 3000))
 
 
+def test_compact_line_drops_summaries_before_the_limit():
+    """Over the limit, the optional summaries go (the last first); the receipt stays."""
+    r = _receipt()
+    r["layer_tok_s"] = {f"set{i}": 1234567.8 for i in range(40)}
+    line = bench.compact_line(r)
+    d = json.loads(line)
+    assert len(line.encode()) <= bench.LINE_LIMIT
+    assert "layer_tok_s" not in d and "provenance" in d
+    for k in bench.REQUIRED:
+        assert k in d, k
+
+
 def test_provenance_helpers():
     assert bench.cpu_model()
     assert bench.usable_cpus() >= 1
