@@ -513,7 +513,7 @@ void oracle_dequant_f16(int fmt, const uint8_t *W, int64_t N, int64_t K, uint16_
                 int e0 = ea < eb ? ea : eb;
                 for (int t = 0; t < 32; t++) {
                     /* dsc*q - dmn exactly, as an integer times 2^e0 (< 2^60) */
-                    int64_t D = ((a * q[32 * j + t]) << (ea - e0)) - (b << (eb - e0));
+                    int64_t D = a * q[32 * j + t] * ((int64_t)1 << (ea - e0)) - b * ((int64_t)1 << (eb - e0));
                     o[32 * j + t] = f16_round_scaled(D, e0);
                 }
             }

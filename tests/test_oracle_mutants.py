@@ -85,8 +85,8 @@ MUTANTS = [
      "int ebits = qe + 25;",
      "int ebits = qe + 24;"),
     ("deq_f16_min_sign",
-     "int64_t D = ((a * q[32 * j + t]) << (ea - e0)) - (b << (eb - e0));",
-     "int64_t D = ((a * q[32 * j + t]) << (ea - e0)) + (b << (eb - e0));"),
+     "int64_t D = a * q[32 * j + t] * ((int64_t)1 << (ea - e0)) - b * ((int64_t)1 << (eb - e0));",
+     "int64_t D = a * q[32 * j + t] * ((int64_t)1 << (ea - e0)) + b * ((int64_t)1 << (eb - e0));"),
     ("deq_f16_neighbour_scale",
      "f16_split(oracle_f64_to_f16(d * sc[j]), &a, &ea);     /* d*sc is exact in fp64 */",
      "f16_split(oracle_f64_to_f16(d * sc[j ^ 1]), &a, &ea);"),
