@@ -11,7 +11,8 @@ between two HIP events on the stream it is launched on.
 
 Timing: untimed steps run first for --settle-ms (default 500 ms, so the shader
 clock has ramped up), then the --warmup steps, then exactly --steps timed
-steps.  Library calls are issued back to back on one stream between two HIP
+steps; each table's shape gets about 200 ms of untimed launches before its
+timed rounds (the clock drops while the host builds the next inputs).  Library calls are issued back to back on one stream between two HIP
 events on that stream.  The step and the long GEMMs are issued eagerly, one
 call at a time (the host stays ahead of the GPU there); the decode-sized GEMVs
 and the LM head, whose kernels are short enough for the host's per-call cost
@@ -373,6 +374,15 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
+    def settle(fn, ms=200.0):
+        """Run fn back to back for about `ms` milliseconds (untimed): after host-side
+        work the clock has dropped, and it takes a few hundred ms of load to ramp up."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < ms * 1e-3:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+
     def capture(fn, n):
         """A HIP graph of n back-to-back calls fn() on `stream` (the library's
         launches are recorded, not run; nothing is allocated inside)."""
@@ -465,7 +475,7 @@ def main():
         yb = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
         qg.qgemm_quantize_workspace(xb, g.M, g.K, wsb, stream)
         fn = lambda: qg.qgemm_gemm_quantized(Wb, g.fmt, wsb, g.M, g.N, g.K, yb, stream)
-        timed(fn, 3)
+        settle(fn)
         # the least of three rounds of at least five launches (a single short
         # round reads the clock dips between tables as kernel time)
         steps = max(5, args.big_steps * 512 // g.M)
@@ -508,8 +518,8 @@ def main():
                     if not share:
                         qg.qgemm_quantize_workspace(xs, g.M, g.K, wss, stream)
                     qg.qgemm_gemm_quantized(Wm, g.fmt, wss, g.M, g.N, g.K, ys, stream)
-            timed(set_step, 2)
-            ms = timed(set_step, args.set_steps) / args.set_steps
+            settle(set_step)
+            ms = min(timed(set_step, args.set_steps) for _ in range(3)) / args.set_steps
             ops = sum(g.ops for g in members)
             sets[f"config{cfg}_M{Mset}"] = {
                 "projections": [f"{g.K}->{g.N} {fmt_name[g.fmt]}" for g in members],
@@ -548,6 +558,7 @@ def main():
             us = {}
             for fn in calls.values():
                 timed(fn, 2)
+            settle(calls["int8"])
             for _ in range(3):
                 for k, fn in calls.items():
                     us[k] = min(us.get(k, 1e30), 1e3 * timed(fn, args.branch_steps) / args.branch_steps)
@@ -629,6 +640,7 @@ def main():
             us = {}
             for fn in calls.values():
                 timed(fn, 2)
+            settle(calls["ffn_fused"])
             for _ in range(3):
                 for k, fn in calls.items():
                     us[k] = min(us.get(k, 1e30), 1e3 * timed(fn, args.fusion_steps) / args.fusion_steps)
