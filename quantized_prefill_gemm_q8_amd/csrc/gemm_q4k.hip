@@ -282,7 +282,7 @@ __device__ __forceinline__ void q4k_lds_body(
       }
     }
 
-#pragma unroll(NW * KS >= 12 ? 1 : 4)
+#pragma unroll
     for (int c = 0; c < 4; c++) {
       uint4 wraw[TN];
 #pragma unroll
