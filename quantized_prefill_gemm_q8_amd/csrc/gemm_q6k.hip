@@ -37,8 +37,8 @@
 //   gemm_q6k_lds_kernel   one stage per super-block (above); large grids,
 //                         2x1 tiles per wave (the decoded codes serve both)
 //   gemm_q6k_half_kernel  one stage per half super-block (128 values), so
-//                         that two stage buffers fit beside the second and
-//                         third workgroup of a CU; one tile per wave, the
+//                         that two stage buffers fit beside three more
+//                         workgroups on a CU; one tile per wave, the
 //                         activation chunks staged column-major (chunk c of
 //                         every row, then chunk c+1), which turns every
 //                         operand read into a per-lane base plus a constant
@@ -544,20 +544,19 @@ static void launch_q6k_half(const uint8_t* W, const QgWorkspace& ws, int64_t M, 
       W, ws.q, ws.dxT, ws.Mp, M, N, K, y);
 }
 
-// Kernel choice (measured on the workloads' shapes): 128x128 blocks of 8
-// waves x 2x1 tiles (one per CU) when their grid fills whole rounds of the
-// chip or so many rounds that a ragged last one matters little (long-K
-// prompts from 2048 rows, the LM head at 512 rows); otherwise half-stage
-// kernels: 64x128 blocks (two per CU) while there are two per CU, then 64x64
-// blocks of 4 waves (up to four per CU), and for fewer 64x64 blocks than CUs
-// the same blocks with the K range split between two groups of 4 waves.
-enum class Q6Pick { k128x128, k64x128, k64x64, k64x64K2 };
+// Kernel choice (measured on the workloads' shapes and their neighbours):
+// 128x128 one-stage blocks of 8 waves x 2x1 tiles (one per CU) when their
+// grid fills whole rounds of the chip or at least eight rounds (long-K
+// prompts from 1024 rows, the LM head at 512 rows); otherwise half-stage
+// 64x64 blocks of 4 waves (up to four per CU; 64x128 blocks measured within
+// 2% of them or 10% slower), with the K range split between two groups of 4
+// waves when there are fewer 64x64 blocks than CUs.
+enum class Q6Pick { k128x128, k64x64, k64x64K2 };
 
 inline Q6Pick pick_q6k(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256;
   const int64_t b128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (b128 >= 2 * kCUs && (b128 % kCUs == 0 || b128 >= 8 * kCUs)) return Q6Pick::k128x128;
-  if (((M + 63) / 64) * ((N + 127) / 128) >= 2 * kCUs) return Q6Pick::k64x128;
+  if (b128 >= kCUs && (b128 % kCUs == 0 || b128 >= 8 * kCUs)) return Q6Pick::k128x128;
   if (((M + 63) / 64) * ((N + 63) / 64) >= kCUs || K < 512) return Q6Pick::k64x64;
   return Q6Pick::k64x64K2;
 }
@@ -567,7 +566,6 @@ inline Q6Pick pick_q6k(int64_t M, int64_t N, int64_t K) {
 const char* qg_gemm_q6k_kernel_name(int64_t M, int64_t N, int64_t K) {
   switch (qg::pick_q6k(M, N, K)) {
     case qg::Q6Pick::k128x128: return "gemm_q6k_lds_kernel<2, 1, 2, 4, 2, 2, 1>";
-    case qg::Q6Pick::k64x128: return "gemm_q6k_half_kernel<1, 1, 2, 4, 2, 4, 1>";
     case qg::Q6Pick::k64x64: return "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 1>";
     case qg::Q6Pick::k64x64K2: return "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 2>";
   }
@@ -578,7 +576,6 @@ hipError_t qg_launch_gemm_q6k(const uint8_t* W, const QgWorkspace& ws, int64_t M
                               int64_t K, float* y, hipStream_t stream) {
   switch (qg::pick_q6k(M, N, K)) {
     case qg::Q6Pick::k128x128: qg::launch_q6k_lds<2, 1, 2, 4, 2, 2, 1>(W, ws, M, N, K, y, stream); break;
-    case qg::Q6Pick::k64x128: qg::launch_q6k_half<1, 1, 2, 4, 2, 4, 1>(W, ws, M, N, K, y, stream); break;
     case qg::Q6Pick::k64x64: qg::launch_q6k_half<1, 1, 2, 2, 2, 4, 1>(W, ws, M, N, K, y, stream); break;
     case qg::Q6Pick::k64x64K2: qg::launch_q6k_half<1, 1, 2, 2, 2, 4, 2>(W, ws, M, N, K, y, stream); break;
   }

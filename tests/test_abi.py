@@ -147,16 +147,17 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 170, 2800, 2816, AUTO) == "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, false>"
     assert kn(Q4, 512, 1024, 1792, AUTO).startswith("gemm_q4k_small_kernel<")   # too few super-blocks
     # Q6_K: 128x128 blocks when their grid fills whole rounds (or many), else
-    # the half-stage kernel at 64x128, 64x64, or 64x64 with a split K range
+    # the half-stage kernel at 64x64, or 64x64 with a split K range
     q6big = "gemm_q6k_lds_kernel<2, 1, 2, 4, 2, 2, 1>"
     assert kn(Q6, 8192, 4096, 12288, AUTO) == q6big and kn(Q6, 2048, 4096, 12288, AUTO) == q6big
+    assert kn(Q6, 1024, 4096, 12288, AUTO) == q6big                     # 256 blocks: one round
     assert kn(Q6, 512, 152064, 4096, AUTO) == q6big                      # 4752 blocks
-    assert kn(Q6, 4096, 2560, 4096, AUTO) == "gemm_q6k_half_kernel<1, 1, 2, 4, 2, 4, 1>"  # 640 blocks
-    assert kn(Q6, 1536, 4096, 12288, AUTO) == "gemm_q6k_half_kernel<1, 1, 2, 4, 2, 4, 1>"
-    assert kn(Q6, 512, 4096, 12288, AUTO) == "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 1>"
-    assert kn(Q6, 512, 2560, 4096, AUTO) == "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 1>"
+    half = "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 1>"
+    assert kn(Q6, 4096, 2560, 4096, AUTO) == half                        # 640 blocks: 2.5 rounds
+    assert kn(Q6, 1536, 4096, 12288, AUTO) == half
+    assert kn(Q6, 512, 4096, 12288, AUTO) == half and kn(Q6, 512, 2560, 4096, AUTO) == half
     assert kn(Q6, 77, 300, 1024, AUTO) == "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 2>"
-    assert kn(Q6, 70, 300, 256, AUTO) == "gemm_q6k_half_kernel<1, 1, 2, 2, 2, 4, 1>"
+    assert kn(Q6, 70, 300, 256, AUTO) == half
     # arguments the entry points would reject
     assert kn(4, 8, 8, 256, AUTO) is None
     assert kn(Q4, 8, 8, 300, AUTO) is None

@@ -286,8 +286,8 @@ def test_skinny_all_row_splits(fmt, K, N):
     (qg.QG_Q4_K, 330, 2700, 1280),     # 64x128 blocks, K split over 2 groups (2 + 3 super-blocks)
     (qg.QG_Q4_K, 170, 2800, 2816),     # 32x64 blocks, K split over 4 groups (2 + 3 + 3 + 3)
     (qg.QG_Q6_K, 2000, 4000, 512),     # one-stage 128x128 tiles (512 blocks: whole rounds), ragged
-    (qg.QG_Q6_K, 1100, 8300, 1280),    # half-stage 64x128 tiles (585 128x128 blocks: a ragged round)
-    (qg.QG_Q6_K, 600, 8300, 512),      # half-stage 64x128 tiles, ragged
+    (qg.QG_Q6_K, 1100, 8300, 1280),    # half-stage 64x64 blocks (585 128x128 blocks: a ragged round)
+    (qg.QG_Q6_K, 600, 8300, 512),      # half-stage 64x64 blocks, ragged
     (qg.QG_Q6_K, 300, 8300, 512),      # half-stage 64x64 blocks
     (qg.QG_Q6_K, 70, 300, 768),        # half-stage 64x64 blocks, K split over 2 groups (1 + 2 super-blocks)
     (qg.QG_Q6_K, 70, 300, 256),        # half-stage 64x64 blocks, one super-block
