@@ -93,6 +93,13 @@ __device__ __forceinline__ uint16_t load_u16(const uint8_t* p) {
 // 4 MB L2) does not evict the weight and activation tiles other workgroups
 // still read (measured 1-5% faster on the workloads' shapes).
 __device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
+// The same at device scope: written through to memory rather than kept in
+// the XCD's L2, where it would push out activation tiles that later
+// workgroups reuse (the one-tile Q4_K kernel at 512x4096->24576: 2 MB fewer
+// L2 fills per launch, the same time).
+__device__ __forceinline__ void store_out_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // fp32 -> bfloat16 bits, rounded to nearest with ties to even (a NaN stays a
 // quiet NaN; values past the largest bfloat16 round to infinity).

@@ -537,7 +537,10 @@ __device__ __forceinline__ void q4k_lds_body(
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int64_t m = m_cta + ml0 + 32 * i + acc_row(r, h);
-        if (m < M) store_out(y + m * N + n, acc[i][j][r]);
+        if (m < M) {
+          if constexpr (TM == 1 && TN == 1 && KS == 1 && !Q5 && !Q8 && !A256) store_out_dev(y + m * N + n, acc[i][j][r]);
+          else store_out(y + m * N + n, acc[i][j][r]);
+        }
       }
   }
 }
