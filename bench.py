@@ -16,7 +16,11 @@ timed rounds (the clock drops while the host builds the next inputs).  Library c
 events on that stream.  The step and the long GEMMs are issued eagerly, one
 call at a time (the host stays ahead of the GPU there); the decode-sized GEMVs
 and the LM head, whose kernels are short enough for the host's per-call cost
-to pace an eager loop, are captured once as a HIP graph and replayed.
+to pace an eager loop, are captured once as a HIP graph and replayed.  Each
+of them is also quoted against a read floor: the library's read probe
+(qgemm_read_probe, one pass over the same bytes in the same buffers, nothing
+written) timed the same way, the least time one launch reading those bytes
+takes here.
 
 Output: every table (the other projection shapes at M = 512 ... 8192, one
 layer's projection set per configuration, the decode-sized GEMV table, the LM
@@ -407,6 +411,19 @@ def main():
         n = min(total, 50)
         return n, max(1, (total + n - 1) // n)
 
+    def read_floor_us(bufs, nbytes, n, r):
+        """Microseconds per launch of the library's read probe over nbytes of each
+        buffer in turn (one pass, nothing written): the floor a bandwidth-bound
+        kernel reading the same bytes from the same place can reach."""
+        nb16 = nbytes // 16 * 16
+        ring = iter(range(1 << 30))
+        nc = max(n, len(bufs))
+        g = capture(lambda: qg.qgemm_read_probe(bufs[next(ring) % len(bufs)], nb16, stream), nc)
+        time_replays(g, 1)
+        us = 1e3 * time_replays(g, r) / (nc * r)
+        del g
+        return us
+
     # ---------------- the headline step: quantise x [512 x 4096] + Q4_K GEMM 4096 -> 24576
     W_h = to_dev(synth.make_weights(hg))
     x_h = to_dev(synth.make_acts(hg))
@@ -668,6 +685,7 @@ def main():
     # 256 MB MALL, so every launch streams its weights from HBM.
     gemv = {}
     seen = set()
+    floors = {}  # weight bytes -> read-probe microseconds over the same cold copies
     gemv_shapes = [g2 for cfg in ((2, 3, 4) if args.gemv_steps > 0 else ()) for g in synth.CONFIGS[cfg]
                    for g2 in ([g] + [dataclasses.replace(g, fmt=f) for f in (qg.QG_Q5_K, qg.QG_Q8_0)]
                               if g.fmt == qg.QG_Q4_K else [g])]
@@ -701,7 +719,10 @@ def main():
             gc = capture(gemv_cold, nc)
             time_replays(gc, 1)
             us_cold = 1e3 * time_replays(gc, r) / (nc * r)
-            del gc, copies
+            del gc
+            if g.w_bytes not in floors:
+                floors[g.w_bytes] = read_floor_us(copies, g.w_bytes, n, r)
+            del copies
             gbs = g.w_bytes / (us * 1e-6) / 1e9
             gbs_cold = g.w_bytes / (us_cold * 1e-6) / 1e9
             gemv[f"K={g.K} N={g.N} {fmt_name[g.fmt]} M={Mg}"] = {
@@ -709,7 +730,9 @@ def main():
                 "weight_bytes": g.w_bytes,
                 "warm_us": round(us, 2), "warm_mall_gbps": round(gbs, 1),
                 "cold_us": round(us_cold, 2), "cold_hbm_gbps": round(gbs_cold, 1),
-                "cold_frac_hbm": round(gbs_cold / PEAK_HBM_GBS, 4)}
+                "cold_frac_hbm": round(gbs_cold / PEAK_HBM_GBS, 4),
+                "read_floor_us": round(floors[g.w_bytes], 2),
+                "cold_over_floor": round(us_cold / floors[g.w_bytes], 3)}
         del Wg, xg
     emit_table("decode_gemv", gemv, tables)
 
@@ -738,11 +761,15 @@ def main():
         lm_kernel_us = 1e3 * time_replays(ga, r) / (n * r)
         time_replays(gc, 1)
         lm_call_us = 1e3 * time_replays(gc, r) / (n * r)
-        del ga, gc, W_lm
+        del ga, gc
+        lm_floor_us = read_floor_us([W_lm], lm.w_bytes, n, r)
+        del W_lm
         lm_gbs = lm.w_bytes / (lm_kernel_us * 1e-6) / 1e9
         lm_out = {"kernel": qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K),
                   "kernel_us": round(lm_kernel_us, 2), "call_us": round(lm_call_us, 2),
                   "gbps": round(lm_gbs, 1), "frac_hbm": round(lm_gbs / PEAK_HBM_GBS, 4),
+                  "read_floor_us": round(lm_floor_us, 2),
+                  "floor_frac_hbm": round(lm.w_bytes / (lm_floor_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                   "traffic": traffic_for(qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K))}
         emit_table("lm_head", dict(lm_out, workload="M=1, K=4096 -> N=152064, Q6_K (skinny path)",
                                    weight_bytes=lm.w_bytes), tables)
@@ -785,7 +812,8 @@ def main():
                      "traffic": traffic_for(kname), "avg_launch_us": round(gemm_us, 2),
                      "ops_per_launch": hg.ops},
         "cpu_baseline": cpu,
-        "lm_head": None if lm_out is None else {k: lm_out[k] for k in ("kernel_us", "gbps", "frac_hbm")},
+        "lm_head": None if lm_out is None else {k: lm_out[k] for k in ("kernel_us", "gbps", "frac_hbm",
+                                                                          "read_floor_us")},
         "large_m": {k: v["frac_int8_peak"] for k, v in big.items()},
         "layer_tok_s": {k: v["prefill_tok_s"] for k, v in sets.items()},
         "provenance": {"git_sha": git_sha(), "source_sha256": source_hash()[:16],

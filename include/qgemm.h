@@ -355,6 +355,16 @@ int qgemm_prefill_noalloc(const void *q_weights, int fmt, const void *x, int x_d
  * entry point, format, M, N, K, the path taken and the kernel launched. */
 int qgemm_sclk_probe(uint64_t *ticks, int iters, void *stream);
 
+/* Read floor, for benchmark receipts of the bandwidth-bound kernels: launches
+ * one kernel on `stream` that reads every byte of src[0 .. bytes) once
+ * (16-byte loads, grid-stride over eight 256-thread workgroups per CU) and
+ * writes nothing.  Its time is the floor that any one launch reading the same
+ * bytes can reach, ramp-up and tail included (a decode GEMV is quoted against
+ * it).  src: device memory, 16-byte aligned (QG_EALIGN otherwise), not
+ * modified; bytes: a multiple of 16, >= 0 (QG_EINVAL otherwise; 0 launches
+ * nothing); src may be NULL only when bytes = 0. */
+int qgemm_read_probe(const void *src, int64_t bytes, void *stream);
+
 /* Planted delay, the falsifier of a benchmark's per-kernel timing rows (the
  * bench check of aprender issue #3598, "EPIC E2 0.73: Verbs Are Fast", prior
  * body, row 1: a delay planted in one kernel must move that kernel's row and

@@ -35,7 +35,7 @@ SYMBOLS = ("qgemm_workspace_bytes", "qgemm_prefill", "qgemm_prefill_ex", "qgemm_
            "qgemm_kernel_name_a256", "qgemm_quantize_act_a256",
            "qgemm_rmsnorm_quantize_workspace", "qgemm_rmsnorm_quantize_act",
            "qgemm_swiglu_workspace_bytes", "qgemm_gemm_quantized_swiglu", "qgemm_prefill_swiglu",
-           "qgemm_kernel_name_swiglu", "qgemm_swiglu", "qgemm_sclk_probe",
+           "qgemm_kernel_name_swiglu", "qgemm_swiglu", "qgemm_sclk_probe", "qgemm_read_probe",
            "qgemm_prefill_noalloc", "qgemm_test_plant_delay")
 
 
@@ -124,6 +124,8 @@ def load() -> ctypes.CDLL:
         lib.qgemm_swiglu.restype = ci
         lib.qgemm_sclk_probe.argtypes = [vp, ci, vp]
         lib.qgemm_sclk_probe.restype = ci
+        lib.qgemm_read_probe.argtypes = [vp, i64, vp]
+        lib.qgemm_read_probe.restype = ci
         lib.qgemm_prefill_noalloc.argtypes = [vp, ci, vp, ci, i64, i64, i64, vp, vp]
         lib.qgemm_prefill_noalloc.restype = ci
         lib.qgemm_test_plant_delay.argtypes = [ci, ci]
@@ -330,6 +332,11 @@ def qgemm_prefill_noalloc(q_weights, fmt, x, M, N, K, y, stream=None):
 
 def qgemm_sclk_probe(ticks, iters, stream=None):
     _check(load().qgemm_sclk_probe(_ptr(ticks), iters, _stream(stream)), "qgemm_sclk_probe")
+
+
+def qgemm_read_probe(src, nbytes, stream=None):
+    """Read nbytes of the device buffer src once (the floor of a bandwidth-bound launch)."""
+    _check(load().qgemm_read_probe(_ptr(src), nbytes, _stream(stream)), "qgemm_read_probe")
 
 
 def qgemm_test_plant_delay(kernel, sleeps):

@@ -560,4 +560,12 @@ int qgemm_sclk_probe(uint64_t* ticks, int iters, void* stream) {
   return launch_status(qg_launch_sclk_probe(ticks, iters, static_cast<hipStream_t>(stream)));
 }
 
+int qgemm_read_probe(const void* src, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || (bytes > 0 && !src)) return QG_EINVAL;
+  if (!aligned(src, 16)) return QG_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(qg_launch_read_probe(src, bytes, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,4 +1,7 @@
-// Shader-clock probe for benchmark receipts (not part of the GEMM path).
+// Benchmark probes (not part of the GEMM path): the shader clock under
+// matrix-core load, and the time a plain read of a weight matrix's bytes takes.
+//
+// Shader-clock probe.
 //
 // The int8 GEMM's throughput is quoted against a peak taken at the chip's
 // top clock, while sustained matrix-core load runs the shader clock lower.
@@ -39,7 +42,35 @@ __global__ __launch_bounds__(256) void sclk_probe_kernel(uint64_t* __restrict__ 
   }
 }
 
+// Read probe: every byte of [src, src + 16*n16) read once in 16-byte loads,
+// grid-stride (thread t reads chunks t, t + T, t + 2T, ...), nothing written.
+// The floor a bandwidth-bound kernel reading the same bytes can reach from
+// one launch (ramp-up and tail included).
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  uint32_t acc = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  asm volatile("" ::"v"(acc));  // the loads stay: their value is used
+}
+
 }  // namespace qg
+
+// grid: eight workgroups of four waves (32 waves) per CU, the fastest of 4-32
+// waves per CU and 1-4 loads in flight per lane for 8.6 MB to 511 MB (cold)
+hipError_t qg_launch_read_probe(const void* src, int64_t bytes, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (bytes == 0) return hipSuccess;
+  qg::read_probe_kernel<<<dim3(static_cast<unsigned>(cus) * 8u), dim3(256), 0, stream>>>(
+      static_cast<const uint4*>(src), bytes / 16);
+  return hipGetLastError();
+}
 
 // grid: four waves per SIMD on every CU of the device
 hipError_t qg_launch_sclk_probe(uint64_t* out, int iters, hipStream_t stream) {

@@ -209,5 +209,7 @@ hipError_t qg_launch_gemm_deq_f16(const uint8_t* W, int fmt, const uint16_t* x16
 const char* qg_gemm_deq_f16_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 // shader-clock probe (benchmark receipts): ticks[0..2] as qgemm_sclk_probe documents
 hipError_t qg_launch_sclk_probe(uint64_t* ticks, int iters, hipStream_t stream);
+// read probe (benchmark floor): bytes read once from src, as qgemm_read_probe documents
+hipError_t qg_launch_read_probe(const void* src, int64_t bytes, hipStream_t stream);
 hipError_t qg_launch_block_partials(const uint8_t* W, int fmt, const int8_t* qx, int64_t M,
                                     int64_t N, int64_t K, int32_t* out, hipStream_t stream);

@@ -613,6 +613,10 @@ __global__ __launch_bounds__(64 * WM * WN * KS) __attribute__((amdgpu_waves_per_
 // wave-private LDS slice ([8][32] per super-block) and are read as 16-byte
 // broadcasts.  The partial tiles are summed through LDS in ascending wave
 // order, so the result does not depend on timing.
+// RN: accumulator elements per lane that hold output rows.  With at most 8
+// rows (decode-sized batches) only elements 0..3 of a lane do (rows 4h + r),
+// so the epilogue, the min term and the activation loads skip the other
+// rows (RN = 4; measured 1.1-1.4x on the decode shapes' grids).
 struct SmallStage {
   v4i a[8];
   uint4 w[4], hdr, qh;  // qh: Q5_K only
@@ -620,7 +624,7 @@ struct SmallStage {
   float4 xs;
 };
 
-template <int SK, bool Q5>
+template <int SK, bool Q5, int RN>
 __device__ __forceinline__ void q4k_small_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
     int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
@@ -635,16 +639,19 @@ __device__ __forceinline__ void q4k_small_body(
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 32;
   const int64_t nsb = K / 256;
   const int64_t sb_begin = kk * nsb / SK, sb_end = (kk + 1) * nsb / SK;
+  static_assert(RN == 4 || RN == 16, "rows per lane");
   int64_t m = m0 + l32, n = n0 + l32;
   m = m < M ? m : M - 1;
   n = n < N ? n : N - 1;
+  const bool arow_used = RN == 16 || l32 < 8;  // activation rows that reach an output row
   const int8_t* arow = qx + m * K + 16 * h;
   const uint8_t* wrow = W + n * nsb * BB;
   const uint16_t* prow = dsp + (m0 + l32) * nsb * 24;  // rows up to the padding (m0 + 31 < Mp)
 
   auto load = [&](int64_t sb, SmallStage& st) {
 #pragma unroll
-    for (int b = 0; b < 8; b++) st.a[b] = *reinterpret_cast<const v4i*>(arow + 256 * sb + 32 * b);
+    for (int b = 0; b < 8; b++)
+      st.a[b] = arow_used ? *reinterpret_cast<const v4i*>(arow + 256 * sb + 32 * b) : v4i{0, 0, 0, 0};
     const uint8_t* blk = wrow + sb * BB;
     st.hdr = *reinterpret_cast<const uint4*>(blk);
 #pragma unroll
@@ -685,7 +692,7 @@ __device__ __forceinline__ void q4k_small_body(
         dxv[4 * g] = v.x; dxv[4 * g + 1] = v.y; dxv[4 * g + 2] = v.z; dxv[4 * g + 3] = v.w;
       }
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
+      for (int r = 0; r < RN; r++) {
         const float u = __builtin_fmaf(bits_to_float(D[r]), dsc, cc);  // fl(I*dsc)
         acc[r] = __builtin_fmaf(u, dxv[r], acc[r]);
       }
@@ -698,7 +705,7 @@ __device__ __forceinline__ void q4k_small_body(
       T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p01, mb, T, 0, 0, 0);
       T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2z, mb, T, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[r] = __builtin_fmaf(T[r], -dmin, acc[r]);
+      for (int r = 0; r < RN; r++) acc[r] = __builtin_fmaf(T[r], -dmin, acc[r]);
     }
     if (sb + 1 < sb_end) cur = nxt;
   }
@@ -706,10 +713,10 @@ __device__ __forceinline__ void q4k_small_body(
   const int64_t nn = n0 + l32;
   if constexpr (SK > 1) {
 #pragma unroll
-    for (int g = 0; g < 4; g++)
+    for (int g = 0; g < RN / 4; g++)
       s_red[kk][g][lane] = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
     __syncthreads();
-    for (int g = kk; g < 4; g += SK) {
+    for (int g = kk; g < RN / 4; g += SK) {
       float4 s4 = s_red[0][g][lane];
       for (int w = 1; w < SK; w++) {
         const float4 v = s_red[w][g][lane];
@@ -727,7 +734,7 @@ __device__ __forceinline__ void q4k_small_body(
   } else {
     if (nn < N) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
+      for (int r = 0; r < RN; r++) {
         const int64_t mm = m0 + acc_row(r, h);
         if (mm < M) store_out(y + mm * N + nn, acc[r]);
       }
@@ -752,30 +759,37 @@ static void launch_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, in
                                                                                  M, F, K, h);
 }
 
-template <int SK>
+template <int SK, int RN>
 __global__ __launch_bounds__(64 * SK) void gemm_q4k_small_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
     int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
     float* __restrict__ y) {
-  q4k_small_body<SK, false>(W, qx, dxT, Mp, dsp, M, N, K, y);
+  q4k_small_body<SK, false, RN>(W, qx, dxT, Mp, dsp, M, N, K, y);
 }
 
-template <int SK>
+template <int SK, int RN>
 __global__ __launch_bounds__(64 * SK) void gemm_q5k_small_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT,
     int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M, int64_t N, int64_t K,
     float* __restrict__ y) {
-  q4k_small_body<SK, true>(W, qx, dxT, Mp, dsp, M, N, K, y);
+  q4k_small_body<SK, true, RN>(W, qx, dxT, Mp, dsp, M, N, K, y);
 }
 
 template <int SK, bool Q5 = false>
 static void launch_small(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K,
                          float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((N + 31) / 32), static_cast<unsigned>((M + 31) / 32));
-  if constexpr (Q5)
-    gemm_q5k_small_kernel<SK><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
-  else
-    gemm_q4k_small_kernel<SK><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+  if constexpr (Q5) {
+    if (M <= 8)
+      gemm_q5k_small_kernel<SK, 4><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+    else
+      gemm_q5k_small_kernel<SK, 16><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+  } else {
+    if (M <= 8)
+      gemm_q4k_small_kernel<SK, 4><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+    else
+      gemm_q4k_small_kernel<SK, 16><<<grid, dim3(64 * SK), 0, stream>>>(W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
+  }
 }
 
 template <int TM, int TN, int WM, int WN, int NS, int OCC, int KS>
@@ -832,7 +846,11 @@ inline double round_fill(int64_t blocks, int64_t slots) {
 }
 
 Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
-  constexpr int64_t kCUs = 256, kTargetWaves = 2048;
+  constexpr int64_t kCUs = 256;
+  // about two waves per SIMD; one for decode-sized batches (their waves
+  // apply a quarter of the epilogue: 1024 measured faster than 2048 at
+  // M = 8 on 2560->9728, 9728->2560 and 4096->24576)
+  const int64_t kTargetWaves = M <= 8 ? 1024 : 2048;
   const int64_t nsb = K / 256;
   const int64_t blocks64x128 = ((M + 63) / 64) * ((N + 127) / 128);
   // 128x256 blocks run one per CU and 64x128 blocks two: the larger blocks
@@ -870,10 +888,10 @@ const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256) 
     case Q4Pick::kLds32x64K4:
       return a256 ? "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, true>"
                   : "gemm_q4k_lds_kernel<1, 1, 1, 2, false, 2, 2, 4, false>";
-    case Q4Pick::kSmall1: return "gemm_q4k_small_kernel<1>";
-    case Q4Pick::kSmall2: return "gemm_q4k_small_kernel<2>";
-    case Q4Pick::kSmall4: return "gemm_q4k_small_kernel<4>";
-    case Q4Pick::kSmall8: return "gemm_q4k_small_kernel<8>";
+    case Q4Pick::kSmall1: return M <= 8 ? "gemm_q4k_small_kernel<1, 4>" : "gemm_q4k_small_kernel<1, 16>";
+    case Q4Pick::kSmall2: return M <= 8 ? "gemm_q4k_small_kernel<2, 4>" : "gemm_q4k_small_kernel<2, 16>";
+    case Q4Pick::kSmall4: return M <= 8 ? "gemm_q4k_small_kernel<4, 4>" : "gemm_q4k_small_kernel<4, 16>";
+    case Q4Pick::kSmall8: return M <= 8 ? "gemm_q4k_small_kernel<8, 4>" : "gemm_q4k_small_kernel<8, 16>";
   }
   return "?";
 }
@@ -957,10 +975,10 @@ const char* qg_gemm_q5k_kernel_name(int64_t M, int64_t N, int64_t K) {
     case Q4Pick::kLds64x128: return "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 2, 1>";
     case Q4Pick::kLds64x128K2:
     case Q4Pick::kLds32x64K4: return "gemm_q5k_lds_kernel<1, 1, 1, 2, 2, 2, 3>";
-    case Q4Pick::kSmall1: return "gemm_q5k_small_kernel<1>";
-    case Q4Pick::kSmall2: return "gemm_q5k_small_kernel<2>";
-    case Q4Pick::kSmall4: return "gemm_q5k_small_kernel<4>";
-    case Q4Pick::kSmall8: return "gemm_q5k_small_kernel<8>";
+    case Q4Pick::kSmall1: return M <= 8 ? "gemm_q5k_small_kernel<1, 4>" : "gemm_q5k_small_kernel<1, 16>";
+    case Q4Pick::kSmall2: return M <= 8 ? "gemm_q5k_small_kernel<2, 4>" : "gemm_q5k_small_kernel<2, 16>";
+    case Q4Pick::kSmall4: return M <= 8 ? "gemm_q5k_small_kernel<4, 4>" : "gemm_q5k_small_kernel<4, 16>";
+    case Q4Pick::kSmall8: return M <= 8 ? "gemm_q5k_small_kernel<8, 4>" : "gemm_q5k_small_kernel<8, 16>";
   }
   return "?";
 }

@@ -37,11 +37,11 @@
 // buffers used in turn).
 //
 // Activations.  When a row takes a single step, every lane works on the same
-// 64 activation values in every step, so it keeps their codes, block scales
-// and the -32 correction of the Q6_K codes in registers (XREG).
-// Otherwise the activation rows are staged in LDS once per workgroup (XLDS)
-// or, when they do not fit, read from global memory where they stay L2-resident
-// (XGLB).
+// 64 activation values in every step, so it can keep their codes, block
+// scales and the -32 correction of the Q6_K codes in registers (XREG: one or
+// two activation rows, or short rows).  Otherwise the activation rows are
+// staged in LDS once per workgroup (XLDS) or, when they do not fit, read from
+// global memory where they stay L2-resident (XGLB).
 //
 // Q6_K codes go to v_dot4_i32_i8 as the unsigned q6 in [0, 63] (below 128, so
 // also valid signed bytes) and the offset is applied through the activation
@@ -496,9 +496,18 @@ inline int64_t skinny_lds_bytes(int fmt, int64_t M, int64_t K) {
   return fmt != QG_Q6_K ? M * K + 2 * M * (K / 32) * 4 : M * K + M * (K / 32) * 4;
 }
 
-inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
-  if (K <= 4096) return kXReg;
-  return skinny_lds_bytes(fmt, M, K) <= kSkMaxLds ? kXLds : kXGlb;
+// Rows of K <= 4096: registers for one or two activation rows, for short
+// rows (K <= 2048, several rows per step) and when every wavefront takes many
+// rows (N > 16384), which pays for loading 3-8 rows x 64 values per lane once
+// (the M = 8 LM head: 179 us, against 217 us from LDS); otherwise LDS, where
+// registers would hold those values for a row or two at one or two
+// wavefronts per SIMD (up to 256 VGPRs: Q6_K 4096->2560 at M = 8 11.5 ->
+// 8.6 us, Q4_K 2560->9728 at M = 4 11.3 -> 8.0 us).  Longer rows: LDS, or
+// global memory (L2) when they do not fit.
+inline int skinny_xmode(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (K <= 4096 && (M <= 2 || K <= 2048 || N > 16384)) return kXReg;
+  if (skinny_lds_bytes(fmt, M, K) <= kSkMaxLds) return kXLds;
+  return K <= 4096 ? kXReg : kXGlb;
 }
 
 // Q6_K coalesced loads (CO) where every step starts on a 16-byte boundary
@@ -509,7 +518,7 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t K) {
 inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
   const int64_t nsb = K / 256;
   if (fmt != QG_Q6_K || !(skinny_rows_per_step(K) > 1 || nsb % 8 == 0) || (N * nsb) % 8 != 0 ||
-      skinny_xmode(fmt, M, K) != kXReg)
+      skinny_xmode(fmt, M, N, K) != kXReg)
     return kCoNone;
   return M <= 2 ? kCoDma : kCoReg;
 }
@@ -517,16 +526,29 @@ inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
 template <int FMT, int MR, int R, int CO>
 static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                    float* y, hipStream_t stream) {
-  // at most four workgroups (16 wavefronts) per CU, all resident at once; as
-  // few wavefronts as keep the same number of row groups per wavefront, so
-  // that the last rows are shared out evenly instead of a few wavefronts
-  // taking one more step than the rest
-  constexpr int64_t kWaves = 256 * 16;
+  // The same number of workgroups on every CU, all resident at once, and the
+  // row groups dealt to the wavefronts in turn, so that no wavefront takes
+  // more than one row group more than another: a CU with one workgroup more
+  // than the rest sets the end of the launch (the LM head ran 104 us with 827
+  // workgroups, 3 or 4 per CU, against 86 us with 768).  Three workgroups per
+  // CU for the coalesced Q6_K loads (32 KB of LDS row buffers each); two for
+  // rows of several steps with the activations staged in LDS when that deals
+  // every wavefront the same number of rows (12288->4096 Q6_K: two rows each,
+  // 11.8 -> 11.1 us; 9728->2560 Q4_K, uneven at two, runs 6.4 us there and
+  // 5.9 at four); four otherwise (the LM head 90 -> 86 us, 2560->9728 Q4_K
+  // 6.4 -> 5.7 us; one-step rows measured slower at two); never more than
+  // the LDS holds at once; fewer workgroups when there are fewer row groups
+  // than wavefronts.
+  constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024;
   const int64_t row_groups = (N + R - 1) / R;
-  const int64_t per_wave = (row_groups + kWaves - 1) / kWaves;
-  const int64_t waves = ((row_groups + per_wave - 1) / per_wave + 3) / 4 * 4;
-  const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
-  switch (skinny_xmode(FMT, MR, K)) {
+  const bool xlds = skinny_xmode(FMT, MR, N, K) == kXLds;
+  const int64_t lds = (CO == kCoNone ? 0 : 4 * (CO == kCoDma ? 2 : 1) * 4096) +
+                      (xlds ? skinny_lds_bytes(FMT, MR, K) : 0);
+  int64_t per_cu = CO == kCoDma ? 3 : xlds && K > 4096 && row_groups % (4 * kCUs * 2) == 0 ? 2 : 4;
+  if (lds > 0 && per_cu > kLdsPerCU / lds) per_cu = kLdsPerCU / lds > 0 ? kLdsPerCU / lds : 1;
+  const int64_t wgs = row_groups < 4 * kCUs * per_cu ? (row_groups + 3) / 4 : kCUs * per_cu;
+  const dim3 grid(static_cast<unsigned>(wgs));
+  switch (skinny_xmode(FMT, MR, N, K)) {
     case kXReg:
       skinny_kernel<FMT, MR, R, kXReg, CO><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
                                                                                  N, K, y);
@@ -590,7 +612,7 @@ const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K)
   thread_local char name[64];
   if (M < 1 || M > QG_SKINNY_MAX_M) return "?";
   snprintf(name, sizeof name, "skinny_kernel<%d, %d, %d, %d, %d>", fmt, static_cast<int>(M),
-           qg::skinny_rows_per_step(K), qg::skinny_xmode(fmt, M, K),
+           qg::skinny_rows_per_step(K), qg::skinny_xmode(fmt, M, N, K),
            qg::skinny_coalesced(fmt, M, N, K));
   return name;
 }

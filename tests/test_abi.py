@@ -130,6 +130,16 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 3, 81, 2048, AUTO) == "skinny_kernel<1, 3, 2, 0, 1>"
     assert kn(Q6, 1, 80, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
     assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1>"
+    # from three rows of K > 2048 the activations go to LDS unless each
+    # wavefront takes many rows (N > 16384)
+    assert kn(Q6, 8, 2560, 4096, AUTO) == "skinny_kernel<1, 8, 1, 1, 0>"
+    assert kn(Q4, 4, 9728, 2560, AUTO) == "skinny_kernel<0, 4, 1, 1, 0>"
+    assert kn(Q4, 4, 24576, 4096, AUTO) == "skinny_kernel<0, 4, 1, 0, 0>"
+    # decode-sized batches on the small-grid kernel: four epilogue rows per
+    # lane, about 1024 waves
+    assert kn(Q4, 8, 24576, 4096, AUTO) == "gemm_q4k_small_kernel<2, 4>"
+    assert kn(Q4, 8, 9728, 2560, AUTO) == "gemm_q4k_small_kernel<4, 4>"
+    assert kn(Q4, 9, 9728, 2560, AUTO) == "gemm_q4k_small_kernel<8, 16>"
     # tiled tile choice by grid size
     assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>"
     assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>"
@@ -321,6 +331,14 @@ def test_sclk_probe_rejects_bad_arguments():
     assert lib.qgemm_sclk_probe(A, 0, None) == -1
     assert lib.qgemm_sclk_probe(A, (1 << 24) + 1, None) == -1
     assert lib.qgemm_sclk_probe(A + 4, 10, None) == -5
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = qg.load()
+    assert lib.qgemm_read_probe(A, -16, None) == -1
+    assert lib.qgemm_read_probe(A, 24, None) == -1
+    assert lib.qgemm_read_probe(None, 16, None) == -1
+    assert lib.qgemm_read_probe(A + 8, 16, None) == -5
 
 
 def test_plant_delay_host_side():

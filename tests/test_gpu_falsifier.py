@@ -9,7 +9,8 @@ times; the output must not change.
 
 Also the path log: QGEMM_TRACE=1 names every call's path and kernel on stderr
 (aprender issue #5475, "Ask", item 2), checked in a child process that starts
-with the variable set."""
+with the variable set; and the read probe the decode GEMVs are quoted against
+(qgemm_read_probe), whose time must grow with the bytes it reads."""
 import os
 import subprocess
 import sys
@@ -109,3 +110,17 @@ def test_trace_names_path_and_kernel():
         want = (f"qgemm: gemm fmt={name} M={M} N={N} K={K} path={'skinny' if skinny else 'tiled'} "
                 f"kernel={qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_AUTO)}")
         assert ln == want, (ln, want)
+
+
+def test_read_probe_time_grows_with_bytes():
+    """The read floor reads what it is given: four times the bytes take well over
+    twice the time (a probe whose loads were dropped would not scale)."""
+    stream = torch.cuda.Stream()
+    small = torch.ones(64 << 20, dtype=torch.uint8, device=DEV)
+    large = torch.ones(256 << 20, dtype=torch.uint8, device=DEV)
+    qg.qgemm_read_probe(large, 0, stream)  # zero bytes: no launch, no error
+    t = _rows({"small": lambda: qg.qgemm_read_probe(small, small.numel(), stream),
+               "large": lambda: qg.qgemm_read_probe(large, large.numel(), stream)}, stream, n=10)
+    print(f"read probe: 64 MiB {t['small']:.1f} us, 256 MiB {t['large']:.1f} us")
+    assert t["large"] > 2.0 * t["small"], t
+

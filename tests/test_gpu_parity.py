@@ -278,6 +278,24 @@ def test_skinny_all_row_splits(fmt, K, N):
               f"skinny M={M} N={N} K={K} {qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)}")
 
 
+@pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q5_K], ids=FMT_ID.get)
+@pytest.mark.parametrize("N,K", [(700, 256), (16400, 1024), (300, 1024), (300, 2816)])
+def test_small_grid_decode_rows(fmt, N, K):
+    """The small-grid kernel on decode-sized batches through the tiled path:
+    M <= 8 takes the variant that applies the epilogue to the four accumulator
+    elements per lane that hold output rows (and loads no other activation
+    rows), M = 9 the full one; ragged N, K split over 1, 2, 4 and 8 waves."""
+    W = synth.pack(fmt, synth.normal(640 + K, (N, K), 0.0, 0.02))
+    wmax = max_abs_w(fmt, W, N, K)
+    for M in (1, 3, 4, 5, 8, 9):
+        name = qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_TILED)
+        assert "_small_kernel<" in name and name.endswith(", 4>" if M <= 8 else ", 16>"), name
+        x = synth.to_bf16_bits(synth.normal(641 + M, (M, K)))
+        ref = oracle.gemm(fmt, W, x, N)
+        check(gpu_prefill(W, fmt, x, N, qg.QG_PATH_TILED), ref, bound(x, np.arange(M), wmax),
+              f"small grid M={M} N={N} K={K} {name}")
+
+
 @pytest.mark.parametrize("fmt,M,N,K", [
     (qg.QG_Q4_K, 2049, 15300, 1024),   # 128x256 tiles, ragged M and N
     (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
