@@ -40,8 +40,12 @@
 // 64 activation values in every step, so it can keep their codes, block
 // scales and the -32 correction of the Q6_K codes in registers (XREG: one or
 // two activation rows, or short rows).  Otherwise the activation rows are
-// staged in LDS once per workgroup (XLDS) or, when they do not fit, read from
-// global memory where they stay L2-resident (XGLB).
+// staged in LDS once per workgroup (XLDS) or, when they do not fit, one
+// 4096-value slice of K at a time (XSLICE): the workgroup stages slice t of
+// every activation row, its wavefronts take the slice's step of each of
+// their rows (up to kSlRows rows at a time, their partial sums kept per
+// row), then the next slice.  Every lane accumulates its super-blocks in the
+// same order in all three modes, so they give the same bits.
 //
 // Q6_K codes go to v_dot4_i32_i8 as the unsigned q6 in [0, 63] (below 128, so
 // also valid signed bytes) and the offset is applied through the activation
@@ -78,7 +82,8 @@ typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 
 constexpr int kSkThreads = 256;
 constexpr int kSkMaxLds = 64 * 1024;
-enum { kXReg = 0, kXLds = 1, kXGlb = 2 };
+enum { kXReg = 0, kXLds = 1, kXSlice = 2 };
+constexpr int kSlRows = 2;  // XSLICE: rows a wavefront carries through the slices at a time
 enum { kCoNone = 0, kCoReg = 1, kCoDma = 2 };
 
 // sum over 16 int8 values
@@ -137,9 +142,12 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kSkThreads / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  // activation rows: codes at xs + m * xk, scales at xd / xS + m * xnb, for
+  // super-blocks from xj0 on (XSLICE: the staged slice)
   const int8_t* xs = qx;
   const float* xd = gdx;
   const float* xS = gdS;
+  int64_t xk = K, xnb = nb, xj0 = 0;
   if constexpr (XM == kXLds) {
     int8_t* lq = reinterpret_cast<int8_t*>(smem);
     float* ld = reinterpret_cast<float*>(smem + MR * K);
@@ -161,7 +169,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   // time the whole grid streams one narrow band of the weight matrix
   const int64_t stride = static_cast<int64_t>(gridDim.x) * (kSkThreads / 64) * R;
   const int64_t row_begin = wave * R;
-  if (row_begin >= N) return;
+  // (XSLICE: a wavefront without rows still stages slices and meets the barriers)
+  if (XM != kXSlice && row_begin >= N) return;
 
   const int grp = lane >> 2, s = lane & 3;
   const int half = s >> 1, lh = s & 1;              // Q6_K lane roles
@@ -361,10 +370,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
             x0 = xr[m][0]; x1 = xr[m][1]; x2 = xr[m][2]; x3 = xr[m][3];
             dx0 = xdr[m][0]; dx1 = xdr[m][1]; dS0 = xdr[m][2]; dS1 = xdr[m][3];
           } else {
-            const uint4* xv = reinterpret_cast<const uint4*>(xs + m * K + 256 * jb + 64 * s);
+            const uint4* xv = reinterpret_cast<const uint4*>(xs + m * xk + 256 * (jb - xj0) + 64 * s);
             x0 = xv[0]; x1 = xv[1]; x2 = xv[2]; x3 = xv[3];
-            const float2 dxv = *reinterpret_cast<const float2*>(xd + m * nb + b0);
-            const float2 dSv = *reinterpret_cast<const float2*>(xS + m * nb + b0);
+            const float2 dxv = *reinterpret_cast<const float2*>(xd + m * xnb + b0 - 8 * xj0);
+            const float2 dSv = *reinterpret_cast<const float2*>(xS + m * xnb + b0 - 8 * xj0);
             dx0 = dxv.x; dx1 = dxv.y; dS0 = dSv.x; dS1 = dSv.y;
           }
           int I0 = dot4(lo[0], x0.x, 0);
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
         for (int m = 0; m < MR; m++) {
           float dxs[4];
           if constexpr (XM != kXReg) {
-            const float4 dxv = *reinterpret_cast<const float4*>(xd + m * nb + b0);
+            const float4 dxv = *reinterpret_cast<const float4*>(xd + m * xnb + b0 - 8 * xj0);
             dxs[0] = dxv.x; dxs[1] = dxv.y; dxs[2] = dxv.z; dxs[3] = dxv.w;
           }
           float a = acc[m];
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
               I = xur[m][c];
               dxc = xdr[m][c];
             } else {
-              xv = *reinterpret_cast<const uint4*>(xs + m * K + 256 * jb + 128 * half + 16 * lh + 32 * c);
+              xv = *reinterpret_cast<const uint4*>(xs + m * xk + 256 * (jb - xj0) + 128 * half + 16 * lh + 32 * c);
               I = -32 * sum16(xv);
               dxc = dxs[c];
             }
@@ -456,6 +465,65 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
       }
     }
   };
+
+  if constexpr (XM == kXSlice) {
+    static_assert(R == 1 && CO == kCoNone, "slices of rows of one step or more");
+    int8_t* lq = reinterpret_cast<int8_t*>(smem);
+    float* ld = reinterpret_cast<float*>(smem + MR * 4096);
+    float* lS = ld + MR * 128;
+    xs = lq;
+    xd = ld;
+    xS = lS;
+    xk = 4096;
+    xnb = 128;
+    // this wavefront's rows, and the most rows any wavefront of the grid has
+    // (every wavefront runs that many chunks, so all meet the same barriers)
+    const int64_t my_rows = row_begin < N ? (N - row_begin + stride - 1) / stride : 0;
+    const int64_t grid_rows = (N + stride - 1) / stride;
+    for (int64_t c0 = 0; c0 < grid_rows; c0 += kSlRows) {
+      const int64_t nr = my_rows - c0;  // rows of this chunk (<= 0: none)
+      float accr[kSlRows][MR];
+#pragma unroll
+      for (int r = 0; r < kSlRows; r++)
+#pragma unroll
+        for (int m = 0; m < MR; m++) accr[r][m] = 0.0f;
+      for (int64_t it = 0; it < ipr; it++) {
+        SkRaw ra = {}, rb = {};
+        __syncthreads();  // no wavefront reads the previous slice any more
+        if (nr > 0) load(c0, it, ra);  // in flight while the slice is staged
+        // slice it: super-blocks 16 it .. 16 it + 15 (fewer in the last) of
+        // each activation row: codes [MR][4096], scales (and dS) [MR][128]
+        const int64_t q0 = 4096 * it, qn = K - q0 < 4096 ? K - q0 : 4096;
+        for (int i = threadIdx.x; i < MR * 256; i += kSkThreads) {
+          const int m = i >> 8, c16 = i & 255;
+          if (16 * c16 < qn)
+            reinterpret_cast<uint4*>(lq + m * 4096)[c16] = reinterpret_cast<const uint4*>(qx + m * K + q0)[c16];
+        }
+        for (int i = threadIdx.x; i < MR * 32; i += kSkThreads) {
+          const int m = i >> 5, c4 = i & 31;
+          if (4 * c4 < qn / 32) {
+            reinterpret_cast<float4*>(ld + m * 128)[c4] = reinterpret_cast<const float4*>(gdx + m * nb + q0 / 32)[c4];
+            if (KQ)
+              reinterpret_cast<float4*>(lS + m * 128)[c4] = reinterpret_cast<const float4*>(gdS + m * nb + q0 / 32)[c4];
+          }
+        }
+        __syncthreads();
+        xj0 = 16 * it;
+        // the chunk's rows, the next one's loads issued before this one is computed
+#pragma unroll
+        for (int r = 0; r < kSlRows; r++) {
+          if (r >= nr) break;
+          if (r + 1 < nr && r + 1 < kSlRows) load(c0 + r + 1, it, (r & 1) ? ra : rb);
+#pragma unroll
+          for (int m = 0; m < MR; m++) acc[m] = accr[r][m];
+          compute(c0 + r, it, (r & 1) ? rb : ra);  // stores the row after its last slice
+#pragma unroll
+          for (int m = 0; m < MR; m++) accr[r][m] = acc[m];
+        }
+      }
+    }
+    return;
+  }
 
   // two register buffers in turn: the loads of step t+1 are issued before
   // step t is computed
@@ -507,7 +575,7 @@ inline int64_t skinny_lds_bytes(int fmt, int64_t M, int64_t K) {
 inline int skinny_xmode(int fmt, int64_t M, int64_t N, int64_t K) {
   if (K <= 4096 && (M <= 2 || K <= 2048 || N > 16384)) return kXReg;
   if (skinny_lds_bytes(fmt, M, K) <= kSkMaxLds) return kXLds;
-  return K <= 4096 ? kXReg : kXGlb;
+  return K <= 4096 ? kXReg : kXSlice;
 }
 
 // Q6_K coalesced loads (CO) where every step starts on a 16-byte boundary
@@ -541,14 +609,15 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
   // than wavefronts.
   constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024;
   const int64_t row_groups = (N + R - 1) / R;
-  const bool xlds = skinny_xmode(FMT, MR, N, K) == kXLds;
-  const int64_t lds = (CO == kCoNone ? 0 : 4 * (CO == kCoDma ? 2 : 1) * 4096) +
-                      (xlds ? skinny_lds_bytes(FMT, MR, K) : 0);
+  const int xm = skinny_xmode(FMT, MR, N, K);
+  const bool xlds = xm == kXLds;
+  const int64_t xbytes = xm == kXLds ? skinny_lds_bytes(FMT, MR, K) : xm == kXSlice ? skinny_lds_bytes(FMT, MR, 4096) : 0;
+  const int64_t lds = (CO == kCoNone ? 0 : 4 * (CO == kCoDma ? 2 : 1) * 4096) + xbytes;
   int64_t per_cu = CO == kCoDma ? 3 : xlds && K > 4096 && row_groups % (4 * kCUs * 2) == 0 ? 2 : 4;
   if (lds > 0 && per_cu > kLdsPerCU / lds) per_cu = kLdsPerCU / lds > 0 ? kLdsPerCU / lds : 1;
   const int64_t wgs = row_groups < 4 * kCUs * per_cu ? (row_groups + 3) / 4 : kCUs * per_cu;
   const dim3 grid(static_cast<unsigned>(wgs));
-  switch (skinny_xmode(FMT, MR, N, K)) {
+  switch (xm) {
     case kXReg:
       skinny_kernel<FMT, MR, R, kXReg, CO><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
                                                                                  N, K, y);
@@ -558,9 +627,12 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
           <<<grid, dim3(kSkThreads), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
               W, ws.q, ws.dx, ws.dS, N, K, y);
       break;
-    default:
-      skinny_kernel<FMT, MR, R, kXGlb, CO><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
-                                                                                 N, K, y);
+    default:  // kXSlice: rows of K > 4096, one row per step, no coalesced loads
+      if constexpr (R == 1 && CO == kCoNone)
+        skinny_kernel<FMT, MR, R, kXSlice, CO><<<grid, dim3(kSkThreads), static_cast<size_t>(xbytes), stream>>>(
+            W, ws.q, ws.dx, ws.dS, N, K, y);
+      else
+        return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -278,6 +278,24 @@ def test_skinny_all_row_splits(fmt, K, N):
               f"skinny M={M} N={N} K={K} {qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)}")
 
 
+@pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q6_K], ids=FMT_ID.get)
+def test_skinny_slices_many_rows(fmt):
+    """The skinny path with the activations staged one 4096-value slice of K
+    at a time (rows too long for the whole of them in LDS): 8300 rows, so
+    every wavefront carries several chunks of rows through the slices, and
+    K = 8448, whose last slice holds one super-block."""
+    N, K = 8300, 8448
+    W = synth.pack(fmt, synth.normal(660 + fmt, (N, K), 0.0, 0.02))
+    wmax = max_abs_w(fmt, W, N, K)
+    for M in (7, 8):
+        name = qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)
+        assert name == f"skinny_kernel<{fmt}, {M}, 1, 2, 0>", name
+        x = synth.to_bf16_bits(synth.normal(661 + M, (M, K)))
+        ref = oracle.gemm(fmt, W, x, N)
+        check(gpu_prefill(W, fmt, x, N, qg.QG_PATH_SKINNY), ref, bound(x, np.arange(M), wmax),
+              f"skinny slices M={M} N={N} K={K} {name}")
+
+
 @pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q5_K], ids=FMT_ID.get)
 @pytest.mark.parametrize("N,K", [(700, 256), (16400, 1024), (300, 1024), (300, 2816)])
 def test_small_grid_decode_rows(fmt, N, K):
