@@ -125,20 +125,44 @@ __device__ __forceinline__ void q4k_lds_body(
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
   // Tile order.  Workgroups go to the eight XCDs in turn (consecutive ids,
-  // x fastest), each XCD with its own L2.  For one-tile waves without a K
-  // split (64x128 blocks, two per CU) XCD k takes the k-th eighth of the
-  // tiles, row tiles fastest, so the row tiles that share a weight tile run
-  // on one XCD at the same time (measured at 512x4096->24576: L2 fills 336 ->
-  // 104 MB per launch, the same time; the 2x2-tile blocks measured slower
-  // this way and keep the grid order).
+  // x fastest), each XCD with its own L2, which fills the activation row
+  // tiles and weight column tiles of the blocks it runs.  For one-tile waves
+  // in 64x128 blocks (one or two K-groups) the block grid is cut into eight
+  // sub-grids of gy/a row tiles by gx/(8/a) column tiles, one per XCD, with
+  // the a in 1, 2, 4, 8 whose sub-grid costs its L2 the fewest bytes (an
+  // activation row brings 21 bytes per 16 values of K: codes, scale, dS
+  // pieces; a weight row 9); a = 1 also where no cut is even: XCD k takes
+  // the k-th eighth of the tiles, row tiles fastest.  Measured: 512x4096->
+  // 24576 (a = 1) L2 fills 336 -> 104 MB per launch, the same time;
+  // 512x9728->2560 (a = 2, two K-groups) 82.5 -> 55.9 MB, the same time;
+  // 4096x9728->2560 (a = 4) 323 -> 316 us.  The 2x2-tile blocks (2-7%) and
+  // the 32x64 blocks with four K-groups (4-6%) measured slower cut this way
+  // and keep the grid order.  Only the block's place changes, not its sums.
   uint32_t mt = blockIdx.y, nt = blockIdx.x;
-  if constexpr (TM == 1 && TN == 1 && KS == 1 && !SW && !Q5 && !Q8 && !A256) {
-    const uint32_t G = gridDim.x * gridDim.y;
+  if constexpr (TM == 1 && TN == 1 && KS <= 2 && !SW && !Q5 && !Q8 && !A256) {
+    const uint32_t gx = gridDim.x, gy = gridDim.y, G = gx * gy;
     if (G % 8 == 0) {
-      const uint32_t L = blockIdx.y * gridDim.x + blockIdx.x;
-      const uint32_t Lp = (L % 8) * (G / 8) + L / 8;
-      mt = Lp % gridDim.y;
-      nt = Lp / gridDim.y;
+      const uint32_t L = blockIdx.y * gx + blockIdx.x;
+      const uint32_t x = L % 8, i = L / 8;  // the XCD, and the block's place in its sequence
+      uint32_t a = 1;
+      float best = static_cast<float>(gy) * (BM * 21.0f) + static_cast<float>((gx + 7) / 8) * (BN * 9.0f);
+      for (uint32_t aa = 2; aa <= 8; aa *= 2) {
+        if (gy % aa != 0 || gx % (8 / aa) != 0) continue;
+        const float c = static_cast<float>(gy / aa) * (BM * 21.0f) + static_cast<float>(gx / (8 / aa)) * (BN * 9.0f);
+        if (c < best) {
+          best = c;
+          a = aa;
+        }
+      }
+      if (a == 1) {
+        const uint32_t Lp = x * (G / 8) + i;
+        mt = Lp % gy;
+        nt = Lp / gy;
+      } else {  // sub-grid (x / b, x % b) of sy x sx tiles, row tiles fastest
+        const uint32_t b = 8 / a, sy = gy / a, sx = gx / b;
+        mt = (x / b) * sy + i % sy;
+        nt = (x % b) * sx + i / sy;
+      }
     }
   }
   const int64_t m_cta = static_cast<int64_t>(mt) * BM;

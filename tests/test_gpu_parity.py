@@ -319,6 +319,8 @@ def test_small_grid_decode_rows(fmt, N, K):
     (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
     (qg.QG_Q4_K, 577, 8240, 768),      # 64x128 tiles at 4 waves/SIMD, ragged (650 blocks: grid order)
     (qg.QG_Q4_K, 577, 8100, 768),      # the same with 640 blocks: the XCD-aware tile order
+    (qg.QG_Q4_K, 1000, 2500, 768),     # 64x128 tiles, the grid cut into an 8x5-tile sub-grid per XCD (a = 2), ragged
+    (qg.QG_Q4_K, 500, 2500, 1280),     # the same with two K-groups (a = 2), ragged
     (qg.QG_Q4_K, 330, 2700, 1280),     # 64x128 blocks, K split over 2 groups (2 + 3 super-blocks)
     (qg.QG_Q4_K, 170, 2800, 2816),     # 32x64 blocks, K split over 4 groups (2 + 3 + 3 + 3)
     (qg.QG_Q6_K, 2000, 4000, 512),     # one-stage 128x128 tiles (512 blocks: whole rounds), ragged
