@@ -763,15 +763,47 @@ def main():
         lm_call_us = 1e3 * time_replays(gc, r) / (n * r)
         del ga, gc
         lm_floor_us = read_floor_us([W_lm], lm.w_bytes, n, r)
-        del W_lm
+        # the same head for eight last tokens (a decode batch), and for all 512
+        # rows of a prompt chunk (what computing the last token only avoids)
+        lm8 = synth.CONFIGS[5][1]
+        x8 = to_dev(synth.make_acts(lm8))
+        ws8 = qg.alloc_workspace(lm8.M, lm8.K, dev)
+        y8 = torch.empty((lm8.M, lm8.N), dtype=torch.float32, device=dev)
+        qg.qgemm_quantize_workspace(x8, lm8.M, lm8.K, ws8, stream)
+
+        def lm8_gemm():
+            qg.qgemm_gemm_quantized(W_lm, lm8.fmt, ws8, lm8.M, lm8.N, lm8.K, y8, stream)
+        timed(lm8_gemm, 20)
+        g8 = capture(lm8_gemm, n)
+        time_replays(g8, 1)
+        lm8_us = 1e3 * time_replays(g8, r) / (n * r)
+        del g8, x8, ws8, y8
+        lm512 = synth.CONFIGS[5][2]
+        x512 = to_dev(synth.make_acts(lm512))
+        ws512 = qg.alloc_workspace(lm512.M, lm512.K, dev)
+        y512 = torch.empty((lm512.M, lm512.N), dtype=torch.float32, device=dev)
+        qg.qgemm_quantize_workspace(x512, lm512.M, lm512.K, ws512, stream)
+        def lm512_gemm():
+            qg.qgemm_gemm_quantized(W_lm, lm512.fmt, ws512, lm512.M, lm512.N, lm512.K, y512, stream)
+        timed(lm512_gemm, 2)
+        lm512_us = 1e3 * timed(lm512_gemm, 5) / 5
+        del x512, ws512, y512, W_lm
         lm_gbs = lm.w_bytes / (lm_kernel_us * 1e-6) / 1e9
         lm_out = {"kernel": qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K),
                   "kernel_us": round(lm_kernel_us, 2), "call_us": round(lm_call_us, 2),
                   "gbps": round(lm_gbs, 1), "frac_hbm": round(lm_gbs / PEAK_HBM_GBS, 4),
                   "read_floor_us": round(lm_floor_us, 2),
                   "floor_frac_hbm": round(lm.w_bytes / (lm_floor_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  "m8_kernel": qg.qgemm_kernel_name(lm8.fmt, lm8.M, lm8.N, lm8.K),
+                  "m8_kernel_us": round(lm8_us, 2),
+                  "m8_frac_hbm": round(lm.w_bytes / (lm8_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  "m512_full_rows": qg.qgemm_kernel_name(lm512.fmt, lm512.M, lm512.N, lm512.K),
+                  "m512_full_rows_us": round(lm512_us, 2),
+                  "m512_full_rows_tops": round(2 * lm512.M * lm512.N * lm512.K / (lm512_us * 1e-6) / 1e12, 1),
+                  "last_token_over_full_rows": round(lm512_us / lm_kernel_us, 1),
                   "traffic": traffic_for(qg.qgemm_kernel_name(lm.fmt, 1, lm.N, lm.K))}
-        emit_table("lm_head", dict(lm_out, workload="M=1, K=4096 -> N=152064, Q6_K (skinny path)",
+        emit_table("lm_head", dict(lm_out, workload="M=1 (and 8), K=4096 -> N=152064, Q6_K (skinny path); "
+                                                     "M=512 full rows on the tiled path",
                                    weight_bytes=lm.w_bytes), tables)
 
     # ---------------- optional: plain copy kernel of known size (profiler counter scale)
