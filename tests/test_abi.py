@@ -113,7 +113,8 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 8, 4096, 4096, SKINNY).startswith("skinny_kernel<0, 8,")
     assert kn(Q4, 1, 4096, 4096, TILED).startswith("gemm_q4k_")
     # skinny work split: rows per step R = 16 / (K/256) when that divides, else 1;
-    # activations in registers up to K = 4096, then LDS, then L2
+    # activations in registers (one or two rows of K <= 4096, short rows, many rows per
+    # wavefront), else in LDS whole, else one 4096-value slice of K at a time
     assert kn(Q6, 1, 152064, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
     assert kn(Q4, 2, 100, 1024, AUTO) == "skinny_kernel<0, 2, 4, 0, 0>"
     assert kn(Q4, 1, 100, 2560, AUTO) == "skinny_kernel<0, 1, 1, 0, 0>"

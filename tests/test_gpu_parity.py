@@ -264,7 +264,8 @@ def test_full_size_sampled(g):
 def test_skinny_all_row_splits(fmt, K, N):
     """Skinny path over K values whose super-block counts select every work split
     (several rows per wavefront step, one row per step, several steps per row,
-    partial last step) and over M rows that do and do not fit the LDS staging;
+    partial last step) and over M rows whose activations sit in registers, in LDS
+    whole, or in LDS one slice of K at a time;
     N = 80 makes every Q6_K matrix a whole number of 16-byte chunks, so the
     coalesced loads run wherever the steps are aligned and K <= 4096 (N = 77
     only for K = 2048 and 4096)."""
