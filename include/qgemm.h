@@ -82,8 +82,10 @@ enum {
 };
 
 /* Largest skinny-path batch.  Under QG_PATH_AUTO, Q6_K and Q8_0 problems with
- * M <= QG_SKINNY_MAX_M rows and Q4_K and Q5_K problems with M <= 5 rows go to
- * the bandwidth-bound skinny kernel, larger M to the tiled matrix-core kernels. */
+ * M <= QG_SKINNY_MAX_M rows go to the bandwidth-bound skinny kernel, and Q4_K
+ * and Q5_K problems with M <= m(N, K) rows: m = 8 for N <= 1024; for K <= 1024,
+ * 4 when N <= 4096 and 2 above; otherwise 6 when N <= 12288 and 4 above.  Larger
+ * M go to the tiled matrix-core kernels (the small-grid one for M <= 8). */
 #define QG_SKINNY_MAX_M 8
 
 /* Workspace bytes needed by qgemm_prefill / qgemm_lm_head for M activation rows
@@ -108,8 +110,8 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t K);
  *   workspace : device scratch of at least qgemm_workspace_bytes(M, K) bytes,
  *               256-byte aligned; its contents are scratch on entry and exit.
  *   stream    : hipStream_t (NULL = default stream).
- * Dispatch: the skinny kernel for M <= QG_SKINNY_MAX_M (Q6_K, Q8_0) or M <= 5 (Q4_K, Q5_K),
- * otherwise the tiled kernels. */
+ * Dispatch: the skinny kernel for M <= QG_SKINNY_MAX_M (Q6_K, Q8_0) or M <= m(N, K)
+ * (Q4_K, Q5_K; m as given at QG_SKINNY_MAX_M), otherwise the tiled kernels. */
 int qgemm_prefill(const void *q_weights, int fmt, const void *x, int x_dtype, int64_t M,
                   int64_t N, int64_t K, float *y, void *workspace, size_t workspace_bytes,
                   void *stream);

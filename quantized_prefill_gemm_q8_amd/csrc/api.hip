@@ -106,12 +106,24 @@ hipError_t launch_tiled(const uint8_t* W, int fmt, const QgWorkspace& ws, int64_
   return qg_launch_gemm_q6k(W, ws, M, N, K, y, s);
 }
 
-// QG_PATH_AUTO: the skinny kernel for M <= 8 Q6_K and Q8_0 rows and M <= 5
-// Q4_K and Q5_K rows (measured over the workloads' projection shapes: from 6
-// Q4_K / Q5_K rows on the tiled kernels are as fast or faster, while the
-// Q6_K and Q8_0 skinny kernels stay ahead up to 8 rows).
-bool auto_skinny(int fmt, int64_t M) {
-  return M <= (fmt == QG_Q6_K || fmt == QG_Q8_0 ? QG_SKINNY_MAX_M : 5);
+// QG_PATH_AUTO: the skinny kernel for Q6_K and Q8_0 problems of M <= 8 rows
+// (ahead of their tiled kernels up to 8 rows).  For Q4_K and Q5_K the
+// small-grid kernel takes over from a row count that depends on the shape,
+// measured on cold weights (each call reading them from HBM) over the decode
+// projections 1024->4096, 1024->7168, 3584->1024, 2560->9728, 9728->2560 and
+// 4096->24576: the small-grid kernel runs one wavefront per 32 weight rows
+// and K-group, so few weight rows leave it short of wavefronts (N <= 1024:
+// skinny up to 8 rows); the skinny kernel's per-row work grows with M, most
+// at K <= 1024 where a wavefront decodes four weight rows per step (skinny up
+// to 4 rows for N <= 4096, 2 above); otherwise up to 6 rows for N <= 12288
+// and 4 above.
+bool auto_skinny(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt == QG_Q6_K || fmt == QG_Q8_0) return M <= QG_SKINNY_MAX_M;
+  int64_t mmax;
+  if (N <= 1024) mmax = 8;
+  else if (K <= 1024) mmax = N <= 4096 ? 4 : 2;
+  else mmax = N <= 12288 ? 6 : 4;
+  return M <= mmax;
 }
 
 }  // namespace
@@ -174,7 +186,7 @@ int qgemm_gemm_quantized(const void* q_weights, int fmt, const void* workspace,
   rc = check_device();
   if (rc) return rc;
   const QgWorkspace ws = carve(const_cast<void*>(workspace), L);
-  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
+  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M, N, K));
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (trace_on())
@@ -223,7 +235,7 @@ const char* qgemm_kernel_name(int fmt, int64_t M, int64_t N, int64_t K, int path
   if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
   if (path != QG_PATH_AUTO && path != QG_PATH_TILED && path != QG_PATH_SKINNY) return NULL;
   if (path == QG_PATH_SKINNY && M > QG_SKINNY_MAX_M) return NULL;
-  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M));
+  const bool skinny = path == QG_PATH_SKINNY || (path == QG_PATH_AUTO && auto_skinny(fmt, M, N, K));
   if (skinny) return qg_gemm_skinny_kernel_name(fmt, M, N, K);
   if (fmt == QG_Q5_K) return qg_gemm_q5k_kernel_name(M, N, K);
   if (fmt == QG_Q8_0) return qg_gemm_q80_kernel_name(M, N, K);
@@ -316,11 +328,11 @@ int qgemm_gemm_quantized_a256(const void* q_weights, int fmt, const void* worksp
   const uint8_t* W = static_cast<const uint8_t*>(q_weights);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (trace_on())
-    trace("gemm_a256", fmt, M, N, K, auto_skinny(fmt, M) ? "skinny" : "tiled",
+    trace("gemm_a256", fmt, M, N, K, auto_skinny(fmt, M, N, K) ? "skinny" : "tiled",
         qgemm_kernel_name_a256(fmt, M, N, K));
   // the skinny and small-grid kernels read the per-block scales, which the
   // per-256 workspace holds too
-  if (auto_skinny(fmt, M)) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
+  if (auto_skinny(fmt, M, N, K)) return launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, N, K, y, s));
   return launch_status(qg_launch_gemm_q4k(W, ws, M, N, K, y, s, true));
 }
 
@@ -345,7 +357,7 @@ int qgemm_prefill_a256(const void* q_weights, int fmt, const void* x, int x_dtyp
 
 const char* qgemm_kernel_name_a256(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt != QG_Q4_K || M < 1 || N < 1 || K < 256 || K % 256 != 0) return NULL;
-  if (auto_skinny(fmt, M)) return qg_gemm_skinny_kernel_name(fmt, M, N, K);
+  if (auto_skinny(fmt, M, N, K)) return qg_gemm_skinny_kernel_name(fmt, M, N, K);
   return qg_gemm_q4k_kernel_name(M, N, K, true);
 }
 
@@ -463,7 +475,7 @@ int qgemm_rmsnorm_quantize_act(const void* x, int x_dtype, const float* g, float
 // into the workspace after the quantised activations and the SwiGLU kernel
 // reads it from there.
 static bool swiglu_fused(int fmt, int64_t M, int64_t F, int64_t K) {
-  return fmt != QG_Q6_K && !auto_skinny(fmt, M) && qg_swiglu_fusable(fmt, M, F, K);
+  return fmt != QG_Q6_K && !auto_skinny(fmt, M, 2 * F, K) && qg_swiglu_fusable(fmt, M, F, K);
 }
 
 static bool swiglu_layout(int fmt, int64_t M, int64_t F, int64_t K, Layout* L, int64_t* total) {
@@ -504,7 +516,7 @@ int qgemm_gemm_quantized_swiglu(const void* q_weights, int fmt, const void* work
         qgemm_kernel_name_swiglu(fmt, M, F, K));
   if (swiglu_fused(fmt, M, F, K)) return launch_status(qg_launch_gemm_swiglu(W, fmt, ws, M, F, K, h, s));
   float* y = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) + L.total);
-  if (auto_skinny(fmt, M)) rc = launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, 2 * F, K, y, s));
+  if (auto_skinny(fmt, M, 2 * F, K)) rc = launch_status(qg_launch_gemm_skinny(W, fmt, ws, M, 2 * F, K, y, s));
   else rc = launch_status(launch_tiled(W, fmt, ws, M, 2 * F, K, y, s));
   if (rc) return rc;
   return launch_status(qg_launch_swiglu(y, M, F, h, s));

@@ -104,9 +104,20 @@ def test_kernel_name_dispatch_rule():
     """Host dispatch (no GPU): which kernel each path and shape selects."""
     kn = qg.qgemm_kernel_name
     Q4, Q6, AUTO, TILED, SKINNY = qg.QG_Q4_K, qg.QG_Q6_K, qg.QG_PATH_AUTO, qg.QG_PATH_TILED, qg.QG_PATH_SKINNY
-    # skinny below the measured crossover: Q4_K and Q5_K up to 5 rows, Q6_K and Q8_0 up to 8
-    assert kn(Q4, 5, 4096, 4096, AUTO).startswith("skinny_kernel<0, 5,")
-    assert kn(Q4, 6, 4096, 4096, AUTO).startswith("gemm_q4k_")
+    # skinny below the measured crossover: Q6_K and Q8_0 up to 8 rows; Q4_K and
+    # Q5_K up to a row count set by the shape (8 for N <= 1024; for K <= 1024, 4
+    # for N <= 4096 and 2 above; otherwise 6 for N <= 12288 and 4 above)
+    assert kn(Q4, 6, 4096, 4096, AUTO).startswith("skinny_kernel<0, 6,")
+    assert kn(Q4, 7, 4096, 4096, AUTO).startswith("gemm_q4k_small_kernel<")
+    assert kn(Q4, 8, 1024, 3584, AUTO).startswith("skinny_kernel<0, 8,")
+    assert kn(Q4, 4, 4096, 1024, AUTO).startswith("skinny_kernel<0, 4,")
+    assert kn(Q4, 5, 4096, 1024, AUTO).startswith("gemm_q4k_small_kernel<")
+    assert kn(qg.QG_Q5_K, 2, 7168, 1024, AUTO).startswith("skinny_kernel<2, 2,")
+    assert kn(qg.QG_Q5_K, 3, 7168, 1024, AUTO).startswith("gemm_q5k_small_kernel<")
+    assert kn(Q4, 6, 2560, 9728, AUTO).startswith("skinny_kernel<0, 6,")
+    assert kn(Q4, 7, 2560, 9728, AUTO).startswith("gemm_q4k_small_kernel<")
+    assert kn(Q4, 4, 24576, 4096, AUTO).startswith("skinny_kernel<0, 4,")
+    assert kn(Q4, 5, 24576, 4096, AUTO).startswith("gemm_q4k_small_kernel<")
     assert kn(qg.QG_Q8_0, 8, 4096, 4096, AUTO).startswith("skinny_kernel<3, 8,")
     assert kn(Q6, 8, 152064, 4096, AUTO).startswith("skinny_kernel<1, 8,")
     assert kn(Q6, 9, 152064, 4096, AUTO).startswith("gemm_q6k_")
@@ -292,8 +303,9 @@ def test_q5k_host_side():
     assert kn(2, 64, 1024, 1024).startswith("gemm_q5k_small_kernel<")
     assert kn(2, 1, 24576, 4096) == "skinny_kernel<2, 1, 1, 0, 0>"
     assert kn(2, 4, 4096, 1024).startswith("skinny_kernel<2, 4,")
-    assert kn(2, 5, 4096, 1024).startswith("skinny_kernel<2, 5,")
-    assert kn(2, 6, 4096, 1024).startswith("gemm_q5k_small_kernel<")
+    assert kn(2, 5, 4096, 1024).startswith("gemm_q5k_small_kernel<")
+    assert kn(2, 6, 2560, 9728).startswith("skinny_kernel<2, 6,")
+    assert kn(2, 7, 2560, 9728).startswith("gemm_q5k_small_kernel<")
     assert kn(2, 8, 4096, 1024, qg.QG_PATH_SKINNY).startswith("skinny_kernel<2, 8,")
     assert qg.qgemm_kernel_name_swiglu(2, 512, 3584, 1024) == "gemm_q5k_swiglu_kernel<1, 1, 2, 4, 2, 2, 1>"
     assert qg.qgemm_swiglu_workspace_bytes(2, 512, 3584, 1024) == qg.qgemm_workspace_bytes(512, 1024)

@@ -315,6 +315,32 @@ def test_small_grid_decode_rows(fmt, N, K):
               f"small grid M={M} N={N} K={K} {name}")
 
 
+DECODE_SHAPES = [(1024, 4096), (1024, 7168), (3584, 1024), (2560, 9728), (9728, 2560), (4096, 24576)]
+
+
+@pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q5_K], ids=FMT_ID.get)
+@pytest.mark.parametrize("K,N", DECODE_SHAPES, ids=[f"{k}to{n}" for k, n in DECODE_SHAPES])
+def test_decode_shapes_auto_path(fmt, K, N):
+    """The automatic path at the decode projections' real shapes, M = 1..8: the
+    skinny kernel up to the shape's row count, the small-grid kernel above it
+    (each side of the switch in every shape), against the oracle on sampled
+    weight rows that include the first and last ones."""
+    W = synth.pack(fmt, synth.normal(680 + K + N, (N, K), 0.0, 0.02))
+    wmax = max_abs_w(fmt, W, N, K)
+    x8 = synth.to_bf16_bits(synth.normal(681 + K, (8, K)))
+    rng = np.random.default_rng(K + N)
+    cols = np.unique(np.concatenate([[0, N - 1], np.arange(N - 8, N), rng.integers(0, N, 40)]))
+    kinds = set()
+    for M in range(1, 9):
+        x = np.ascontiguousarray(x8[:M])
+        name = qg.qgemm_kernel_name(fmt, M, N, K)
+        kinds.add(name.split("<")[0])
+        y = gpu_prefill(W, fmt, x, N)
+        ref = oracle.gemm(fmt, W, x, N, cols=cols)
+        check(y[:, cols], ref, bound(x, np.arange(M), wmax), f"decode M={M} N={N} K={K} {name}")
+    assert "skinny_kernel" in kinds, kinds
+
+
 @pytest.mark.parametrize("fmt,M,N,K", [
     (qg.QG_Q4_K, 2049, 15300, 1024),   # 128x256 tiles, ragged M and N
     (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
