@@ -318,13 +318,18 @@ def test_small_grid_decode_rows(fmt, N, K):
 DECODE_SHAPES = [(1024, 4096), (1024, 7168), (3584, 1024), (2560, 9728), (9728, 2560), (4096, 24576)]
 
 
-@pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q5_K], ids=FMT_ID.get)
-@pytest.mark.parametrize("K,N", DECODE_SHAPES, ids=[f"{k}to{n}" for k, n in DECODE_SHAPES])
+DECODE_CASES = ([(f, k, n) for f in (qg.QG_Q4_K, qg.QG_Q5_K, qg.QG_Q8_0) for k, n in DECODE_SHAPES]
+                + [(qg.QG_Q6_K, 4096, 2560), (qg.QG_Q6_K, 12288, 4096)])
+
+
+@pytest.mark.parametrize("fmt,K,N", DECODE_CASES, ids=[f"{FMT_ID[f]}-{k}to{n}" for f, k, n in DECODE_CASES])
 def test_decode_shapes_auto_path(fmt, K, N):
-    """The automatic path at the decode projections' real shapes, M = 1..8: the
-    skinny kernel up to the shape's row count, the small-grid kernel above it
-    (each side of the switch in every shape), against the oracle on sampled
-    weight rows that include the first and last ones."""
+    """The automatic path at the decode projections' real shapes, M = 1..8,
+    against the oracle on sampled weight rows that include the first and last
+    ones.  Q4_K and Q5_K: the skinny kernel up to the shape's row count, the
+    small-grid kernel above it (each side of the switch in every shape); Q6_K
+    and Q8_0: the skinny kernel throughout, its activations in registers, whole
+    in LDS or one K slice at a time as M and K select."""
     W = synth.pack(fmt, synth.normal(680 + K + N, (N, K), 0.0, 0.02))
     wmax = max_abs_w(fmt, W, N, K)
     x8 = synth.to_bf16_bits(synth.normal(681 + K, (8, K)))
