@@ -97,12 +97,17 @@ __device__ __forceinline__ v8bf mins_bf16(uint32_t m_lo, uint32_t m_hi) {
 // Q8: Q8_0 blocks (eight 34-byte blocks of an fp16 d and 32 int8 codes per
 // 256 values): the codes go to the matrix core as they are, dsc = d per
 // 32-value block, no min term (no dS pieces staged).
+// EXT: the stage ring lives in the caller's LDS buffer ext_lds (a kernel that
+// runs two block shapes), the block's place is (mt_in, nt_in) and output rows
+// are ldy floats apart; otherwise the body declares its ring, takes its place
+// from the grid and writes rows N floats apart.
 template <int TM, int TN, int WM, int WN, bool DPP, int NS, int KS, bool A256, bool SW, bool Q5 = false,
-          bool Q8 = false>
+          bool Q8 = false, bool EXT = false>
 __device__ __forceinline__ void q4k_lds_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
     const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ y, uint16_t* __restrict__ hout, int64_t F) {
+    int64_t N, int64_t K, float* __restrict__ y, uint16_t* __restrict__ hout, int64_t F,
+    uint8_t* ext_lds = nullptr, uint32_t mt_in = 0, uint32_t nt_in = 0, int64_t ldy = 0) {
   static_assert(!SW || (WN % 2 == 0 && !A256 && !DPP), "SwiGLU pairs waves wn and wn + WN/2");
   static_assert(!(Q5 || Q8) || (!A256 && !DPP), "Q5_K and Q8_0 run the per-32 method");
   constexpr int NW = WM * WN;  // waves per group
@@ -117,7 +122,13 @@ __device__ __forceinline__ void q4k_lds_body(
   constexpr int STAGE = A_BYTES + W_BYTES + X_BYTES + P_BYTES;
   static_assert(KS * NS * STAGE <= 160 * 1024, "LDS budget");
   static_assert(KS == 1 || (KS - 1) * NW * TM * TN * 4096 <= KS * NS * STAGE, "reduction space");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KS * NS * STAGE];
+  uint8_t* lds;
+  if constexpr (EXT) {
+    lds = ext_lds;
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_ring[KS * NS * STAGE];
+    lds = lds_ring;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -138,8 +149,8 @@ __device__ __forceinline__ void q4k_lds_body(
   // 4096x9728->2560 (a = 4) 323 -> 316 us.  The 2x2-tile blocks (2-7%) and
   // the 32x64 blocks with four K-groups (4-6%) measured slower cut this way
   // and keep the grid order.  Only the block's place changes, not its sums.
-  uint32_t mt = blockIdx.y, nt = blockIdx.x;
-  if constexpr (TM == 1 && TN == 1 && KS <= 2 && !SW && !Q5 && !Q8 && !A256) {
+  uint32_t mt = EXT ? mt_in : blockIdx.y, nt = EXT ? nt_in : blockIdx.x;
+  if constexpr (TM == 1 && TN == 1 && KS <= 2 && !SW && !Q5 && !Q8 && !A256 && !EXT) {
     const uint32_t gx = gridDim.x, gy = gridDim.y, G = gx * gy;
     if (G % 8 == 0) {
       const uint32_t L = blockIdx.y * gx + blockIdx.x;
@@ -570,8 +581,9 @@ __device__ __forceinline__ void q4k_lds_body(
       for (int r = 0; r < 16; r++) {
         const int64_t m = m_cta + ml0 + 32 * i + acc_row(r, h);
         if (m < M) {
-          if constexpr (TM == 1 && TN == 1 && KS == 1 && !Q5 && !Q8 && !A256) store_out_dev(y + m * N + n, acc[i][j][r]);
-          else store_out(y + m * N + n, acc[i][j][r]);
+          float* const p = y + m * (EXT ? ldy : N) + n;
+          if constexpr (TM == 1 && TN == 1 && KS == 1 && !Q5 && !Q8 && !A256) store_out_dev(p, acc[i][j][r]);
+          else store_out(p, acc[i][j][r]);
         }
       }
   }
@@ -854,9 +866,66 @@ static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64
       W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y);
 }
 
+// Mixed block shapes for grids whose 128x256 blocks would leave the last round
+// partly empty (512x4096->24576: 384 of them on 256 CUs): columns [0, N1) in
+// 128x256 blocks of 2x2-tile waves, exactly one round of them, and columns
+// [N1, N) in 64x256 blocks of 1x2-tile waves (half the work each), one more
+// round at most; one workgroup of 8 waves per CU in either shape, so the
+// second round starts as the first ends.  Every output element still adds its
+// 32-value blocks in K order, so the result equals any other one-K-group
+// tile shape's bit for bit.  Measured at 512x4096->24576: the two shapes as
+// separate launches 141 us against 159 for the one-tile kernel.
+constexpr int q4k_ring_bytes(int BM, int BN) {  // two stages of the body's A, W, DX, DSP regions
+  return 2 * 1024 * ((BM * 16 + 63) / 64 + (BN * (kQ4Bytes / 16) + 63) / 64 + (BM * 2 + 63) / 64 +
+                     (BM * 3 + 63) / 64);
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gemm_q4k_mix_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dx,
+    const float* __restrict__ dxT, int64_t Mp, const uint16_t* __restrict__ dsp, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ y, int64_t N1) {
+  static_assert(q4k_ring_bytes(128, 256) >= q4k_ring_bytes(64, 256), "one ring serves both shapes");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[q4k_ring_bytes(128, 256)];
+  const uint32_t gxb = static_cast<uint32_t>(N1 / 256), gyb = static_cast<uint32_t>((M + 127) / 128);
+  const uint32_t L = blockIdx.x;
+  if (L < gxb * gyb) {
+    q4k_lds_body<2, 2, 2, 4, false, 2, 1, false, false, false, false, true>(
+        W, qx, dx, dxT, Mp, dsp, M, N1, K, y, nullptr, 0, lds, L / gxb, L % gxb, N);
+  } else {
+    const uint32_t L2 = L - gxb * gyb, gxs = static_cast<uint32_t>((N - N1 + 255) / 256);
+    q4k_lds_body<1, 2, 2, 4, false, 2, 1, false, false, false, false, true>(
+        W + N1 * (K / 256) * kQ4Bytes, qx, dx, dxT, Mp, dsp, M, N - N1, K, y + N1, nullptr, 0, lds, L2 / gxs,
+        L2 % gxs, N);
+  }
+}
+
+static void launch_mix(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K, float* y,
+                       int64_t N1, hipStream_t stream) {
+  const int64_t blocks = (N1 / 256) * ((M + 127) / 128) + ((N - N1 + 255) / 256) * ((M + 63) / 64);
+  gemm_q4k_mix_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream>>>(
+      W, ws.q, ws.dx, ws.dxT, ws.Mp, ws.dsp, M, N, K, y, N1);
+}
+
 }  // namespace qg
 
 namespace {
+
+// The mixed-block launch (gemm_q4k_mix_kernel) where the 128x256 blocks of a
+// problem would fill one round and part of another: N1 = the columns of
+// exactly one round of them (256 / row tiles column tiles, a whole number),
+// and the 64x256 blocks of the remaining columns at most one more round and at
+// least half of one.  Returns N1, or 0 for the other kernels.
+int64_t q4k_mix_columns(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kCUs = 256;
+  if (M < 256 || K < 512) return 0;
+  const int64_t gyb = (M + 127) / 128, gx = (N + 255) / 256;
+  if (kCUs % gyb != 0) return 0;
+  const int64_t c1 = kCUs / gyb;
+  if (c1 >= gx) return 0;
+  const int64_t small = (gx - c1) * ((M + 63) / 64);
+  if (small > kCUs || 2 * small < kCUs) return 0;
+  return c1 * 256;
+}
 
 // Kernel choice for a Q4_K problem (measured on the workloads' shapes):
 // long prompts (M >= 2048) with enough 128x256 tiles to cover every CU, and
@@ -907,6 +976,7 @@ Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
 
 // Kernel names as a profiler lists them (A256 is the last template argument).
 const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256) {
+  if (!a256 && q4k_mix_columns(M, N, K) > 0) return "gemm_q4k_mix_kernel";
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256:
       return a256 ? "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, true>"
@@ -936,6 +1006,10 @@ const char* qg_gemm_q4k_kernel_name(int64_t M, int64_t N, int64_t K, bool a256) 
 // result with its per-block epilogue.
 hipError_t qg_launch_gemm_q4k(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N,
                               int64_t K, float* y, hipStream_t stream, bool a256) {
+  if (const int64_t N1 = a256 ? 0 : q4k_mix_columns(M, N, K); N1 > 0) {
+    qg::launch_mix(W, ws, M, N, K, y, N1, stream);
+    return hipGetLastError();
+  }
   switch (pick_q4k(M, N, K)) {
     case Q4Pick::kLds128x256:
       if (a256) qg::launch_lds<1, 1, 2, 4, false, 2, 4, 1, true>(W, ws, M, N, K, y, stream);

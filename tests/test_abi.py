@@ -154,13 +154,23 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q4, 9, 9728, 2560, AUTO) == "gemm_q4k_small_kernel<8, 16>"
     # tiled tile choice by grid size
     assert kn(Q4, 8192, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>"
-    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>"
+    # one round of 128x256 blocks plus 64x256 blocks over the other columns
+    # (512 rows: 256 + 256 blocks), where 128x256 blocks alone would leave a
+    # second round half empty
+    assert kn(Q4, 512, 24576, 4096, AUTO) == "gemm_q4k_mix_kernel"
+    assert kn(Q4, 500, 20500, 768, AUTO) == "gemm_q4k_mix_kernel"
+    assert kn(Q4, 256, 45000, 512, AUTO) == "gemm_q4k_mix_kernel"
+    assert kn(Q4, 300, 20500, 768, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>"  # 3 row tiles
+    assert kn(Q4, 512, 18000, 4096, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>"  # short 2nd round
+    assert qg.qgemm_kernel_name_a256(0, 512, 24576, 4096) != "gemm_q4k_mix_kernel"
     # long prompts: 128x256 blocks unless their last round is much emptier than 64x128's
     big, mid = ("gemm_q4k_lds_kernel<2, 2, 2, 4, false, 2, 2, 1, false>",
                 "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>")
     assert kn(Q4, 2048, 24576, 4096, AUTO) == big and kn(Q4, 8192, 24576, 4096, AUTO) == big
     assert kn(Q4, 4096, 9728, 2560, AUTO) == big
-    assert kn(Q4, 4096, 2560, 9728, AUTO) == mid      # 320 large blocks on 256 CUs
+    # 320 large blocks on 256 CUs: one round of them, the other columns in 128 64x256 blocks
+    assert kn(Q4, 4096, 2560, 9728, AUTO) == "gemm_q4k_mix_kernel"
+    assert kn(Q4, 3000, 2560, 9728, AUTO) == mid      # 24 row tiles: no whole round of large blocks
     assert kn(Q4, 64, 1024, 1024, AUTO).startswith("gemm_q4k_small_kernel<")
     # few output blocks: K split inside the workgroup
     assert kn(Q4, 512, 2560, 9728, AUTO) == "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 2, false>"

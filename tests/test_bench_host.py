@@ -94,7 +94,7 @@ def _receipt(**over):
                       "M": 512, "K": 4096, "N": 24576, "fmt": "Q4_K", "projections": [[4096, 24576]]},
            "prefill_tok_s": 3.0e6, "quant_us": 5.1, "gemm_us": 160.2,
            "step_ms_p10_p50_p90": [0.16, 0.17, 0.18], "wall_s_timed": 0.02,
-           "roofline": {"bound": "mfma", "kernel": "gemm_q4k_lds_kernel<1, 1, 2, 4, false, 2, 4, 1, false>",
+           "roofline": {"bound": "mfma", "kernel": "gemm_q4k_mix_kernel",
                         "achieved": 643.1, "peak": 5000.0, "unit": "TOPS", "frac": 0.1286,
                         "traffic": 123456789, "avg_launch_us": 160.2, "ops_per_launch": 103079215104},
            "cpu_baseline": {"value": 0.0958, "unit": "TOPS", "cores": 16, "nproc": 16,

@@ -346,6 +346,29 @@ def test_decode_shapes_auto_path(fmt, K, N):
     assert "skinny_kernel" in kinds, kinds
 
 
+@pytest.mark.parametrize("M,N,K", [(500, 20500, 768), (256, 45000, 512)])
+def test_mixed_blocks(M, N, K):
+    """The mixed-block launch (one round of 128x256 blocks, then 64x256 blocks
+    over the remaining columns), ragged in M and in the last column tile: against
+    the oracle on sampled rows x columns on both sides of the column split, and
+    bit for bit against the one-tile kernel, which a shorter batch of the same
+    rows runs (every output element adds its blocks in K order either way)."""
+    assert qg.qgemm_kernel_name(qg.QG_Q4_K, M, N, K) == "gemm_q4k_mix_kernel"
+    W = synth.pack(qg.QG_Q4_K, synth.normal(690 + K, (N, K), 0.0, 0.02))
+    x = synth.to_bf16_bits(synth.normal(691 + M, (M, K)))
+    y = gpu_prefill(W, qg.QG_Q4_K, x, N)
+    n1 = 256 * (256 // ((M + 127) // 128))  # the column split
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(M - 5, M), rng.integers(0, M, 10)]))
+    cols = np.unique(np.concatenate([[0, n1 - 1, n1, N - 1], np.arange(N - 6, N), rng.integers(0, N, 40)]))
+    ref = oracle.gemm(qg.QG_Q4_K, W, x, N, rows=rows, cols=cols)
+    check(y[np.ix_(rows, cols)], ref, bound(x, rows, max_abs_w(qg.QG_Q4_K, W, N, K)), f"mixed {M}x{N}x{K}")
+    mm = 192 if M > 256 else 100
+    short = qg.qgemm_kernel_name(qg.QG_Q4_K, mm, N, K)
+    assert short != "gemm_q4k_mix_kernel", short
+    assert np.array_equal(y[:mm], gpu_prefill(W, qg.QG_Q4_K, np.ascontiguousarray(x[:mm]), N)), short
+
+
 @pytest.mark.parametrize("fmt,M,N,K", [
     (qg.QG_Q4_K, 2049, 15300, 1024),   # 128x256 tiles, ragged M and N
     (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
