@@ -371,7 +371,7 @@ def test_mixed_blocks(M, N, K):
 
 @pytest.mark.parametrize("fmt,M,N,K", [
     (qg.QG_Q4_K, 2049, 15300, 1024),   # 128x256 tiles, ragged M and N
-    (qg.QG_Q4_K, 4096, 2560, 1024),    # 64x128 tiles: 128x256 would leave a 3/4-empty round
+    (qg.QG_Q4_K, 4096, 2560, 1024),    # one round of 128x256 blocks, then 128 64x256 blocks (mixed launch)
     (qg.QG_Q4_K, 577, 8240, 768),      # 64x128 tiles at 4 waves/SIMD, ragged (650 blocks: grid order)
     (qg.QG_Q4_K, 577, 8100, 768),      # the same with 640 blocks: the XCD-aware tile order
     (qg.QG_Q4_K, 1000, 2500, 768),     # 64x128 tiles, the grid cut into an 8x5-tile sub-grid per XCD (a = 2), ragged
