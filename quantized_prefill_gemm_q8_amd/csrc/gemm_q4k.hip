@@ -899,6 +899,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 }
 
+// The same two block shapes with the SwiGLU epilogue (W holds the 2F gate and
+// up rows; h [M][F] bfloat16): a block covers 128 output columns in either
+// shape, gate and up rows of each, so both take their place in the full grid
+// of F/128 column tiles (the large blocks the first F1/128 of them).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gemm_q4k_swiglu_mix_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ dxT, int64_t Mp,
+    const uint16_t* __restrict__ dsp, int64_t M, int64_t F, int64_t K, uint16_t* __restrict__ h, int64_t F1) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[q4k_ring_bytes(128, 256)];
+  const uint32_t gxb = static_cast<uint32_t>(F1 / 128), gyb = static_cast<uint32_t>((M + 127) / 128);
+  const uint32_t L = blockIdx.x;
+  if (L < gxb * gyb) {
+    q4k_lds_body<2, 2, 2, 4, false, 2, 1, false, true, false, false, true>(
+        W, qx, nullptr, dxT, Mp, dsp, M, 2 * F, K, nullptr, h, F, lds, L / gxb, L % gxb, 0);
+  } else {
+    const uint32_t L2 = L - gxb * gyb, gxs = static_cast<uint32_t>((F - F1 + 127) / 128);
+    q4k_lds_body<1, 2, 2, 4, false, 2, 1, false, true, false, false, true>(
+        W, qx, nullptr, dxT, Mp, dsp, M, 2 * F, K, nullptr, h, F, lds, L2 / gxs, gxb + L2 % gxs, 0);
+  }
+}
+
+static void launch_swiglu_mix(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F, int64_t K,
+                              uint16_t* h, int64_t F1, hipStream_t stream) {
+  const int64_t blocks = (F1 / 128) * ((M + 127) / 128) + ((F - F1 + 127) / 128) * ((M + 63) / 64);
+  gemm_q4k_swiglu_mix_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream>>>(
+      W, ws.q, ws.dxT, ws.Mp, ws.dsp, M, F, K, h, F1);
+}
+
 static void launch_mix(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t N, int64_t K, float* y,
                        int64_t N1, hipStream_t stream) {
   const int64_t blocks = (N1 / 256) * ((M + 127) / 128) + ((N - N1 + 255) / 256) * ((M + 63) / 64);
@@ -1047,6 +1074,7 @@ bool qg_q4k_swiglu_fusable(int64_t M, int64_t F, int64_t K) {
 
 const char* qg_gemm_q4k_swiglu_kernel_name(int64_t M, int64_t F, int64_t K) {
   if (!qg_q4k_swiglu_fusable(M, F, K)) return nullptr;
+  if (q4k_mix_columns(M, 2 * F, K) > 0) return "gemm_q4k_swiglu_mix_kernel";
   switch (pick_q4k(M, 2 * F, K)) {
     case Q4Pick::kLds128x256: return "gemm_q4k_swiglu_kernel<2, 2, 2, 4, 2, 2, 1>";
     case Q4Pick::kLds64x128: return "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>";
@@ -1059,6 +1087,10 @@ const char* qg_gemm_q4k_swiglu_kernel_name(int64_t M, int64_t F, int64_t K) {
 hipError_t qg_launch_gemm_q4k_swiglu(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64_t F,
                                      int64_t K, uint16_t* h, hipStream_t stream) {
   if (!qg_q4k_swiglu_fusable(M, F, K)) return hipErrorInvalidValue;
+  if (const int64_t N1 = q4k_mix_columns(M, 2 * F, K); N1 > 0) {
+    qg::launch_swiglu_mix(W, ws, M, F, K, h, N1 / 2, stream);
+    return hipGetLastError();
+  }
   switch (pick_q4k(M, 2 * F, K)) {
     case Q4Pick::kLds128x256: qg::launch_swiglu<2, 2, 2, 4, 2, 2, 1>(W, ws, M, F, K, h, stream); break;
     case Q4Pick::kLds64x128: qg::launch_swiglu<1, 1, 2, 4, 2, 4, 1>(W, ws, M, F, K, h, stream); break;

@@ -275,7 +275,8 @@ def test_fusion_host_side():
     assert wsz(0, 4, 8, 300) == 0
     kn = qg.qgemm_kernel_name_swiglu
     assert kn(0, 512, 3584, 1024) == "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>"
-    assert kn(0, 512, 12288, 4096) == "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>"
+    assert kn(0, 512, 12288, 4096) == "gemm_q4k_swiglu_mix_kernel"   # 128x256 then 64x256 blocks
+    assert kn(0, 512, 9000, 4096) == "gemm_q4k_swiglu_kernel<1, 1, 2, 4, 2, 4, 1>"   # short second round
     assert kn(0, 8192, 12288, 4096) == "gemm_q4k_swiglu_kernel<2, 2, 2, 4, 2, 2, 1>"
     assert kn(0, 64, 512, 1024).startswith("gemm_q4k_small_kernel<")
     assert kn(0, 3, 1000, 256).startswith("skinny_kernel<0, 3,")

@@ -184,6 +184,7 @@ def check_swiglu(h_bits, W, fmt, x, F, rows, cols, what):
 
 # shapes selecting every kernel the SwiGLU entry points dispatch
 SW_SHAPES = [(qg.QG_Q4_K, 512, 3584, 1024),     # fused, 64x128 blocks
+             (qg.QG_Q4_K, 500, 10250, 768),     # fused, one round of 128x256 then 64x256 blocks (ragged)
              (qg.QG_Q4_K, 2100, 5000, 512),     # fused, 128x256 blocks (ragged M and F)
              (qg.QG_Q4_K, 200, 3000, 1024),     # fused, 64x128 blocks with two K-groups
              (qg.QG_Q4_K, 100, 2100, 2048),     # fused, 32x64 blocks with four K-groups
@@ -216,6 +217,7 @@ def test_gemm_swiglu_parity(fmt, M, F, K):
 
 
 @pytest.mark.parametrize("fmt,M,F,K", [(qg.QG_Q4_K, 512, 3584, 1024), (qg.QG_Q4_K, 2100, 5000, 512),
+                                       (qg.QG_Q4_K, 500, 10250, 768),
                                        (qg.QG_Q4_K, 200, 3000, 1024), (qg.QG_Q4_K, 100, 2100, 2048),
                                        (qg.QG_Q5_K, 512, 3584, 1024), (qg.QG_Q5_K, 200, 3000, 1024),
                                        (qg.QG_Q8_0, 512, 3584, 1024), (qg.QG_Q8_0, 300, 700, 768),
@@ -223,7 +225,7 @@ def test_gemm_swiglu_parity(fmt, M, F, K):
 def test_fused_equals_gemm_then_swiglu(fmt, M, F, K):
     """The fused kernel's h is bit-identical to the plain GEMM's fp32 output fed
     to the SwiGLU kernel."""
-    assert "_swiglu_kernel<" in qg.qgemm_kernel_name_swiglu(fmt, M, F, K)
+    assert "_swiglu_" in qg.qgemm_kernel_name_swiglu(fmt, M, F, K)
     W = synth.pack(fmt, synth.normal(1150 + F, (2 * F, K), 0.0, 0.02))
     x = synth.to_bf16_bits(synth.normal(1151 + M, (M, K)))
     h = gpu_swiglu(W, fmt, x, F)
@@ -266,7 +268,7 @@ def test_gemm_swiglu_workload_sampled(cfg, name):
     gm = next(g for g in synth.CONFIGS[cfg] if g.name == name)
     F = gm.N // 2
     W, x = synth.make_weights(gm), synth.make_acts(gm)
-    assert qg.qgemm_kernel_name_swiglu(gm.fmt, gm.M, F, gm.K).startswith("gemm_q4k_swiglu_kernel<")
+    assert qg.qgemm_kernel_name_swiglu(gm.fmt, gm.M, F, gm.K).startswith("gemm_q4k_swiglu_")
     h = gpu_swiglu(W, gm.fmt, x, F)
     rng = np.random.default_rng(1170 + cfg)
     rows = np.unique(np.concatenate([[0, gm.M - 1], rng.integers(0, gm.M, 12)]))
