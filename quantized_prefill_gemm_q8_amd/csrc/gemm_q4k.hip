@@ -955,7 +955,7 @@ int64_t q4k_mix_columns(int64_t M, int64_t N, int64_t K) {
 }
 
 // Kernel choice for a Q4_K problem (measured on the workloads' shapes):
-// prompts of 1024 rows or more with enough 128x256 tiles to cover every CU,
+// prompts of 512 rows or more with enough 128x256 tiles to cover every CU,
 // and whose rounds of them take less time than the rounds of 64x128 blocks,
 // take workgroups of 8 waves x 2x2 tiles; otherwise, with enough 64x128 blocks,
 // workgroups of 8 waves x one tile at 4 waves per SIMD (two workgroups per
@@ -979,14 +979,15 @@ Q4Pick pick_q4k(int64_t M, int64_t N, int64_t K) {
   // larger blocks does twice the work at about 1.19x the rate (2x2-tile waves
   // share their decoded weights and row scales): the larger blocks where
   // their rounds, times 2 / 1.19, are fewer than the 64x128 blocks' rounds.
-  // Measured: 1024x4096->16384 201 against 224 us, 1024x2048->32768 207
-  // against 224, 1536x4096->24576 477 against 491-511, 1536x2560->9728 119
-  // against 136; the other way 768x4096->24576 271 against 246,
-  // 1024x2560->9728 114 against 88, 4096x9728->2560 452 against ~300-350.
+  // Measured: 512x4096->32768 192 against 217 us, 512x2048->49152 159 against
+  // 170, 896x4096->24576 280 against 304, 1024x4096->16384 201 against 224,
+  // 1536x4096->24576 477 against 491-511, 1536x2560->9728 119 against 136; the
+  // other way 640x2048->32768 149 against 140, 768x4096->24576 271 against
+  // 246, 1024x2560->9728 114 against 88, 4096x9728->2560 452 against ~300-350.
   const int64_t blocks128x256 = ((M + 127) / 128) * ((N + 255) / 256);
   const int64_t rounds128 = (blocks128x256 + kCUs - 1) / kCUs;
   const int64_t rounds64 = (blocks64x128 + 2 * kCUs - 1) / (2 * kCUs);
-  if (M >= 1024 && blocks128x256 >= kCUs && 168 * rounds128 < 100 * rounds64) return Q4Pick::kLds128x256;
+  if (M >= 512 && blocks128x256 >= kCUs && 168 * rounds128 < 100 * rounds64) return Q4Pick::kLds128x256;
   if (blocks64x128 >= kCUs) return Q4Pick::kLds64x128;
   if (M >= 48 && blocks64x128 * 2 >= kCUs && nsb >= 4) return Q4Pick::kLds64x128K2;
   if (M >= 24 && ((M + 31) / 32) * ((N + 63) / 64) >= kCUs && nsb >= 8) return Q4Pick::kLds32x64K4;
