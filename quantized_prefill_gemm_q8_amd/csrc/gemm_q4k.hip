@@ -873,8 +873,9 @@ static void launch_lds(const uint8_t* W, const QgWorkspace& ws, int64_t M, int64
 // round at most; one workgroup of 8 waves per CU in either shape, so the
 // second round starts as the first ends.  Every output element still adds its
 // 32-value blocks in K order, so the result equals any other one-K-group
-// tile shape's bit for bit.  Measured at 512x4096->24576: the two shapes as
-// separate launches 141 us against 159 for the one-tile kernel.
+// tile shape's bit for bit.  Measured at 512x4096->24576: 139-144 us against
+// 151-166 for the one-tile kernel (three rounds of two 64x128 blocks per CU)
+// and 162-167 for 128x256 blocks alone (one and a half rounds).
 constexpr int q4k_ring_bytes(int BM, int BN) {  // two stages of the body's A, W, DX, DSP regions
   return 2 * 1024 * ((BM * 16 + 63) / 64 + (BN * (kQ4Bytes / 16) + 63) / 64 + (BM * 2 + 63) / 64 +
                      (BM * 3 + 63) / 64);
