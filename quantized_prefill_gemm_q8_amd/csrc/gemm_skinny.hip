@@ -80,7 +80,6 @@ struct SkRaw {
 
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 
-constexpr int kSkThreads = 256;
 constexpr int kSkMaxLds = 64 * 1024;
 enum { kXReg = 0, kXLds = 1, kXSlice = 2 };
 constexpr int kSlRows = 2;  // XSLICE: rows a wavefront carries through the slices at a time
@@ -116,6 +115,7 @@ __device__ __forceinline__ float group_sum_last(float v) {
 
 // FMT: QG_Q4_K / QG_Q5_K / QG_Q6_K / QG_Q8_0.  MR: activation rows.  R: rows per wavefront step
 // (16/nsb when that divides, else 1).  XM: where the activations are read.
+// TH: threads per workgroup (256, 512 or 1024; see skinny_threads).
 // CO (Q6_K only): coalesced loads.  A step's sixteen super-blocks are 3360
 // contiguous bytes; when every step starts 16-byte aligned and the matrix ends
 // on a 16-byte boundary, lane l loads the step's aligned chunks l, l+64, l+128
@@ -125,8 +125,8 @@ __device__ __forceinline__ float group_sum_last(float v) {
 // register buffers, as the field loads); kCoDma: global_load_lds_dwordx4 puts
 // them straight into two LDS buffers (no registers held; used for one or two
 // activation rows, where it measured fastest).
-template <int FMT, int MR, int R, int XM, int CO>
-__global__ __launch_bounds__(kSkThreads) void skinny_kernel(
+template <int FMT, int MR, int R, int XM, int CO, int TH>
+__global__ __launch_bounds__(TH) void skinny_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qx, const float* __restrict__ gdx,
     const float* __restrict__ gdS, int64_t N, int64_t K, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -134,12 +134,12 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
   constexpr bool KQ = FMT != QG_Q6_K;  // Q4_K, Q5_K, Q8_0: 64 values per lane, two per-32 blocks
   constexpr bool Q5 = FMT == QG_Q5_K, Q8 = FMT == QG_Q8_0;
   constexpr int NBUF = CO == kCoDma ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t rowbuf[CO ? kSkThreads / 64 : 1][NBUF][CO ? 4096 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t rowbuf[CO ? TH / 64 : 1][NBUF][CO ? 4096 : 16];
   constexpr int BB = FMT == QG_Q4_K ? kQ4Bytes : Q5 ? kQ5Bytes : Q8 ? 8 * kQ8Bytes : kQ6Bytes;
   constexpr int G = 64 / R;  // lanes per row within a step
   const int64_t nsb = K / 256, nb = K / 32;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kSkThreads / 64) +
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (TH / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // activation rows: codes at xs + m * xk, scales at xd / xS + m * xnb, for
@@ -153,9 +153,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
     float* ld = reinterpret_cast<float*>(smem + MR * K);
     float* lS = ld + MR * nb;
     const int64_t nq = MR * K / 16, nd = MR * nb / 4;
-    for (int64_t i = threadIdx.x; i < nq; i += kSkThreads)
+    for (int64_t i = threadIdx.x; i < nq; i += TH)
       reinterpret_cast<uint4*>(lq)[i] = reinterpret_cast<const uint4*>(qx)[i];
-    for (int64_t i = threadIdx.x; i < nd; i += kSkThreads) {
+    for (int64_t i = threadIdx.x; i < nd; i += TH) {
       reinterpret_cast<float4*>(ld)[i] = reinterpret_cast<const float4*>(gdx)[i];
       if (KQ) reinterpret_cast<float4*>(lS)[i] = reinterpret_cast<const float4*>(gdS)[i];
     }
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
 
   // wavefront w takes rows w*R + k*stride (+ 0..R-1), k = 0, 1, ...: at any
   // time the whole grid streams one narrow band of the weight matrix
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * (kSkThreads / 64) * R;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * (TH / 64) * R;
   const int64_t row_begin = wave * R;
   // (XSLICE: a wavefront without rows still stages slices and meets the barriers)
   if (XM != kXSlice && row_begin >= N) return;
@@ -494,12 +494,12 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(
         // slice it: super-blocks 16 it .. 16 it + 15 (fewer in the last) of
         // each activation row: codes [MR][4096], scales (and dS) [MR][128]
         const int64_t q0 = 4096 * it, qn = K - q0 < 4096 ? K - q0 : 4096;
-        for (int i = threadIdx.x; i < MR * 256; i += kSkThreads) {
+        for (int i = threadIdx.x; i < MR * 256; i += TH) {
           const int m = i >> 8, c16 = i & 255;
           if (16 * c16 < qn)
             reinterpret_cast<uint4*>(lq + m * 4096)[c16] = reinterpret_cast<const uint4*>(qx + m * K + q0)[c16];
         }
-        for (int i = threadIdx.x; i < MR * 32; i += kSkThreads) {
+        for (int i = threadIdx.x; i < MR * 32; i += TH) {
           const int m = i >> 5, c4 = i & 31;
           if (4 * c4 < qn / 32) {
             reinterpret_cast<float4*>(ld + m * 128)[c4] = reinterpret_cast<const float4*>(gdx + m * nb + q0 / 32)[c4];
@@ -578,6 +578,44 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t N, int64_t K) {
   return K <= 4096 ? kXReg : kXSlice;
 }
 
+// Launch shapes measured against the default of 256-thread workgroups (Q4_K
+// and Q6_K matrices of one row per wavefront step, cold weights; every shape
+// gives the same bits).  Where each workgroup stages long activation rows in
+// LDS, fewer and larger workgroups stage them fewer times and still hold 16
+// wavefronts per CU: one of 1024 threads per CU (12288->4096 Q6_K at M = 2 /
+// 3 / 4: 13.7 -> 12.3, 17.4 -> 13.2, 18.9 -> 14.2 us; 9728->2560 Q4_K at
+// M = 5 11.6 -> 10.6, M = 2-4 within 1%); two of 512 threads for rows of
+// K <= 4096 over many weight rows (2560->9728 Q4_K at M = 3-6: 2-3%) and
+// for 4096-value slices over a multiple of 4096 weight rows from six
+// activation rows (12288->4096 Q6_K at M = 6 / 7 / 8: 22.5 -> 21.8, 24.8 ->
+// 24.1, 27.2 -> 25.6 us; at M = 5 0.5-1.3% slower).
+// The same kinds of shapes elsewhere (4096->2560 Q6_K from three activation
+// rows, 3584->1024 Q4_K, 9728->2560 Q4_K in slices, 12288->4096 Q6_K at
+// M = 1 and in slices at M = 5) measured no faster or slower and keep the
+// default.
+enum class SkPlan { kDefault, k1024x1, k512x2, k256x2 };
+
+inline SkPlan skinny_plan(int fmt, int64_t M, int64_t N, int64_t K) {
+  if ((fmt != QG_Q4_K && fmt != QG_Q6_K) || skinny_rows_per_step(K) != 1) return SkPlan::kDefault;
+  const int xm = skinny_xmode(fmt, M, N, K);
+  if (xm == kXLds && K > 4096 && M >= 2 && N >= 2048) return SkPlan::k1024x1;
+  if (xm == kXLds && K <= 4096 && N >= 8192) return SkPlan::k512x2;
+  if (xm == kXSlice && N % 4096 == 0 && M >= 6) return SkPlan::k512x2;
+  // Q6_K rows of 4096 values over at most 16384 weight rows, one or two
+  // activation rows: field loads and two workgroups per CU, not the
+  // coalesced loads (4096->2560 at M = 1 / 2: 5.09 -> 4.49, 5.87 -> 4.88 us)
+  if (fmt == QG_Q6_K && xm == kXReg && M <= 2 && N <= 16384) return SkPlan::k256x2;
+  return SkPlan::kDefault;
+}
+
+inline int skinny_threads(int fmt, int64_t M, int64_t N, int64_t K) {
+  switch (skinny_plan(fmt, M, N, K)) {
+    case SkPlan::k1024x1: return 1024;
+    case SkPlan::k512x2: return 512;
+    default: return 256;
+  }
+}
+
 // Q6_K coalesced loads (CO) where every step starts on a 16-byte boundary
 // (several rows per step, or rows of a multiple of 8 super-blocks), the matrix
 // is a whole number of 16-byte chunks and the activations sit in registers
@@ -586,50 +624,61 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t N, int64_t K) {
 inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
   const int64_t nsb = K / 256;
   if (fmt != QG_Q6_K || !(skinny_rows_per_step(K) > 1 || nsb % 8 == 0) || (N * nsb) % 8 != 0 ||
-      skinny_xmode(fmt, M, N, K) != kXReg)
+      skinny_xmode(fmt, M, N, K) != kXReg || skinny_plan(fmt, M, N, K) == SkPlan::k256x2)
     return kCoNone;
   return M <= 2 ? kCoDma : kCoReg;
 }
 
-template <int FMT, int MR, int R, int CO>
+template <int FMT, int MR, int R, int CO, int TH>
 static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                    float* y, hipStream_t stream) {
   // The same number of workgroups on every CU, all resident at once, and the
   // row groups dealt to the wavefronts in turn, so that no wavefront takes
   // more than one row group more than another: a CU with one workgroup more
   // than the rest sets the end of the launch (the LM head ran 104 us with 827
-  // workgroups, 3 or 4 per CU, against 86 us with 768).  Three workgroups per
-  // CU for the coalesced Q6_K loads (32 KB of LDS row buffers each); two for
-  // rows of several steps with the activations staged in LDS when that deals
-  // every wavefront the same number of rows (12288->4096 Q6_K: two rows each,
-  // 11.8 -> 11.1 us; 9728->2560 Q4_K, uneven at two, runs 6.4 us there and
-  // 5.9 at four); four otherwise (the LM head 90 -> 86 us, 2560->9728 Q4_K
-  // 6.4 -> 5.7 us; one-step rows measured slower at two); never more than
-  // the LDS holds at once; fewer workgroups when there are fewer row groups
-  // than wavefronts.
-  constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024;
+  // workgroups, 3 or 4 per CU, against 86 us with 768).  For 256-thread
+  // workgroups: three per CU for the coalesced Q6_K loads (32 KB of LDS row
+  // buffers each); two for rows of several steps with the activations staged
+  // in LDS when that deals every wavefront the same number of rows
+  // (12288->4096 Q6_K: two rows each, 11.8 -> 11.1 us; 9728->2560 Q4_K,
+  // uneven at two, runs 6.4 us there and 5.9 at four); four otherwise (the LM
+  // head 90 -> 86 us, 2560->9728 Q4_K 6.4 -> 5.7 us; one-step rows measured
+  // slower at two); never more than the LDS holds at once; fewer workgroups
+  // when there are fewer row groups than wavefronts.  Other workgroup sizes
+  // and counts per skinny_plan.
+  constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024, WPG = TH / 64;
   const int64_t row_groups = (N + R - 1) / R;
   const int xm = skinny_xmode(FMT, MR, N, K);
   const bool xlds = xm == kXLds;
   const int64_t xbytes = xm == kXLds ? skinny_lds_bytes(FMT, MR, K) : xm == kXSlice ? skinny_lds_bytes(FMT, MR, 4096) : 0;
-  const int64_t lds = (CO == kCoNone ? 0 : 4 * (CO == kCoDma ? 2 : 1) * 4096) + xbytes;
-  int64_t per_cu = CO == kCoDma ? 3 : xlds && K > 4096 && row_groups % (4 * kCUs * 2) == 0 ? 2 : 4;
+  const int64_t lds = (CO == kCoNone ? 0 : WPG * (CO == kCoDma ? 2 : 1) * 4096) + xbytes;
+  int64_t per_cu;
+  switch (skinny_plan(FMT, MR, N, K)) {
+    case SkPlan::k1024x1: per_cu = 1; break;
+    case SkPlan::k512x2:
+    case SkPlan::k256x2: per_cu = 2; break;
+    default: per_cu = CO == kCoDma ? 3 : xlds && K > 4096 && row_groups % (WPG * kCUs * 2) == 0 ? 2 : 4;
+  }
   if (lds > 0 && per_cu > kLdsPerCU / lds) per_cu = kLdsPerCU / lds > 0 ? kLdsPerCU / lds : 1;
-  const int64_t wgs = row_groups < 4 * kCUs * per_cu ? (row_groups + 3) / 4 : kCUs * per_cu;
+  const int64_t wgs = row_groups < WPG * kCUs * per_cu ? (row_groups + WPG - 1) / WPG : kCUs * per_cu;
   const dim3 grid(static_cast<unsigned>(wgs));
+  // (skinny_plan takes 512 threads only with staged activations and 1024 only
+  // with whole rows in LDS; other combinations are not built)
   switch (xm) {
     case kXReg:
-      skinny_kernel<FMT, MR, R, kXReg, CO><<<grid, dim3(kSkThreads), 0, stream>>>(W, ws.q, ws.dx, ws.dS,
-                                                                                 N, K, y);
+      if constexpr (TH == 256)
+        skinny_kernel<FMT, MR, R, kXReg, CO, TH><<<grid, dim3(TH), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
+      else
+        return hipErrorInvalidValue;
       break;
     case kXLds:
-      skinny_kernel<FMT, MR, R, kXLds, CO>
-          <<<grid, dim3(kSkThreads), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
+      skinny_kernel<FMT, MR, R, kXLds, CO, TH>
+          <<<grid, dim3(TH), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
               W, ws.q, ws.dx, ws.dS, N, K, y);
       break;
     default:  // kXSlice: rows of K > 4096, one row per step, no coalesced loads
-      if constexpr (R == 1 && CO == kCoNone)
-        skinny_kernel<FMT, MR, R, kXSlice, CO><<<grid, dim3(kSkThreads), static_cast<size_t>(xbytes), stream>>>(
+      if constexpr (R == 1 && CO == kCoNone && TH <= 512)
+        skinny_kernel<FMT, MR, R, kXSlice, CO, TH><<<grid, dim3(TH), static_cast<size_t>(xbytes), stream>>>(
             W, ws.q, ws.dx, ws.dS, N, K, y);
       else
         return hipErrorInvalidValue;
@@ -637,17 +686,30 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
   return hipGetLastError();
 }
 
+template <int FMT, int MR, int R, int CO>
+static hipError_t launch_skinny_co(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
+                                   float* y, hipStream_t stream) {
+  if constexpr (R == 1 && CO == kCoNone && (FMT == QG_Q4_K || FMT == QG_Q6_K)) {
+    switch (skinny_threads(FMT, MR, N, K)) {
+      case 1024: return launch_skinny_rc<FMT, MR, R, CO, 1024>(W, ws, N, K, y, stream);
+      case 512: return launch_skinny_rc<FMT, MR, R, CO, 512>(W, ws, N, K, y, stream);
+      default: break;
+    }
+  }
+  return launch_skinny_rc<FMT, MR, R, CO, 256>(W, ws, N, K, y, stream);
+}
+
 template <int FMT, int MR, int R>
 static hipError_t launch_skinny_r(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                   float* y, hipStream_t stream) {
   if constexpr (FMT == QG_Q6_K) {
     switch (skinny_coalesced(FMT, MR, N, K)) {
-      case kCoDma: return launch_skinny_rc<FMT, MR, R, kCoDma>(W, ws, N, K, y, stream);
-      case kCoReg: return launch_skinny_rc<FMT, MR, R, kCoReg>(W, ws, N, K, y, stream);
+      case kCoDma: return launch_skinny_co<FMT, MR, R, kCoDma>(W, ws, N, K, y, stream);
+      case kCoReg: return launch_skinny_co<FMT, MR, R, kCoReg>(W, ws, N, K, y, stream);
       default: break;
     }
   }
-  return launch_skinny_rc<FMT, MR, R, kCoNone>(W, ws, N, K, y, stream);
+  return launch_skinny_co<FMT, MR, R, kCoNone>(W, ws, N, K, y, stream);
 }
 
 template <int FMT, int MR>
@@ -683,9 +745,9 @@ static hipError_t launch_skinny_fmt(const uint8_t* W, const QgWorkspace& ws, int
 const char* qg_gemm_skinny_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   thread_local char name[64];
   if (M < 1 || M > QG_SKINNY_MAX_M) return "?";
-  snprintf(name, sizeof name, "skinny_kernel<%d, %d, %d, %d, %d>", fmt, static_cast<int>(M),
+  snprintf(name, sizeof name, "skinny_kernel<%d, %d, %d, %d, %d, %d>", fmt, static_cast<int>(M),
            qg::skinny_rows_per_step(K), qg::skinny_xmode(fmt, M, N, K),
-           qg::skinny_coalesced(fmt, M, N, K));
+           qg::skinny_coalesced(fmt, M, N, K), qg::skinny_threads(fmt, M, N, K));
   return name;
 }
 

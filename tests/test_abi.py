@@ -126,27 +126,38 @@ def test_kernel_name_dispatch_rule():
     # skinny work split: rows per step R = 16 / (K/256) when that divides, else 1;
     # activations in registers (one or two rows of K <= 4096, short rows, many rows per
     # wavefront), else in LDS whole, else one 4096-value slice of K at a time
-    assert kn(Q6, 1, 152064, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
-    assert kn(Q4, 2, 100, 1024, AUTO) == "skinny_kernel<0, 2, 4, 0, 0>"
-    assert kn(Q4, 1, 100, 2560, AUTO) == "skinny_kernel<0, 1, 1, 0, 0>"
-    assert kn(Q6, 8, 100, 4352, AUTO) == "skinny_kernel<1, 8, 1, 1, 0>"
-    assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2, 0>"
+    assert kn(Q6, 1, 152064, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2, 256>"
+    assert kn(Q4, 2, 100, 1024, AUTO) == "skinny_kernel<0, 2, 4, 0, 0, 256>"
+    assert kn(Q4, 1, 100, 2560, AUTO) == "skinny_kernel<0, 1, 1, 0, 0, 256>"
+    assert kn(Q6, 8, 100, 4352, AUTO) == "skinny_kernel<1, 8, 1, 1, 0, 256>"
+    assert kn(Q4, 8, 100, 12288, SKINNY) == "skinny_kernel<0, 8, 1, 2, 0, 256>"
     # Q6_K coalesced loads (last parameter: 2 straight into LDS for M <= 2,
     # 1 through registers above, 0 field loads) need aligned steps (several
     # rows per step, or rows of a multiple of 8 super-blocks), a matrix of
     # whole 16-byte chunks and the activations in registers (K <= 4096)
-    assert kn(Q6, 1, 4096, 12288, AUTO) == "skinny_kernel<1, 1, 1, 1, 0>"
-    assert kn(Q6, 1, 77, 1024, AUTO) == "skinny_kernel<1, 1, 4, 0, 0>"    # 77*4 % 8 != 0
-    assert kn(Q6, 2, 78, 1024, AUTO) == "skinny_kernel<1, 2, 4, 0, 2>"
-    assert kn(Q6, 1, 80, 2560, AUTO) == "skinny_kernel<1, 1, 1, 0, 0>"    # 10 super-blocks a row
-    assert kn(Q6, 3, 81, 2048, AUTO) == "skinny_kernel<1, 3, 2, 0, 1>"
-    assert kn(Q6, 1, 80, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 2>"
-    assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1>"
+    assert kn(Q6, 1, 4096, 12288, AUTO) == "skinny_kernel<1, 1, 1, 1, 0, 256>"
+    assert kn(Q6, 1, 77, 1024, AUTO) == "skinny_kernel<1, 1, 4, 0, 0, 256>"    # 77*4 % 8 != 0
+    assert kn(Q6, 2, 78, 1024, AUTO) == "skinny_kernel<1, 2, 4, 0, 2, 256>"
+    assert kn(Q6, 1, 80, 2560, AUTO) == "skinny_kernel<1, 1, 1, 0, 0, 256>"    # 10 super-blocks a row
+    assert kn(Q6, 3, 81, 2048, AUTO) == "skinny_kernel<1, 3, 2, 0, 1, 256>"
+    assert kn(Q6, 1, 80, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 0, 256>"  # field loads at N <= 16384
+    assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1, 256>"
     # from three rows of K > 2048 the activations go to LDS unless each
     # wavefront takes many rows (N > 16384)
-    assert kn(Q6, 8, 2560, 4096, AUTO) == "skinny_kernel<1, 8, 1, 1, 0>"
-    assert kn(Q4, 4, 9728, 2560, AUTO) == "skinny_kernel<0, 4, 1, 1, 0>"
-    assert kn(Q4, 4, 24576, 4096, AUTO) == "skinny_kernel<0, 4, 1, 0, 0>"
+    assert kn(Q6, 8, 2560, 4096, AUTO) == "skinny_kernel<1, 8, 1, 1, 0, 256>"
+    assert kn(Q4, 4, 9728, 2560, AUTO) == "skinny_kernel<0, 4, 1, 1, 0, 512>"
+    assert kn(Q4, 4, 24576, 4096, AUTO) == "skinny_kernel<0, 4, 1, 0, 0, 256>"
+    # launch plans (last parameter: threads per workgroup) for Q4_K and Q6_K rows
+    # of one step or more: 1024 for whole rows of K > 4096 in LDS over at least
+    # 2048 weight rows, 512 for rows of K <= 4096 in LDS over at least 8192
+    # weight rows and for slices over a multiple of 4096 weight rows from M = 6
+    assert kn(Q6, 4, 4096, 12288, AUTO) == "skinny_kernel<1, 4, 1, 1, 0, 1024>"
+    assert kn(Q6, 8, 4096, 12288, AUTO) == "skinny_kernel<1, 8, 1, 2, 0, 512>"
+    assert kn(Q6, 5, 4096, 12288, AUTO) == "skinny_kernel<1, 5, 1, 2, 0, 256>"
+    assert kn(Q4, 5, 2560, 9728, AUTO) == "skinny_kernel<0, 5, 1, 1, 0, 1024>"
+    assert kn(Q6, 2, 1000, 12288, AUTO) == "skinny_kernel<1, 2, 1, 1, 0, 256>"
+    assert kn(Q4, 6, 2560, 9728, AUTO) == "skinny_kernel<0, 6, 1, 2, 0, 256>"
+    assert kn(qg.QG_Q5_K, 4, 2560, 9728, AUTO) == "skinny_kernel<2, 4, 1, 1, 0, 256>"
     # decode-sized batches on the small-grid kernel: four epilogue rows per
     # lane, about 1024 waves
     assert kn(Q4, 8, 24576, 4096, AUTO) == "gemm_q4k_small_kernel<2, 4>"
@@ -312,7 +323,7 @@ def test_q5k_host_side():
     assert kn(2, 8192, 24576, 4096) == "gemm_q5k_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
     assert kn(2, 512, 1024, 3584) == "gemm_q5k_lds_kernel<1, 1, 1, 2, 2, 2, 3>"
     assert kn(2, 64, 1024, 1024).startswith("gemm_q5k_small_kernel<")
-    assert kn(2, 1, 24576, 4096) == "skinny_kernel<2, 1, 1, 0, 0>"
+    assert kn(2, 1, 24576, 4096) == "skinny_kernel<2, 1, 1, 0, 0, 256>"
     assert kn(2, 4, 4096, 1024).startswith("skinny_kernel<2, 4,")
     assert kn(2, 5, 4096, 1024).startswith("gemm_q5k_small_kernel<")
     assert kn(2, 6, 2560, 9728).startswith("skinny_kernel<2, 6,")
@@ -338,7 +349,7 @@ def test_q80_host_side():
     assert kn(3, 8192, 24576, 4096) == "gemm_q80_lds_kernel<1, 1, 2, 4, 2, 2, 1>"
     assert kn(3, 512, 1024, 3584) == "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 3>"
     assert kn(3, 64, 1024, 512) == "gemm_q80_lds_kernel<1, 1, 1, 2, 2, 2, 1>"
-    assert kn(3, 1, 24576, 4096) == "skinny_kernel<3, 1, 1, 0, 0>"
+    assert kn(3, 1, 24576, 4096) == "skinny_kernel<3, 1, 1, 0, 0, 256>"
     assert kn(3, 8, 4096, 1024, qg.QG_PATH_SKINNY).startswith("skinny_kernel<3, 8,")
     assert qg.qgemm_kernel_name_swiglu(3, 512, 3584, 1024) == "gemm_q80_swiglu_kernel<1, 1, 2, 4, 2, 2, 1>"
     assert qg.qgemm_kernel_name_swiglu(3, 300, 700, 768) == "gemm_q80_swiglu_kernel<1, 1, 1, 2, 2, 2, 3>"

@@ -290,11 +290,45 @@ def test_skinny_slices_many_rows(fmt):
     wmax = max_abs_w(fmt, W, N, K)
     for M in (7, 8):
         name = qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)
-        assert name == f"skinny_kernel<{fmt}, {M}, 1, 2, 0>", name
+        assert name == f"skinny_kernel<{fmt}, {M}, 1, 2, 0, 256>", name
         x = synth.to_bf16_bits(synth.normal(661 + M, (M, K)))
         ref = oracle.gemm(fmt, W, x, N)
         check(gpu_prefill(W, fmt, x, N, qg.QG_PATH_SKINNY), ref, bound(x, np.arange(M), wmax),
               f"skinny slices M={M} N={N} K={K} {name}")
+
+
+# (fmt, K, N, {M: threads per workgroup}): every launch plan of the skinny
+# kernel, over weight-row counts that leave some wavefronts a row more than
+# others (or, at 8192, none)
+SKINNY_PLANS = [
+    (qg.QG_Q6_K, 12288, 4100, {2: 1024, 4: 1024, 5: 256}),  # rows in LDS; slices, N % 4096 != 0
+    (qg.QG_Q4_K, 9728, 2050, {2: 1024, 5: 1024, 6: 256}),
+    (qg.QG_Q6_K, 8448, 8192, {6: 1024, 8: 512}),            # rows in LDS; slices over 2 x 4096 rows
+    (qg.QG_Q4_K, 2560, 8197, {1: 256, 3: 512, 6: 512}),     # registers; rows of K <= 4096 in LDS
+    (qg.QG_Q6_K, 4096, 2561, {1: 256, 2: 256, 3: 256}),     # field loads (no coalesced loads); LDS
+]
+
+
+@pytest.mark.parametrize("fmt,K,N,plans", SKINNY_PLANS,
+                         ids=[f"{FMT_ID[f]}-{k}to{n}" for f, k, n, _ in SKINNY_PLANS])
+def test_skinny_launch_plans(fmt, K, N, plans):
+    """The skinny kernel in each workgroup size and count it launches with
+    (1024 threads, one workgroup per CU; 512 threads, two; 256 threads, two
+    or more) against the oracle on sampled weight rows that include the last
+    ones, which the wavefronts with one row more than the rest compute."""
+    W = synth.pack(fmt, synth.normal(700 + K + N, (N, K), 0.0, 0.02))
+    wmax = max_abs_w(fmt, W, N, K)
+    rng = np.random.default_rng(K * N)
+    cols = np.unique(np.concatenate([[0, N - 1], np.arange(N - 40, N), rng.integers(0, N, 40)]))
+    for M, th in plans.items():
+        name = qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)
+        assert name.endswith(f", {th}>"), name
+        if fmt == qg.QG_Q6_K and K == 4096 and M <= 2:
+            assert name == f"skinny_kernel<1, {M}, 1, 0, 0, 256>", name  # field loads
+        x = synth.to_bf16_bits(synth.normal(701 + M, (M, K)))
+        y = gpu_prefill(W, fmt, x, N, qg.QG_PATH_SKINNY)
+        ref = oracle.gemm(fmt, W, x, N, cols=cols)
+        check(y[:, cols], ref, bound(x, np.arange(M), wmax), f"skinny plan M={M} N={N} K={K} {name}")
 
 
 @pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q5_K], ids=FMT_ID.get)
