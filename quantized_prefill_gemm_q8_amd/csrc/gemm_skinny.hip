@@ -629,6 +629,23 @@ inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
   return M <= 2 ? kCoDma : kCoReg;
 }
 
+// Workgroups of a skinny kernel that one CU holds at once (its registers and
+// static LDS; the caller counts the activation rows in dynamic LDS), from the
+// runtime's occupancy calculator, once per kernel.
+template <int FMT, int MR, int R, int XM, int CO, int TH>
+static int64_t skinny_resident() {
+  static const int64_t n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, skinny_kernel<FMT, MR, R, XM, CO, TH>, TH, 0) !=
+            hipSuccess || b < 1) {
+      (void)hipGetLastError();  // unknown: no limit from it
+      return int64_t{1} << 20;
+    }
+    return static_cast<int64_t>(b);
+  }();
+  return n;
+}
+
 template <int FMT, int MR, int R, int CO, int TH>
 static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                    float* y, hipStream_t stream) {
@@ -644,8 +661,11 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
   // uneven at two, runs 6.4 us there and 5.9 at four); four otherwise (the LM
   // head 90 -> 86 us, 2560->9728 Q4_K 6.4 -> 5.7 us; one-step rows measured
   // slower at two); never more than the LDS holds at once; fewer workgroups
-  // when there are fewer row groups than wavefronts.  Other workgroup sizes
-  // and counts per skinny_plan.
+  // when there are fewer row groups than wavefronts, and never more than the
+  // CU holds at once by its registers: the workgroups past that run as a
+  // second, partial round (the LM head at M = 3 / 4, 130 and 154 VGPRs, three
+  // 256-thread workgroups per CU: 126.6 -> 107.2 and 128.8 -> 112.1 us
+  // against four).  Other workgroup sizes and counts per skinny_plan.
   constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024, WPG = TH / 64;
   const int64_t row_groups = (N + R - 1) / R;
   const int xm = skinny_xmode(FMT, MR, N, K);
@@ -660,26 +680,30 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
     default: per_cu = CO == kCoDma ? 3 : xlds && K > 4096 && row_groups % (WPG * kCUs * 2) == 0 ? 2 : 4;
   }
   if (lds > 0 && per_cu > kLdsPerCU / lds) per_cu = kLdsPerCU / lds > 0 ? kLdsPerCU / lds : 1;
-  const int64_t wgs = row_groups < WPG * kCUs * per_cu ? (row_groups + WPG - 1) / WPG : kCUs * per_cu;
-  const dim3 grid(static_cast<unsigned>(wgs));
+  auto grid = [&](int64_t resident) {
+    const int64_t pc = per_cu < resident ? per_cu : resident;
+    return dim3(static_cast<unsigned>(row_groups < WPG * kCUs * pc ? (row_groups + WPG - 1) / WPG : kCUs * pc));
+  };
   // (skinny_plan takes 512 threads only with staged activations and 1024 only
   // with whole rows in LDS; other combinations are not built)
   switch (xm) {
     case kXReg:
       if constexpr (TH == 256)
-        skinny_kernel<FMT, MR, R, kXReg, CO, TH><<<grid, dim3(TH), 0, stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
+        skinny_kernel<FMT, MR, R, kXReg, CO, TH><<<grid(skinny_resident<FMT, MR, R, kXReg, CO, TH>()), dim3(TH), 0,
+                                                   stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
       else
         return hipErrorInvalidValue;
       break;
     case kXLds:
       skinny_kernel<FMT, MR, R, kXLds, CO, TH>
-          <<<grid, dim3(TH), static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(
-              W, ws.q, ws.dx, ws.dS, N, K, y);
+          <<<grid(skinny_resident<FMT, MR, R, kXLds, CO, TH>()), dim3(TH),
+             static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
       break;
     default:  // kXSlice: rows of K > 4096, one row per step, no coalesced loads
       if constexpr (R == 1 && CO == kCoNone && TH <= 512)
-        skinny_kernel<FMT, MR, R, kXSlice, CO, TH><<<grid, dim3(TH), static_cast<size_t>(xbytes), stream>>>(
-            W, ws.q, ws.dx, ws.dS, N, K, y);
+        skinny_kernel<FMT, MR, R, kXSlice, CO, TH><<<grid(skinny_resident<FMT, MR, R, kXSlice, CO, TH>()), dim3(TH),
+                                                     static_cast<size_t>(xbytes), stream>>>(W, ws.q, ws.dx, ws.dS,
+                                                                                              N, K, y);
       else
         return hipErrorInvalidValue;
   }
