@@ -331,6 +331,27 @@ def test_skinny_launch_plans(fmt, K, N, plans):
         check(y[:, cols], ref, bound(x, np.arange(M), wmax), f"skinny plan M={M} N={N} K={K} {name}")
 
 
+def test_lm_head_decode_batches():
+    """The LM head's full shape (4096 -> 152064 Q6_K) at M = 3, 4 and 6, between
+    the workload's M = 1 and 8: the register-staged skinny kernel, whose
+    workgroups per CU are capped at what a CU holds (three, three and two),
+    on sampled weight rows that include the last ones."""
+    g = synth.CONFIGS[5][1]
+    assert g.M == 8 and g.N == 152064, g
+    W = synth.make_weights(g)
+    x8 = synth.make_acts(g)
+    wmax = max_abs_w(g.fmt, W, g.N, g.K)
+    rng = np.random.default_rng(g.w_seed + 3)
+    cols = np.unique(np.concatenate([[0, g.N - 1], np.arange(g.N - 64, g.N), rng.integers(0, g.N, 96)]))
+    for M in (3, 4, 6):
+        x = np.ascontiguousarray(x8[:M])
+        name = qg.qgemm_kernel_name(g.fmt, M, g.N, g.K)
+        assert name == f"skinny_kernel<1, {M}, 1, 0, 1, 256>", name
+        y = gpu_prefill(W, g.fmt, x, g.N)
+        ref = oracle.gemm(g.fmt, W, x, g.N, cols=cols)
+        check(y[:, cols], ref, bound(x, np.arange(M), wmax), f"lm head M={M} {name}")
+
+
 @pytest.mark.parametrize("fmt", [qg.QG_Q4_K, qg.QG_Q5_K], ids=FMT_ID.get)
 @pytest.mark.parametrize("N,K", [(700, 256), (16400, 1024), (300, 1024), (300, 2816)])
 def test_small_grid_decode_rows(fmt, N, K):
