@@ -593,7 +593,7 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t N, int64_t K) {
 // rows, 3584->1024 Q4_K, 9728->2560 Q4_K in slices, 12288->4096 Q6_K at
 // M = 1 and in slices at M = 5) measured no faster or slower and keep the
 // default.
-enum class SkPlan { kDefault, k1024x1, k512x2, k256x2 };
+enum class SkPlan { kDefault, k1024x1, k512x2, k512x1, k256x2 };
 
 inline SkPlan skinny_plan(int fmt, int64_t M, int64_t N, int64_t K) {
   if ((fmt != QG_Q4_K && fmt != QG_Q6_K) || skinny_rows_per_step(K) != 1) return SkPlan::kDefault;
@@ -605,13 +605,19 @@ inline SkPlan skinny_plan(int fmt, int64_t M, int64_t N, int64_t K) {
   // activation rows: field loads and two workgroups per CU, not the
   // coalesced loads (4096->2560 at M = 1 / 2: 5.09 -> 4.49, 5.87 -> 4.88 us)
   if (fmt == QG_Q6_K && xm == kXReg && M <= 2 && N <= 16384) return SkPlan::k256x2;
+  // Q6_K rows of 4096 values over more than 16384 weight rows (the LM head)
+  // from five activation rows, coalesced loads through registers: one
+  // 512-thread workgroup per CU (M = 8 175.6 -> 164.6 and 177.1 -> 165.2 us,
+  // M = 5 / 6 1-2.5%, M = 7 within 1%)
+  if (fmt == QG_Q6_K && xm == kXReg && M >= 5 && N > 16384) return SkPlan::k512x1;
   return SkPlan::kDefault;
 }
 
 inline int skinny_threads(int fmt, int64_t M, int64_t N, int64_t K) {
   switch (skinny_plan(fmt, M, N, K)) {
     case SkPlan::k1024x1: return 1024;
-    case SkPlan::k512x2: return 512;
+    case SkPlan::k512x2:
+    case SkPlan::k512x1: return 512;
     default: return 256;
   }
 }
@@ -674,7 +680,8 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
   const int64_t lds = (CO == kCoNone ? 0 : WPG * (CO == kCoDma ? 2 : 1) * 4096) + xbytes;
   int64_t per_cu;
   switch (skinny_plan(FMT, MR, N, K)) {
-    case SkPlan::k1024x1: per_cu = 1; break;
+    case SkPlan::k1024x1:
+    case SkPlan::k512x1: per_cu = 1; break;
     case SkPlan::k512x2:
     case SkPlan::k256x2: per_cu = 2; break;
     default: per_cu = CO == kCoDma ? 3 : xlds && K > 4096 && row_groups % (WPG * kCUs * 2) == 0 ? 2 : 4;
@@ -684,20 +691,24 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
     const int64_t pc = per_cu < resident ? per_cu : resident;
     return dim3(static_cast<unsigned>(row_groups < WPG * kCUs * pc ? (row_groups + WPG - 1) / WPG : kCUs * pc));
   };
-  // (skinny_plan takes 512 threads only with staged activations and 1024 only
-  // with whole rows in LDS; other combinations are not built)
+  // (skinny_plan takes 1024 threads only with whole rows in LDS, 512 with
+  // staged activations or, for Q6_K, with coalesced loads through registers;
+  // other combinations are not built)
   switch (xm) {
     case kXReg:
-      if constexpr (TH == 256)
+      if constexpr (TH == 256 || (TH == 512 && CO == kCoReg))
         skinny_kernel<FMT, MR, R, kXReg, CO, TH><<<grid(skinny_resident<FMT, MR, R, kXReg, CO, TH>()), dim3(TH), 0,
                                                    stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
       else
         return hipErrorInvalidValue;
       break;
     case kXLds:
-      skinny_kernel<FMT, MR, R, kXLds, CO, TH>
-          <<<grid(skinny_resident<FMT, MR, R, kXLds, CO, TH>()), dim3(TH),
-             static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
+      if constexpr (TH == 256 || CO == kCoNone)
+        skinny_kernel<FMT, MR, R, kXLds, CO, TH>
+            <<<grid(skinny_resident<FMT, MR, R, kXLds, CO, TH>()), dim3(TH),
+               static_cast<size_t>(skinny_lds_bytes(FMT, MR, K)), stream>>>(W, ws.q, ws.dx, ws.dS, N, K, y);
+      else
+        return hipErrorInvalidValue;
       break;
     default:  // kXSlice: rows of K > 4096, one row per step, no coalesced loads
       if constexpr (R == 1 && CO == kCoNone && TH <= 512)
@@ -713,11 +724,13 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
 template <int FMT, int MR, int R, int CO>
 static hipError_t launch_skinny_co(const uint8_t* W, const QgWorkspace& ws, int64_t N, int64_t K,
                                    float* y, hipStream_t stream) {
-  if constexpr (R == 1 && CO == kCoNone && (FMT == QG_Q4_K || FMT == QG_Q6_K)) {
-    switch (skinny_threads(FMT, MR, N, K)) {
-      case 1024: return launch_skinny_rc<FMT, MR, R, CO, 1024>(W, ws, N, K, y, stream);
-      case 512: return launch_skinny_rc<FMT, MR, R, CO, 512>(W, ws, N, K, y, stream);
-      default: break;
+  if constexpr (R == 1 && (FMT == QG_Q4_K || FMT == QG_Q6_K)) {
+    const int th = skinny_threads(FMT, MR, N, K);
+    if constexpr (CO == kCoNone) {
+      if (th == 1024) return launch_skinny_rc<FMT, MR, R, CO, 1024>(W, ws, N, K, y, stream);
+      if (th == 512) return launch_skinny_rc<FMT, MR, R, CO, 512>(W, ws, N, K, y, stream);
+    } else if constexpr (CO == kCoReg) {
+      if (th == 512) return launch_skinny_rc<FMT, MR, R, CO, 512>(W, ws, N, K, y, stream);
     }
   }
   return launch_skinny_rc<FMT, MR, R, CO, 256>(W, ws, N, K, y, stream);

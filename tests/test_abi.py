@@ -141,7 +141,9 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 1, 80, 2560, AUTO) == "skinny_kernel<1, 1, 1, 0, 0, 256>"    # 10 super-blocks a row
     assert kn(Q6, 3, 81, 2048, AUTO) == "skinny_kernel<1, 3, 2, 0, 1, 256>"
     assert kn(Q6, 1, 80, 4096, AUTO) == "skinny_kernel<1, 1, 1, 0, 0, 256>"  # field loads at N <= 16384
-    assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1, 256>"
+    assert kn(Q6, 8, 152064, 4096, AUTO) == "skinny_kernel<1, 8, 1, 0, 1, 512>"  # from M = 5: 512 threads
+    assert kn(Q6, 5, 152064, 4096, AUTO) == "skinny_kernel<1, 5, 1, 0, 1, 512>"
+    assert kn(Q6, 4, 152064, 4096, AUTO) == "skinny_kernel<1, 4, 1, 0, 1, 256>"
     # from three rows of K > 2048 the activations go to LDS unless each
     # wavefront takes many rows (N > 16384)
     assert kn(Q6, 8, 2560, 4096, AUTO) == "skinny_kernel<1, 8, 1, 1, 0, 256>"

@@ -333,9 +333,10 @@ def test_skinny_launch_plans(fmt, K, N, plans):
 
 def test_lm_head_decode_batches():
     """The LM head's full shape (4096 -> 152064 Q6_K) at M = 3, 4 and 6, between
-    the workload's M = 1 and 8: the register-staged skinny kernel, whose
-    workgroups per CU are capped at what a CU holds (three, three and two),
-    on sampled weight rows that include the last ones."""
+    the workload's M = 1 and 8: the register-staged skinny kernel in 256-thread
+    workgroups capped at what a CU holds (three per CU at M = 3 and 4) and in
+    one 512-thread workgroup per CU (M = 6), on sampled weight rows that
+    include the last ones."""
     g = synth.CONFIGS[5][1]
     assert g.M == 8 and g.N == 152064, g
     W = synth.make_weights(g)
@@ -346,7 +347,7 @@ def test_lm_head_decode_batches():
     for M in (3, 4, 6):
         x = np.ascontiguousarray(x8[:M])
         name = qg.qgemm_kernel_name(g.fmt, M, g.N, g.K)
-        assert name == f"skinny_kernel<1, {M}, 1, 0, 1, 256>", name
+        assert name == f"skinny_kernel<1, {M}, 1, 0, 1, {512 if M >= 5 else 256}>", name
         y = gpu_prefill(W, g.fmt, x, g.N)
         ref = oracle.gemm(g.fmt, W, x, g.N, cols=cols)
         check(y[:, cols], ref, bound(x, np.arange(M), wmax), f"lm head M={M} {name}")
