@@ -595,21 +595,31 @@ inline int skinny_xmode(int fmt, int64_t M, int64_t N, int64_t K) {
 // default.
 enum class SkPlan { kDefault, k1024x1, k512x2, k512x1, k256x2 };
 
+// Q6_K steps that start on 16-byte boundaries (several rows per step, or rows
+// of a multiple of 8 super-blocks) in a matrix of whole 16-byte chunks: where
+// the coalesced loads can run
+inline bool skinny_aligned(int fmt, int64_t N, int64_t K) {
+  const int64_t nsb = K / 256;
+  return fmt == QG_Q6_K && (skinny_rows_per_step(K) > 1 || nsb % 8 == 0) && (N * nsb) % 8 == 0;
+}
+
 inline SkPlan skinny_plan(int fmt, int64_t M, int64_t N, int64_t K) {
   if ((fmt != QG_Q4_K && fmt != QG_Q6_K) || skinny_rows_per_step(K) != 1) return SkPlan::kDefault;
   const int xm = skinny_xmode(fmt, M, N, K);
   if (xm == kXLds && K > 4096 && M >= 2 && N >= 2048) return SkPlan::k1024x1;
   if (xm == kXLds && K <= 4096 && N >= 8192) return SkPlan::k512x2;
   if (xm == kXSlice && N % 4096 == 0 && M >= 6) return SkPlan::k512x2;
-  // Q6_K rows of 4096 values over at most 16384 weight rows, one or two
-  // activation rows: field loads and two workgroups per CU, not the
-  // coalesced loads (4096->2560 at M = 1 / 2: 5.09 -> 4.49, 5.87 -> 4.88 us)
+  // Q6_K rows with the activations in registers over at most 16384 weight
+  // rows, one or two activation rows: field loads and two workgroups per CU,
+  // not the coalesced loads (4096->2560 at M = 1 / 2: 5.09 -> 4.49, 5.87 ->
+  // 4.88 us)
   if (fmt == QG_Q6_K && xm == kXReg && M <= 2 && N <= 16384) return SkPlan::k256x2;
-  // Q6_K rows of 4096 values over more than 16384 weight rows (the LM head)
-  // from five activation rows, coalesced loads through registers: one
-  // 512-thread workgroup per CU (M = 8 175.6 -> 164.6 and 177.1 -> 165.2 us,
-  // M = 5 / 6 1-2.5%, M = 7 within 1%)
-  if (fmt == QG_Q6_K && xm == kXReg && M >= 5 && N > 16384) return SkPlan::k512x1;
+  // Q6_K rows with the activations in registers over more than 16384 weight
+  // rows (the LM head) from five activation rows, with the coalesced loads
+  // through registers: one 512-thread workgroup per CU (4096->152064 at
+  // M = 8 175.6 -> 164.6 and 177.1 -> 165.2 us, M = 5 / 6 1-2.5%, M = 7
+  // within 1%)
+  if (xm == kXReg && M >= 5 && N > 16384 && skinny_aligned(fmt, N, K)) return SkPlan::k512x1;
   return SkPlan::kDefault;
 }
 
@@ -622,15 +632,12 @@ inline int skinny_threads(int fmt, int64_t M, int64_t N, int64_t K) {
   }
 }
 
-// Q6_K coalesced loads (CO) where every step starts on a 16-byte boundary
-// (several rows per step, or rows of a multiple of 8 super-blocks), the matrix
-// is a whole number of 16-byte chunks and the activations sit in registers
-// (with them in LDS or L2, measured slower): straight into LDS for up to two
-// activation rows, through registers above
+// Q6_K coalesced loads (CO) where the steps are aligned (skinny_aligned) and
+// the activations sit in registers (with them in LDS or L2, measured slower):
+// straight into LDS for up to two activation rows, through registers above
 inline int skinny_coalesced(int fmt, int64_t M, int64_t N, int64_t K) {
-  const int64_t nsb = K / 256;
-  if (fmt != QG_Q6_K || !(skinny_rows_per_step(K) > 1 || nsb % 8 == 0) || (N * nsb) % 8 != 0 ||
-      skinny_xmode(fmt, M, N, K) != kXReg || skinny_plan(fmt, M, N, K) == SkPlan::k256x2)
+  if (!skinny_aligned(fmt, N, K) || skinny_xmode(fmt, M, N, K) != kXReg ||
+      skinny_plan(fmt, M, N, K) == SkPlan::k256x2)
     return kCoNone;
   return M <= 2 ? kCoDma : kCoReg;
 }
@@ -670,7 +677,7 @@ static hipError_t launch_skinny_rc(const uint8_t* W, const QgWorkspace& ws, int6
   // when there are fewer row groups than wavefronts, and never more than the
   // CU holds at once by its registers: the workgroups past that run as a
   // second, partial round (the LM head at M = 3 / 4, 130 and 154 VGPRs, three
-  // 256-thread workgroups per CU: 126.6 -> 107.2 and 128.8 -> 112.1 us
+  // 256-thread workgroups per CU: 124.9 -> 105.6 and 128.9 -> 112.8 us
   // against four).  Other workgroup sizes and counts per skinny_plan.
   constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024, WPG = TH / 64;
   const int64_t row_groups = (N + R - 1) / R;

@@ -160,6 +160,8 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 2, 1000, 12288, AUTO) == "skinny_kernel<1, 2, 1, 1, 0, 256>"
     assert kn(Q4, 6, 2560, 9728, AUTO) == "skinny_kernel<0, 6, 1, 2, 0, 256>"
     assert kn(qg.QG_Q5_K, 4, 2560, 9728, AUTO) == "skinny_kernel<2, 4, 1, 1, 0, 256>"
+    assert kn(Q6, 5, 151936, 2560, AUTO) == "skinny_kernel<1, 5, 1, 0, 0, 256>"  # unaligned: field loads
+    assert kn(Q6, 5, 16400, 4096, AUTO) == "skinny_kernel<1, 5, 1, 0, 1, 512>"
     # decode-sized batches on the small-grid kernel: four epilogue rows per
     # lane, about 1024 waves
     assert kn(Q4, 8, 24576, 4096, AUTO) == "gemm_q4k_small_kernel<2, 4>"
@@ -412,3 +414,34 @@ def test_noalloc_rejects_before_any_launch():
     # 4096 x 4096 needs 26 MB of workspace: more than the static 16 MiB
     assert qg.qgemm_workspace_bytes(4096, 4096) > qg.QG_NOALLOC_SCRATCH_BYTES
     assert f(A, 0, A, 1, 4096, 256, 4096, A, None) == qg.QG_ENOSCRATCH
+
+
+def test_skinny_plans_are_built():
+    """Every skinny kernel the dispatch names is one the library builds: 512
+    threads with the activations staged in LDS or slices (no coalesced loads),
+    or for Q6_K with the coalesced loads through registers; 1024 threads with
+    whole rows in LDS; both only for Q4_K and Q6_K rows of one step or more."""
+    Ks = [256, 512, 1024, 2048, 2560, 3072, 3584, 4096, 4352, 6144, 8192, 9728, 12288]
+    Ns = [77, 80, 1000, 2048, 2560, 4096, 8192, 9728, 16384, 16400, 24576, 151936, 152064]
+    seen = set()
+    for fmt in (qg.QG_Q4_K, qg.QG_Q6_K, qg.QG_Q5_K, qg.QG_Q8_0):
+        for M in range(1, qg.QG_SKINNY_MAX_M + 1):
+            for K in Ks:
+                for N in Ns:
+                    name = qg.qgemm_kernel_name(fmt, M, N, K, qg.QG_PATH_SKINNY)
+                    f, m, r, xm, co, th = (int(v) for v in name[len("skinny_kernel<"):-1].split(","))
+                    assert (f, m) == (fmt, M), name
+                    assert r == (16 // (K // 256) if K // 256 in (1, 2, 4, 8) else 1), name
+                    if xm == 2:
+                        assert r == 1 and co == 0, name
+                    if co != 0:
+                        assert fmt == qg.QG_Q6_K and xm == 0, name
+                    if th == 512:
+                        assert fmt in (qg.QG_Q4_K, qg.QG_Q6_K) and r == 1, name
+                        assert (xm in (1, 2) and co == 0) or (xm == 0 and co == 1), name
+                    elif th == 1024:
+                        assert fmt in (qg.QG_Q4_K, qg.QG_Q6_K) and r == 1 and xm == 1 and co == 0, name
+                    else:
+                        assert th == 256, name
+                    seen.add(th)
+    assert seen == {256, 512, 1024}, seen

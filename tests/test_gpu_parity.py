@@ -306,6 +306,8 @@ SKINNY_PLANS = [
     (qg.QG_Q6_K, 8448, 8192, {6: 1024, 8: 512}),            # rows in LDS; slices over 2 x 4096 rows
     (qg.QG_Q4_K, 2560, 8197, {1: 256, 3: 512, 6: 512}),     # registers; rows of K <= 4096 in LDS
     (qg.QG_Q6_K, 4096, 2561, {1: 256, 2: 256, 3: 256}),     # field loads (no coalesced loads); LDS
+    (qg.QG_Q6_K, 4096, 16400, {5: 512, 8: 512}),            # coalesced loads through registers, 512
+    (qg.QG_Q6_K, 2560, 20000, {5: 256, 8: 256}),            # unaligned steps: field loads, 256
 ]
 
 
