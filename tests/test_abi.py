@@ -160,6 +160,8 @@ def test_kernel_name_dispatch_rule():
     assert kn(Q6, 2, 1000, 12288, AUTO) == "skinny_kernel<1, 2, 1, 1, 0, 256>"
     assert kn(Q4, 6, 2560, 9728, AUTO) == "skinny_kernel<0, 6, 1, 2, 0, 256>"
     assert kn(qg.QG_Q5_K, 4, 2560, 9728, AUTO) == "skinny_kernel<2, 4, 1, 1, 0, 256>"
+    assert kn(qg.QG_Q5_K, 4, 9728, 2560, AUTO) == "skinny_kernel<2, 4, 1, 1, 0, 512>"
+    assert kn(qg.QG_Q8_0, 8, 9728, 2560, AUTO) == "skinny_kernel<3, 8, 1, 1, 0, 512>"
     assert kn(Q6, 5, 151936, 2560, AUTO) == "skinny_kernel<1, 5, 1, 0, 0, 256>"  # unaligned: field loads
     assert kn(Q6, 5, 16400, 4096, AUTO) == "skinny_kernel<1, 5, 1, 0, 1, 512>"
     # decode-sized batches on the small-grid kernel: four epilogue rows per
@@ -418,9 +420,10 @@ def test_noalloc_rejects_before_any_launch():
 
 def test_skinny_plans_are_built():
     """Every skinny kernel the dispatch names is one the library builds: 512
-    threads with the activations staged in LDS or slices (no coalesced loads),
-    or for Q6_K with the coalesced loads through registers; 1024 threads with
-    whole rows in LDS; both only for Q4_K and Q6_K rows of one step or more."""
+    threads with the activations staged in LDS (any format) or in slices (Q4_K,
+    Q6_K), without coalesced loads, or for Q6_K with the coalesced loads through
+    registers; 1024 threads with whole rows in LDS (Q4_K, Q6_K); both only for
+    rows of one step or more."""
     Ks = [256, 512, 1024, 2048, 2560, 3072, 3584, 4096, 4352, 6144, 8192, 9728, 12288]
     Ns = [77, 80, 1000, 2048, 2560, 4096, 8192, 9728, 16384, 16400, 24576, 151936, 152064]
     seen = set()
@@ -437,8 +440,9 @@ def test_skinny_plans_are_built():
                     if co != 0:
                         assert fmt == qg.QG_Q6_K and xm == 0, name
                     if th == 512:
-                        assert fmt in (qg.QG_Q4_K, qg.QG_Q6_K) and r == 1, name
-                        assert (xm in (1, 2) and co == 0) or (xm == 0 and co == 1), name
+                        assert r == 1, name
+                        assert ((xm in (1, 2) and co == 0 and (xm == 1 or fmt in (qg.QG_Q4_K, qg.QG_Q6_K)))
+                                or (xm == 0 and co == 1)), name
                     elif th == 1024:
                         assert fmt in (qg.QG_Q4_K, qg.QG_Q6_K) and r == 1 and xm == 1 and co == 0, name
                     else:
